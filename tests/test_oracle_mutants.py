@@ -1,0 +1,88 @@
+"""The pins catch plausible mistakes: each mutant below plants one mistake in a
+copy of the oracle's C source (built into a temporary directory; the real
+oracle is untouched) and at least one pin of test_oracle_pins must fail on it.
+"""
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import test_oracle_pins as pins
+from oracle import _SRC, CFLAGS, _bind
+
+# (name, original text, planted mistake)
+MUTANTS = [
+    ("beta swapped in m", "float mi = beta1 * *m + omb1 * g;", "float mi = beta2 * *m + omb1 * g;"),
+    ("g not squared in v", "float vi = beta2 * *v + omb2 * (g * g);", "float vi = beta2 * *v + omb2 * g;"),
+    ("eps inside sqrt", "return mi / (sqrtf(vi * rbc2) + eps);", "return mi / sqrtf(vi * rbc2 + eps);"),
+    ("no bias correction of m", "out[0] = (float)((double)lr / (1.0 - b1t));", "out[0] = lr;"),
+    ("no bias correction of v", "out[1] = (float)(1.0 / (1.0 - b2t));", "out[1] = 1.0f;"),
+    ("t off by one", "double b1t = pow_by_squaring((double)beta1, t);",
+     "double b1t = pow_by_squaring((double)beta1, t + 1);"),
+    ("wrong bit in powering", "if (t & 1) r = r * b;", "if (t & 2) r = r * b;"),
+    ("decay dropped (mixed)", "float w = master[i] * decay - step_size * u;", "float w = master[i] - step_size * u;"),
+    ("decay is 1-wd", "out[2] = (float)(1.0 - (double)lr * (double)wd);", "out[2] = (float)(1.0 - (double)wd);"),
+    ("update sign (mixed)", "float w = master[i] * decay - step_size * u;", "float w = master[i] * decay + step_size * u;"),
+    ("no unscale (mixed)", ": oracle_bf16_to_f32(g16[i])) * inv_scale;", ": oracle_bf16_to_f32(g16[i]));"),
+    ("Kahan compensation sign", "c[i] = oracle_f32_to_bf16(sum - absorbed);", "c[i] = oracle_f32_to_bf16(sum + absorbed);"),
+    ("Kahan compensation dropped", "float sum = oracle_bf16_to_f32(c[i]) + d;", "float sum = d;"),
+    ("Kahan decay dropped", "float d = -(lrwd * pf) - step_size * u;", "float d = -step_size * u;"),
+    ("Kahan m/v stores swapped", "m[i] = oracle_f32_to_bf16(mi);", "m[i] = oracle_f32_to_bf16(vi);"),
+    ("bf16 ties away from zero", "if (drop > 0x8000u || (drop == 0x8000u && (keep & 1u))) keep += 1u;",
+     "if (drop >= 0x8000u) keep += 1u;"),
+    ("bf16 truncation", "if (drop > 0x8000u || (drop == 0x8000u && (keep & 1u))) keep += 1u;", ";"),
+    ("f16 subnormal boundary", "int q_exp = (e < -14) ? -24 : e - 10;", "int q_exp = (e < -15) ? -24 : e - 10;"),
+    ("f16 overflow threshold", "if (a >= 65520.0)", "if (a >= 65504.0)"),
+    ("f16 widen exponent bias", "mag = ldexpf((float)(1024 + f), e - 25);", "mag = ldexpf((float)(1024 + f), e - 24);"),
+    ("NaN not detected (f16)", "if ((g[i] & 0x7c00u) == 0x7c00u) return 1;",
+     "if ((g[i] & 0x7fffu) == 0x7c00u) return 1;"),
+    ("f16 ties", "if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) == 1.0)) r += 1.0;",
+     "if (frac >= 0.5) r += 1.0;"),
+]
+
+# fastest first; each entry is (pin, extra args)
+PINS = [
+    (pins.test_scalars_match_library_pow, ()),
+    (pins.test_step1_closed_form, (1e-8,)),
+    (pins.test_step1_closed_form, (1e-3,)),
+    (pins.test_step1_decay_only_from_nonzero_weight, ()),
+    (pins.test_f16_scaled_equals_bf16_unscaled, ()),
+    (pins.test_kahan_step1_agrees_with_mixed, ()),
+    (pins.test_constant_gradient_closed_form, ()),
+    (pins.test_beta_zero_is_decayed_sign_sgd, ()),
+    (pins.test_skip_on_nonfinite_f16, (0x7C01,)),
+    (pins.test_skip_on_nonfinite_f16, (0x7C00,)),
+    (pins.test_bf16_widen_exhaustive, ()),
+    (pins.test_f16_widen_exhaustive, ()),
+    (pins.test_bf16_narrow_vs_torch, ()),
+    (pins.test_f16_narrow_vs_numpy, ()),
+    (pins.test_kahan_tracks_constant_tiny_updates, ()),
+    (pins.test_zero_gradient_kahan_tracks_decay, ()),
+]
+
+
+@pytest.fixture(scope="module")
+def tmpdir_mut():
+    with tempfile.TemporaryDirectory() as d:
+        yield d
+
+
+@pytest.mark.parametrize("name,orig,bad", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_killed(tmpdir_mut, name, orig, bad):
+    src = open(_SRC).read()
+    assert src.count(orig) >= 1, f"mutation site for {name!r} not found"
+    mutated = src.replace(orig, bad, 1)
+    tag = "".join(ch if ch.isalnum() else "_" for ch in name)
+    csrc = os.path.join(tmpdir_mut, f"{tag}.c")
+    so = os.path.join(tmpdir_mut, f"lib{tag}.so")
+    open(csrc, "w").write(mutated)
+    subprocess.run(["gcc", *CFLAGS, "-o", so, csrc, "-lm"], check=True)
+    lib = _bind(ctypes.CDLL(so))
+    for pin, args in PINS:
+        try:
+            pin(lib, *args)
+        except AssertionError:
+            return  # killed
+    pytest.fail(f"mutant {name!r} survived every pin")
