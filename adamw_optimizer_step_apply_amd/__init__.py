@@ -1,0 +1,207 @@
+"""Python binding of the MI355X fused AdamW step (``libadamw_amd.so``).
+
+Argument marshalling only: every step of the optimizer runs in the library's
+HIP kernels.  The functions carry the names of the C ABI in ``include/adamw.h``
+and accept torch tensors (their ``data_ptr()`` is passed) or raw integer device
+addresses.  PyTorch supplies device memory and streams; with ``stream=None`` the
+work goes on ``torch.cuda.current_stream()``.
+
+There is no fallback: if the shared library has not been built the import
+fails, and every non-OK status raises :class:`AdamWError`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Sequence
+
+import torch  # loads the HIP runtime the library then binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libadamw_amd.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m adamw_optimizer_step_apply_amd.build` "
+                      "(or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# enums of adamw.h
+OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_HIP = 0, 1, 2, 3, 4
+F32, BF16, F16 = 0, 1, 2
+MIXED, PURE_KAHAN = 0, 1
+STREAM_PARAM, STREAM_GRAD, STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_AUX = range(5)
+NUM_STREAMS = 5
+_STATUS = {0: "ADAMW_OK", 1: "ADAMW_E_INVALID", 2: "ADAMW_E_UNSUPPORTED", 3: "ADAMW_E_NOMEM", 4: "ADAMW_E_HIP"}
+
+EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_check_finite", "adamw_last_error",
+            "adamw_release_workspace", "adamw_abi_version", "adamw_plan_inspect", "adamw_set_chunk_elems")
+
+
+class adamw_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("inv_loss_scale", ctypes.c_float)]
+
+
+class adamw_tensor_list(ctypes.Structure):
+    _fields_ = [("n_tensors", ctypes.c_int64), ("numel", ctypes.POINTER(ctypes.c_int64)),
+                ("ptr", ctypes.POINTER(ctypes.c_void_p) * NUM_STREAMS),
+                ("shard_begin", ctypes.c_int64), ("shard_end", ctypes.c_int64), ("flat_mask", ctypes.c_uint32)]
+
+
+_vp = ctypes.c_void_p
+_lib.adamw_step.restype = ctypes.c_int
+_lib.adamw_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp,
+                            ctypes.POINTER(adamw_hparams), _vp, _vp, _vp]
+_lib.adamw_multi_tensor_step.restype = ctypes.c_int
+_lib.adamw_multi_tensor_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list),
+                                         ctypes.POINTER(adamw_hparams), _vp, _vp, _vp]
+_lib.adamw_check_finite.restype = ctypes.c_int
+_lib.adamw_check_finite.argtypes = [ctypes.c_int, ctypes.POINTER(adamw_tensor_list), _vp, _vp]
+_lib.adamw_last_error.restype = ctypes.c_char_p
+_lib.adamw_last_error.argtypes = []
+_lib.adamw_release_workspace.restype = None
+_lib.adamw_release_workspace.argtypes = []
+_lib.adamw_abi_version.restype = ctypes.c_int
+_lib.adamw_abi_version.argtypes = []
+_lib.adamw_plan_inspect.restype = ctypes.c_int64
+_lib.adamw_plan_inspect.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list), ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
+_lib.adamw_set_chunk_elems.restype = ctypes.c_int64
+_lib.adamw_set_chunk_elems.argtypes = [ctypes.c_int64]
+
+
+class AdamWError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+@dataclass
+class HParams:
+    """AdamW hyper-parameters (fp32 in the library).  Defaults: the opt-1.3b
+    recipe of "[pure bf16 training] w/ AnyPrecisionAdamW and Kahan summation"
+    (lr 0.0002, betas 0.9/0.95, weight decay 0.1) and eps 1e-8."""
+    lr: float = 2e-4
+    beta1: float = 0.9
+    beta2: float = 0.95
+    eps: float = 1e-8
+    weight_decay: float = 0.1
+    inv_loss_scale: float = 1.0
+
+    def c(self) -> adamw_hparams:
+        return adamw_hparams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, self.inv_loss_scale)
+
+
+def _addr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int):
+    if status != OK:
+        raise AdamWError(status, (_lib.adamw_last_error() or b"").decode())
+
+
+def _hp(hp) -> adamw_hparams:
+    if isinstance(hp, adamw_hparams):
+        return hp
+    if hp is None:
+        hp = HParams()
+    return hp.c()
+
+
+class TensorList:
+    """Marshals a tensor list into an ``adamw_tensor_list`` and keeps the ctypes
+    arrays alive.  ``streams`` is a sequence of 5 sequences (param, grad,
+    exp_avg, exp_avg_sq, aux) of tensors or addresses; a stream flagged in
+    ``flat_mask`` holds one flat shard buffer; ``None`` leaves a stream unset."""
+
+    def __init__(self, numels: Sequence[int], streams, shard_begin: int = 0, shard_end: int = -1,
+                 flat_mask: int = 0):
+        n = len(numels)
+        self._numel = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in numels])
+        self._arrays = []
+        s = adamw_tensor_list()
+        s.n_tensors = n
+        s.numel = ctypes.cast(self._numel, ctypes.POINTER(ctypes.c_int64))
+        for k in range(NUM_STREAMS):
+            items = streams[k] if k < len(streams) else None
+            if items is None:
+                s.ptr[k] = ctypes.POINTER(ctypes.c_void_p)()
+                continue
+            arr = (ctypes.c_void_p * max(len(items), 1))(*[_addr(x) for x in items])
+            self._arrays.append(arr)
+            s.ptr[k] = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        s.shard_begin = int(shard_begin)
+        s.shard_end = int(shard_end)
+        s.flat_mask = int(flat_mask)
+        self.c = s
+        self.numels = [int(x) for x in numels]
+
+
+def adamw_step(mode: int, p_dtype: int, n: int, param, grad, exp_avg, exp_avg_sq, aux, hp, d_step,
+               d_found_inf=None, stream=None) -> None:
+    """One AdamW step over one contiguous range of ``n`` elements (C ABI adamw_step)."""
+    h = _hp(hp)
+    _check(_lib.adamw_step(mode, p_dtype, int(n), _addr(param), _addr(grad), _addr(exp_avg), _addr(exp_avg_sq),
+                           _addr(aux), ctypes.byref(h), _addr(d_step), _addr(d_found_inf), _stream(stream)))
+
+
+def adamw_multi_tensor_step(mode: int, p_dtype: int, tensors: TensorList, hp, d_step, d_found_inf=None,
+                            stream=None) -> None:
+    """One AdamW step over a tensor list or its ZeRO shard (C ABI adamw_multi_tensor_step)."""
+    h = _hp(hp)
+    _check(_lib.adamw_multi_tensor_step(mode, p_dtype, ctypes.byref(tensors.c), ctypes.byref(h), _addr(d_step),
+                                        _addr(d_found_inf), _stream(stream)))
+
+
+def adamw_check_finite(g_dtype: int, grads: TensorList, d_found_inf, stream=None) -> None:
+    """Zero ``d_found_inf``, then set it to 1 if any gradient is inf/NaN (C ABI adamw_check_finite)."""
+    _check(_lib.adamw_check_finite(g_dtype, ctypes.byref(grads.c), _addr(d_found_inf), _stream(stream)))
+
+
+def adamw_last_error() -> str:
+    return (_lib.adamw_last_error() or b"").decode()
+
+
+def adamw_release_workspace() -> None:
+    _lib.adamw_release_workspace()
+
+
+def adamw_abi_version() -> int:
+    return _lib.adamw_abi_version()
+
+
+def adamw_plan_inspect(mode: int, p_dtype: int, tensors: TensorList, for_check: bool = False):
+    """The chunk plan as a list of (tensor, offset_in_tensor, count, is_vector, flat_pos, segment)."""
+    n = _lib.adamw_plan_inspect(mode, p_dtype, ctypes.byref(tensors.c), int(for_check), None, 0)
+    if n < 0:
+        raise AdamWError(E_INVALID, adamw_last_error())
+    buf = (ctypes.c_int64 * (6 * max(n, 1)))()
+    n2 = _lib.adamw_plan_inspect(mode, p_dtype, ctypes.byref(tensors.c), int(for_check), buf, n)
+    assert n2 == n
+    return [tuple(buf[6 * i:6 * i + 6]) for i in range(n)]
+
+
+def adamw_set_chunk_elems(elems: int) -> int:
+    r = _lib.adamw_set_chunk_elems(int(elems))
+    if r < 0:
+        raise AdamWError(E_INVALID, f"chunk size {elems} rejected")
+    return r
+
+
+def library_path() -> str:
+    return LIB_PATH

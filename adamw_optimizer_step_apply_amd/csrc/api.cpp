@@ -1,0 +1,345 @@
+// api.cpp -- the C ABI declared in include/adamw.h: validation, plan caching,
+// per-(device, stream) workspace, and the launch sequence
+//   [check: zero flag -> check kernel]   (adamw_check_finite)
+//   [step:  prologue  -> update kernel]  (adamw_step / adamw_multi_tensor_step)
+// Nothing here synchronises with the device except when a workspace has to
+// grow (the old buffer may still be read by work queued on its stream).
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "adamw.h"
+#include "layout.hpp"
+#include "plan.hpp"
+
+namespace adamw {
+
+hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32_t* d_found_inf,
+                           LaunchScalars* d_scalars, hipStream_t stream);
+hipError_t launch_update(adamw_mode mode, adamw_dtype p_dtype, const DevSeg* segs, const DevChunk* chunks,
+                         int64_t n_chunks, const LaunchScalars* d_scalars, hipStream_t stream);
+hipError_t launch_check(adamw_dtype g_dtype, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
+                        int32_t* d_flag, hipStream_t stream);
+
+namespace {
+
+thread_local std::string g_err;
+
+adamw_status fail(adamw_status st, const std::string& msg)
+{
+    g_err = msg;
+    return st;
+}
+
+adamw_status hip_fail(const char* what, hipError_t e)
+{
+    g_err = std::string(what) + ": " + hipGetErrorString(e);
+    return ADAMW_E_HIP;
+}
+
+// A device-resident copy of one plan (segment table followed by chunk table),
+// uploaded through a pinned staging buffer.
+struct PlanSlot {
+    void* dev = nullptr;
+    size_t dev_cap = 0;
+    void* host = nullptr;
+    size_t host_cap = 0;
+    hipEvent_t uploaded = nullptr;
+    bool upload_in_flight = false;
+    std::vector<int64_t> key;
+    bool valid = false;
+    int64_t n_segs = 0, n_chunks = 0;
+
+    const DevSeg* segs() const { return static_cast<const DevSeg*>(dev); }
+    const DevChunk* chunks() const
+    {
+        return reinterpret_cast<const DevChunk*>(static_cast<const char*>(dev) + n_segs * sizeof(DevSeg));
+    }
+
+    void release()
+    {
+        if (dev) (void)hipFree(dev);
+        if (host) (void)hipHostFree(host);
+        if (uploaded) (void)hipEventDestroy(uploaded);
+        dev = host = nullptr;
+        uploaded = nullptr;
+        dev_cap = host_cap = 0;
+        valid = false;
+        key.clear();
+    }
+};
+
+struct StreamWorkspace {
+    LaunchScalars* scalars = nullptr;   // device, kScalarsBytes
+    PlanSlot step, check;
+    std::mutex mu;                      // one call at a time per stream
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, uintptr_t>, std::unique_ptr<StreamWorkspace>> g_ws;
+int64_t g_chunk_elems = kDefaultChunkElems;
+
+adamw_status get_workspace(hipStream_t stream, StreamWorkspace** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto& ws = g_ws[{dev, (uintptr_t)stream}];
+    if (!ws) ws.reset(new StreamWorkspace());
+    *out = ws.get();
+    return ADAMW_OK;
+}
+
+// Makes `slot` hold the plan of (mode, dtype, list, for_check), re-planning and
+// uploading only if any input differs from the cached one.
+adamw_status ensure_plan(PlanSlot& slot, adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
+                         bool for_check, int64_t chunk_elems, hipStream_t stream)
+{
+    std::vector<int64_t> key;
+    plan_key(mode, p_dtype, list, for_check, chunk_elems, key);
+    if (slot.valid && key == slot.key) return ADAMW_OK;
+
+    Plan plan;
+    std::string err;
+    adamw_status st = build_plan(mode, p_dtype, list, for_check, chunk_elems, &plan, err);
+    if (st != ADAMW_OK) return fail(st, err);
+
+    const size_t seg_bytes = plan.segs.size() * sizeof(DevSeg);
+    const size_t bytes = seg_bytes + plan.chunks.size() * sizeof(DevChunk);
+    hipError_t e;
+    if (!slot.uploaded) {
+        e = hipEventCreateWithFlags(&slot.uploaded, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail("hipEventCreate", e);
+    }
+    // the staging buffer may still feed the previous upload
+    if (slot.upload_in_flight) {
+        e = hipEventSynchronize(slot.uploaded);
+        if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
+        slot.upload_in_flight = false;
+    }
+    if (bytes > slot.host_cap) {
+        if (slot.host) (void)hipHostFree(slot.host);
+        slot.host = nullptr;
+        size_t cap = bytes + bytes / 4 + 4096;
+        e = hipHostMalloc(&slot.host, cap, hipHostMallocDefault);
+        if (e != hipSuccess) { slot.host_cap = 0; slot.valid = false; return fail(ADAMW_E_NOMEM, "hipHostMalloc failed"); }
+        slot.host_cap = cap;
+    }
+    if (bytes > slot.dev_cap) {
+        if (slot.dev) {
+            // queued kernels on this stream may still read the old table
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail("hipStreamSynchronize", e);
+            (void)hipFree(slot.dev);
+            slot.dev = nullptr;
+        }
+        size_t cap = bytes + bytes / 4 + 4096;
+        e = hipMalloc(&slot.dev, cap);
+        if (e != hipSuccess) { slot.dev_cap = 0; slot.valid = false; return fail(ADAMW_E_NOMEM, "hipMalloc of the chunk table failed"); }
+        slot.dev_cap = cap;
+    }
+    if (bytes) {
+        memcpy(slot.host, plan.segs.data(), seg_bytes);
+        memcpy(static_cast<char*>(slot.host) + seg_bytes, plan.chunks.data(), plan.chunks.size() * sizeof(DevChunk));
+        e = hipMemcpyAsync(slot.dev, slot.host, bytes, hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) { slot.valid = false; return hip_fail("hipMemcpyAsync (chunk table)", e); }
+        e = hipEventRecord(slot.uploaded, stream);
+        if (e != hipSuccess) { slot.valid = false; return hip_fail("hipEventRecord", e); }
+        slot.upload_in_flight = true;
+    }
+    slot.n_segs = (int64_t)plan.segs.size();
+    slot.n_chunks = (int64_t)plan.chunks.size();
+    slot.key.swap(key);
+    slot.valid = true;
+    return ADAMW_OK;
+}
+
+adamw_status check_hparams(const adamw_hparams* hp)
+{
+    if (!hp) return fail(ADAMW_E_INVALID, "hparams is null");
+    const float v[6] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->inv_loss_scale};
+    for (float x : v)
+        if (!std::isfinite(x)) return fail(ADAMW_E_INVALID, "hyper-parameters must be finite");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(ADAMW_E_INVALID, "beta1 and beta2 must lie in [0, 1)");
+    if (hp->eps < 0.0f) return fail(ADAMW_E_INVALID, "eps < 0");
+    if (hp->lr < 0.0f) return fail(ADAMW_E_INVALID, "lr < 0");
+    if (hp->weight_decay < 0.0f) return fail(ADAMW_E_INVALID, "weight_decay < 0");
+    if (!(hp->inv_loss_scale > 0.0f)) return fail(ADAMW_E_INVALID, "inv_loss_scale must be > 0");
+    return ADAMW_OK;
+}
+
+adamw_status basic_list_check(const adamw_tensor_list* list)
+{
+    if (!list) return fail(ADAMW_E_INVALID, "tensor list is null");
+    if (list->n_tensors < 0) return fail(ADAMW_E_INVALID, "n_tensors < 0");
+    if (list->n_tensors > 0 && !list->numel) return fail(ADAMW_E_INVALID, "numel array is null");
+    return ADAMW_OK;
+}
+
+adamw_status do_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, const adamw_hparams* hp,
+                     int32_t* d_step, const int32_t* d_found_inf, void* hip_stream)
+{
+    g_err.clear();
+    std::string err;
+    adamw_status st = check_mode(mode, p_dtype, false, err);
+    if (st != ADAMW_OK) return fail(st, err);
+    if ((st = check_hparams(hp)) != ADAMW_OK) return st;
+    if (!d_step) return fail(ADAMW_E_INVALID, "d_step is null");
+    if ((uintptr_t)d_step % 4 || (uintptr_t)d_found_inf % 4)
+        return fail(ADAMW_E_INVALID, "d_step / d_found_inf must be 4-byte aligned");
+    if ((st = basic_list_check(list)) != ADAMW_OK) return st;
+
+    // the whole list is validated before the first HIP call
+    const int64_t chunk_elems = g_chunk_elems;
+    st = build_plan(mode, p_dtype, list, false, chunk_elems, nullptr, err);
+    if (st != ADAMW_OK) return fail(st, err);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    StreamWorkspace* ws = nullptr;
+    if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
+    std::lock_guard<std::mutex> lk(ws->mu);
+    hipError_t e;
+    if (!ws->scalars) {
+        e = hipMalloc(reinterpret_cast<void**>(&ws->scalars), kScalarsBytes);
+        if (e != hipSuccess) { ws->scalars = nullptr; return fail(ADAMW_E_NOMEM, "hipMalloc of the scalar block failed"); }
+    }
+    if ((st = ensure_plan(ws->step, mode, p_dtype, list, false, chunk_elems, stream)) != ADAMW_OK) return st;
+    e = launch_prologue(*hp, d_step, d_found_inf, ws->scalars, stream);
+    if (e != hipSuccess) return hip_fail("prologue launch", e);
+    e = launch_update(mode, p_dtype, ws->step.segs(), ws->step.chunks(), ws->step.n_chunks, ws->scalars, stream);
+    if (e != hipSuccess) return hip_fail("update launch", e);
+    return ADAMW_OK;
+}
+
+}  // namespace
+}  // namespace adamw
+
+using namespace adamw;
+
+extern "C" {
+
+adamw_status adamw_multi_tensor_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
+                                     const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
+                                     void* hip_stream)
+{
+    return do_step(mode, p_dtype, list, hp, d_step, d_found_inf, hip_stream);
+}
+
+adamw_status adamw_step(adamw_mode mode, adamw_dtype p_dtype, int64_t n, void* param, const void* grad,
+                        void* exp_avg, void* exp_avg_sq, void* aux, const adamw_hparams* hp, int32_t* d_step,
+                        const int32_t* d_found_inf, void* hip_stream)
+{
+    g_err.clear();
+    if (n < 0) return fail(ADAMW_E_INVALID, "n < 0");
+    void* p0 = param;
+    void* p1 = const_cast<void*>(grad);
+    void* p2 = exp_avg;
+    void* p3 = exp_avg_sq;
+    void* p4 = aux;
+    void* const a0[1] = {p0};
+    void* const a1[1] = {p1};
+    void* const a2[1] = {p2};
+    void* const a3[1] = {p3};
+    void* const a4[1] = {p4};
+    const int64_t numel[1] = {n};
+    adamw_tensor_list list;
+    list.n_tensors = 1;
+    list.numel = numel;
+    list.ptr[0] = a0;
+    list.ptr[1] = a1;
+    list.ptr[2] = a2;
+    list.ptr[3] = a3;
+    list.ptr[4] = a4;
+    list.shard_begin = 0;
+    list.shard_end = -1;
+    list.flat_mask = 0;
+    if (n > 0 && (!param || !grad || !exp_avg || !exp_avg_sq || !aux))
+        return fail(ADAMW_E_INVALID, "a required buffer pointer is null");
+    return do_step(mode, p_dtype, &list, hp, d_step, d_found_inf, hip_stream);
+}
+
+adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* grads, int32_t* d_found_inf,
+                                void* hip_stream)
+{
+    g_err.clear();
+    std::string err;
+    adamw_status st = check_mode(ADAMW_MIXED, g_dtype, true, err);
+    if (st != ADAMW_OK) return fail(st, err);
+    if (!d_found_inf || (uintptr_t)d_found_inf % 4) return fail(ADAMW_E_INVALID, "d_found_inf is null or misaligned");
+    if ((st = basic_list_check(grads)) != ADAMW_OK) return st;
+    const int64_t chunk_elems = g_chunk_elems;
+    st = build_plan(ADAMW_MIXED, g_dtype, grads, true, chunk_elems, nullptr, err);
+    if (st != ADAMW_OK) return fail(st, err);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    StreamWorkspace* ws = nullptr;
+    if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
+    std::lock_guard<std::mutex> lk(ws->mu);
+    if ((st = ensure_plan(ws->check, ADAMW_MIXED, g_dtype, grads, true, chunk_elems, stream)) != ADAMW_OK)
+        return st;
+    hipError_t e = launch_check(g_dtype, ws->check.segs(), ws->check.chunks(), ws->check.n_chunks, d_found_inf, stream);
+    if (e != hipSuccess) return hip_fail("check launch", e);
+    return ADAMW_OK;
+}
+
+const char* adamw_last_error(void) { return g_err.c_str(); }
+
+void adamw_release_workspace(void)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto& kv : g_ws) {
+        StreamWorkspace* ws = kv.second.get();
+        if (ws->scalars) (void)hipFree(ws->scalars);
+        ws->scalars = nullptr;
+        ws->step.release();
+        ws->check.release();
+    }
+    g_ws.clear();
+}
+
+int adamw_abi_version(void) { return ADAMW_ABI_VERSION; }
+
+int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, int for_check,
+                           int64_t* out, int64_t cap)
+{
+    g_err.clear();
+    Plan plan;
+    std::string err;
+    adamw_status st = build_plan(mode, p_dtype, list, for_check != 0, g_chunk_elems, &plan, err);
+    if (st != ADAMW_OK) {
+        g_err = err;
+        return -1;
+    }
+    const int64_t n = (int64_t)plan.chunks.size();
+    for (int64_t i = 0; i < n && i < cap && out; ++i) {
+        const DevChunk& c = plan.chunks[(size_t)i];
+        const SegInfo& si = plan.info[c.seg];
+        int64_t* r = out + 6 * i;
+        r[0] = si.tensor;
+        r[1] = si.tensor_off + (int64_t)c.off;
+        r[2] = (int64_t)(c.n_kind & kCountMask);
+        r[3] = (c.n_kind & kVecBit) ? 1 : 0;
+        r[4] = si.flat + (int64_t)c.off;
+        r[5] = (int64_t)c.seg;
+    }
+    return n;
+}
+
+int64_t adamw_set_chunk_elems(int64_t elems)
+{
+    if (elems == 0) elems = kDefaultChunkElems;
+    if (elems < 2048 || elems > (INT64_C(1) << 22) || elems % 2048) return -1;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_chunk_elems = elems;
+    return elems;
+}
+
+}  // extern "C"

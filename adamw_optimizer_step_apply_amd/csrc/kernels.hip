@@ -1,0 +1,427 @@
+// kernels.hip -- gfx950 (CDNA4) kernels of the fused AdamW step.
+//
+// The step is a pure stream: every element is read once and written once, with
+// no reuse, so there is nothing to stage in LDS and no contraction for the
+// matrix cores.  The kernels are shaped for HBM: every lane moves whole 16-byte
+// words (8 elements of a 16-bit stream, 4 of an fp32 stream), consecutive lanes
+// touch consecutive words, and each lane keeps two packs of loads in flight
+// before it computes.  The math is fp32 in registers.
+//
+// Kernels:
+//   prologue_kernel      one lane: reads the skip flag and the step counter,
+//                        forms the step's scalars in binary64, advances the counter
+//   update_kernel<MODE>  one workgroup per chunk: the AdamW element update
+//   zero_flag_kernel /
+//   check_kernel<F16>    the fp16-AMP overflow test (any inf/NaN gradient)
+//
+// Element rule (the AdamW of Loshchilov & Hutter, Algorithm 2, with Adam's bias
+// correction from Kingma & Ba, Algorithm 1; named on the pages "Distributed
+// optimizer support for BERT", Usage, and "[pure bf16 training] w/
+// AnyPrecisionAdamW and Kahan summation", the opt-1.3b command):
+//   m = b1*m + (1-b1)*g ; v = b2*v + (1-b2)*(g*g) ; u = m / (sqrt(v*rbc2) + eps)
+//   mixed: w = w*decay - step_size*u, p = round16(w)
+//   Kahan: d = -(lrwd*p) - step_size*u ; s = c + d ; p' = rbf16(p + s) ; c = rbf16(s - (p' - p))
+// Each operation is one binary32 operation in that order; the library is
+// compiled with -ffp-contract=off so no multiply-add is fused, sqrt and
+// division are the correctly rounded ones, and fp32 subnormals are kept.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "adamw.h"
+#include "layout.hpp"
+
+namespace adamw {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Device addresses taken from the segment table are plain integers; casting them
+// to the global address space lets the compiler emit global_load/global_store
+// (rather than flat accesses, which also test the LDS aperture).
+#define GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ GLOBAL T* gptr(uint64_t addr, uint64_t elem_off)
+{
+    return reinterpret_cast<GLOBAL T*>(addr) + elem_off;
+}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// 16-bit <-> fp32.  A 32-bit word holds two 16-bit elements, the lower-addressed
+// one in the low half.
+// ---------------------------------------------------------------------------
+
+template <bool F16>
+__device__ __forceinline__ f32x2 widen2(uint32_t w)
+{
+    if constexpr (F16) {
+        return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);   // v_cvt_f32_f16 (exact)
+    } else {
+        f32x2 r;
+        r.x = __uint_as_float(w << 16);            // bf16 is the top half of an fp32
+        r.y = __uint_as_float(w & 0xffff0000u);
+        return r;
+    }
+}
+
+// Round two fp32 values to nearest-even 16-bit and pack them (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32 under the default round-to-nearest-even mode).
+template <bool F16>
+__device__ __forceinline__ uint32_t narrow2(float lo, float hi)
+{
+    f32x2 x = {lo, hi};
+    if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+template <bool F16>
+__device__ __forceinline__ float widen1(uint16_t h)
+{
+    if constexpr (F16) return (float)__builtin_bit_cast(_Float16, h);
+    else return __uint_as_float((uint32_t)h << 16);
+}
+
+template <bool F16>
+__device__ __forceinline__ uint16_t narrow1(float x)
+{
+    if constexpr (F16) return __builtin_bit_cast(uint16_t, (_Float16)x);
+    else return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// ---------------------------------------------------------------------------
+// Element math
+// ---------------------------------------------------------------------------
+
+struct Coef {
+    float step_size, rbc2, decay, lrwd, omb1, omb2, beta1, beta2, eps, inv_scale;
+};
+
+// Moments and the bias-corrected Adam direction u = m_hat / (sqrt(v_hat) + eps),
+// with 1/(1-b1^t) carried by step_size.
+__device__ __forceinline__ float adam_dir(float g, float& m, float& v, const Coef& c)
+{
+    m = c.beta1 * m + c.omb1 * g;
+    v = c.beta2 * v + c.omb2 * (g * g);
+    return m / (__builtin_sqrtf(v * c.rbc2) + c.eps);
+}
+
+// Mixed precision: fp32 master w (in place); returns the new w.
+__device__ __forceinline__ float mixed_elem(float g16, float& w, float& m, float& v, const Coef& c)
+{
+    const float g = g16 * c.inv_scale;
+    const float u = adam_dir(g, m, v, c);
+    w = w * c.decay - c.step_size * u;
+    return w;
+}
+
+// Kahan: returns the fp32 sum p + s to be rounded into the new bf16 p, and the
+// pending increment s through `s_out`.
+__device__ __forceinline__ float kahan_sum(float g16, float pf, float cf, float& m, float& v, const Coef& c,
+                                           float& s_out)
+{
+    const float g = g16 * c.inv_scale;
+    const float u = adam_dir(g, m, v, c);
+    const float d = -(c.lrwd * pf) - c.step_size * u;
+    const float s = cf + d;
+    s_out = s;
+    return pf + s;
+}
+
+// ---------------------------------------------------------------------------
+// Prologue: one lane.  skip = *found_inf != 0; otherwise t = *step + 1, the
+// step's scalars, and *step = t.
+// ---------------------------------------------------------------------------
+
+__device__ double pow_sq(double b, int64_t t)
+{
+    // beta^t by right-to-left binary powering: square the base every round,
+    // multiply it into the result for every set bit of t.
+    double r = 1.0;
+    for (; t > 0; t >>= 1) {
+        if (t & 1) r = r * b;
+        b = b * b;
+    }
+    return r;
+}
+
+__global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, const int32_t* __restrict__ found_inf,
+                                LaunchScalars* __restrict__ out)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    LaunchScalars s{};
+    if (found_inf && *found_inf != 0) {
+        s.skip = 1;
+        *out = s;
+        return;
+    }
+    const int64_t t = (int64_t)*step + 1;
+    const double lr = (double)hp.lr, wd = (double)hp.weight_decay;
+    const double b1t = pow_sq((double)hp.beta1, t);
+    const double b2t = pow_sq((double)hp.beta2, t);
+    s.skip = 0;
+    s.t = (int32_t)t;
+    s.step_size = (float)(lr / (1.0 - b1t));
+    s.rbc2 = (float)(1.0 / (1.0 - b2t));
+    s.decay = (float)(1.0 - lr * wd);
+    s.lrwd = (float)(lr * wd);
+    s.omb1 = 1.0f - hp.beta1;
+    s.omb2 = 1.0f - hp.beta2;
+    s.beta1 = hp.beta1;
+    s.beta2 = hp.beta2;
+    s.eps = hp.eps;
+    s.inv_scale = hp.inv_loss_scale;
+    *out = s;
+    *step = (int32_t)t;
+}
+
+// ---------------------------------------------------------------------------
+// Update kernel
+// ---------------------------------------------------------------------------
+
+constexpr int kUnroll = 2;
+
+__device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
+{
+    Coef c;
+    c.step_size = sc->step_size;
+    c.rbc2 = sc->rbc2;
+    c.decay = sc->decay;
+    c.lrwd = sc->lrwd;
+    c.omb1 = sc->omb1;
+    c.omb2 = sc->omb2;
+    c.beta1 = sc->beta1;
+    c.beta2 = sc->beta2;
+    c.eps = sc->eps;
+    c.inv_scale = sc->inv_scale;
+    return c;
+}
+
+// MODE 0: mixed bf16, 1: mixed fp16, 2: pure bf16 + Kahan
+template <int MODE>
+__global__ __launch_bounds__(kBlock) void update_kernel(const DevSeg* __restrict__ segs,
+                                                        const DevChunk* __restrict__ chunks,
+                                                        const LaunchScalars* __restrict__ sc)
+{
+    if (sc->skip) return;
+    constexpr bool F16 = (MODE == 1);
+    const Coef c = load_coef(sc);
+    const DevChunk ch = chunks[blockIdx.x];
+    const DevSeg& sg = segs[ch.seg];
+    const uint32_t n = ch.n_kind & kCountMask;
+    const uint64_t off = ch.off;
+    const uint32_t tid = threadIdx.x;
+
+    if constexpr (MODE != 2) {
+        GLOBAL uint16_t* __restrict__ p = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_PARAM], off);
+        const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
+        GLOBAL float* __restrict__ m = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
+        GLOBAL float* __restrict__ v = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG_SQ], off);
+        GLOBAL float* __restrict__ w = gptr<float>(sg.ptr[ADAMW_STREAM_AUX], off);
+        if (ch.n_kind & kVecBit) {
+            const uint32_t npack = n / kPack;
+            const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
+            GLOBAL u32x4* __restrict__ p4 = reinterpret_cast<GLOBAL u32x4*>(p);
+            GLOBAL f32x4* __restrict__ m4 = reinterpret_cast<GLOBAL f32x4*>(m);
+            GLOBAL f32x4* __restrict__ v4 = reinterpret_cast<GLOBAL f32x4*>(v);
+            GLOBAL f32x4* __restrict__ w4 = reinterpret_cast<GLOBAL f32x4*>(w);
+            for (uint32_t k0 = tid; k0 < npack; k0 += kBlock * kUnroll) {
+                u32x4 G[kUnroll];
+                f32x4 M[kUnroll][2], V[kUnroll][2], W[kUnroll][2];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const uint32_t k = k0 + u * kBlock;
+                    if (k < npack) {
+                        G[u] = g4[k];
+                        W[u][0] = w4[2 * k]; W[u][1] = w4[2 * k + 1];
+                        M[u][0] = m4[2 * k]; M[u][1] = m4[2 * k + 1];
+                        V[u][0] = v4[2 * k]; V[u][1] = v4[2 * k + 1];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const uint32_t k = k0 + u * kBlock;
+                    if (k < npack) {
+                        float* wf = reinterpret_cast<float*>(W[u]);
+                        float* mf = reinterpret_cast<float*>(M[u]);
+                        float* vf = reinterpret_cast<float*>(V[u]);
+                        const uint32_t gw[4] = {G[u].x, G[u].y, G[u].z, G[u].w};
+                        uint32_t pw[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const f32x2 gg = widen2<F16>(gw[j]);
+                            const float a = mixed_elem(gg.x, wf[2 * j], mf[2 * j], vf[2 * j], c);
+                            const float b = mixed_elem(gg.y, wf[2 * j + 1], mf[2 * j + 1], vf[2 * j + 1], c);
+                            pw[j] = narrow2<F16>(a, b);
+                        }
+                        w4[2 * k] = W[u][0]; w4[2 * k + 1] = W[u][1];
+                        m4[2 * k] = M[u][0]; m4[2 * k + 1] = M[u][1];
+                        v4[2 * k] = V[u][0]; v4[2 * k + 1] = V[u][1];
+                        p4[k] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+                    }
+                }
+            }
+        } else {
+            for (uint32_t i = tid; i < n; i += kBlock) {
+                float wi = w[i], mi = m[i], vi = v[i];
+                const float nw = mixed_elem(widen1<F16>(g[i]), wi, mi, vi, c);
+                w[i] = wi;
+                m[i] = mi;
+                v[i] = vi;
+                p[i] = narrow1<F16>(nw);
+            }
+        }
+    } else {
+        GLOBAL uint16_t* __restrict__ p = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_PARAM], off);
+        const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
+        GLOBAL uint16_t* __restrict__ m = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
+        GLOBAL uint16_t* __restrict__ v = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_EXP_AVG_SQ], off);
+        GLOBAL uint16_t* __restrict__ cc = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_AUX], off);
+        if (ch.n_kind & kVecBit) {
+            const uint32_t npack = n / kPack;
+            const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
+            GLOBAL u32x4* __restrict__ p4 = reinterpret_cast<GLOBAL u32x4*>(p);
+            GLOBAL u32x4* __restrict__ m4 = reinterpret_cast<GLOBAL u32x4*>(m);
+            GLOBAL u32x4* __restrict__ v4 = reinterpret_cast<GLOBAL u32x4*>(v);
+            GLOBAL u32x4* __restrict__ c4 = reinterpret_cast<GLOBAL u32x4*>(cc);
+            for (uint32_t k0 = tid; k0 < npack; k0 += kBlock * kUnroll) {
+                u32x4 G[kUnroll], P[kUnroll], M[kUnroll], V[kUnroll], C[kUnroll];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const uint32_t k = k0 + u * kBlock;
+                    if (k < npack) {
+                        G[u] = g4[k]; P[u] = p4[k]; M[u] = m4[k]; V[u] = v4[k]; C[u] = c4[k];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const uint32_t k = k0 + u * kBlock;
+                    if (k < npack) {
+                        const uint32_t gw[4] = {G[u].x, G[u].y, G[u].z, G[u].w};
+                        const uint32_t pw[4] = {P[u].x, P[u].y, P[u].z, P[u].w};
+                        const uint32_t mw[4] = {M[u].x, M[u].y, M[u].z, M[u].w};
+                        const uint32_t vw[4] = {V[u].x, V[u].y, V[u].z, V[u].w};
+                        const uint32_t cw[4] = {C[u].x, C[u].y, C[u].z, C[u].w};
+                        uint32_t po[4], mo[4], vo[4], co[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const f32x2 gg = widen2<false>(gw[j]);
+                            const f32x2 pp = widen2<false>(pw[j]);
+                            const f32x2 cf = widen2<false>(cw[j]);
+                            const f32x2 m2 = widen2<false>(mw[j]);
+                            const f32x2 v2 = widen2<false>(vw[j]);
+                            float ma = m2.x, mb = m2.y, va = v2.x, vb = v2.y, sa, sb;
+                            const float ta = kahan_sum(gg.x, pp.x, cf.x, ma, va, c, sa);
+                            const float tb = kahan_sum(gg.y, pp.y, cf.y, mb, vb, c, sb);
+                            po[j] = narrow2<false>(ta, tb);
+                            const f32x2 pn = widen2<false>(po[j]);
+                            co[j] = narrow2<false>(sa - (pn.x - pp.x), sb - (pn.y - pp.y));
+                            mo[j] = narrow2<false>(ma, mb);
+                            vo[j] = narrow2<false>(va, vb);
+                        }
+                        p4[k] = u32x4{po[0], po[1], po[2], po[3]};
+                        m4[k] = u32x4{mo[0], mo[1], mo[2], mo[3]};
+                        v4[k] = u32x4{vo[0], vo[1], vo[2], vo[3]};
+                        c4[k] = u32x4{co[0], co[1], co[2], co[3]};
+                    }
+                }
+            }
+        } else {
+            for (uint32_t i = tid; i < n; i += kBlock) {
+                const float pf = widen1<false>(p[i]);
+                float mi = widen1<false>(m[i]), vi = widen1<false>(v[i]), s;
+                const float tot = kahan_sum(widen1<false>(g[i]), pf, widen1<false>(cc[i]), mi, vi, c, s);
+                const uint16_t pn = narrow1<false>(tot);
+                cc[i] = narrow1<false>(s - (widen1<false>(pn) - pf));
+                p[i] = pn;
+                m[i] = narrow1<false>(mi);
+                v[i] = narrow1<false>(vi);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Overflow check
+// ---------------------------------------------------------------------------
+
+__global__ void zero_flag_kernel(int32_t* __restrict__ flag)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) *flag = 0;
+}
+
+// Nonzero iff one of the two 16-bit elements in w has an all-ones exponent
+// field (EXP = 0x7c00 for fp16, 0x7f80 for bf16).
+template <uint32_t EXP>
+__device__ __forceinline__ uint32_t nonfinite2(uint32_t w)
+{
+    const uint32_t x = ~w & (EXP | (EXP << 16));
+    return (uint32_t)((x & 0xffffu) == 0) | (uint32_t)((x >> 16) == 0);
+}
+
+template <bool F16>
+__global__ __launch_bounds__(kBlock) void check_kernel(const DevSeg* __restrict__ segs,
+                                                       const DevChunk* __restrict__ chunks,
+                                                       int32_t* __restrict__ flag)
+{
+    constexpr uint32_t EXP = F16 ? 0x7c00u : 0x7f80u;
+    const DevChunk ch = chunks[blockIdx.x];
+    const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(segs[ch.seg].ptr[ADAMW_STREAM_GRAD], ch.off);
+    const uint32_t n = ch.n_kind & kCountMask;
+    uint32_t bad = 0;
+    if (ch.n_kind & kVecBit) {
+        const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
+        const uint32_t npack = n / kPack;
+        for (uint32_t k = threadIdx.x; k < npack; k += kBlock) {
+            const u32x4 q = g4[k];
+            bad |= nonfinite2<EXP>(q.x) | nonfinite2<EXP>(q.y) | nonfinite2<EXP>(q.z) | nonfinite2<EXP>(q.w);
+        }
+    } else {
+        for (uint32_t i = threadIdx.x; i < n; i += kBlock) bad |= (uint32_t)((g[i] & EXP) == EXP);
+    }
+    // one atomic per wavefront that saw a non-finite value
+    if (__any((int)bad) && (threadIdx.x % warpSize) == 0)
+        __hip_atomic_fetch_or(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32_t* d_found_inf,
+                           LaunchScalars* d_scalars, hipStream_t stream)
+{
+    hipLaunchKernelGGL(prologue_kernel, dim3(1), dim3(64), 0, stream, hp, d_step, d_found_inf, d_scalars);
+    return hipGetLastError();
+}
+
+hipError_t launch_update(adamw_mode mode, adamw_dtype p_dtype, const DevSeg* segs, const DevChunk* chunks,
+                         int64_t n_chunks, const LaunchScalars* d_scalars, hipStream_t stream)
+{
+    if (n_chunks <= 0) return hipSuccess;
+    const dim3 grid((unsigned)n_chunks), block(kBlock);
+    if (mode == ADAMW_PURE_KAHAN)
+        hipLaunchKernelGGL(update_kernel<2>, grid, block, 0, stream, segs, chunks, d_scalars);
+    else if (p_dtype == ADAMW_F16)
+        hipLaunchKernelGGL(update_kernel<1>, grid, block, 0, stream, segs, chunks, d_scalars);
+    else
+        hipLaunchKernelGGL(update_kernel<0>, grid, block, 0, stream, segs, chunks, d_scalars);
+    return hipGetLastError();
+}
+
+hipError_t launch_check(adamw_dtype g_dtype, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
+                        int32_t* d_flag, hipStream_t stream)
+{
+    hipLaunchKernelGGL(zero_flag_kernel, dim3(1), dim3(64), 0, stream, d_flag);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n_chunks <= 0) return e;
+    const dim3 grid((unsigned)n_chunks), block(kBlock);
+    if (g_dtype == ADAMW_F16)
+        hipLaunchKernelGGL(check_kernel<true>, grid, block, 0, stream, segs, chunks, d_flag);
+    else
+        hipLaunchKernelGGL(check_kernel<false>, grid, block, 0, stream, segs, chunks, d_flag);
+    return hipGetLastError();
+}
+
+}  // namespace adamw

@@ -1,0 +1,58 @@
+// layout.hpp -- device-side launch metadata shared by the host planner and the
+// gfx950 kernels of the fused AdamW step.
+//
+// A launch processes a list of segments (a tensor, or the part of a tensor that
+// falls inside a ZeRO shard).  Each segment is split into chunks; one
+// workgroup processes one chunk.  Chunks of the "vector" kind hold a multiple
+// of 8 elements whose addresses in every stream are 16-byte aligned, so every
+// lane moves whole dwordx4 words; the other kind ("element") covers peeled
+// heads and tails and segments whose streams cannot be aligned together.
+#pragma once
+
+#include <stdint.h>
+
+namespace adamw {
+
+constexpr int kStreams = 5;            // param, grad, exp_avg, exp_avg_sq, aux
+constexpr int kBlock = 256;            // threads per workgroup: four wave64s
+constexpr int kPack = 8;               // elements per lane per dwordx4 of a 16-bit stream
+constexpr uint32_t kVecBit = 0x80000000u;
+constexpr uint32_t kCountMask = 0x7fffffffu;
+constexpr int64_t kDefaultChunkElems = 16384;   // vector chunk: 8 packs per lane
+constexpr int64_t kElemChunkElems = 4096;       // element chunk: 16 elements per lane
+
+// One segment: the device address of its element 0 in each stream (0 for a
+// stream the launch does not touch).
+struct alignas(64) DevSeg {
+    uint64_t ptr[kStreams];
+    uint64_t pad[3];
+};
+
+// One workgroup's work: elements [off, off + count) of segment `seg`;
+// kVecBit in n_kind marks the vector kind.
+struct alignas(16) DevChunk {
+    uint32_t seg;
+    uint32_t n_kind;
+    uint64_t off;
+};
+
+// Scalars of one step, written by the prologue kernel and read by the update
+// kernel on the same stream.
+struct alignas(64) LaunchScalars {
+    int32_t skip;        // nonzero: the step is not taken, nothing is written
+    int32_t t;           // 1-based index of the step taken
+    float step_size;     // lr / (1 - beta1^t)
+    float rbc2;          // 1 / (1 - beta2^t)
+    float decay;         // 1 - lr*wd
+    float lrwd;          // lr*wd
+    float omb1;          // 1 - beta1 (fp32)
+    float omb2;          // 1 - beta2 (fp32)
+    float beta1;
+    float beta2;
+    float eps;
+    float inv_scale;
+};
+
+constexpr int64_t kScalarsBytes = 256;
+
+}  // namespace adamw

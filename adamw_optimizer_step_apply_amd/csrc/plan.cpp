@@ -1,0 +1,217 @@
+// plan.cpp -- host planner for the fused AdamW launch (no HIP calls).
+//
+// The list's elements are numbered by their position in the flat concatenation
+// of the tensors in list order.  One data-parallel rank owns the positions
+// [shard_begin, shard_end) (ZeRO optimizer-state sharding as in "Distributed
+// optimizer support for BERT"); a tensor that straddles an edge contributes
+// only its elements inside the range.  Each contributing piece becomes a
+// segment; each segment is cut into workgroup chunks:
+//
+//   [head: element chunk] [body: vector chunks, 16-byte aligned in every stream] [tail: element chunk]
+//
+// The head is the smallest count h < 8 that brings every stream's address to a
+// 16-byte boundary at the same element; if no such h exists (streams misaligned
+// relative to each other) the whole segment is cut into element chunks.
+#include "plan.hpp"
+
+#include <stdio.h>
+
+namespace adamw {
+
+static bool stream_active(int s, bool for_check) { return for_check ? s == ADAMW_STREAM_GRAD : true; }
+
+int stream_esize(adamw_mode mode, adamw_dtype p_dtype, int s, bool for_check)
+{
+    (void)p_dtype;
+    if (!stream_active(s, for_check)) return 0;
+    if (for_check || s == ADAMW_STREAM_PARAM || s == ADAMW_STREAM_GRAD) return 2;
+    return mode == ADAMW_MIXED ? 4 : 2;
+}
+
+adamw_status check_mode(adamw_mode mode, adamw_dtype p_dtype, bool for_check, std::string& err)
+{
+    if (for_check) {
+        if (p_dtype != ADAMW_F16 && p_dtype != ADAMW_BF16) {
+            err = "adamw_check_finite: g_dtype must be ADAMW_F16 or ADAMW_BF16";
+            return ADAMW_E_UNSUPPORTED;
+        }
+        return ADAMW_OK;
+    }
+    if (mode == ADAMW_MIXED) {
+        if (p_dtype != ADAMW_BF16 && p_dtype != ADAMW_F16) {
+            err = "ADAMW_MIXED needs p_dtype ADAMW_BF16 or ADAMW_F16";
+            return ADAMW_E_UNSUPPORTED;
+        }
+        return ADAMW_OK;
+    }
+    if (mode == ADAMW_PURE_KAHAN) {
+        if (p_dtype != ADAMW_BF16) {
+            err = "ADAMW_PURE_KAHAN needs p_dtype ADAMW_BF16";
+            return ADAMW_E_UNSUPPORTED;
+        }
+        return ADAMW_OK;
+    }
+    err = "unknown adamw_mode";
+    return ADAMW_E_UNSUPPORTED;
+}
+
+static const char* kStreamName[kStreams] = {"param", "grad", "exp_avg", "exp_avg_sq", "aux"};
+
+static void push_chunks(Plan& p, uint32_t seg, int64_t off, int64_t count, int64_t per, bool vec)
+{
+    while (count > 0) {
+        int64_t n = count < per ? count : per;
+        DevChunk c;
+        c.seg = seg;
+        c.n_kind = (uint32_t)n | (vec ? kVecBit : 0u);
+        c.off = (uint64_t)off;
+        p.chunks.push_back(c);
+        off += n;
+        count -= n;
+    }
+}
+
+adamw_status build_plan(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, bool for_check,
+                        int64_t chunk_elems, Plan* outp, std::string& err)
+{
+    char buf[256];
+    Plan scratch;
+    Plan& out = outp ? *outp : scratch;   // validation only when outp is null
+    out = Plan();
+    const bool build = outp != nullptr;
+    adamw_status st = check_mode(mode, p_dtype, for_check, err);
+    if (st != ADAMW_OK) return st;
+    if (!list) { err = "tensor list is null"; return ADAMW_E_INVALID; }
+    const int64_t nt = list->n_tensors;
+    if (nt < 0) { err = "n_tensors < 0"; return ADAMW_E_INVALID; }
+    if (nt > 0 && !list->numel) { err = "numel array is null"; return ADAMW_E_INVALID; }
+    if (list->flat_mask >> kStreams) { err = "flat_mask has bits above stream 4"; return ADAMW_E_INVALID; }
+
+    int64_t total = 0;
+    for (int64_t i = 0; i < nt; ++i) {
+        int64_t n = list->numel[i];
+        if (n < 0) {
+            snprintf(buf, sizeof buf, "numel[%lld] = %lld < 0", (long long)i, (long long)n);
+            err = buf;
+            return ADAMW_E_INVALID;
+        }
+        if (n > (INT64_C(1) << 56) || total > (INT64_C(1) << 56)) { err = "list too large"; return ADAMW_E_INVALID; }
+        total += n;
+    }
+    const int64_t b = list->shard_begin;
+    const int64_t e = list->shard_end < 0 ? total : list->shard_end;
+    if (list->shard_end < -1 || b < 0 || b > e || e > total) {
+        snprintf(buf, sizeof buf, "shard range [%lld, %lld) outside [0, %lld]", (long long)b,
+                 (long long)list->shard_end, (long long)total);
+        err = buf;
+        return ADAMW_E_INVALID;
+    }
+
+    int esz[kStreams];
+    bool flat[kStreams];
+    for (int s = 0; s < kStreams; ++s) {
+        esz[s] = stream_esize(mode, p_dtype, s, for_check);
+        flat[s] = (list->flat_mask >> s) & 1u;
+        if (!esz[s]) continue;
+        bool needed = flat[s] ? (e > b) : (nt > 0);
+        if (needed && !list->ptr[s]) {
+            snprintf(buf, sizeof buf, "pointer array of stream %s is null", kStreamName[s]);
+            err = buf;
+            return ADAMW_E_INVALID;
+        }
+        if (flat[s] && e > b) {
+            uintptr_t a = (uintptr_t)list->ptr[s][0];
+            if (!a || a % (uintptr_t)esz[s]) {
+                snprintf(buf, sizeof buf, "flat %s buffer is null or not %d-byte aligned", kStreamName[s], esz[s]);
+                err = buf;
+                return ADAMW_E_INVALID;
+            }
+        }
+    }
+    if (chunk_elems < 2048 || chunk_elems % 2048) { err = "bad chunk size"; return ADAMW_E_INVALID; }
+
+    int64_t base = 0, nseg = 0;
+    for (int64_t i = 0; i < nt; ++i) {
+        const int64_t n = list->numel[i];
+        const int64_t lo = b > base ? b : base;
+        const int64_t hi = e < base + n ? e : base + n;
+        if (lo < hi) {
+            SegInfo si{i, lo - base, lo, hi - lo};
+            DevSeg d{};
+            for (int s = 0; s < kStreams; ++s) {
+                if (!esz[s]) continue;
+                uintptr_t a;
+                if (flat[s]) {
+                    a = (uintptr_t)list->ptr[s][0] + (uintptr_t)((lo - b) * esz[s]);
+                } else {
+                    uintptr_t t0 = (uintptr_t)list->ptr[s][i];
+                    if (!t0 || t0 % (uintptr_t)esz[s]) {
+                        snprintf(buf, sizeof buf, "%s pointer of tensor %lld is null or not %d-byte aligned",
+                                 kStreamName[s], (long long)i, esz[s]);
+                        err = buf;
+                        return ADAMW_E_INVALID;
+                    }
+                    a = t0 + (uintptr_t)((lo - base) * esz[s]);
+                }
+                d.ptr[s] = (uint64_t)a;
+            }
+            if (nseg >= (int64_t)UINT32_MAX) { err = "too many segments"; return ADAMW_E_INVALID; }
+            const uint32_t seg = (uint32_t)nseg++;
+            if (!build) { base += n; continue; }
+            out.segs.push_back(d);
+            out.info.push_back(si);
+
+            // head peel: smallest h in [0, 8) aligning every active stream to 16 bytes
+            int head = -1;
+            for (int h = 0; h < kPack && head < 0; ++h) {
+                bool ok = true;
+                for (int s = 0; s < kStreams && ok; ++s)
+                    if (esz[s]) ok = ((d.ptr[s] + (uint64_t)h * esz[s]) % 16u) == 0;
+                if (ok) head = h;
+            }
+            const int64_t cnt = si.count;
+            if (head < 0 || head >= cnt) {
+                push_chunks(out, seg, 0, cnt, kElemChunkElems, false);
+            } else {
+                const int64_t body = (cnt - head) / kPack * kPack;
+                push_chunks(out, seg, 0, head, kElemChunkElems, false);
+                push_chunks(out, seg, head, body, chunk_elems, true);
+                push_chunks(out, seg, head + body, cnt - head - body, kElemChunkElems, false);
+            }
+        }
+        base += n;
+    }
+    if (out.chunks.size() > (size_t)INT32_MAX) { err = "too many chunks for one launch"; return ADAMW_E_INVALID; }
+    out.total = e - b;
+    return ADAMW_OK;
+}
+
+void plan_key(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, bool for_check,
+              int64_t chunk_elems, std::vector<int64_t>& key)
+{
+    const int64_t nt = list->n_tensors;
+    key.clear();
+    key.reserve(8 + (size_t)nt * 6);
+    key.push_back((int64_t)mode);
+    key.push_back((int64_t)p_dtype);
+    key.push_back(for_check ? 1 : 0);
+    key.push_back(chunk_elems);
+    key.push_back(nt);
+    key.push_back(list->shard_begin);
+    key.push_back(list->shard_end);
+    key.push_back((int64_t)list->flat_mask);
+    for (int64_t i = 0; i < nt; ++i) key.push_back(list->numel[i]);
+    for (int s = 0; s < kStreams; ++s) {
+        if (!stream_esize(mode, p_dtype, s, for_check) || !list->ptr[s]) {
+            key.push_back(-1);
+            continue;
+        }
+        if ((list->flat_mask >> s) & 1u) {
+            key.push_back((int64_t)(uintptr_t)list->ptr[s][0]);
+        } else {
+            for (int64_t i = 0; i < nt; ++i) key.push_back((int64_t)(uintptr_t)list->ptr[s][i]);
+        }
+    }
+}
+
+}  // namespace adamw

@@ -1,0 +1,201 @@
+/*
+ * adamw.h -- C ABI of the MI355X (gfx950) fused AdamW optimizer step.
+ *
+ * One call updates a whole list of parameter tensors (or one data-parallel
+ * rank's share of it) in place on the GPU: one HBM pass over param, grad,
+ * exp_avg, exp_avg_sq and an auxiliary buffer, with the arithmetic in fp32
+ * registers.
+ *
+ * The operation.  AdamW: Adam's bias-corrected moment estimates (Kingma & Ba,
+ * "Adam", ICLR 2015, Algorithm 1) with weight decay decoupled from the
+ * gradient (Loshchilov & Hutter, "Decoupled Weight Decay Regularization",
+ * ICLR 2019, Algorithm 2).  The pages that motivate this library name it and
+ * its settings without printing the rule: "Distributed optimizer support for
+ * BERT" (Usage: fused_adam / distributed_fused_adam; the A40 and A100 tables,
+ * "BF16 with O2 optimizations") and "[pure bf16 training] w/ AnyPrecisionAdamW
+ * and Kahan summation" (the opt-1.3b command: lr 0.0002, betas 0.9/0.95,
+ * weight decay 0.1; --optim_args with bf16 momentum, variance and Kahan
+ * compensation buffer).  With t the 1-based index of the step being taken:
+ *
+ *   g   = grad * inv_loss_scale
+ *   m   = beta1*m + (1-beta1)*g
+ *   v   = beta2*v + (1-beta2)*g*g
+ *   u   = m / (sqrt(v / (1-beta2^t)) + eps)
+ *   ADAMW_MIXED:      w = w*(1 - lr*wd) - (lr/(1-beta1^t))*u;  param = round16(w)
+ *   ADAMW_PURE_KAHAN: d = -(lr*wd)*p - (lr/(1-beta1^t))*u
+ *                     s = c + d;  p' = round_bf16(p + s);  c = round_bf16(s - (p' - p))
+ *
+ * Numerics: every element operation is one IEEE binary32 operation rounded to
+ * nearest even, in the order written above, without fused multiply-add;
+ * sqrt and division are correctly rounded; subnormals are kept.  The
+ * per-launch scalars 1/(1-beta1^t) etc. are formed in binary64 from +,-,*,/
+ * (beta^t by right-to-left square-and-multiply) and rounded once to fp32.
+ * Narrowing to bf16/fp16 rounds to nearest even.
+ *
+ * Streams.  Index s of the five per-element buffers:
+ *   0 param       ADAMW_MIXED: bf16 or fp16 (= p_dtype), written only
+ *                 ADAMW_PURE_KAHAN: bf16, read and written
+ *   1 grad        same 16-bit dtype as param; read only, never unscaled in place
+ *   2 exp_avg     ADAMW_MIXED: fp32 / ADAMW_PURE_KAHAN: bf16 (first moment m)
+ *   3 exp_avg_sq  ADAMW_MIXED: fp32 / ADAMW_PURE_KAHAN: bf16 (second moment v)
+ *   4 aux         ADAMW_MIXED: fp32 master weight w / ADAMW_PURE_KAHAN: bf16
+ *                 compensation c
+ * Every buffer is contiguous, 1-D, in device memory, aligned to its element
+ * size.  16-byte alignment is not required but is what the fast path uses;
+ * misaligned heads and tails are peeled, and a segment whose streams cannot
+ * be aligned together is processed element by element.
+ *
+ * Step counter and skip flag.  *d_step (device int32) is the number of steps
+ * taken so far; a step that is taken uses t = *d_step + 1 and stores t.  If
+ * d_found_inf is non-null and *d_found_inf != 0 when the step runs (stream
+ * order), nothing is written at all and *d_step is left as it is: the fp16
+ * loss-scaling skip.  The caller fills the flag with adamw_check_finite.
+ *
+ * Ownership and execution.  The caller owns every tensor, d_step, d_found_inf
+ * and the stream; the library never frees or reallocates them.  All work is
+ * enqueued on hip_stream (a hipStream_t; NULL = the null stream) and the call
+ * returns without synchronising.  The library owns only a small device
+ * workspace per (device, stream) holding the launch scalars and the chunk
+ * table, grown on demand and kept until adamw_release_workspace().  The host
+ * arrays inside adamw_tensor_list are read during the call only.
+ *
+ * Errors.  Arguments are validated before anything is enqueued; on an error
+ * nothing is enqueued, no buffer is touched, and adamw_last_error() describes
+ * it.  A HIP failure while enqueuing returns ADAMW_E_HIP.  Faults inside a
+ * kernel surface at the caller's next synchronisation.
+ *
+ * Concurrency.  Calls may come from several host threads.  Calls on different
+ * streams run independently (each stream has its own workspace); two calls
+ * must not update the same buffers concurrently.
+ */
+#ifndef ADAMW_H
+#define ADAMW_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADAMW_ABI_VERSION 1
+
+typedef enum {
+    ADAMW_OK = 0,
+    ADAMW_E_INVALID = 1,      /* bad argument: null, negative size, range, alignment, hyper-parameter */
+    ADAMW_E_UNSUPPORTED = 2,  /* mode / dtype combination not provided */
+    ADAMW_E_NOMEM = 3,        /* workspace allocation failed */
+    ADAMW_E_HIP = 4           /* a HIP call failed while enqueuing */
+} adamw_status;
+
+typedef enum { ADAMW_F32 = 0, ADAMW_BF16 = 1, ADAMW_F16 = 2 } adamw_dtype;
+
+typedef enum {
+    ADAMW_MIXED = 0,       /* 16-bit param/grad (bf16 or fp16) + fp32 master, exp_avg, exp_avg_sq */
+    ADAMW_PURE_KAHAN = 1   /* bf16 param, grad, exp_avg, exp_avg_sq + bf16 Kahan compensation */
+} adamw_mode;
+
+enum {
+    ADAMW_STREAM_PARAM = 0,
+    ADAMW_STREAM_GRAD = 1,
+    ADAMW_STREAM_EXP_AVG = 2,
+    ADAMW_STREAM_EXP_AVG_SQ = 3,
+    ADAMW_STREAM_AUX = 4,
+    ADAMW_NUM_STREAMS = 5
+};
+
+/* Hyper-parameters, as fp32.  Requirements: all finite; 0 <= beta1, beta2 < 1;
+ * eps >= 0; lr >= 0; weight_decay >= 0; inv_loss_scale > 0 (1.0f = no
+ * unscaling; 1/65536 for fp16 loss scale 65536). */
+typedef struct {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;
+    float inv_loss_scale;
+} adamw_hparams;
+
+/* A ragged list of tensors, optionally restricted to one data-parallel rank's
+ * ZeRO shard: the elements [shard_begin, shard_end) of the list's flat
+ * concatenation in list order (the optimizer-state sharding of "Distributed
+ * optimizer support for BERT": each rank keeps and updates 1/DP of the
+ * state).  Tensors may straddle the shard's edges; only their elements inside
+ * the range are touched.  shard_begin = 0, shard_end = -1 means the whole list.
+ *
+ * ptr[s] is a host array of device pointers for stream s:
+ *   flat_mask bit s == 0: ptr[s][i] is tensor i's buffer (numel[i] elements);
+ *   flat_mask bit s == 1: ptr[s][0] is ONE flat buffer of shard_end-shard_begin
+ *                         elements holding this rank's share, element 0 being
+ *                         flat position shard_begin (e.g. a reduce-scattered
+ *                         gradient shard, or ZeRO-sharded master/m/v).
+ * numel is a host array of n_tensors element counts (each >= 0). */
+typedef struct {
+    int64_t n_tensors;
+    const int64_t* numel;
+    void* const* ptr[ADAMW_NUM_STREAMS];
+    int64_t shard_begin;
+    int64_t shard_end;
+    uint32_t flat_mask;
+} adamw_tensor_list;
+
+/* One AdamW step over one contiguous range of n elements (a single tensor, or
+ * one rank's flat shard with every pointer already offset to it).
+ * param, grad, exp_avg, exp_avg_sq, aux: device buffers of n elements in the
+ * layouts above.  p_dtype: ADAMW_BF16 or ADAMW_F16 in ADAMW_MIXED, ADAMW_BF16
+ * in ADAMW_PURE_KAHAN.  n == 0 is valid (the counter still advances unless
+ * skipped).  See the file comment for d_step / d_found_inf. */
+adamw_status adamw_step(adamw_mode mode, adamw_dtype p_dtype, int64_t n,
+                        void* param, const void* grad, void* exp_avg, void* exp_avg_sq, void* aux,
+                        const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
+                        void* hip_stream);
+
+/* One AdamW step over a ragged tensor list (or its shard), in one launch of
+ * the update kernel: the chunked multi-tensor form of the fused optimizer
+ * ("fused_adam" in "Distributed optimizer support for BERT").  Same element
+ * rule, dtypes, counter and skip semantics as adamw_step. */
+adamw_status adamw_multi_tensor_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
+                                     const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
+                                     void* hip_stream);
+
+/* fp16-AMP overflow check: stores 0 to *d_found_inf (stream ordered), then 1
+ * if any gradient element of the list (stream 1 only; shard range and
+ * flat_mask bit 1 honoured) has an all-ones exponent field, i.e. is inf or NaN.
+ * g_dtype: ADAMW_F16 or ADAMW_BF16.  Scaled gradients are tested as stored,
+ * before any unscaling.  Intended order: adamw_check_finite, then the step
+ * with the same d_found_inf (an all-reduce(max) of the flag across ranks
+ * would sit between the two in a multi-GPU job). */
+adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* grads, int32_t* d_found_inf,
+                                void* hip_stream);
+
+/* Description of the last error on the calling thread ("" if none).  Valid
+ * until the next call into the library on that thread. */
+const char* adamw_last_error(void);
+
+/* Frees every workspace the library holds (all devices and streams).  The
+ * caller must make sure no enqueued step is still running. */
+void adamw_release_workspace(void);
+
+/* ADAMW_ABI_VERSION of the built library. */
+int adamw_abi_version(void);
+
+/* Planner introspection, for tests: no GPU work, no HIP call.  Builds the
+ * chunk plan that adamw_multi_tensor_step (for_check = 0) or
+ * adamw_check_finite (for_check = 1) would launch, and writes up to cap rows
+ * of 6 int64 each to out:
+ *   {tensor index, element offset inside the tensor, element count,
+ *    kind (0 = element-wise, 1 = 16-byte vector), flat position, segment}.
+ * Returns the number of chunks (which may exceed cap), or -1 on an invalid
+ * argument (see adamw_last_error). */
+int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, int for_check,
+                           int64_t* out, int64_t cap);
+
+/* Tuning knob: elements per vector chunk (one workgroup's share), a multiple
+ * of 2048 in [2048, 1<<22]; 0 restores the built-in default.  Affects plans
+ * built after the call.  Returns the value now in force, or -1 if rejected. */
+int64_t adamw_set_chunk_elems(int64_t elems);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAMW_H */

@@ -1,0 +1,145 @@
+"""Helpers of the GPU parity tests: run the HIP library and the CPU oracle on the
+same seeded bytes and compare to the stated bar.
+
+Bar (per element, after the last step):
+* fp32 state (master, exp_avg, exp_avg_sq of mixed mode): relative error
+  |gpu - oracle| / |oracle| <= 2e-6, and exact equality where the oracle is 0;
+* 16-bit outputs (param, bf16 moments, Kahan compensation): at most 1 ulp apart,
+  measured as the distance of the sign-magnitude codes on the ordered line;
+* NaN on one side only is a failure; step counters and skip flags exactly equal.
+The kernels are designed to be bit-exact with the oracle (same operation order,
+no contraction, correctly rounded sqrt/div, RNE narrowing), so the number of
+differing bit patterns is also reported and expected to be 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import adamw_optimizer_step_apply_amd as A
+import oracle
+import workloads
+
+MODE = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN}
+DT = {"bf16": A.BF16, "f16": A.F16}
+F32_KEYS = {"mixed": ("m", "v", "master"), "kahan": ()}
+REL_TOL = 2e-6
+ULP_TOL = 1
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
+
+def ordered16(a: np.ndarray) -> np.ndarray:
+    a = a.astype(np.int32)
+    return np.where(a & 0x8000, -(a & 0x7FFF), a)
+
+
+def compare(name: str, got: np.ndarray, ref: np.ndarray, is_f32: bool, p_is_f16: bool = False) -> dict:
+    """Checks one stream against the bar; returns statistics (raises on failure)."""
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    if is_f32:
+        gb, rb = got.view(np.uint32), ref.view(np.uint32)
+        gn, rn = np.isnan(got), np.isnan(ref)
+    else:
+        gb, rb = got, ref
+        expo = 0x7C00 if p_is_f16 else 0x7F80
+        gn = ((got & expo) == expo) & ((got & (0x3FF if p_is_f16 else 0x7F)) != 0)
+        rn = ((ref & expo) == expo) & ((ref & (0x3FF if p_is_f16 else 0x7F)) != 0)
+    assert np.array_equal(gn, rn), f"{name}: NaN pattern differs at {np.flatnonzero(gn != rn)[:8]}"
+    ok = ~rn
+    diff_bits = int(np.count_nonzero(gb[ok] != rb[ok]))
+    stats = {"stream": name, "n": int(got.size), "bit_mismatches": diff_bits}
+    if is_f32:
+        g64, r64 = got[ok].astype(np.float64), ref[ok].astype(np.float64)
+        zero = r64 == 0
+        assert np.all(g64[zero] == 0), f"{name}: nonzero where the oracle is 0"
+        nz = ~zero
+        rel = np.abs(g64[nz] - r64[nz]) / np.abs(r64[nz]) if nz.any() else np.zeros(1)
+        rel = rel[np.isfinite(rel)] if rel.size else np.zeros(1)
+        stats["max_rel"] = float(rel.max()) if rel.size else 0.0
+        assert stats["max_rel"] <= REL_TOL, f"{name}: max relative error {stats['max_rel']:.3e} > {REL_TOL}"
+    else:
+        d = np.abs(ordered16(got[ok]) - ordered16(ref[ok]))
+        stats["max_ulp"] = int(d.max()) if d.size else 0
+        assert stats["max_ulp"] <= ULP_TOL, f"{name}: {stats['max_ulp']} ulp apart"
+    return stats
+
+
+def shift_stream(arena: workloads.Arena, key: str, shift: int):
+    """Moves stream ``key`` of the arena ``shift`` elements up in a fresh buffer,
+    so its tensors start at a different 16-byte phase than the other streams."""
+    if not shift:
+        return
+    old = arena.bufs[key]
+    buf = torch.empty(old.numel() + shift, dtype=old.dtype, device=old.device)
+    buf[:shift].zero_()
+    buf[shift:].copy_(old)
+    arena.bufs[key] = buf[shift:]
+    arena.bufs["_" + key + "_owner"] = buf
+
+
+class Case:
+    """A tensor list on the GPU (one arena per stream) and its host mirror."""
+
+    def __init__(self, mode, numels, seed, *, p_dtype="bf16", align_elems=128, loss_scale=1.0,
+                 random_moments=False, shifts=None, device="cuda"):
+        self.mode, self.p_dtype, self.seed, self.loss_scale = mode, p_dtype, seed, loss_scale
+        self.numels = [int(n) for n in numels]
+        self.arena = workloads.make_state(mode, self.numels, device, seed, p_dtype=p_dtype,
+                                          align_elems=align_elems, loss_scale=loss_scale,
+                                          random_moments=random_moments)
+        for k, s in (shifts or {}).items():
+            shift_stream(self.arena, k, s)
+        self.keys = workloads.STREAMS[mode]
+        self.host = {k: to_np(self.arena.bufs[k]) for k in self.keys}
+        self.d_step = torch.zeros(1, dtype=torch.int32, device=device)
+        self.step = 0
+
+    # -- lists ------------------------------------------------------------
+    def tensor_list(self, shard_begin=0, shard_end=-1):
+        streams = [[self.arena.view(k, i) for i in range(len(self.numels))] for k in self.keys]
+        return A.TensorList(self.numels, streams, shard_begin, shard_end)
+
+    def oracle_tensors(self):
+        return [{k: self.host[k][o:o + n] for k in self.keys}
+                for o, n in zip(self.arena.offsets, self.numels)]
+
+    # -- steps ------------------------------------------------------------
+    def refill_grads(self, step_index: int):
+        workloads.refill_grads(self.arena, self.seed, step_index, p_dtype=self.p_dtype,
+                               loss_scale=self.loss_scale)
+        self.host["g"] = to_np(self.arena.bufs["g"])
+
+    def gpu_step(self, hp: A.HParams, shard=(0, -1), found_inf=None, tl=None):
+        tl = tl or self.tensor_list(*shard)
+        A.adamw_multi_tensor_step(MODE[self.mode], DT[self.p_dtype], tl, hp, self.d_step, found_inf)
+
+    def oracle_step(self, hp: oracle.HParams, shard=(0, -1), check_overflow=False):
+        self.step = oracle.step_list(self.mode, self.oracle_tensors(), hp, self.step,
+                                     p_is_f16=self.p_dtype == "f16", check_overflow=check_overflow,
+                                     shard_begin=shard[0], shard_end=shard[1])
+
+    def compare_all(self, label=""):
+        torch.cuda.synchronize()
+        assert int(self.d_step.item()) == self.step, f"{label}: step counter {int(self.d_step.item())} != {self.step}"
+        stats = []
+        for k in self.keys:
+            stats.append(compare(f"{label}:{k}", to_np(self.arena.bufs[k]), self.host[k],
+                                 k in F32_KEYS[self.mode], self.p_dtype == "f16"))
+        return stats
+
+
+def hp_pair(lr=2e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, inv_scale=1.0):
+    """The same fp32 hyper-parameters for the library and the oracle."""
+    f = [float(np.float32(x)) for x in (lr, beta1, beta2, eps, weight_decay, inv_scale)]
+    return A.HParams(*f), oracle.HParams(*f)
+
+
+def free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()

@@ -1,0 +1,391 @@
+"""GPU parity: the HIP library against the CPU oracle, element by element, on
+seeded inputs small enough for the oracle to finish in seconds yet spanning
+many workgroup chunks, peeled heads and ragged tails.  See gpu_util for the bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import Case, compare, free, hp_pair, to_np
+
+import adamw_optimizer_step_apply_amd as A
+
+pytestmark = pytest.mark.gpu
+
+EDGE_SIZES = [0, 1, 7, 8, 9, 15, 16, 17, 2047, 2048, 2049, 16383, 16384, 16385, 100_003, 3, 40_000]
+
+
+def _run(case: Case, steps: int, hp_kw=None, label=""):
+    hg, ho = hp_pair(**(hp_kw or {}))
+    for s in range(steps):
+        if s:
+            case.refill_grads(s)
+        case.gpu_step(hg)
+        case.oracle_step(ho)
+    stats = case.compare_all(label)
+    print(label, stats, flush=True)
+    return stats
+
+
+def test_single_tensor_1m_mixed_10_steps():
+    """One flat tensor of 1,048,576 elements, mixed bf16/fp32, 10 steps with a
+    fresh seeded gradient each step (the single-tensor workload)."""
+    case = Case("mixed", [1 << 20], seed=101)
+    stats = _run(case, 10, label="single_1m")
+    assert all(s["bit_mismatches"] == 0 for s in stats)
+    free()
+
+
+@pytest.mark.parametrize("align", [128, 1, 3])
+@pytest.mark.parametrize("mode,p_dtype", [("mixed", "bf16"), ("mixed", "f16"), ("kahan", "bf16")])
+def test_edge_sizes(mode, p_dtype, align):
+    """Sizes around the 8-element pack and the chunk size, packed at several
+    alignments (align=1 or 3 puts most tensors off a 16-byte boundary)."""
+    scale = 65536.0 if p_dtype == "f16" else 1.0
+    case = Case(mode, EDGE_SIZES, seed=202 + align, p_dtype=p_dtype, align_elems=align, loss_scale=scale,
+                random_moments=True)
+    _run(case, 4, hp_kw={"inv_scale": 1.0 / scale}, label=f"edges-{mode}-{p_dtype}-a{align}")
+    free()
+
+
+@pytest.mark.parametrize("shifts", [{"g": 1}, {"master": 1}, {"p": 3, "g": 3, "m": 2, "v": 2, "master": 2},
+                                    {"m": 1, "v": 3}, {"g": 8}])
+def test_streams_at_different_phases(shifts):
+    """Streams whose tensors start at different 16-byte phases: either a common
+    head peel exists or the planner falls back to element chunks."""
+    case = Case("mixed", EDGE_SIZES, seed=303, shifts=shifts, random_moments=True)
+    _run(case, 3, label=f"shift-{shifts}")
+    free()
+
+
+def test_kahan_phases():
+    case = Case("kahan", EDGE_SIZES, seed=304, shifts={"c": 1, "p": 5}, random_moments=True)
+    _run(case, 3, label="kahan-shift")
+    free()
+
+
+@pytest.mark.parametrize("hp_kw", [dict(eps=1e-3), dict(lr=1e-2, weight_decay=0.5),
+                                   dict(beta1=0.0, beta2=0.0), dict(beta1=0.5, beta2=0.75, weight_decay=0.0),
+                                   dict(lr=0.0, weight_decay=0.0)],
+                         ids=["eps", "strong-decay", "beta0", "betas", "lr0"])
+@pytest.mark.parametrize("mode", ["mixed", "kahan"])
+def test_hyperparameter_variants(mode, hp_kw):
+    case = Case(mode, [5000, 33, 20000], seed=404, random_moments=True)
+    _run(case, 3, hp_kw=hp_kw, label=f"hp-{mode}-{hp_kw}")
+    free()
+
+
+def test_zero_shard_union_equals_full_step():
+    """Four ranks, each stepping its 1/4 shard of the flat list with its own
+    step counter, leave the same state as one full-list step (the single-GPU
+    form of the pages' ZeRO on/off comparison), and both match the oracle."""
+    numels = [1000, 12345, 7, 50000, 16, 4099]
+    total = sum(numels)
+    full = Case("mixed", numels, seed=505)
+    parts = Case("mixed", numels, seed=505)
+    hg, ho = hp_pair()
+    full.gpu_step(hg)
+    full.oracle_step(ho)
+    counters = []
+    for r in range(4):
+        b, e = r * total // 4, (r + 1) * total // 4
+        ctr = torch.zeros(1, dtype=torch.int32, device="cuda")
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, parts.tensor_list(b, e), hg, ctr)
+        counters.append(ctr)
+    torch.cuda.synchronize()
+    assert [int(c.item()) for c in counters] == [1, 1, 1, 1]
+    for k in parts.keys:
+        assert torch.equal(parts.arena.bufs[k], full.arena.bufs[k]), k
+    full.compare_all("union-full")
+    free()
+
+
+@pytest.mark.parametrize("rank", [0, 1, 2, 3])
+def test_zero_shard_vs_oracle(rank):
+    """One rank's shard for 3 steps: elements outside the shard stay untouched."""
+    numels = [3000, 777, 9, 65536 + 5, 128]
+    total = sum(numels)
+    b, e = rank * total // 4, (rank + 1) * total // 4
+    case = Case("mixed", numels, seed=606, random_moments=True)
+    hg, ho = hp_pair()
+    for s in range(3):
+        if s:
+            case.refill_grads(s)
+        case.gpu_step(hg, shard=(b, e))
+        case.oracle_step(ho, shard=(b, e))
+    case.compare_all(f"shard-r{rank}")
+    free()
+
+
+def test_flat_shard_buffers():
+    """Gradient, master, m and v as one flat buffer of the rank's shard (a
+    reduce-scattered gradient and ZeRO-sharded state), params per tensor."""
+    numels = [4000, 1500, 8, 30000, 77]
+    total = sum(numels)
+    b, e = total // 4, 3 * total // 4
+    ref = Case("mixed", numels, seed=707, align_elems=1, random_moments=True)
+    flat = Case("mixed", numels, seed=707, align_elems=1, random_moments=True)
+    hg, _ = hp_pair()
+    # packed tight (align 1): the flat shard of a stream is a plain slice of its arena
+    shard = {k: flat.arena.bufs[k][b:e].clone() for k in ("g", "m", "v", "master")}
+    streams = [[flat.arena.view("p", i) for i in range(len(numels))],
+               [shard["g"]], [shard["m"]], [shard["v"]], [shard["master"]]]
+    tl = A.TensorList(numels, streams, b, e, flat_mask=0b11110)
+    A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl, hg, flat.d_step)
+    ref.gpu_step(hg, shard=(b, e))
+    torch.cuda.synchronize()
+    assert torch.equal(flat.arena.bufs["p"], ref.arena.bufs["p"])
+    for k in ("m", "v", "master"):
+        assert torch.equal(shard[k], ref.arena.bufs[k][b:e]), k
+    free()
+
+
+def test_skip_flag_leaves_everything_unchanged():
+    case = Case("mixed", EDGE_SIZES, seed=808, random_moments=True)
+    hg, ho = hp_pair()
+    case.gpu_step(hg)
+    case.oracle_step(ho)
+    before = {k: v.clone() for k, v in case.arena.bufs.items()}
+    flag = torch.ones(1, dtype=torch.int32, device="cuda")
+    case.refill_grads(1)
+    before["g"] = case.arena.bufs["g"].clone()
+    case.gpu_step(hg, found_inf=flag)
+    torch.cuda.synchronize()
+    assert int(case.d_step.item()) == 1
+    for k, v in before.items():
+        assert torch.equal(case.arena.bufs[k], v), k
+    flag.zero_()
+    case.gpu_step(hg, found_inf=flag)
+    case.oracle_step(ho)
+    case.compare_all("after-skip")
+    assert case.step == 2
+    free()
+
+
+@pytest.mark.parametrize("g_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("bad", ["inf", "-inf", "nan"])
+def test_check_finite_and_skip(g_dtype, bad):
+    """fp16-AMP: the check kernel flags an inf/NaN planted at a seeded tensor and
+    element; the following step is skipped; a clean gradient is not flagged."""
+    scale = 65536.0 if g_dtype == "f16" else 1.0
+    mode = "mixed"
+    case = Case(mode, EDGE_SIZES, seed=909, p_dtype=g_dtype, loss_scale=scale, align_elems=3)
+    tl = case.tensor_list()
+    flag = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    A.adamw_check_finite(A.F16 if g_dtype == "f16" else A.BF16, tl, flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    rng = np.random.default_rng(11)
+    for trial in range(6):
+        i = int(rng.choice([j for j, n in enumerate(EDGE_SIZES) if n]))
+        j = int(rng.integers(0, EDGE_SIZES[i]))
+        view = case.arena.view("g", i)
+        old = view[j].clone()
+        view[j] = float(bad)
+        A.adamw_check_finite(A.F16 if g_dtype == "f16" else A.BF16, tl, flag)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 1, (trial, i, j)
+        host_g = to_np(case.arena.bufs["g"])
+        assert oracle.any_nonfinite(host_g, g_dtype == "f16")
+        before = {k: v.clone() for k, v in case.arena.bufs.items()}
+        hg, _ = hp_pair(inv_scale=1.0 / scale)
+        case.gpu_step(hg, tl=tl, found_inf=flag)
+        torch.cuda.synchronize()
+        assert int(case.d_step.item()) == 0
+        for k, v in before.items():
+            assert torch.equal(case.arena.bufs[k], v), k
+        view[j] = old
+    A.adamw_check_finite(A.F16 if g_dtype == "f16" else A.BF16, tl, flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    free()
+
+
+@pytest.mark.parametrize("g_dtype", ["f16", "bf16"])
+def test_check_finite_all_patterns(g_dtype):
+    """Every 16-bit pattern: the finite ones never raise the flag; each non-finite
+    one raises it wherever it sits (vector or element chunk)."""
+    is16 = g_dtype == "f16"
+    allp = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    expo = 0x7C00 if is16 else 0x7F80
+    finite = allp[(allp & expo) != expo]
+    bad = allp[(allp & expo) == expo]
+    dt = torch.float16 if is16 else torch.bfloat16
+    base = torch.from_numpy(finite.view(np.int16).copy()).cuda()
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    buf = torch.zeros(finite.size + 16, dtype=torch.int16, device="cuda")
+    buf[:finite.size] = base
+    g = buf.view(dt)
+    sizes = [1, 7, finite.size - 8]       # element chunk, element chunk, vector body + tail
+    offs = [0, 1, 8]
+    views = [g[o:o + n] for o, n in zip(offs, sizes)]
+    tl = A.TensorList(sizes, [None, views, None, None, None])
+    A.adamw_check_finite(A.F16 if is16 else A.BF16, tl, flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    rng = np.random.default_rng(12)
+    positions = [0, 1, 5, 8, 9, 100, 2048 * 8 + 3, finite.size - 1]
+    for pat in rng.choice(bad, size=min(64, bad.size), replace=False):
+        pos = int(rng.choice(positions))
+        old = int(buf[pos].item())
+        buf[pos] = int(np.int16(np.uint16(pat).view(np.int16)))
+        A.adamw_check_finite(A.F16 if is16 else A.BF16, tl, flag)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 1, hex(int(pat))
+        buf[pos] = old
+    free()
+
+
+@pytest.mark.parametrize("p_dtype", ["bf16", "f16"])
+def test_narrowing_through_the_kernel(p_dtype):
+    """With lr = wd = 0 and g = 0 the master is unchanged and the 16-bit param is
+    its nearest-even rounding: the kernel's conversion against the oracle's on
+    4M random fp32 patterns plus rounding ties and range edges."""
+    rng = np.random.default_rng(13)
+    raw = rng.integers(0, 2 ** 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    x = raw.view(np.float32)
+    x = x[np.isfinite(x)]
+    ties = []
+    for hi in rng.integers(0, 1 << 16, size=4000, dtype=np.uint32):
+        for lo in (0x7FFF, 0x8000, 0x8001, 0x1000, 0x0FFF, 0x2000, 0x1FFF):
+            ties.append((int(hi) << 16) | lo)
+    t = np.array(ties, np.uint32).view(np.float32)
+    sp = np.array([65504.0, 65519.99, 65520.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14, 0.0, -0.0,
+                   np.finfo(np.float32).max, np.finfo(np.float32).tiny, 1e-45], np.float32)
+    w = np.concatenate([x, t[np.isfinite(t)], sp, -sp]).astype(np.float32)
+    n = w.size
+    dt = torch.float16 if p_dtype == "f16" else torch.bfloat16
+    master = torch.from_numpy(w).cuda()
+    p = torch.zeros(n, dtype=dt, device="cuda")
+    g = torch.zeros(n, dtype=dt, device="cuda")
+    m = torch.zeros(n, dtype=torch.float32, device="cuda")
+    v = torch.zeros(n, dtype=torch.float32, device="cuda")
+    step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hg, ho = hp_pair(lr=0.0, weight_decay=0.0)
+    A.adamw_step(A.MIXED, A.F16 if p_dtype == "f16" else A.BF16, n, p, g, m, v, master, hg, step)
+    torch.cuda.synchronize()
+    hm = w.copy()
+    hp16 = np.zeros(n, np.uint16)
+    oracle.adamw_mixed(hp16, np.zeros(n, np.uint16), hm, np.zeros(n, np.float32), np.zeros(n, np.float32),
+                       ho, 1, p_is_f16=p_dtype == "f16")
+    assert np.array_equal(to_np(master).view(np.uint32), w.view(np.uint32))
+    got = to_np(p)
+    assert np.array_equal(got, hp16), f"{np.count_nonzero(got != hp16)} conversions differ"
+    free()
+
+
+@pytest.mark.parametrize("p_dtype", ["bf16", "f16"])
+def test_widening_through_the_kernel(p_dtype):
+    """With beta1 = 0 the new first moment is the widened gradient: all 65,536
+    16-bit patterns (inf and NaN included) through the vector and element paths."""
+    allp = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    gbits = np.concatenate([allp, allp[:3]])          # 65539: vector body + a 3-element tail
+    n = gbits.size
+    dt = torch.float16 if p_dtype == "f16" else torch.bfloat16
+    g = torch.from_numpy(gbits.view(np.int16).copy()).cuda().view(dt)
+    p = torch.zeros(n, dtype=dt, device="cuda")
+    m = torch.zeros(n, dtype=torch.float32, device="cuda")
+    v = torch.zeros(n, dtype=torch.float32, device="cuda")
+    w = torch.zeros(n, dtype=torch.float32, device="cuda")
+    step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hg, ho = hp_pair(beta1=0.0)
+    A.adamw_step(A.MIXED, A.F16 if p_dtype == "f16" else A.BF16, n, p, g, m, v, w, hg, step)
+    hs = {"p": np.zeros(n, np.uint16), "g": gbits.copy(), "m": np.zeros(n, np.float32),
+          "v": np.zeros(n, np.float32), "master": np.zeros(n, np.float32)}
+    oracle.adamw_mixed(hs["p"], hs["g"], hs["master"], hs["m"], hs["v"], ho, 1, p_is_f16=p_dtype == "f16")
+    torch.cuda.synchronize()
+    for k, t in (("m", m), ("v", v), ("master", w)):
+        compare(f"widen-{k}", to_np(t), hs[k], True)
+    compare("widen-p", to_np(p), hs["p"], False, p_dtype == "f16")
+    free()
+
+
+def test_resume_is_bitwise():
+    """10 steps == 5 steps, copy every buffer and the counter to fresh memory, 5 more."""
+    numels = [3000, 17, 40000]
+    a = Case("kahan", numels, seed=1111, random_moments=True)
+    b = Case("kahan", numels, seed=1111, random_moments=True)
+    hg, _ = hp_pair()
+    for s in range(10):
+        if s:
+            a.refill_grads(s)
+        a.gpu_step(hg)
+    for s in range(5):
+        if s:
+            b.refill_grads(s)
+        b.gpu_step(hg)
+    # "checkpoint": move everything to new allocations
+    for k in list(b.arena.bufs):
+        b.arena.bufs[k] = b.arena.bufs[k].clone()
+    b.d_step = b.d_step.clone()
+    for s in range(5, 10):
+        b.refill_grads(s)
+        b.gpu_step(hg)
+    torch.cuda.synchronize()
+    assert int(a.d_step.item()) == int(b.d_step.item()) == 10
+    for k in a.keys:
+        assert torch.equal(a.arena.bufs[k], b.arena.bufs[k]), k
+    free()
+
+
+def test_side_streams_and_plan_cache():
+    """Work on two non-default streams with alternating lists: each stream keeps
+    its own workspace, and a list with new pointers is re-planned."""
+    hg, ho = hp_pair()
+    c1 = Case("mixed", [5000, 3], seed=1212)
+    c2 = Case("mixed", [5000, 3], seed=1313)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for it in range(3):
+        for case, st in ((c1, s1), (c2, s2), (c2, s1), (c1, s2)):
+            with torch.cuda.stream(st):
+                case.gpu_step(hg)
+            st.synchronize()
+            case.oracle_step(ho)
+    c1.compare_all("streams-c1")
+    c2.compare_all("streams-c2")
+    free()
+
+
+def test_invalid_calls_enqueue_nothing():
+    case = Case("mixed", [100, 200], seed=1414)
+    before = {k: v.clone() for k, v in case.arena.bufs.items()}
+    hg, _ = hp_pair()
+    bad = [
+        lambda: A.adamw_multi_tensor_step(A.MIXED, A.F32, case.tensor_list(), hg, case.d_step),
+        lambda: A.adamw_multi_tensor_step(A.PURE_KAHAN, A.F16, case.tensor_list(), hg, case.d_step),
+        lambda: A.adamw_multi_tensor_step(A.MIXED, A.BF16, case.tensor_list(0, 10_000), hg, case.d_step),
+        lambda: A.adamw_multi_tensor_step(A.MIXED, A.BF16, case.tensor_list(), A.HParams(beta1=1.0), case.d_step),
+        lambda: A.adamw_multi_tensor_step(A.MIXED, A.BF16, case.tensor_list(), A.HParams(eps=-1.0), case.d_step),
+        lambda: A.adamw_multi_tensor_step(A.MIXED, A.BF16, case.tensor_list(), A.HParams(lr=float("nan")),
+                                          case.d_step),
+        lambda: A.adamw_multi_tensor_step(A.MIXED, A.BF16, case.tensor_list(), hg, None),
+        lambda: A.adamw_step(A.MIXED, A.BF16, 100, case.arena.view("p", 0), None, case.arena.view("m", 0),
+                             case.arena.view("v", 0), case.arena.view("master", 0), hg, case.d_step),
+        lambda: A.adamw_step(A.MIXED, A.BF16, 100, case.arena.bufs["p"][1:].data_ptr() + 1, case.arena.bufs["g"],
+                             case.arena.bufs["m"], case.arena.bufs["v"], case.arena.bufs["master"], hg, case.d_step),
+    ]
+    for f in bad:
+        with pytest.raises(A.AdamWError):
+            f()
+    torch.cuda.synchronize()
+    assert int(case.d_step.item()) == 0
+    for k, v in before.items():
+        assert torch.equal(case.arena.bufs[k], v), k
+    free()
+
+
+def test_empty_list_advances_counter():
+    step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tl = A.TensorList([], [[], [], [], [], []])
+    hg, _ = hp_pair()
+    A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl, hg, step)
+    A.adamw_step(A.PURE_KAHAN, A.BF16, 0, None, None, None, None, None, hg, step)
+    flag = torch.ones(1, dtype=torch.int32, device="cuda")
+    A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl, hg, step, flag)
+    torch.cuda.synchronize()
+    assert int(step.item()) == 2
+    A.adamw_check_finite(A.F16, tl, flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0

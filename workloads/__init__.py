@@ -233,7 +233,9 @@ def refill_grads(arena: Arena, seed, step, *, p_dtype="bf16", loss_scale=1.0):
     g.copy_(grads(g.numel(), g.device, seed, step, dtype=half, scale=loss_scale))
 
 
-STREAMS = {"mixed": ("p", "g", "master", "m", "v"), "kahan": ("p", "g", "m", "v", "c")}
+# Buffers of each mode in the order of the C ABI's streams:
+# param, grad, exp_avg, exp_avg_sq, aux (fp32 master in mixed mode, bf16 Kahan compensation otherwise).
+STREAMS = {"mixed": ("p", "g", "m", "v", "master"), "kahan": ("p", "g", "m", "v", "c")}
 
 # Resident bytes per parameter of each stream layout (what one rank holds).
 RESIDENT_BYTES = {
