@@ -131,13 +131,31 @@ class Case:
         for k in self.keys:
             stats.append(compare(f"{label}:{k}", to_np(self.arena.bufs[k]), self.host[k],
                                  k in F32_KEYS[self.mode], self.p_dtype == "f16"))
+        log_stats(stats)
         return stats
+
+
+def log_stats(stats):
+    """Appends comparison statistics to $PARITY_STATS (JSON lines) when set."""
+    import json
+    import os
+    path = os.environ.get("PARITY_STATS")
+    if path:
+        with open(path, "a") as f:
+            for st in stats:
+                f.write(json.dumps(st) + "\n")
 
 
 def hp_pair(lr=2e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, inv_scale=1.0):
     """The same fp32 hyper-parameters for the library and the oracle."""
     f = [float(np.float32(x)) for x in (lr, beta1, beta2, eps, weight_decay, inv_scale)]
     return A.HParams(*f), oracle.HParams(*f)
+
+
+def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """Bitwise equality (torch.equal treats NaN as unequal to itself)."""
+    view = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[a.element_size()]
+    return a.dtype == b.dtype and torch.equal(a.view(view), b.view(view))
 
 
 def free():

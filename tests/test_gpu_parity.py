@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import Case, compare, free, hp_pair, to_np
+from gpu_util import Case, compare, free, hp_pair, same_bits, to_np
 
 import adamw_optimizer_step_apply_amd as A
 
@@ -96,7 +96,7 @@ def test_zero_shard_union_equals_full_step():
     torch.cuda.synchronize()
     assert [int(c.item()) for c in counters] == [1, 1, 1, 1]
     for k in parts.keys:
-        assert torch.equal(parts.arena.bufs[k], full.arena.bufs[k]), k
+        assert same_bits(parts.arena.bufs[k], full.arena.bufs[k]), k
     full.compare_all("union-full")
     free()
 
@@ -135,9 +135,9 @@ def test_flat_shard_buffers():
     A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl, hg, flat.d_step)
     ref.gpu_step(hg, shard=(b, e))
     torch.cuda.synchronize()
-    assert torch.equal(flat.arena.bufs["p"], ref.arena.bufs["p"])
+    assert same_bits(flat.arena.bufs["p"], ref.arena.bufs["p"])
     for k in ("m", "v", "master"):
-        assert torch.equal(shard[k], ref.arena.bufs[k][b:e]), k
+        assert same_bits(shard[k], ref.arena.bufs[k][b:e]), k
     free()
 
 
@@ -154,7 +154,7 @@ def test_skip_flag_leaves_everything_unchanged():
     torch.cuda.synchronize()
     assert int(case.d_step.item()) == 1
     for k, v in before.items():
-        assert torch.equal(case.arena.bufs[k], v), k
+        assert same_bits(case.arena.bufs[k], v), k
     flag.zero_()
     case.gpu_step(hg, found_inf=flag)
     case.oracle_step(ho)
@@ -194,7 +194,7 @@ def test_check_finite_and_skip(g_dtype, bad):
         torch.cuda.synchronize()
         assert int(case.d_step.item()) == 0
         for k, v in before.items():
-            assert torch.equal(case.arena.bufs[k], v), k
+            assert same_bits(case.arena.bufs[k], v), k
         view[j] = old
     A.adamw_check_finite(A.F16 if g_dtype == "f16" else A.BF16, tl, flag)
     torch.cuda.synchronize()
@@ -325,7 +325,7 @@ def test_resume_is_bitwise():
     torch.cuda.synchronize()
     assert int(a.d_step.item()) == int(b.d_step.item()) == 10
     for k in a.keys:
-        assert torch.equal(a.arena.bufs[k], b.arena.bufs[k]), k
+        assert same_bits(a.arena.bufs[k], b.arena.bufs[k]), k
     free()
 
 
@@ -372,7 +372,7 @@ def test_invalid_calls_enqueue_nothing():
     torch.cuda.synchronize()
     assert int(case.d_step.item()) == 0
     for k, v in before.items():
-        assert torch.equal(case.arena.bufs[k], v), k
+        assert same_bits(case.arena.bufs[k], v), k
     free()
 
 
