@@ -25,7 +25,7 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m adamw_optimizer_step_apply_amd.build` "
                       "(or __graft_entry__.build())")
 
-_lib = ctypes.CDLL(LIB_PATH)
+_lib = None
 
 # enums of adamw.h
 OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_HIP = 0, 1, 2, 3, 4
@@ -51,25 +51,39 @@ class adamw_tensor_list(ctypes.Structure):
 
 
 _vp = ctypes.c_void_p
-_lib.adamw_step.restype = ctypes.c_int
-_lib.adamw_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp,
-                            ctypes.POINTER(adamw_hparams), _vp, _vp, _vp]
-_lib.adamw_multi_tensor_step.restype = ctypes.c_int
-_lib.adamw_multi_tensor_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list),
-                                         ctypes.POINTER(adamw_hparams), _vp, _vp, _vp]
-_lib.adamw_check_finite.restype = ctypes.c_int
-_lib.adamw_check_finite.argtypes = [ctypes.c_int, ctypes.POINTER(adamw_tensor_list), _vp, _vp]
-_lib.adamw_last_error.restype = ctypes.c_char_p
-_lib.adamw_last_error.argtypes = []
-_lib.adamw_release_workspace.restype = None
-_lib.adamw_release_workspace.argtypes = []
-_lib.adamw_abi_version.restype = ctypes.c_int
-_lib.adamw_abi_version.argtypes = []
-_lib.adamw_plan_inspect.restype = ctypes.c_int64
-_lib.adamw_plan_inspect.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list), ctypes.c_int,
-                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
-_lib.adamw_set_chunk_elems.restype = ctypes.c_int64
-_lib.adamw_set_chunk_elems.argtypes = [ctypes.c_int64]
+
+
+def _load(path: str) -> None:
+    """Loads the library at ``path`` and declares its C signatures."""
+    global _lib
+    lib = ctypes.CDLL(path)
+    _declare(lib)
+    _lib = lib
+
+
+def _declare(_lib):
+    _lib.adamw_step.restype = ctypes.c_int
+    _lib.adamw_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp,
+                                ctypes.POINTER(adamw_hparams), _vp, _vp, _vp]
+    _lib.adamw_multi_tensor_step.restype = ctypes.c_int
+    _lib.adamw_multi_tensor_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list),
+                                             ctypes.POINTER(adamw_hparams), _vp, _vp, _vp]
+    _lib.adamw_check_finite.restype = ctypes.c_int
+    _lib.adamw_check_finite.argtypes = [ctypes.c_int, ctypes.POINTER(adamw_tensor_list), _vp, _vp]
+    _lib.adamw_last_error.restype = ctypes.c_char_p
+    _lib.adamw_last_error.argtypes = []
+    _lib.adamw_release_workspace.restype = None
+    _lib.adamw_release_workspace.argtypes = []
+    _lib.adamw_abi_version.restype = ctypes.c_int
+    _lib.adamw_abi_version.argtypes = []
+    _lib.adamw_plan_inspect.restype = ctypes.c_int64
+    _lib.adamw_plan_inspect.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list), ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
+    _lib.adamw_set_chunk_elems.restype = ctypes.c_int64
+    _lib.adamw_set_chunk_elems.argtypes = [ctypes.c_int64]
+
+
+_load(LIB_PATH)
 
 
 class AdamWError(RuntimeError):

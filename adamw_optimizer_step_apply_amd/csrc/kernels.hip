@@ -180,7 +180,56 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
 // Update kernel
 // ---------------------------------------------------------------------------
 
-constexpr int kUnroll = 2;
+// Packs each lane loads before computing (memory-level parallelism), and the
+// cache policy of the streaming accesses per mode: bit 0 = non-temporal loads,
+// bit 1 = non-temporal stores (every element is touched exactly once per step).
+#ifndef ADAMW_UNROLL
+#define ADAMW_UNROLL 1
+#endif
+#ifndef ADAMW_NT_MIXED
+#define ADAMW_NT_MIXED 2
+#endif
+#ifndef ADAMW_NT_KAHAN
+#define ADAMW_NT_KAHAN 3
+#endif
+#ifndef ADAMW_NT_CHECK
+#define ADAMW_NT_CHECK 1
+#endif
+
+template <int NT, typename T>
+__device__ __forceinline__ T ld(const GLOBAL T* p)
+{
+    if constexpr (NT & 1) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <int NT, typename T>
+__device__ __forceinline__ void st(GLOBAL T* p, T v)
+{
+    if constexpr (NT & 2) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+#ifndef ADAMW_XCD_SWIZZLE
+#define ADAMW_XCD_SWIZZLE 1
+#endif
+constexpr int kUnroll = ADAMW_UNROLL;
+
+// Workgroup -> chunk.  The dispatcher hands workgroup b to XCD b % 8 (the
+// MI355X has 8 XCDs).  With the swizzle, XCD x walks one contiguous run of
+// chunks, so the workgroups in flight on an XCD stream neighbouring addresses.
+// The map is a bijection on [0, nb) for any nb: XCD x owns q + (x < r) chunks,
+// q = nb / 8, r = nb % 8.
+__device__ __forceinline__ uint32_t chunk_index(uint32_t b, uint32_t nb)
+{
+#if ADAMW_XCD_SWIZZLE
+    const uint32_t q = nb >> 3, r = nb & 7u, x = b & 7u, j = b >> 3;
+    return x * q + (x < r ? x : r) + j;
+#else
+    (void)nb;
+    return b;
+#endif
+}
 
 __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
 {
@@ -198,16 +247,26 @@ __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
     return c;
 }
 
+#ifndef ADAMW_WPE
+#define ADAMW_WPE 0
+#endif
+#if ADAMW_WPE
+#define ADAMW_WPE_ATTR __attribute__((amdgpu_waves_per_eu(1, ADAMW_WPE)))
+#else
+#define ADAMW_WPE_ATTR
+#endif
+
 // MODE 0: mixed bf16, 1: mixed fp16, 2: pure bf16 + Kahan
 template <int MODE>
-__global__ __launch_bounds__(kBlock) void update_kernel(const DevSeg* __restrict__ segs,
+__global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const DevSeg* __restrict__ segs,
                                                         const DevChunk* __restrict__ chunks,
                                                         const LaunchScalars* __restrict__ sc)
 {
     if (sc->skip) return;
     constexpr bool F16 = (MODE == 1);
+    constexpr int NTM = ADAMW_NT_MIXED, NTK = ADAMW_NT_KAHAN;
     const Coef c = load_coef(sc);
-    const DevChunk ch = chunks[blockIdx.x];
+    const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
     const DevSeg& sg = segs[ch.seg];
     const uint32_t n = ch.n_kind & kCountMask;
     const uint64_t off = ch.off;
@@ -233,10 +292,10 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const DevSeg* __restrict
                 for (int u = 0; u < kUnroll; ++u) {
                     const uint32_t k = k0 + u * kBlock;
                     if (k < npack) {
-                        G[u] = g4[k];
-                        W[u][0] = w4[2 * k]; W[u][1] = w4[2 * k + 1];
-                        M[u][0] = m4[2 * k]; M[u][1] = m4[2 * k + 1];
-                        V[u][0] = v4[2 * k]; V[u][1] = v4[2 * k + 1];
+                        G[u] = ld<NTM>(g4 + k);
+                        W[u][0] = ld<NTM>(w4 + 2 * k); W[u][1] = ld<NTM>(w4 + 2 * k + 1);
+                        M[u][0] = ld<NTM>(m4 + 2 * k); M[u][1] = ld<NTM>(m4 + 2 * k + 1);
+                        V[u][0] = ld<NTM>(v4 + 2 * k); V[u][1] = ld<NTM>(v4 + 2 * k + 1);
                     }
                 }
 #pragma unroll
@@ -255,10 +314,10 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const DevSeg* __restrict
                             const float b = mixed_elem(gg.y, wf[2 * j + 1], mf[2 * j + 1], vf[2 * j + 1], c);
                             pw[j] = narrow2<F16>(a, b);
                         }
-                        w4[2 * k] = W[u][0]; w4[2 * k + 1] = W[u][1];
-                        m4[2 * k] = M[u][0]; m4[2 * k + 1] = M[u][1];
-                        v4[2 * k] = V[u][0]; v4[2 * k + 1] = V[u][1];
-                        p4[k] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+                        st<NTM>(w4 + 2 * k, W[u][0]); st<NTM>(w4 + 2 * k + 1, W[u][1]);
+                        st<NTM>(m4 + 2 * k, M[u][0]); st<NTM>(m4 + 2 * k + 1, M[u][1]);
+                        st<NTM>(v4 + 2 * k, V[u][0]); st<NTM>(v4 + 2 * k + 1, V[u][1]);
+                        st<NTM>(p4 + k, u32x4{pw[0], pw[1], pw[2], pw[3]});
                     }
                 }
             }
@@ -291,7 +350,8 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const DevSeg* __restrict
                 for (int u = 0; u < kUnroll; ++u) {
                     const uint32_t k = k0 + u * kBlock;
                     if (k < npack) {
-                        G[u] = g4[k]; P[u] = p4[k]; M[u] = m4[k]; V[u] = v4[k]; C[u] = c4[k];
+                        G[u] = ld<NTK>(g4 + k); P[u] = ld<NTK>(p4 + k); M[u] = ld<NTK>(m4 + k); V[u] = ld<NTK>(v4 + k);
+                        C[u] = ld<NTK>(c4 + k);
                     }
                 }
 #pragma unroll
@@ -320,10 +380,10 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const DevSeg* __restrict
                             mo[j] = narrow2<false>(ma, mb);
                             vo[j] = narrow2<false>(va, vb);
                         }
-                        p4[k] = u32x4{po[0], po[1], po[2], po[3]};
-                        m4[k] = u32x4{mo[0], mo[1], mo[2], mo[3]};
-                        v4[k] = u32x4{vo[0], vo[1], vo[2], vo[3]};
-                        c4[k] = u32x4{co[0], co[1], co[2], co[3]};
+                        st<NTK>(p4 + k, u32x4{po[0], po[1], po[2], po[3]});
+                        st<NTK>(m4 + k, u32x4{mo[0], mo[1], mo[2], mo[3]});
+                        st<NTK>(v4 + k, u32x4{vo[0], vo[1], vo[2], vo[3]});
+                        st<NTK>(c4 + k, u32x4{co[0], co[1], co[2], co[3]});
                     }
                 }
             }
@@ -366,7 +426,7 @@ __global__ __launch_bounds__(kBlock) void check_kernel(const DevSeg* __restrict_
                                                        int32_t* __restrict__ flag)
 {
     constexpr uint32_t EXP = F16 ? 0x7c00u : 0x7f80u;
-    const DevChunk ch = chunks[blockIdx.x];
+    const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
     const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(segs[ch.seg].ptr[ADAMW_STREAM_GRAD], ch.off);
     const uint32_t n = ch.n_kind & kCountMask;
     uint32_t bad = 0;
@@ -374,7 +434,7 @@ __global__ __launch_bounds__(kBlock) void check_kernel(const DevSeg* __restrict_
         const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
         const uint32_t npack = n / kPack;
         for (uint32_t k = threadIdx.x; k < npack; k += kBlock) {
-            const u32x4 q = g4[k];
+            const u32x4 q = ld<ADAMW_NT_CHECK>(g4 + k);
             bad |= nonfinite2<EXP>(q.x) | nonfinite2<EXP>(q.y) | nonfinite2<EXP>(q.z) | nonfinite2<EXP>(q.w);
         }
     } else {
@@ -396,17 +456,29 @@ hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32
     return hipGetLastError();
 }
 
+// Occupancy cap, per mode: the update kernel uses no LDS, but reserving this
+// much per workgroup leaves room for only 160 KiB / bytes workgroups on a CU.
+// Measured on MI355X with the OPT-1.3B list, two resident workgroups per CU
+// (eight waves) stream faster than the register-limited five or six: fewer
+// concurrent streams keep more DRAM rows open.
+#ifndef ADAMW_LDS_MIXED
+#define ADAMW_LDS_MIXED 81920
+#endif
+#ifndef ADAMW_LDS_KAHAN
+#define ADAMW_LDS_KAHAN 81920
+#endif
+
 hipError_t launch_update(adamw_mode mode, adamw_dtype p_dtype, const DevSeg* segs, const DevChunk* chunks,
                          int64_t n_chunks, const LaunchScalars* d_scalars, hipStream_t stream)
 {
     if (n_chunks <= 0) return hipSuccess;
     const dim3 grid((unsigned)n_chunks), block(kBlock);
     if (mode == ADAMW_PURE_KAHAN)
-        hipLaunchKernelGGL(update_kernel<2>, grid, block, 0, stream, segs, chunks, d_scalars);
+        hipLaunchKernelGGL(update_kernel<2>, grid, block, ADAMW_LDS_KAHAN, stream, segs, chunks, d_scalars);
     else if (p_dtype == ADAMW_F16)
-        hipLaunchKernelGGL(update_kernel<1>, grid, block, 0, stream, segs, chunks, d_scalars);
+        hipLaunchKernelGGL(update_kernel<1>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
     else
-        hipLaunchKernelGGL(update_kernel<0>, grid, block, 0, stream, segs, chunks, d_scalars);
+        hipLaunchKernelGGL(update_kernel<0>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
     return hipGetLastError();
 }
 

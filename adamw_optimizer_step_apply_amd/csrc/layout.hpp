@@ -18,7 +18,7 @@ constexpr int kBlock = 256;            // threads per workgroup: four wave64s
 constexpr int kPack = 8;               // elements per lane per dwordx4 of a 16-bit stream
 constexpr uint32_t kVecBit = 0x80000000u;
 constexpr uint32_t kCountMask = 0x7fffffffu;
-constexpr int64_t kDefaultChunkElems = 16384;   // vector chunk: 8 packs per lane
+constexpr int64_t kDefaultChunkElems = 2048;    // vector chunk: one pack per lane, one pass
 constexpr int64_t kElemChunkElems = 4096;       // element chunk: 16 elements per lane
 
 // One segment: the device address of its element 0 in each stream (0 for a

@@ -135,7 +135,7 @@ def test_plan_partitions_random_lists(seed):
         ptrs.append([base + int(o) * esz[s] + 256 * i for i, o in enumerate(offs)])
     tl = A.TensorList(numels, ptrs, b, e if rng.random() < 0.8 or e != total else -1)
     rows = A.adamw_plan_inspect(mode, A.BF16, tl)
-    check_plan(rows, numels, b, e, ptrs, esz, 16384)
+    check_plan(rows, numels, b, e, ptrs, esz, A.adamw_set_chunk_elems(0))
     if seed % 3 == 0:
         # all streams at one phase: at most 2 element rows per segment
         segs = {}
@@ -159,7 +159,7 @@ def test_plan_bert_shards():
         b, e = wl.shard(r)
         tl = A.TensorList(numels, ptrs, b, e)
         rows = A.adamw_plan_inspect(A.MIXED, A.BF16, tl)
-        check_plan(rows, numels, b, e, ptrs, esz, 16384)
+        check_plan(rows, numels, b, e, ptrs, esz, A.adamw_set_chunk_elems(0))
         nseg.append(len({row[5] for row in rows}))
     assert nseg[0] == 1 and all(n > 1 for n in nseg[1:])
 
@@ -177,12 +177,12 @@ def test_chunk_size_knob():
     numels = [100_000]
     tl = _tl(numels)
     try:
-        assert A.adamw_set_chunk_elems(4096) == 4096
+        assert A.adamw_set_chunk_elems(8192) == 8192
         rows = A.adamw_plan_inspect(A.MIXED, A.BF16, tl)
-        assert max(r[2] for r in rows) == 4096
+        assert max(r[2] for r in rows) == 8192
         with pytest.raises(A.AdamWError):
             A.adamw_set_chunk_elems(1000)
     finally:
         A.adamw_set_chunk_elems(0)
     rows = A.adamw_plan_inspect(A.MIXED, A.BF16, tl)
-    assert max(r[2] for r in rows) == 16384
+    assert max(r[2] for r in rows) == A.adamw_set_chunk_elems(0) == 2048
