@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 #include <map>
 #include <memory>
@@ -77,9 +78,14 @@ struct PlanSlot {
     }
 };
 
+// Plans cached per stream, most recently used first.  A training loop that
+// alternates a few lists (e.g. two parameter groups, or a step and its
+// overflow check) keeps each one's table resident instead of re-uploading it.
+constexpr size_t kPlansPerStream = 8;
+
 struct StreamWorkspace {
     LaunchScalars* scalars = nullptr;   // device, kScalarsBytes
-    PlanSlot step, check;
+    std::vector<std::unique_ptr<PlanSlot>> plans;
     std::mutex mu;                      // one call at a time per stream
 };
 
@@ -99,14 +105,27 @@ adamw_status get_workspace(hipStream_t stream, StreamWorkspace** out)
     return ADAMW_OK;
 }
 
-// Makes `slot` hold the plan of (mode, dtype, list, for_check), re-planning and
-// uploading only if any input differs from the cached one.
-adamw_status ensure_plan(PlanSlot& slot, adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
-                         bool for_check, int64_t chunk_elems, hipStream_t stream)
+// Returns (in *out) a slot of `ws` holding the device plan of (mode, dtype,
+// list, for_check): a cached one if every input matches, else the least
+// recently used slot, re-planned and re-uploaded.
+adamw_status ensure_plan(StreamWorkspace& ws, adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
+                         bool for_check, int64_t chunk_elems, hipStream_t stream, PlanSlot** out)
 {
     std::vector<int64_t> key;
     plan_key(mode, p_dtype, list, for_check, chunk_elems, key);
-    if (slot.valid && key == slot.key) return ADAMW_OK;
+    auto& plans = ws.plans;
+    for (size_t i = 0; i < plans.size(); ++i) {
+        if (plans[i]->valid && plans[i]->key == key) {
+            std::rotate(plans.begin(), plans.begin() + (ptrdiff_t)i, plans.begin() + (ptrdiff_t)i + 1);
+            *out = plans.front().get();
+            return ADAMW_OK;
+        }
+    }
+    if (plans.size() < kPlansPerStream) plans.emplace_back(new PlanSlot());
+    std::rotate(plans.begin(), plans.end() - 1, plans.end());   // LRU slot to the front
+    PlanSlot& slot = *plans.front();
+    slot.valid = false;
+    *out = &slot;
 
     Plan plan;
     std::string err;
@@ -212,10 +231,11 @@ adamw_status do_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_li
         e = hipMalloc(reinterpret_cast<void**>(&ws->scalars), kScalarsBytes);
         if (e != hipSuccess) { ws->scalars = nullptr; return fail(ADAMW_E_NOMEM, "hipMalloc of the scalar block failed"); }
     }
-    if ((st = ensure_plan(ws->step, mode, p_dtype, list, false, chunk_elems, stream)) != ADAMW_OK) return st;
+    PlanSlot* plan = nullptr;
+    if ((st = ensure_plan(*ws, mode, p_dtype, list, false, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
     e = launch_prologue(*hp, d_step, d_found_inf, ws->scalars, stream);
     if (e != hipSuccess) return hip_fail("prologue launch", e);
-    e = launch_update(mode, p_dtype, ws->step.segs(), ws->step.chunks(), ws->step.n_chunks, ws->scalars, stream);
+    e = launch_update(mode, p_dtype, plan->segs(), plan->chunks(), plan->n_chunks, ws->scalars, stream);
     if (e != hipSuccess) return hip_fail("update launch", e);
     return ADAMW_OK;
 }
@@ -283,9 +303,10 @@ adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* gr
     StreamWorkspace* ws = nullptr;
     if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
     std::lock_guard<std::mutex> lk(ws->mu);
-    if ((st = ensure_plan(ws->check, ADAMW_MIXED, g_dtype, grads, true, chunk_elems, stream)) != ADAMW_OK)
+    PlanSlot* plan = nullptr;
+    if ((st = ensure_plan(*ws, ADAMW_MIXED, g_dtype, grads, true, chunk_elems, stream, &plan)) != ADAMW_OK)
         return st;
-    hipError_t e = launch_check(g_dtype, ws->check.segs(), ws->check.chunks(), ws->check.n_chunks, d_found_inf, stream);
+    hipError_t e = launch_check(g_dtype, plan->segs(), plan->chunks(), plan->n_chunks, d_found_inf, stream);
     if (e != hipSuccess) return hip_fail("check launch", e);
     return ADAMW_OK;
 }
@@ -299,8 +320,8 @@ void adamw_release_workspace(void)
         StreamWorkspace* ws = kv.second.get();
         if (ws->scalars) (void)hipFree(ws->scalars);
         ws->scalars = nullptr;
-        ws->step.release();
-        ws->check.release();
+        for (auto& p : ws->plans) p->release();
+        ws->plans.clear();
     }
     g_ws.clear();
 }

@@ -389,3 +389,18 @@ def test_empty_list_advances_counter():
     A.adamw_check_finite(A.F16, tl, flag)
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
+
+
+def test_plan_cache_eviction_cycle():
+    """More lists than the per-stream plan cache holds, cycled twice on one
+    stream: every call must use its own list's table (evicted ones re-planned)."""
+    hg, ho = hp_pair()
+    cases = [Case("mixed" if i % 2 else "kahan", [3000 + 97 * i, 5 + i, 17000 - 31 * i], seed=1500 + i)
+             for i in range(11)]
+    for rnd in range(2):
+        for c in cases:
+            c.gpu_step(hg)
+            c.oracle_step(ho)
+    for i, c in enumerate(cases):
+        c.compare_all(f"evict-{i}")
+    free()
