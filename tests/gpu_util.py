@@ -161,3 +161,77 @@ def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
 def free():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+
+
+class SampledCase:
+    """A full-size workload on the GPU with the oracle following a sample of its
+    elements.  The update is elementwise, so the oracle stepping only the sampled
+    elements (with the same per-step scalars) is exact for them.
+
+    Samples: the first and last 8 elements of every tensor, plus ``n_random``
+    uniform positions of the flat list; optionally restricted bookkeeping for a
+    ZeRO shard [b, e): samples outside it must come back unchanged."""
+
+    def __init__(self, mode, numels, seed, *, p_dtype="bf16", loss_scale=1.0, n_random=1 << 21,
+                 shard=(0, -1), device="cuda"):
+        self.mode, self.p_dtype, self.seed, self.loss_scale = mode, p_dtype, seed, loss_scale
+        self.numels = [int(n) for n in numels]
+        self.arena = workloads.make_state(mode, self.numels, device, seed, p_dtype=p_dtype, align_elems=128,
+                                          loss_scale=loss_scale)
+        self.keys = workloads.STREAMS[mode]
+        total = sum(self.numels)
+        b, e = shard[0], (total if shard[1] < 0 else shard[1])
+        self.shard = (b, shard[1])
+        starts = np.concatenate([[0], np.cumsum(self.numels)]).astype(np.int64)
+        rng = np.random.default_rng(np.random.SeedSequence([seed, 77]))
+        flat = [rng.integers(0, total, size=n_random, dtype=np.int64)]
+        for i, n in enumerate(self.numels):
+            k = min(8, n)
+            flat.append(starts[i] + np.arange(k))
+            flat.append(starts[i] + n - k + np.arange(k))
+        flat = np.unique(np.concatenate(flat))
+        tens = np.searchsorted(starts, flat, side="right") - 1
+        arena_idx = np.asarray(self.arena.offsets, np.int64)[tens] + (flat - starts[tens])
+        self.flat = flat
+        self.inside = (flat >= b) & (flat < e)
+        self.idx = torch.from_numpy(arena_idx).to(device)
+        self.host = {k: to_np(self.arena.bufs[k][self.idx]) for k in self.keys}
+        self.initial = {k: v.copy() for k, v in self.host.items()}
+        self.d_step = torch.zeros(1, dtype=torch.int32, device=device)
+        self.step = 0
+
+    def tensor_list(self):
+        streams = [[self.arena.view(k, i) for i in range(len(self.numels))] for k in self.keys]
+        return A.TensorList(self.numels, streams, *self.shard)
+
+    def refill_grads(self, step_index):
+        workloads.refill_grads(self.arena, self.seed, step_index, p_dtype=self.p_dtype, loss_scale=self.loss_scale)
+        self.host["g"] = to_np(self.arena.bufs["g"][self.idx])
+
+    def oracle_step(self, ho: oracle.HParams, skip=False):
+        if skip:
+            return
+        t = self.step + 1
+        sel = np.flatnonzero(self.inside)
+        sub = {k: np.ascontiguousarray(self.host[k][sel]) for k in self.keys}
+        if self.mode == "mixed":
+            oracle.adamw_mixed(sub["p"], sub["g"], sub["master"], sub["m"], sub["v"], ho, t,
+                               p_is_f16=self.p_dtype == "f16")
+        else:
+            oracle.adamw_kahan(sub["p"], sub["g"], sub["m"], sub["v"], sub["c"], ho, t)
+        for k in self.keys:
+            self.host[k][sel] = sub[k]
+        self.step = t
+
+    def compare_all(self, label=""):
+        torch.cuda.synchronize()
+        assert int(self.d_step.item()) == self.step, f"{label}: step counter {int(self.d_step.item())} != {self.step}"
+        stats = []
+        for k in self.keys:
+            got = to_np(self.arena.bufs[k][self.idx])
+            stats.append(compare(f"{label}:{k}", got, self.host[k], k in F32_KEYS[self.mode], self.p_dtype == "f16"))
+            out = ~self.inside
+            if k != "g" and out.any():
+                assert np.array_equal(got[out], self.initial[k][out]), f"{label}:{k} changed outside the shard"
+        log_stats(stats)
+        return stats

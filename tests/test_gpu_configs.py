@@ -1,0 +1,138 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration that
+bench.py times (allocation-aligned arenas, default chunking).  The oracle follows
+sampled elements (every tensor's first and last 8 plus ~2M uniform positions) or,
+where it finishes in seconds, every element.  Bar: see gpu_util."""
+import numpy as np
+import pytest
+import torch
+
+import adamw_optimizer_step_apply_amd as A
+import oracle
+import workloads
+from gpu_util import Case, SampledCase, free, hp_pair, same_bits, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def test_bert_rank0_shard_all_elements_20_steps():
+    """The BERT list at DP=4, rank 0's shard (13,059,840 elements, inside the
+    word embedding), 20 steps, compared element by element over the whole list
+    (the other ranks' elements must stay untouched)."""
+    wl = workloads.get("bert_52m")
+    b, e = wl.shard(0)
+    case = Case("mixed", wl.numels, seed=2001)
+    hg, ho = hp_pair()
+    for s in range(wl.steps):
+        if s:
+            case.refill_grads(s)
+        case.gpu_step(hg, shard=(b, e))
+        case.oracle_step(ho, shard=(b, e))
+    stats = case.compare_all("bert-r0")
+    _print(stats)
+    free()
+
+
+@pytest.mark.parametrize("rank", [1, 2, 3])
+def test_bert_other_rank_shards_sampled(rank):
+    """Ranks 1-3: shards that start and end inside tensors and span several."""
+    wl = workloads.get("bert_52m")
+    shard = wl.shard(rank)
+    case = SampledCase("mixed", wl.numels, seed=2100 + rank, shard=shard, n_random=1 << 20)
+    hg, ho = hp_pair()
+    tl = case.tensor_list()
+    for s in range(wl.steps):
+        if s:
+            case.refill_grads(s)
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl, hg, case.d_step)
+        case.oracle_step(ho)
+    _print(case.compare_all(f"bert-r{rank}"))
+    free()
+
+
+def test_opt125m_kahan_100_steps_warmup():
+    """OPT-125m list, pure bf16 + Kahan, 100 steps of the linear warmup schedule
+    (lr 2e-4 * t/500), a fresh seeded gradient every step."""
+    wl = workloads.get("opt_125m")
+    case = SampledCase("kahan", wl.numels, seed=3001)
+    tl = case.tensor_list()
+    for s in range(wl.steps):
+        if s:
+            case.refill_grads(s)
+        lr = oracle.warmup_linear_lr(s + 1)
+        hg, ho = hp_pair(lr=lr)
+        A.adamw_multi_tensor_step(A.PURE_KAHAN, A.BF16, tl, hg, case.d_step)
+        case.oracle_step(ho)
+        if s + 1 in (10, 100):
+            _print(case.compare_all(f"opt125m-t{s + 1}"))
+    free()
+
+
+@pytest.mark.parametrize("mode", ["mixed", "kahan"])
+def test_opt13b_full_size_10_steps(mode):
+    """OPT-1.3B list (1,315,753,984 params), 10 steps, the shape bench.py times."""
+    wl = workloads.get("opt_1_3b")
+    case = SampledCase(mode, wl.numels, seed=4001 if mode == "mixed" else 4002)
+    tl = case.tensor_list()
+    hg, ho = hp_pair()
+    code = A.MIXED if mode == "mixed" else A.PURE_KAHAN
+    for s in range(wl.steps):
+        if s:
+            case.refill_grads(s)
+        A.adamw_multi_tensor_step(code, A.BF16, tl, hg, case.d_step)
+        case.oracle_step(ho)
+    _print(case.compare_all(f"opt13b-{mode}"))
+    del case, tl
+    free()
+
+
+def _host_any_nonfinite(g: torch.Tensor, block=1 << 28) -> bool:
+    for i in range(0, g.numel(), block):
+        if oracle.any_nonfinite(to_np(g[i:i + block]), True):
+            return True
+    return False
+
+
+def test_ragged_10k_fp16_overflow_skip():
+    """10,000 tensors, log-uniform sizes in [1, 2^22] (2.77e9 elements), fp16
+    params and grads scaled by 65536, fp32 master/m/v.  Every step runs the
+    overflow check, then the step with the flag.  One seeded step plants +inf at
+    a seeded tensor and element: the flag must be set (as the oracle's scan of
+    all gradients says) and every buffer and the counter left bit-identical."""
+    wl = workloads.get("ragged_10k")
+    scale = wl.loss_scale
+    case = SampledCase("mixed", wl.numels, seed=5001, p_dtype="f16", loss_scale=scale, n_random=1 << 21)
+    tl = case.tensor_list()
+    hg, ho = hp_pair(inv_scale=1.0 / scale)
+    rng = np.random.default_rng(np.random.SeedSequence([5, 1]))
+    inject_step = int(rng.integers(1, wl.steps + 1))
+    t_inj = int(rng.integers(0, len(wl.numels)))
+    e_inj = int(rng.integers(0, wl.numels[t_inj]))
+    _print("inject at step", inject_step, "tensor", t_inj, "element", e_inj, "of", wl.numels[t_inj])
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for s in range(wl.steps + 1):
+        if s:
+            case.refill_grads(s)
+        if s == inject_step:
+            case.arena.view("g", t_inj)[e_inj] = float("inf")
+        A.adamw_check_finite(A.F16, tl, flag)
+        torch.cuda.synchronize()
+        want = _host_any_nonfinite(case.arena.bufs["g"])
+        assert int(flag.item()) == int(want) == int(s == inject_step), (s, int(flag.item()), want)
+        if want:
+            before = {k: case.arena.bufs[k].clone() for k in ("p", "m", "v", "master")}
+            step_before = int(case.d_step.item())
+        A.adamw_multi_tensor_step(A.MIXED, A.F16, tl, hg, case.d_step, flag)
+        case.oracle_step(ho, skip=want)
+        if want:
+            torch.cuda.synchronize()
+            assert int(case.d_step.item()) == step_before
+            for k, v in before.items():
+                assert same_bits(case.arena.bufs[k], v), f"{k} changed on a skipped step"
+            del before
+    _print(case.compare_all("ragged10k"))
+    del case, tl
+    free()
