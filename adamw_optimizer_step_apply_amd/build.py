@@ -34,23 +34,32 @@ FLAGS = [
 ]
 
 
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "libbench_probe.so")
+
+
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+    _hipcc([os.path.join(CSRC, s) for s in SOURCES], LIB_PATH, verbose)
+    # the benchmark's memory-ceiling probes (never loaded by the library)
+    _hipcc([PROBE_SRC], PROBE_LIB, verbose)
+    return LIB_PATH
+
+
+def _hipcc(srcs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed ({r.returncode}) building {LIB_NAME}")
+        raise RuntimeError(f"hipcc failed ({r.returncode}) building {os.path.basename(out)}")
     # the host pass does not know the gfx feature name; anything else is worth seeing
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
     rest = [ln for ln in (r.stdout + r.stderr).splitlines() if ln.strip() and noise not in ln]
     if rest:
         sys.stderr.write("\n".join(rest) + "\n")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":

@@ -12,16 +12,20 @@ reused across steps.
 value = parameter updates per second over the timed steps (2 x N per step, one
 per mode), in Gparam/s.  Alongside it: per-mode Gparam/s and algorithmic HBM
 GB/s (28 B/param mixed, 18 B/param Kahan), the roofline of the dominant kernel
-(the mixed update) from HIP events recorded on the launch stream, and the CPU
-oracle timed on a bounded sample on the host cores.
+(the mixed update) from HIP events recorded on the launch stream, the same-mix
+ceiling measured by bench_probe.hip, and the CPU oracle timed on a bounded
+sample on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu]
-       python bench.py --calib-copy     (plain device copy of known size, for
-                                         scaling the rocprofv3 byte counters)
+Usage:
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-probe]
+  python bench.py --workload ragged_10k --modes f16amp   (overflow check + fp16 step, 10k tensors)
+  python bench.py --probe-only                            (memory ceilings only)
+  python bench.py --calib-copy                            (plain 4 GiB copy, to scale rocprofv3 byte counters)
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -31,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published peak
-BYTES = {"mixed": 28, "kahan": 18}
+BYTES = {"mixed": 28, "kahan": 18, "f16amp": 28, "check": 2}
 
 
 def parse():
@@ -40,10 +44,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="opt_1_3b")
-    ap.add_argument("--modes", default="mixed,kahan")
+    ap.add_argument("--modes", default=None, help="comma list of mixed,kahan,f16amp")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-probe", action="store_true", help="skip the same-mix ceiling probes")
+    ap.add_argument("--probe-only", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=160_000_000,
-                    help="elements of the OPT-1.3B list the oracle steps once per mode")
+                    help="elements of the list the oracle steps once per mode")
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--chunk-elems", type=int, default=0)
     return ap.parse_args()
@@ -62,44 +68,107 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes_each_way": n * 4, "launches": 3}), flush=True)
 
 
-def make_mode_state(mode, numels, device, seed):
+def _time_launches(fn, reps, stream):
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    fn()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return ms[len(ms) // 2]
+
+
+def probes(n, stream):
+    """Same-mix ceilings at n elements (median of 7 launches each), in GB/s."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "libbench_probe.so"))
+    lib.probe_launch.restype = ctypes.c_int
+    lib.probe_launch.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 5 + [ctypes.c_uint64, ctypes.c_void_p]
+    n = n // 8 * 8
+    s = stream.cuda_stream
+    out = {}
+
+    def run(kind, bufs, count, nbytes, name):
+        ptrs = [b.data_ptr() for b in bufs] + [0] * (5 - len(bufs))
+
+        def f():
+            rc = lib.probe_launch(kind, *ptrs, count, s)
+            if rc:
+                raise RuntimeError(f"probe launch failed: {rc}")
+        ms = _time_launches(f, 7, stream)
+        out[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+    dev = "cuda"
+    g = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    p = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    w, m, v = (torch.ones(n, dtype=torch.float32, device=dev) for _ in range(3))
+    run(0, [g, w, m, v, p], n, 28 * n, "mixed_mix")
+    del w, m, v
+    m16, v16, c16 = (torch.ones(n, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    run(1, [g, p, m16, v16, c16], n, 18 * n, "kahan_mix")
+    del g, p, m16, v16, c16
+    f = 1 << 31                                   # 8 GiB of fp32
+    src = torch.ones(f, dtype=torch.float32, device=dev)
+    dst = torch.zeros_like(src)
+    run(2, [src, dst], f, 8 * f, "copy")
+    run(3, [src, dst], f, 4 * f, "read")
+    run(4, [dst], f, 4 * f, "write")
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
     import workloads
-    arena = workloads.make_state(mode, numels, device, seed, align_elems=128)
+    arena = workloads.make_state(mode, numels, device, seed, align_elems=128, p_dtype=p_dtype,
+                                 loss_scale=loss_scale)
     keys = workloads.STREAMS[mode]
     streams = [[arena.view(k, i) for i in range(len(numels))] for k in keys]
     return arena, streams
 
 
-def cpu_baseline(numels, sample):
+def cpu_baseline(numels, sample, modes):
     """The oracle as it is (one host thread), one step per mode over the first
-    `sample` elements of the list; scaled to param-updates/s of the two-mode step."""
+    `sample` elements of the list; scaled to param-updates/s of the bench step."""
     import numpy as np
     import torch
 
     import oracle
     import workloads
     n = min(sample, sum(numels))
-    g = workloads.grads(n, "cpu", 7, 0, dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    w = workloads.normal(n, workloads.INIT_STD, "cpu", "master", 7).numpy()
     hp = oracle.HParams()
     secs = {}
-    p16 = np.zeros(n, np.uint16)
-    m = np.zeros(n, np.float32)
-    v = np.zeros(n, np.float32)
-    t0 = time.perf_counter()
-    oracle.adamw_mixed(p16, g, w, m, v, hp, 1)
-    secs["mixed"] = time.perf_counter() - t0
-    del m, v
-    pk = oracle.f32_to_bf16(w)
-    del w
-    mk, vk, ck = (np.zeros(n, np.uint16) for _ in range(3))
-    t0 = time.perf_counter()
-    oracle.adamw_kahan(pk, g, mk, vk, ck, hp, 1)
-    secs["kahan"] = time.perf_counter() - t0
-    per_param = secs["mixed"] / n + secs["kahan"] / n
-    return {"value": round(2.0 / per_param / 1e9, 4), "unit": "Gparam/s", "cores": 1, "kind": "oracle",
-            "sample": f"one mixed and one Kahan step over the first {n:,} parameters of the OPT-1.3B list "
-                      f"(host-resident, 1 thread): {secs['mixed']:.2f} s + {secs['kahan']:.2f} s",
+    w = workloads.normal(n, workloads.INIT_STD, "cpu", "master", 7).numpy()
+    if "f16amp" in modes:
+        g = workloads.grads(n, "cpu", 7, 0, dtype=torch.float16, scale=65536.0).view(torch.int16).numpy().view(np.uint16)
+        hp16 = oracle.HParams(inv_scale=1.0 / 65536)
+        p16, m, v = np.zeros(n, np.uint16), np.zeros(n, np.float32), np.zeros(n, np.float32)
+        t0 = time.perf_counter()
+        assert not oracle.any_nonfinite(g, True)
+        oracle.adamw_mixed(p16, g, w, m, v, hp16, 1, p_is_f16=True)
+        secs["f16amp"] = time.perf_counter() - t0
+    else:
+        g = workloads.grads(n, "cpu", 7, 0, dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        if "mixed" in modes:
+            p16, m, v = np.zeros(n, np.uint16), np.zeros(n, np.float32), np.zeros(n, np.float32)
+            t0 = time.perf_counter()
+            oracle.adamw_mixed(p16, g, w.copy(), m, v, hp, 1)
+            secs["mixed"] = time.perf_counter() - t0
+            del m, v
+        if "kahan" in modes:
+            pk = oracle.f32_to_bf16(w)
+            mk, vk, ck = (np.zeros(n, np.uint16) for _ in range(3))
+            t0 = time.perf_counter()
+            oracle.adamw_kahan(pk, g, mk, vk, ck, hp, 1)
+            secs["kahan"] = time.perf_counter() - t0
+    per_param = sum(s / n for s in secs.values())
+    return {"value": round(len(secs) / per_param / 1e9, 4), "unit": "Gparam/s", "cores": 1, "kind": "oracle",
+            "sample": f"one step per mode ({', '.join(secs)}) over the first {n:,} parameters of the list, "
+                      f"host-resident, 1 thread: " + " + ".join(f"{s:.2f} s" for s in secs.values()),
             "host_cpus": os.cpu_count()}
 
 
@@ -122,21 +191,42 @@ def main():
     wl = workloads.get(args.workload)
     numels = wl.numels
     N = wl.total
-    modes = [m for m in args.modes.split(",") if m]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.probe_only:
+        print(json.dumps({"probes_gb_s": probes(N, stream), "n": N}), flush=True)
+        return
+    modes = (args.modes or ("f16amp" if wl.p_dtype == "f16" else "mixed,kahan")).split(",")
 
     state = {}
     for i, mode in enumerate(modes):
-        arena, streams = make_mode_state(mode, numels, dev, seed=100 + i)
+        if mode == "f16amp":
+            arena, streams = make_mode_state("mixed", numels, dev, 100 + i, p_dtype="f16", loss_scale=wl.loss_scale)
+        else:
+            arena, streams = make_mode_state(mode, numels, dev, seed=100 + i)
         state[mode] = (arena, A.TensorList(numels, streams), torch.zeros(1, dtype=torch.int32, device=dev))
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
     hp = A.HParams()
-    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN}
+    hp16 = A.HParams(inv_loss_scale=1.0 / wl.loss_scale)
 
-    def one(mode):
+    def one(mode, ev=None):
         _, tl, ctr = state[mode]
-        A.adamw_multi_tensor_step(code[mode], A.BF16, tl, hp, ctr, None, stream)
+        if mode == "f16amp":
+            if ev:
+                ev[0].record(stream)
+            A.adamw_check_finite(A.F16, tl, flag, stream)
+            if ev:
+                ev[1].record(stream)
+            A.adamw_multi_tensor_step(A.MIXED, A.F16, tl, hp16, ctr, flag, stream)
+            if ev:
+                ev[2].record(stream)
+            return
+        if ev:
+            ev[0].record(stream)
+        A.adamw_multi_tensor_step(A.MIXED if mode == "mixed" else A.PURE_KAHAN, A.BF16, tl, hp, ctr, None, stream)
+        if ev:
+            ev[2].record(stream)
 
     for _ in range(args.warmup):
         for mode in modes:
@@ -144,24 +234,30 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = {m: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-          for m in modes}
+    ev = {m: [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)] for m in modes}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
         for mode in modes:
-            a, b = ev[mode][s]
-            a.record(stream)
-            one(mode)
-            b.record(stream)
+            one(mode, ev[mode][s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     per_mode = {}
     for mode in modes:
-        ms = [a.elapsed_time(b) for a, b in ev[mode]]
+        if mode == "f16amp":
+            chk = [a.elapsed_time(b) for a, b, _ in ev[mode]]
+            upd = [b.elapsed_time(c) for _, b, c in ev[mode]]
+            c_avg = sum(chk) / K
+            per_mode["check"] = {"ms_avg": round(c_avg, 4), "gb_s": round(N * 2 / (c_avg * 1e-3) / 1e9, 1),
+                                 "frac_of_hbm_peak": round(N * 2 / (c_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "bytes_per_param": 2}
+            ms = upd
+        else:
+            ms = [a.elapsed_time(c) for a, _, c in ev[mode]]
         avg = sum(ms) / len(ms)
-        per_mode[mode] = {
+        key = "f16amp_step" if mode == "f16amp" else mode
+        per_mode[key] = {
             "ms_avg": round(avg, 4), "ms_min": round(min(ms), 4),
             "gparam_s": round(N / (avg * 1e-3) / 1e9, 2),
             "gb_s": round(N * BYTES[mode] / (avg * 1e-3) / 1e9, 1),
@@ -170,15 +266,18 @@ def main():
         }
     ms_step = wall / K * 1e3
     value = len(modes) * N / (wall / K) / 1e9
-    dom = "mixed" if "mixed" in modes else modes[0]
-    achieved = N * BYTES[dom] / (per_mode[dom]["ms_avg"] * 1e-3) / 1e9
+    dom = modes[0]
+    dom_key = "f16amp_step" if dom == "f16amp" else dom
+    achieved = per_mode[dom_key]["gb_s"]
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", "traffic_opt_1_3b.json")
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
     if os.path.exists(tpath):
         with open(tpath) as f:
             t = json.load(f)
         if t.get("kernel_source_sha") == _kernel_sha():
             traffic = t.get("traffic_bytes_per_launch", {}).get(dom)
+    names = {"mixed": "mixed (bf16 p/g + fp32 master/m/v)", "kahan": "pure bf16 + bf16 Kahan compensation",
+             "f16amp": "fp16-AMP overflow check + mixed fp16 step (loss scale 65536)"}
     out = {
         "metric": "AdamW step Gparams/s + achieved HBM GB/s (% of peak), OPT-1.3B shape, 1 GPU",
         "value": round(value, 3),
@@ -193,20 +292,26 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {len(numels)} tensors, {N:,} params; one step = "
-                               + " then ".join({"mixed": "mixed (bf16 p/g + fp32 master/m/v)",
-                                                "kahan": "pure bf16 + bf16 Kahan compensation"}[m]
-                                               for m in modes),
+                               + " then ".join(names[m] for m in modes),
                    "n_params": N, "n_tensors": len(numels), "modes": modes,
                    "hparams": {"lr": hp.lr, "beta1": hp.beta1, "beta2": hp.beta2, "eps": hp.eps,
                                "weight_decay": hp.weight_decay}},
         "per_mode": per_mode,
-        "roofline": {"bound": "hbm", "kernel": f"update_kernel ({dom})", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": f"update_kernel ({dom})", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "device": torch.cuda.get_device_name(dev),
     }
+    if not args.no_probe:
+        del state
+        torch.cuda.empty_cache()
+        pr = probes(N, stream)
+        out["ceilings_gb_s"] = pr
+        for mode, key in (("mixed", "mixed_mix"), ("kahan", "kahan_mix"), ("f16amp_step", "mixed_mix")):
+            if mode in per_mode:
+                per_mode[mode]["frac_of_same_mix_probe"] = round(per_mode[mode]["gb_s"] / pr[key], 4)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(numels, args.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(numels, args.cpu_sample, modes)
     print(json.dumps(out), flush=True)
 
 

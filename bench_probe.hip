@@ -1,0 +1,119 @@
+// bench_probe.hip -- memory-system ceilings for bench.py --probe (gfx950).
+//
+// Kernels that move exactly the bytes of the fused AdamW step's streams, in the
+// same launch shape as the library's update kernel (256 lanes, one 8-element
+// pack per lane, one pass per workgroup, XCD-contiguous chunk order, two
+// workgroups per CU), but do no optimizer arithmetic.  Their rate is the ceiling
+// of the access pattern itself; the update kernel's rate divided by it says how
+// much of the pattern's bandwidth the arithmetic costs.  A plain copy, a
+// read-only and a write-only kernel give the HBM ceilings of simpler mixes.
+//
+// This file is measurement infrastructure: the library never loads it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define GLOBAL __attribute__((address_space(1)))
+
+namespace {
+
+__device__ __forceinline__ uint64_t chunk_of(uint32_t b, uint32_t nb)
+{
+    const uint32_t q = nb >> 3, r = nb & 7u, x = b & 7u, j = b >> 3;
+    return (uint64_t)x * q + (x < r ? x : r) + j;
+}
+
+// mixed mix: read g (2 B) and w, m, v (4 B); write w, m, v (4 B) and p (2 B)
+__global__ __launch_bounds__(256) void mixed_mix(const GLOBAL u32x4* g, GLOBAL f32x4* w, GLOBAL f32x4* m,
+                                                 GLOBAL f32x4* v, GLOBAL u32x4* p, uint64_t npack)
+{
+    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    if (k >= npack) return;
+    const u32x4 gv = g[k];
+    const f32x4 w0 = w[2 * k], w1 = w[2 * k + 1], m0 = m[2 * k], m1 = m[2 * k + 1], v0 = v[2 * k], v1 = v[2 * k + 1];
+    const f32x4 a = w0 + m0, b = w1 + v1;
+    __builtin_nontemporal_store(a, w + 2 * k);
+    __builtin_nontemporal_store(b, w + 2 * k + 1);
+    __builtin_nontemporal_store(m1, m + 2 * k);
+    __builtin_nontemporal_store(m0, m + 2 * k + 1);
+    __builtin_nontemporal_store(v1, v + 2 * k);
+    __builtin_nontemporal_store(v0, v + 2 * k + 1);
+    __builtin_nontemporal_store(gv ^ __builtin_bit_cast(u32x4, a), p + k);
+}
+
+// Kahan mix: read g, p, m, v, c (2 B each); write p, m, v, c
+__global__ __launch_bounds__(256) void kahan_mix(const GLOBAL u32x4* g, GLOBAL u32x4* p, GLOBAL u32x4* m,
+                                                 GLOBAL u32x4* v, GLOBAL u32x4* c, uint64_t npack)
+{
+    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    if (k >= npack) return;
+    const u32x4 a = __builtin_nontemporal_load(g + k), b = __builtin_nontemporal_load(p + k);
+    const u32x4 d = __builtin_nontemporal_load(m + k), e = __builtin_nontemporal_load(v + k);
+    const u32x4 f = __builtin_nontemporal_load(c + k);
+    __builtin_nontemporal_store(a ^ b, p + k);
+    __builtin_nontemporal_store(d ^ a, m + k);
+    __builtin_nontemporal_store(e ^ a, v + k);
+    __builtin_nontemporal_store(f ^ a, c + k);
+}
+
+__global__ __launch_bounds__(256) void copy_mix(const GLOBAL f32x4* src, GLOBAL f32x4* dst, uint64_t n4)
+{
+    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    if (k < n4) __builtin_nontemporal_store(__builtin_nontemporal_load(src + k), dst + k);
+}
+
+__global__ __launch_bounds__(256) void read_mix(const GLOBAL f32x4* src, GLOBAL float* sink, uint64_t n4)
+{
+    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    if (k >= n4) return;
+    const f32x4 x = src[k];
+    // never true for the finite inputs bench.py uses; keeps the load live
+    if (x.x + x.y + x.z + x.w == -12345.0f) sink[threadIdx.x] = x.x;
+}
+
+__global__ __launch_bounds__(256) void write_mix(GLOBAL f32x4* dst, uint64_t n4)
+{
+    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    if (k < n4) dst[k] = f32x4{1.0f, 2.0f, 3.0f, (float)(k & 1023)};
+}
+
+constexpr size_t kLds = 81920;   // two resident workgroups per CU, as the update kernel
+
+}  // namespace
+
+// kind: 0 mixed (n elements), 1 Kahan (n elements), 2 copy, 3 read, 4 write (n floats).
+// a..e: the buffers of the kind, in the order of the kernel's parameters.
+// n must be a multiple of 8.  Returns the hipError_t of the launch.
+extern "C" int probe_launch(int kind, void* a, void* b, void* c, void* d, void* e, uint64_t n, void* stream)
+{
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n % 8) return (int)hipErrorInvalidValue;
+    const uint64_t items = (kind <= 1) ? n / 8 : n / 4;
+    const uint64_t grid = (items + 255) / 256;
+    if (grid == 0 || grid > 0x7fffffffull) return (int)hipErrorInvalidValue;
+    switch (kind) {
+    case 0:
+        hipLaunchKernelGGL(mixed_mix, dim3((unsigned)grid), dim3(256), kLds, s, (const GLOBAL u32x4*)a,
+                           (GLOBAL f32x4*)b, (GLOBAL f32x4*)c, (GLOBAL f32x4*)d, (GLOBAL u32x4*)e, items);
+        break;
+    case 1:
+        hipLaunchKernelGGL(kahan_mix, dim3((unsigned)grid), dim3(256), kLds, s, (const GLOBAL u32x4*)a,
+                           (GLOBAL u32x4*)b, (GLOBAL u32x4*)c, (GLOBAL u32x4*)d, (GLOBAL u32x4*)e, items);
+        break;
+    case 2:
+        hipLaunchKernelGGL(copy_mix, dim3((unsigned)grid), dim3(256), 0, s, (const GLOBAL f32x4*)a,
+                           (GLOBAL f32x4*)b, items);
+        break;
+    case 3:
+        hipLaunchKernelGGL(read_mix, dim3((unsigned)grid), dim3(256), 0, s, (const GLOBAL f32x4*)a,
+                           (GLOBAL float*)b, items);
+        break;
+    case 4:
+        hipLaunchKernelGGL(write_mix, dim3((unsigned)grid), dim3(256), 0, s, (GLOBAL f32x4*)a, items);
+        break;
+    default:
+        return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
