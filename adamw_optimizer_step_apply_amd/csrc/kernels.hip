@@ -195,6 +195,7 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
 #ifndef ADAMW_NT_CHECK
 #define ADAMW_NT_CHECK 1
 #endif
+constexpr int kCheckUnroll = kCheckChunkMult;
 
 template <int NT, typename T>
 __device__ __forceinline__ T ld(const GLOBAL T* p)
@@ -431,11 +432,21 @@ __global__ __launch_bounds__(kBlock) void check_kernel(const DevSeg* __restrict_
     const uint32_t n = ch.n_kind & kCountMask;
     uint32_t bad = 0;
     if (ch.n_kind & kVecBit) {
+        // a check chunk is kCheckUnroll times a step chunk: each lane issues all
+        // its loads before testing any, so one pass covers the chunk
         const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
         const uint32_t npack = n / kPack;
-        for (uint32_t k = threadIdx.x; k < npack; k += kBlock) {
-            const u32x4 q = ld<ADAMW_NT_CHECK>(g4 + k);
-            bad |= nonfinite2<EXP>(q.x) | nonfinite2<EXP>(q.y) | nonfinite2<EXP>(q.z) | nonfinite2<EXP>(q.w);
+        for (uint32_t k0 = threadIdx.x; k0 < npack; k0 += kBlock * kCheckUnroll) {
+            u32x4 q[kCheckUnroll];
+#pragma unroll
+            for (int u = 0; u < kCheckUnroll; ++u) {
+                const uint32_t k = k0 + u * kBlock;
+                q[u] = k < npack ? ld<ADAMW_NT_CHECK>(g4 + k) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < kCheckUnroll; ++u)
+                bad |= nonfinite2<EXP>(q[u].x) | nonfinite2<EXP>(q[u].y) | nonfinite2<EXP>(q[u].z) |
+                       nonfinite2<EXP>(q[u].w);
         }
     } else {
         for (uint32_t i = threadIdx.x; i < n; i += kBlock) bad |= (uint32_t)((g[i] & EXP) == EXP);

@@ -20,6 +20,13 @@ constexpr uint32_t kVecBit = 0x80000000u;
 constexpr uint32_t kCountMask = 0x7fffffffu;
 constexpr int64_t kDefaultChunkElems = 2048;    // vector chunk: one pack per lane, one pass
 constexpr int64_t kElemChunkElems = 4096;       // element chunk: 16 elements per lane
+// The overflow check moves 2 B per element (the step 18-28 B): its chunks are
+// this many step chunks long, so a workgroup's fixed cost (two dependent table
+// loads) is spread over as many bytes as a step workgroup moves.
+#ifndef ADAMW_CHECK_CHUNK_MULT
+#define ADAMW_CHECK_CHUNK_MULT 8
+#endif
+constexpr int kCheckChunkMult = ADAMW_CHECK_CHUNK_MULT;
 
 // One segment: the device address of its element 0 in each stream (0 for a
 // stream the launch does not touch).

@@ -129,6 +129,7 @@ adamw_status build_plan(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor
         }
     }
     if (chunk_elems < 2048 || chunk_elems % 2048) { err = "bad chunk size"; return ADAMW_E_INVALID; }
+    if (for_check) chunk_elems *= kCheckChunkMult;
 
     int64_t base = 0, nseg = 0;
     for (int64_t i = 0; i < nt; ++i) {

@@ -2,9 +2,11 @@
 
 One bench step is the whole hot path over the OPT-1.3B parameter list (386
 tensors, 1,315,753,984 parameters, each tensor its own allocation-aligned
-buffer): a mixed-precision step (bf16 param/grad + fp32 master, exp_avg,
-exp_avg_sq) followed by a pure-bf16 step with bf16 Kahan compensation, each one
-call of adamw_multi_tensor_step (prologue + one update-kernel launch).  Inputs
+buffer) in both of its modes: a mixed-precision step (bf16 param/grad + fp32
+master, exp_avg, exp_avg_sq) and a pure-bf16 step with bf16 Kahan compensation,
+each one call of adamw_multi_tensor_step (prologue + one update-kernel launch).
+The timed region runs K mixed steps then K Kahan steps (two consecutive phases,
+as two training runs would); --interleave alternates them instead.  Inputs
 are synthetic and seeded (master ~ N(0, 0.02), grads ~ N(0, 1e-3), moments 0) and
 already resident in HBM when the timed region starts; the gradient buffers are
 reused across steps.
@@ -52,6 +54,8 @@ def parse():
                     help="elements of the list the oracle steps once per mode")
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--chunk-elems", type=int, default=0)
+    ap.add_argument("--interleave", action="store_true",
+                    help="alternate the modes every step instead of timing them as consecutive phases")
     return ap.parse_args()
 
 
@@ -233,13 +237,17 @@ def main():
             one(mode)
     torch.cuda.synchronize()
 
+    # Timed region: K steps of every mode.  By default the modes run as
+    # consecutive phases (K mixed steps, then K Kahan steps): they are separate
+    # training configurations, and a real loop runs one of them.  --interleave
+    # alternates them every step instead.
     K = args.steps
     ev = {m: [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)] for m in modes}
+    order = [(s, m) for s in range(K) for m in modes] if args.interleave else [(s, m) for m in modes for s in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(K):
-        for mode in modes:
-            one(mode, ev[mode][s])
+    for s, mode in order:
+        one(mode, ev[mode][s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -292,7 +300,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {len(numels)} tensors, {N:,} params; one step = "
-                               + " then ".join(names[m] for m in modes),
+                               + " then ".join(names[m] for m in modes)
+                               + (" (modes alternated every step)" if args.interleave else
+                                  " (timed as consecutive phases of K steps each)"),
                    "n_params": N, "n_tensors": len(numels), "modes": modes,
                    "hparams": {"lr": hp.lr, "beta1": hp.beta1, "beta2": hp.beta2, "eps": hp.eps,
                                "weight_decay": hp.weight_decay}},
