@@ -159,8 +159,9 @@ def cpu_baseline(numels, sample, modes):
         g = workloads.grads(n, "cpu", 7, 0, dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
         if "mixed" in modes:
             p16, m, v = np.zeros(n, np.uint16), np.zeros(n, np.float32), np.zeros(n, np.float32)
+            wm = w.copy()
             t0 = time.perf_counter()
-            oracle.adamw_mixed(p16, g, w.copy(), m, v, hp, 1)
+            oracle.adamw_mixed(p16, g, wm, m, v, hp, 1)
             secs["mixed"] = time.perf_counter() - t0
             del m, v
         if "kahan" in modes:
