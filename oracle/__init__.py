@@ -53,6 +53,7 @@ def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
 
 _U16P = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
 _F32P = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+_U32P = np.ctypeslib.ndpointer(np.uint32, flags="C_CONTIGUOUS")
 _I64 = ctypes.c_int64
 _F = ctypes.c_float
 
@@ -72,6 +73,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                       _F, _F, _F, _F, _F, _F, _I64]),
         "oracle_adamw_bf16_naive": (None, [_I64, _U16P, _U16P, _U16P, _U16P,
                                            _F, _F, _F, _F, _F, _F, _I64]),
+        "oracle_adamw_mixed_split": (None, [_I64, _U16P, _U16P, _U16P, _F32P, _F32P,
+                                            _F, _F, _F, _F, _F, _F, _I64]),
+        "oracle_split_make_n": (None, [_U32P, _U16P, _U16P, _I64]),
+        "oracle_split_join_n": (None, [_U16P, _U16P, _U32P, _I64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -210,6 +215,37 @@ def adamw_bf16_naive(p, g, m, v, hp: HParams, t: int, lib=None):
                                 lr, b1, b2, eps, wd, s, int(t))
 
 
+def split_make(w, lib=None):
+    """Split fp32 masters (any array viewable as uint32 bits) into (p, r) uint16 halves."""
+    lib = lib or load()
+    wb = np.ascontiguousarray(np.asarray(w).view(np.uint32)).reshape(-1)
+    p = np.empty(wb.size, np.uint16)
+    r = np.empty(wb.size, np.uint16)
+    lib.oracle_split_make_n(wb, p, r, wb.size)
+    return p, r
+
+
+def split_join(p, r, lib=None) -> np.ndarray:
+    """The fp32 masters (as float32) that (p, r) halves encode."""
+    lib = lib or load()
+    p, r = _u16(p).reshape(-1), _u16(r).reshape(-1)
+    w = np.empty(p.size, np.uint32)
+    lib.oracle_split_join_n(p, r, w, p.size)
+    return w.view(np.float32)
+
+
+def adamw_mixed_split(p, g, r, m, v, hp: HParams, t: int, lib=None):
+    """Mixed step on the split master: bf16 p (read and written), int16 remainder r
+    (as uint16 bits), fp32 m/v."""
+    lib = lib or load()
+    n = m.size
+    for a, dt in ((p, np.uint16), (g, np.uint16), (r, np.uint16), (m, np.float32), (v, np.float32)):
+        assert a.dtype == dt and a.flags.c_contiguous and a.size == n
+    lr, b1, b2, eps, wd, s = hp.f32()
+    lib.oracle_adamw_mixed_split(n, p.reshape(-1), g.reshape(-1), r.reshape(-1), m.reshape(-1), v.reshape(-1),
+                                 lr, b1, b2, eps, wd, s, int(t))
+
+
 def any_nonfinite(g16, is_f16: bool, lib=None) -> bool:
     """True iff any 16-bit gradient is inf or NaN (exponent field all ones)."""
     lib = lib or load()
@@ -224,6 +260,7 @@ def any_nonfinite(g16, is_f16: bool, lib=None) -> bool:
 
 MIXED = "mixed"
 KAHAN = "kahan"
+SPLIT = "split"
 
 
 def shard_pieces(numels, shard_begin: int = 0, shard_end: int | None = None):
@@ -250,7 +287,7 @@ def step_list(mode: str, tensors: list, hp: HParams, step: int, *, p_is_f16=Fals
     """Take one AdamW step over a tensor list; return the new step counter.
 
     ``tensors`` is a list of dicts of flat numpy arrays: mixed mode uses keys
-    ``p, g, master, m, v``; Kahan mode ``p, g, m, v, c``.  With
+    ``p, g, master, m, v``; split mode ``p, g, r, m, v``; Kahan mode ``p, g, m, v, c``.  With
     ``check_overflow`` the step is skipped (nothing written, counter kept) when
     any gradient of the whole list is inf/NaN.  Only elements inside
     ``[shard_begin, shard_end)`` of the flat concatenation are updated.
@@ -266,6 +303,11 @@ def step_list(mode: str, tensors: list, hp: HParams, step: int, *, p_is_f16=Fals
             sl = {k: np.ascontiguousarray(tt[k][lo:hi]) for k in ("p", "g", "master", "m", "v")}
             adamw_mixed(sl["p"], sl["g"], sl["master"], sl["m"], sl["v"], hp, t, p_is_f16, lib)
             for k in ("p", "master", "m", "v"):
+                tt[k][lo:hi] = sl[k]
+        elif mode == SPLIT:
+            sl = {k: np.ascontiguousarray(tt[k][lo:hi]) for k in ("p", "g", "r", "m", "v")}
+            adamw_mixed_split(sl["p"], sl["g"], sl["r"], sl["m"], sl["v"], hp, t, lib)
+            for k in ("p", "r", "m", "v"):
                 tt[k][lo:hi] = sl[k]
         elif mode == KAHAN:
             sl = {k: np.ascontiguousarray(tt[k][lo:hi]) for k in ("p", "g", "m", "v", "c")}

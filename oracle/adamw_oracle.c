@@ -246,6 +246,56 @@ void oracle_adamw_kahan(int64_t n, uint16_t* p, const uint16_t* g,
     }
 }
 
+/* Split master: the fp32 master w is held as two 16-bit halves, the bf16 model
+ * parameter p and an int16 remainder r, with w's bit pattern equal to
+ * (p << 16) + r in 32-bit two's-complement arithmetic (a reading of the "16-bit
+ * master param" in the ZeRO saving estimate of "Distributed optimizer support
+ * for BERT").  Splitting picks the p that leaves the smallest remainder: the
+ * nearest bf16, ties away from zero, which keeps r within [-32768, 32767]; a
+ * NaN master keeps a quiet-NaN p. */
+uint32_t oracle_split_join(uint16_t p, uint16_t r)
+{
+    int32_t rem = (int32_t)(int16_t)r;
+    return (uint32_t)(((uint32_t)p << 16) + (uint32_t)rem);
+}
+
+void oracle_split_make(uint32_t w, uint16_t* p, uint16_t* r)
+{
+    uint32_t hi;
+    if (isnan(bits_to_f32(w))) {
+        hi = (w >> 16) | 0x0040u;
+    } else {
+        uint32_t low = w & 0xffffu;
+        hi = (w >> 16) + (low >= 0x8000u ? 1u : 0u);   /* nearest; the tie goes up in magnitude */
+    }
+    *p = (uint16_t)hi;
+    *r = (uint16_t)(w - (hi << 16));
+}
+
+/* Mixed step with the split master: join, the mixed update of w, split. */
+void oracle_adamw_mixed_split(int64_t n, uint16_t* p, const uint16_t* g16, uint16_t* r,
+                              float* m, float* v,
+                              float lr, float beta1, float beta2, float eps, float wd,
+                              float inv_scale, int64_t t)
+{
+    float s[6];
+    oracle_scalars(t, lr, beta1, beta2, wd, s);
+    float step_size = s[0], rbc2 = s[1], decay = s[2];
+    for (int64_t i = 0; i < n; ++i) {
+        float g = oracle_bf16_to_f32(g16[i]) * inv_scale;
+        float u = adam_moments(g, &m[i], &v[i], beta1, beta2, s[4], s[5], rbc2, eps);
+        float w = bits_to_f32(oracle_split_join(p[i], r[i]));
+        w = w * decay - step_size * u;
+        oracle_split_make(f32_to_bits(w), &p[i], &r[i]);
+    }
+}
+
+/* Batch forms for the tests. */
+void oracle_split_make_n(const uint32_t* w, uint16_t* p, uint16_t* r, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) oracle_split_make(w[i], &p[i], &r[i]); }
+void oracle_split_join_n(const uint16_t* p, const uint16_t* r, uint32_t* w, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) w[i] = oracle_split_join(p[i], r[i]); }
+
 /* Pure bf16 without compensation: the same step applied directly to bf16 p.
  * Used by the tests as the control that Kahan summation is measured against. */
 void oracle_adamw_bf16_naive(int64_t n, uint16_t* p, const uint16_t* g,

@@ -40,6 +40,10 @@ MUTANTS = [
      "if ((g[i] & 0x7fffu) == 0x7c00u) return 1;"),
     ("f16 ties", "if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) == 1.0)) r += 1.0;",
      "if (frac >= 0.5) r += 1.0;"),
+    ("split tie goes down", "hi = (w >> 16) + (low >= 0x8000u ? 1u : 0u);", "hi = (w >> 16) + (low > 0x8000u ? 1u : 0u);"),
+    ("split truncates", "hi = (w >> 16) + (low >= 0x8000u ? 1u : 0u);", "hi = (w >> 16);"),
+    ("remainder zero-extended", "int32_t rem = (int32_t)(int16_t)r;", "int32_t rem = (int32_t)r;"),
+    ("split decay dropped", "w = w * decay - step_size * u;\n        oracle_split_make", "w = w - step_size * u;\n        oracle_split_make"),
 ]
 
 # fastest first; each entry is (pin, extra args)
@@ -61,6 +65,11 @@ PINS = [
     (pins.test_kahan_tracks_constant_tiny_updates, ()),
     (pins.test_zero_gradient_kahan_tracks_decay, ()),
 ]
+SPLIT_PINS = [
+    (pins.test_split_step_equals_mixed_step, (pins.HParams(),)),
+    (pins.test_split_join_roundtrip, ()),
+    (pins.test_split_param_is_a_nearest_bf16, ()),
+]
 
 
 @pytest.fixture(scope="module")
@@ -80,7 +89,7 @@ def test_mutant_is_killed(tmpdir_mut, name, orig, bad):
     open(csrc, "w").write(mutated)
     subprocess.run(["gcc", *CFLAGS, "-o", so, csrc, "-lm"], check=True)
     lib = _bind(ctypes.CDLL(so))
-    for pin, args in PINS:
+    for pin, args in (SPLIT_PINS + PINS if name.startswith("split") or "remainder" in name else PINS + SPLIT_PINS):
         try:
             pin(lib, *args)
         except AssertionError:

@@ -564,3 +564,68 @@ def test_recipe_defaults():
     assert (d.lr, d.beta1, d.beta2, d.weight_decay) == (hp["learning_rate"], hp["adam_beta1"],
                                                         hp["adam_beta2"], hp["weight_decay"])
     assert hp["optim_args"]["momentum_dtype"] == hp["optim_args"]["compensation_buffer_dtype"] == "bfloat16"
+
+
+# ---------------------------------------------------------------------------
+# Split master (16-bit param + 16-bit remainder)
+# ---------------------------------------------------------------------------
+
+def _pattern_sweep(n_random=1 << 22):
+    rng = np.random.default_rng(21)
+    stride = np.arange(0, 1 << 32, 4099, dtype=np.uint64).astype(np.uint32)     # ~1M patterns over the whole space
+    rnd = rng.integers(0, 1 << 32, size=n_random, dtype=np.uint64).astype(np.uint32)
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    his = rng.integers(0, 1 << 16, size=20000, dtype=np.uint64).astype(np.uint32)
+    edges = ((his[:, None] << 16) | lows[None, :]).reshape(-1)
+    special = np.array([0x7F7FFFFF, 0xFF7FFFFF, 0x7F800000, 0xFF800000, 0x00000000, 0x80000000,
+                        0x00008000, 0x80008000, 0x0000FFFF, 0x7F7F8000], np.uint32)
+    return np.concatenate([stride, rnd, edges, special])
+
+
+def test_split_join_roundtrip(olib):
+    """join(split(w)) == w bit for bit for every non-NaN pattern tried (a stride
+    through all 2^32 patterns, 4M random ones, and every rounding boundary), and a
+    NaN master joins back to a NaN."""
+    w = _pattern_sweep()
+    p, r = oracle.split_make(w, olib)
+    back = oracle.split_join(p, r, olib).view(np.uint32)
+    nan = np.isnan(w.view(np.float32))
+    assert np.array_equal(back[~nan], w[~nan])
+    assert np.all(np.isnan(back[nan].view(np.float32)))
+
+
+def test_split_param_is_a_nearest_bf16(olib):
+    """The bf16 half is a nearest bf16 to the master: it equals torch's
+    round-to-nearest-even except on exact ties, where it is the one of larger
+    magnitude; the remainder always fits in int16."""
+    w = _pattern_sweep()
+    w = w[np.isfinite(w.view(np.float32))]
+    p, r = oracle.split_make(w, olib)
+    rne = bf16_bits(w.view(np.float32))
+    tie = (w & 0xFFFF) == 0x8000
+    assert np.array_equal(p[~tie], rne[~tie])
+    assert np.array_equal(p[tie].astype(np.uint32), (w[tie] >> 16) + 1)
+    rem = r.view(np.int16).astype(np.int64)
+    assert np.array_equal((p.astype(np.int64) << 16) + rem, w.astype(np.int64))
+
+
+@pytest.mark.parametrize("hp", [HParams(), HParams(lr=1e-2, weight_decay=0.5, eps=1e-4)], ids=["recipe", "strong"])
+def test_split_step_equals_mixed_step(olib, hp):
+    """The split master is an exact encoding of the fp32 master, so k split steps
+    leave join(p, r) bit-identical to k mixed steps from the same master, with the
+    same moments, and p is the split of that master."""
+    rng = np.random.default_rng(22)
+    n, k = 50_000, 8
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    w0[:64] = np.array([0x3C808000 + i for i in range(64)], np.uint32).view(np.float32)   # ties
+    master, mm, vm, p16 = w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    ps, rs = oracle.split_make(w0, olib)
+    ms, vs = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, k + 1):
+        g = bf16_bits(rng.standard_normal(n) * 1e-3)
+        oracle.adamw_mixed(p16, g, master, mm, vm, hp, t, lib=olib)
+        oracle.adamw_mixed_split(ps, g, rs, ms, vs, hp, t, lib=olib)
+    assert np.array_equal(oracle.split_join(ps, rs, olib).view(np.uint32), master.view(np.uint32))
+    assert np.array_equal(ms, mm) and np.array_equal(vs, vm)
+    pe, _ = oracle.split_make(master, olib)
+    assert np.array_equal(ps, pe)
