@@ -129,6 +129,23 @@ __device__ __forceinline__ float kahan_sum(float g16, float pf, float cf, float&
     return pf + s;
 }
 
+// Split master: w's bits = (p << 16) + r, r an int16 (two's complement, mod 2^32).
+__device__ __forceinline__ uint32_t join_bits(uint32_t p16, uint32_t r16)
+{
+    return (p16 << 16) + (uint32_t)(int32_t)(int16_t)(uint16_t)r16;
+}
+
+// p = nearest bf16 of w, ties away from zero (bit 15 of the dropped half rounds the
+// magnitude up), so the remainder w - (p << 16) lies in [-32768, 32767]; a NaN
+// keeps its high half with the quiet bit set.  Returns p; r through `r16`.
+__device__ __forceinline__ uint32_t split_bits(uint32_t w, uint32_t& r16)
+{
+    const bool nan = (w & 0x7fffffffu) > 0x7f800000u;
+    const uint32_t hi = nan ? ((w >> 16) | 0x0040u) : (w >> 16) + ((w >> 15) & 1u);
+    r16 = (w - (hi << 16)) & 0xffffu;
+    return hi & 0xffffu;
+}
+
 // ---------------------------------------------------------------------------
 // Prologue: one lane.  skip = *found_inf != 0; otherwise t = *step + 1, the
 // step's scalars, and *step = t.
@@ -257,14 +274,15 @@ __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
 #define ADAMW_WPE_ATTR
 #endif
 
-// MODE 0: mixed bf16, 1: mixed fp16, 2: pure bf16 + Kahan
+// MODE 0: mixed bf16, 1: mixed fp16, 2: pure bf16 + Kahan, 3: mixed bf16 with the
+// master split into param + int16 remainder
 template <int MODE>
 __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const DevSeg* __restrict__ segs,
                                                         const DevChunk* __restrict__ chunks,
                                                         const LaunchScalars* __restrict__ sc)
 {
     if (sc->skip) return;
-    constexpr bool F16 = (MODE == 1);
+    constexpr bool F16 = (MODE == 1);   // MODE 3 uses bf16 param/grad
     constexpr int NTM = ADAMW_NT_MIXED, NTK = ADAMW_NT_KAHAN;
     const Coef c = load_coef(sc);
     const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
@@ -273,7 +291,74 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
     const uint64_t off = ch.off;
     const uint32_t tid = threadIdx.x;
 
-    if constexpr (MODE != 2) {
+    if constexpr (MODE == 3) {
+        GLOBAL uint16_t* __restrict__ p = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_PARAM], off);
+        const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
+        GLOBAL float* __restrict__ m = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
+        GLOBAL float* __restrict__ v = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG_SQ], off);
+        GLOBAL uint16_t* __restrict__ r = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_AUX], off);
+        if (ch.n_kind & kVecBit) {
+            const uint32_t npack = n / kPack;
+            const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
+            GLOBAL u32x4* __restrict__ p4 = reinterpret_cast<GLOBAL u32x4*>(p);
+            GLOBAL u32x4* __restrict__ r4 = reinterpret_cast<GLOBAL u32x4*>(r);
+            GLOBAL f32x4* __restrict__ m4 = reinterpret_cast<GLOBAL f32x4*>(m);
+            GLOBAL f32x4* __restrict__ v4 = reinterpret_cast<GLOBAL f32x4*>(v);
+            for (uint32_t k0 = tid; k0 < npack; k0 += kBlock * kUnroll) {
+                u32x4 G[kUnroll], P[kUnroll], R[kUnroll];
+                f32x4 M[kUnroll][2], V[kUnroll][2];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const uint32_t k = k0 + u * kBlock;
+                    if (k < npack) {
+                        G[u] = ld<NTM>(g4 + k); P[u] = ld<NTM>(p4 + k); R[u] = ld<NTM>(r4 + k);
+                        M[u][0] = ld<NTM>(m4 + 2 * k); M[u][1] = ld<NTM>(m4 + 2 * k + 1);
+                        V[u][0] = ld<NTM>(v4 + 2 * k); V[u][1] = ld<NTM>(v4 + 2 * k + 1);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const uint32_t k = k0 + u * kBlock;
+                    if (k < npack) {
+                        float* mf = reinterpret_cast<float*>(M[u]);
+                        float* vf = reinterpret_cast<float*>(V[u]);
+                        const uint32_t gw[4] = {G[u].x, G[u].y, G[u].z, G[u].w};
+                        const uint32_t pw[4] = {P[u].x, P[u].y, P[u].z, P[u].w};
+                        const uint32_t rw[4] = {R[u].x, R[u].y, R[u].z, R[u].w};
+                        uint32_t po[4], ro[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const f32x2 gg = widen2<false>(gw[j]);
+                            float wa = __uint_as_float(join_bits(pw[j] & 0xffffu, rw[j] & 0xffffu));
+                            float wb = __uint_as_float(join_bits(pw[j] >> 16, rw[j] >> 16));
+                            mixed_elem(gg.x, wa, mf[2 * j], vf[2 * j], c);
+                            mixed_elem(gg.y, wb, mf[2 * j + 1], vf[2 * j + 1], c);
+                            uint32_t ra, rb;
+                            const uint32_t pa = split_bits(__float_as_uint(wa), ra);
+                            const uint32_t pb = split_bits(__float_as_uint(wb), rb);
+                            po[j] = pa | (pb << 16);
+                            ro[j] = ra | (rb << 16);
+                        }
+                        st<NTM>(m4 + 2 * k, M[u][0]); st<NTM>(m4 + 2 * k + 1, M[u][1]);
+                        st<NTM>(v4 + 2 * k, V[u][0]); st<NTM>(v4 + 2 * k + 1, V[u][1]);
+                        st<NTM>(p4 + k, u32x4{po[0], po[1], po[2], po[3]});
+                        st<NTM>(r4 + k, u32x4{ro[0], ro[1], ro[2], ro[3]});
+                    }
+                }
+            }
+        } else {
+            for (uint32_t i = tid; i < n; i += kBlock) {
+                float wi = __uint_as_float(join_bits(p[i], r[i])), mi = m[i], vi = v[i];
+                mixed_elem(widen1<false>(g[i]), wi, mi, vi, c);
+                uint32_t ri;
+                const uint32_t pi = split_bits(__float_as_uint(wi), ri);
+                m[i] = mi;
+                v[i] = vi;
+                p[i] = (uint16_t)pi;
+                r[i] = (uint16_t)ri;
+            }
+        }
+    } else if constexpr (MODE != 2) {
         GLOBAL uint16_t* __restrict__ p = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_PARAM], off);
         const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
         GLOBAL float* __restrict__ m = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
@@ -486,6 +571,8 @@ hipError_t launch_update(adamw_mode mode, adamw_dtype p_dtype, const DevSeg* seg
     const dim3 grid((unsigned)n_chunks), block(kBlock);
     if (mode == ADAMW_PURE_KAHAN)
         hipLaunchKernelGGL(update_kernel<2>, grid, block, ADAMW_LDS_KAHAN, stream, segs, chunks, d_scalars);
+    else if (mode == ADAMW_MIXED_SPLIT)
+        hipLaunchKernelGGL(update_kernel<3>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
     else if (p_dtype == ADAMW_F16)
         hipLaunchKernelGGL(update_kernel<1>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
     else

@@ -25,7 +25,9 @@ int stream_esize(adamw_mode mode, adamw_dtype p_dtype, int s, bool for_check)
     (void)p_dtype;
     if (!stream_active(s, for_check)) return 0;
     if (for_check || s == ADAMW_STREAM_PARAM || s == ADAMW_STREAM_GRAD) return 2;
-    return mode == ADAMW_MIXED ? 4 : 2;
+    if (mode == ADAMW_MIXED) return 4;
+    if (mode == ADAMW_MIXED_SPLIT) return s == ADAMW_STREAM_AUX ? 2 : 4;
+    return 2;
 }
 
 adamw_status check_mode(adamw_mode mode, adamw_dtype p_dtype, bool for_check, std::string& err)
@@ -44,9 +46,10 @@ adamw_status check_mode(adamw_mode mode, adamw_dtype p_dtype, bool for_check, st
         }
         return ADAMW_OK;
     }
-    if (mode == ADAMW_PURE_KAHAN) {
+    if (mode == ADAMW_PURE_KAHAN || mode == ADAMW_MIXED_SPLIT) {
         if (p_dtype != ADAMW_BF16) {
-            err = "ADAMW_PURE_KAHAN needs p_dtype ADAMW_BF16";
+            err = mode == ADAMW_PURE_KAHAN ? "ADAMW_PURE_KAHAN needs p_dtype ADAMW_BF16"
+                                           : "ADAMW_MIXED_SPLIT needs p_dtype ADAMW_BF16";
             return ADAMW_E_UNSUPPORTED;
         }
         return ADAMW_OK;

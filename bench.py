@@ -37,7 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published peak
-BYTES = {"mixed": 28, "kahan": 18, "f16amp": 28, "check": 2}
+BYTES = {"mixed": 28, "kahan": 18, "split": 26, "f16amp": 28, "check": 2}
 
 
 def parse():
@@ -112,6 +112,10 @@ def probes(n, stream):
     w, m, v = (torch.ones(n, dtype=torch.float32, device=dev) for _ in range(3))
     run(0, [g, w, m, v, p], n, 28 * n, "mixed_mix")
     del w, m, v
+    r16 = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    m32, v32 = (torch.ones(n, dtype=torch.float32, device=dev) for _ in range(2))
+    run(5, [g, p, r16, m32, v32], n, 26 * n, "split_mix")
+    del m32, v32
     m16, v16, c16 = (torch.ones(n, dtype=torch.bfloat16, device=dev) for _ in range(3))
     run(1, [g, p, m16, v16, c16], n, 18 * n, "kahan_mix")
     del g, p, m16, v16, c16
@@ -164,6 +168,13 @@ def cpu_baseline(numels, sample, modes):
             oracle.adamw_mixed(p16, g, wm, m, v, hp, 1)
             secs["mixed"] = time.perf_counter() - t0
             del m, v
+        if "split" in modes:
+            ps, rs = oracle.split_make(w)
+            ms_, vs_ = np.zeros(n, np.float32), np.zeros(n, np.float32)
+            t0 = time.perf_counter()
+            oracle.adamw_mixed_split(ps, g, rs, ms_, vs_, hp, 1)
+            secs["split"] = time.perf_counter() - t0
+            del ms_, vs_, ps, rs
         if "kahan" in modes:
             pk = oracle.f32_to_bf16(w)
             mk, vk, ck = (np.zeros(n, np.uint16) for _ in range(3))
@@ -229,7 +240,8 @@ def main():
             return
         if ev:
             ev[0].record(stream)
-        A.adamw_multi_tensor_step(A.MIXED if mode == "mixed" else A.PURE_KAHAN, A.BF16, tl, hp, ctr, None, stream)
+        code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
+        A.adamw_multi_tensor_step(code, A.BF16, tl, hp, ctr, None, stream)
         if ev:
             ev[2].record(stream)
 
@@ -286,6 +298,7 @@ def main():
         if t.get("kernel_source_sha") == _kernel_sha():
             traffic = t.get("traffic_bytes_per_launch", {}).get(dom)
     names = {"mixed": "mixed (bf16 p/g + fp32 master/m/v)", "kahan": "pure bf16 + bf16 Kahan compensation",
+             "split": "mixed with the master split into bf16 param + int16 remainder",
              "f16amp": "fp16-AMP overflow check + mixed fp16 step (loss scale 65536)"}
     out = {
         "metric": "AdamW step Gparams/s + achieved HBM GB/s (% of peak), OPT-1.3B shape, 1 GPU",
@@ -318,7 +331,8 @@ def main():
         torch.cuda.empty_cache()
         pr = probes(N, stream)
         out["ceilings_gb_s"] = pr
-        for mode, key in (("mixed", "mixed_mix"), ("kahan", "kahan_mix"), ("f16amp_step", "mixed_mix")):
+        for mode, key in (("mixed", "mixed_mix"), ("kahan", "kahan_mix"), ("f16amp_step", "mixed_mix"),
+                          ("split", "split_mix")):
             if mode in per_mode:
                 per_mode[mode]["frac_of_same_mix_probe"] = round(per_mode[mode]["gb_s"] / pr[key], 4)
     if not args.no_cpu:

@@ -42,6 +42,22 @@ __global__ __launch_bounds__(256) void mixed_mix(const GLOBAL u32x4* g, GLOBAL f
     __builtin_nontemporal_store(gv ^ __builtin_bit_cast(u32x4, a), p + k);
 }
 
+// split-master mix: read g, p, r (2 B) and m, v (4 B); write p, r (2 B) and m, v (4 B)
+__global__ __launch_bounds__(256) void split_mix(const GLOBAL u32x4* g, GLOBAL u32x4* p, GLOBAL u32x4* r,
+                                                 GLOBAL f32x4* m, GLOBAL f32x4* v, uint64_t npack)
+{
+    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    if (k >= npack) return;
+    const u32x4 gv = g[k], pv = p[k], rv = r[k];
+    const f32x4 m0 = m[2 * k], m1 = m[2 * k + 1], v0 = v[2 * k], v1 = v[2 * k + 1];
+    __builtin_nontemporal_store(m1, m + 2 * k);
+    __builtin_nontemporal_store(m0 + v0, m + 2 * k + 1);
+    __builtin_nontemporal_store(v1, v + 2 * k);
+    __builtin_nontemporal_store(v0, v + 2 * k + 1);
+    __builtin_nontemporal_store(pv ^ gv, p + k);
+    __builtin_nontemporal_store(rv ^ gv, r + k);
+}
+
 // Kahan mix: read g, p, m, v, c (2 B each); write p, m, v, c
 __global__ __launch_bounds__(256) void kahan_mix(const GLOBAL u32x4* g, GLOBAL u32x4* p, GLOBAL u32x4* m,
                                                  GLOBAL u32x4* v, GLOBAL u32x4* c, uint64_t npack)
@@ -82,14 +98,14 @@ constexpr size_t kLds = 81920;   // two resident workgroups per CU, as the updat
 
 }  // namespace
 
-// kind: 0 mixed (n elements), 1 Kahan (n elements), 2 copy, 3 read, 4 write (n floats).
+// kind: 0 mixed, 1 Kahan, 5 split master (n elements); 2 copy, 3 read, 4 write (n floats).
 // a..e: the buffers of the kind, in the order of the kernel's parameters.
 // n must be a multiple of 8.  Returns the hipError_t of the launch.
 extern "C" int probe_launch(int kind, void* a, void* b, void* c, void* d, void* e, uint64_t n, void* stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (n % 8) return (int)hipErrorInvalidValue;
-    const uint64_t items = (kind <= 1) ? n / 8 : n / 4;
+    const uint64_t items = (kind <= 1 || kind == 5) ? n / 8 : n / 4;
     const uint64_t grid = (items + 255) / 256;
     if (grid == 0 || grid > 0x7fffffffull) return (int)hipErrorInvalidValue;
     switch (kind) {
@@ -100,6 +116,10 @@ extern "C" int probe_launch(int kind, void* a, void* b, void* c, void* d, void* 
     case 1:
         hipLaunchKernelGGL(kahan_mix, dim3((unsigned)grid), dim3(256), kLds, s, (const GLOBAL u32x4*)a,
                            (GLOBAL u32x4*)b, (GLOBAL u32x4*)c, (GLOBAL u32x4*)d, (GLOBAL u32x4*)e, items);
+        break;
+    case 5:
+        hipLaunchKernelGGL(split_mix, dim3((unsigned)grid), dim3(256), kLds, s, (const GLOBAL u32x4*)a,
+                           (GLOBAL u32x4*)b, (GLOBAL u32x4*)c, (GLOBAL f32x4*)d, (GLOBAL f32x4*)e, items);
         break;
     case 2:
         hipLaunchKernelGGL(copy_mix, dim3((unsigned)grid), dim3(256), 0, s, (const GLOBAL f32x4*)a,

@@ -24,6 +24,15 @@
  *   ADAMW_MIXED:      w = w*(1 - lr*wd) - (lr/(1-beta1^t))*u;  param = round16(w)
  *   ADAMW_PURE_KAHAN: d = -(lr*wd)*p - (lr/(1-beta1^t))*u
  *                     s = c + d;  p' = round_bf16(p + s);  c = round_bf16(s - (p' - p))
+ *   ADAMW_MIXED_SPLIT: the ADAMW_MIXED rule on w = join(param, remainder), then
+ *                     (param, remainder) = split(w), where join(p, r) is the fp32 whose
+ *                     bit pattern is (p << 16) + r in 32-bit two's complement (r read as
+ *                     int16) and split(w) takes p = w's nearest bf16, ties away from zero
+ *                     (so r = w - (p << 16) always fits int16), and p = w's high half with
+ *                     the quiet bit set for a NaN w.  join(split(w)) == w for every
+ *                     non-NaN w, so the master is exact fp32 (a reading of the "16-bit
+ *                     master param" in the ZeRO saving estimate of "Distributed
+ *                     optimizer support for BERT").
  *
  * Numerics: every element operation is one IEEE binary32 operation rounded to
  * nearest even, in the order written above, without fused multiply-add;
@@ -39,7 +48,9 @@
  *   2 exp_avg     ADAMW_MIXED: fp32 / ADAMW_PURE_KAHAN: bf16 (first moment m)
  *   3 exp_avg_sq  ADAMW_MIXED: fp32 / ADAMW_PURE_KAHAN: bf16 (second moment v)
  *   4 aux         ADAMW_MIXED: fp32 master weight w / ADAMW_PURE_KAHAN: bf16
- *                 compensation c
+ *                 compensation c / ADAMW_MIXED_SPLIT: int16 remainder of the master
+ *   (ADAMW_MIXED_SPLIT: param is bf16 and read as well as written; exp_avg and
+ *   exp_avg_sq are fp32.)
  * Every buffer is contiguous, 1-D, in device memory, aligned to its element
  * size.  16-byte alignment is not required but is what the fast path uses;
  * misaligned heads and tails are peeled, and a segment whose streams cannot
@@ -91,7 +102,9 @@ typedef enum { ADAMW_F32 = 0, ADAMW_BF16 = 1, ADAMW_F16 = 2 } adamw_dtype;
 
 typedef enum {
     ADAMW_MIXED = 0,       /* 16-bit param/grad (bf16 or fp16) + fp32 master, exp_avg, exp_avg_sq */
-    ADAMW_PURE_KAHAN = 1   /* bf16 param, grad, exp_avg, exp_avg_sq + bf16 Kahan compensation */
+    ADAMW_PURE_KAHAN = 1,  /* bf16 param, grad, exp_avg, exp_avg_sq + bf16 Kahan compensation */
+    ADAMW_MIXED_SPLIT = 2  /* ADAMW_MIXED with the fp32 master split into the bf16 param and an
+                              int16 remainder: 14 B/param resident instead of 16, 26 B moved */
 } adamw_mode;
 
 enum {
@@ -142,7 +155,7 @@ typedef struct {
  * one rank's flat shard with every pointer already offset to it).
  * param, grad, exp_avg, exp_avg_sq, aux: device buffers of n elements in the
  * layouts above.  p_dtype: ADAMW_BF16 or ADAMW_F16 in ADAMW_MIXED, ADAMW_BF16
- * in ADAMW_PURE_KAHAN.  n == 0 is valid (the counter still advances unless
+ * in ADAMW_PURE_KAHAN and ADAMW_MIXED_SPLIT.  n == 0 is valid (the counter still advances unless
  * skipped).  See the file comment for d_step / d_found_inf. */
 adamw_status adamw_step(adamw_mode mode, adamw_dtype p_dtype, int64_t n,
                         void* param, const void* grad, void* exp_avg, void* exp_avg_sq, void* aux,

@@ -20,16 +20,35 @@ import adamw_optimizer_step_apply_amd as A
 import oracle
 import workloads
 
-MODE = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN}
+MODE = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}
 DT = {"bf16": A.BF16, "f16": A.F16}
-F32_KEYS = {"mixed": ("m", "v", "master"), "kahan": ()}
+F32_KEYS = {"mixed": ("m", "v", "master"), "kahan": (), "split": ("m", "v")}
+
+
+def join_master(p: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """fp32 masters encoded by split (bf16 high half p, int16 remainder r)."""
+    w = (p.astype(np.int64) << 16) + r.view(np.int16).astype(np.int64)
+    return (w & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+
+
+def compare_streams(label, mode, got: dict, ref: dict, keys, p_is_f16=False):
+    """compare() over a mode's streams; a split master is compared as the joined
+    fp32 master (the fp32 bar) plus its bf16 half (the 16-bit bar)."""
+    stats = []
+    for k in keys:
+        if mode == "split" and k == "r":
+            stats.append(compare(f"{label}:master(p,r)", join_master(got["p"], got["r"]),
+                                 join_master(ref["p"], ref["r"]), True))
+            continue
+        stats.append(compare(f"{label}:{k}", got[k], ref[k], k in F32_KEYS[mode], p_is_f16))
+    return stats
 REL_TOL = 2e-6
 ULP_TOL = 1
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:
     t = t.detach()
-    if t.dtype in (torch.bfloat16, torch.float16):
+    if t.dtype in (torch.bfloat16, torch.float16, torch.int16):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     return t.contiguous().cpu().numpy()
 
@@ -127,10 +146,8 @@ class Case:
     def compare_all(self, label=""):
         torch.cuda.synchronize()
         assert int(self.d_step.item()) == self.step, f"{label}: step counter {int(self.d_step.item())} != {self.step}"
-        stats = []
-        for k in self.keys:
-            stats.append(compare(f"{label}:{k}", to_np(self.arena.bufs[k]), self.host[k],
-                                 k in F32_KEYS[self.mode], self.p_dtype == "f16"))
+        got = {k: to_np(self.arena.bufs[k]) for k in self.keys}
+        stats = compare_streams(label, self.mode, got, self.host, self.keys, self.p_dtype == "f16")
         log_stats(stats)
         return stats
 
@@ -217,6 +234,8 @@ class SampledCase:
         if self.mode == "mixed":
             oracle.adamw_mixed(sub["p"], sub["g"], sub["master"], sub["m"], sub["v"], ho, t,
                                p_is_f16=self.p_dtype == "f16")
+        elif self.mode == "split":
+            oracle.adamw_mixed_split(sub["p"], sub["g"], sub["r"], sub["m"], sub["v"], ho, t)
         else:
             oracle.adamw_kahan(sub["p"], sub["g"], sub["m"], sub["v"], sub["c"], ho, t)
         for k in self.keys:
@@ -226,12 +245,11 @@ class SampledCase:
     def compare_all(self, label=""):
         torch.cuda.synchronize()
         assert int(self.d_step.item()) == self.step, f"{label}: step counter {int(self.d_step.item())} != {self.step}"
-        stats = []
+        got = {k: to_np(self.arena.bufs[k][self.idx]) for k in self.keys}
+        stats = compare_streams(label, self.mode, got, self.host, self.keys, self.p_dtype == "f16")
+        out = ~self.inside
         for k in self.keys:
-            got = to_np(self.arena.bufs[k][self.idx])
-            stats.append(compare(f"{label}:{k}", got, self.host[k], k in F32_KEYS[self.mode], self.p_dtype == "f16"))
-            out = ~self.inside
             if k != "g" and out.any():
-                assert np.array_equal(got[out], self.initial[k][out]), f"{label}:{k} changed outside the shard"
+                assert np.array_equal(got[k][out], self.initial[k][out]), f"{label}:{k} changed outside the shard"
         log_stats(stats)
         return stats

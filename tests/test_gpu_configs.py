@@ -71,14 +71,14 @@ def test_opt125m_kahan_100_steps_warmup():
     free()
 
 
-@pytest.mark.parametrize("mode", ["mixed", "kahan"])
+@pytest.mark.parametrize("mode", ["mixed", "kahan", "split"])
 def test_opt13b_full_size_10_steps(mode):
     """OPT-1.3B list (1,315,753,984 params), 10 steps, the shape bench.py times."""
     wl = workloads.get("opt_1_3b")
-    case = SampledCase(mode, wl.numels, seed=4001 if mode == "mixed" else 4002)
+    case = SampledCase(mode, wl.numels, seed={"mixed": 4001, "kahan": 4002, "split": 4003}[mode])
     tl = case.tensor_list()
     hg, ho = hp_pair()
-    code = A.MIXED if mode == "mixed" else A.PURE_KAHAN
+    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
     for s in range(wl.steps):
         if s:
             case.refill_grads(s)

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import Case, compare, free, hp_pair, same_bits, to_np
+from gpu_util import Case, compare, free, hp_pair, join_master, same_bits, to_np
 
 import adamw_optimizer_step_apply_amd as A
 
@@ -38,7 +38,8 @@ def test_single_tensor_1m_mixed_10_steps():
 
 
 @pytest.mark.parametrize("align", [128, 1, 3])
-@pytest.mark.parametrize("mode,p_dtype", [("mixed", "bf16"), ("mixed", "f16"), ("kahan", "bf16")])
+@pytest.mark.parametrize("mode,p_dtype", [("mixed", "bf16"), ("mixed", "f16"), ("kahan", "bf16"),
+                                          ("split", "bf16")])
 def test_edge_sizes(mode, p_dtype, align):
     """Sizes around the 8-element pack and the chunk size, packed at several
     alignments (align=1 or 3 puts most tensors off a 16-byte boundary)."""
@@ -69,7 +70,7 @@ def test_kahan_phases():
                                    dict(beta1=0.0, beta2=0.0), dict(beta1=0.5, beta2=0.75, weight_decay=0.0),
                                    dict(lr=0.0, weight_decay=0.0)],
                          ids=["eps", "strong-decay", "beta0", "betas", "lr0"])
-@pytest.mark.parametrize("mode", ["mixed", "kahan"])
+@pytest.mark.parametrize("mode", ["mixed", "kahan", "split"])
 def test_hyperparameter_variants(mode, hp_kw):
     case = Case(mode, [5000, 33, 20000], seed=404, random_moments=True)
     _run(case, 3, hp_kw=hp_kw, label=f"hp-{mode}-{hp_kw}")
@@ -403,4 +404,33 @@ def test_plan_cache_eviction_cycle():
             c.oracle_step(ho)
     for i, c in enumerate(cases):
         c.compare_all(f"evict-{i}")
+    free()
+
+
+def test_split_master_tracks_mixed_master():
+    """The split kernel on (p, r) and the mixed kernel on the fp32 master they
+    encode stay bit-identical in the master and the moments over 10 steps; the
+    split's bf16 half is the master's nearest bf16 (ties away from zero)."""
+    numels = [70000, 9, 4099, 2048]
+    sp = Case("split", numels, seed=1600, random_moments=True)
+    mx = Case("mixed", numels, seed=1600, random_moments=True)
+    # the mixed case starts from the master the split case encodes, with the same moments
+    w0 = join_master(to_np(sp.arena.bufs["p"]), to_np(sp.arena.bufs["r"]))
+    mx.arena.bufs["master"].copy_(torch.from_numpy(w0))
+    for k in ("m", "v", "g"):
+        mx.arena.bufs[k].copy_(sp.arena.bufs[k])
+    hg, _ = hp_pair()
+    for s in range(10):
+        if s:
+            sp.refill_grads(s)
+            mx.arena.bufs["g"].copy_(sp.arena.bufs["g"])
+        sp.gpu_step(hg)
+        mx.gpu_step(hg)
+    torch.cuda.synchronize()
+    wj = join_master(to_np(sp.arena.bufs["p"]), to_np(sp.arena.bufs["r"]))
+    assert np.array_equal(wj.view(np.uint32), to_np(mx.arena.bufs["master"]).view(np.uint32))
+    for k in ("m", "v"):
+        assert same_bits(sp.arena.bufs[k], mx.arena.bufs[k]), k
+    pe, _ = oracle.split_make(wj)
+    assert np.array_equal(to_np(sp.arena.bufs["p"]), pe)
     free()

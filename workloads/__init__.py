@@ -161,6 +161,15 @@ def normal(n, std, device, *seed_parts, dtype=None):
     return x if dtype is None else x.to(dtype)
 
 
+def randint16(n, device, *seed_parts):
+    """``n`` uniformly random 16-bit patterns (as an int16 tensor)."""
+    import torch
+    x = torch.empty(int(n), dtype=torch.int16, device=device)
+    if n:
+        x.random_(-32768, 32768, generator=_gen(device, *seed_parts))
+    return x
+
+
 def grads(n, device, *seed_parts, dtype, scale=1.0):
     """Gradients N(0, GRAD_STD^2), multiplied by ``scale`` (the loss scale),
     then rounded to the 16-bit ``dtype``."""
@@ -191,6 +200,7 @@ def make_state(mode, numels, device, seed, *, p_dtype="bf16", align_elems=128, l
     """Allocate and fill the optimizer state of a tensor list in one arena per stream.
 
     mixed: p (bf16|f16) = round(master), g (same 16-bit dtype), master/m/v fp32.
+    split: p = bf16 round(N(0, 0.02)), r = uniform random int16, m/v fp32.
     kahan: p, g, m, v, c all bf16; p = round(N(0, 0.02)).
     m = v = c = 0 unless ``random_moments`` (then m ~ N(0, 1e-3), v ~ N(0, 1e-3)^2,
     and for Kahan c ~ N(0, 1e-6)), to start the update from a generic state.
@@ -204,6 +214,18 @@ def make_state(mode, numels, device, seed, *, p_dtype="bf16", align_elems=128, l
     if mode == "mixed":
         a.bufs["master"] = master
         a.bufs["p"] = master.to(half)
+        if random_moments:
+            a.bufs["m"] = normal(total, GRAD_STD, device, "m", seed)
+            a.bufs["v"] = normal(total, GRAD_STD, device, "v", seed).square()
+        else:
+            a.bufs["m"] = torch.zeros(total, dtype=torch.float32, device=device)
+            a.bufs["v"] = torch.zeros(total, dtype=torch.float32, device=device)
+    elif mode == "split":
+        # the master as two 16-bit halves: a bf16 high half and a uniformly random
+        # int16 low half (every pair encodes some fp32 master near the bf16 value)
+        a.bufs["p"] = master.to(torch.bfloat16)
+        del master
+        a.bufs["r"] = randint16(total, device, "remainder", seed)
         if random_moments:
             a.bufs["m"] = normal(total, GRAD_STD, device, "m", seed)
             a.bufs["v"] = normal(total, GRAD_STD, device, "v", seed).square()
@@ -235,13 +257,15 @@ def refill_grads(arena: Arena, seed, step, *, p_dtype="bf16", loss_scale=1.0):
 
 # Buffers of each mode in the order of the C ABI's streams:
 # param, grad, exp_avg, exp_avg_sq, aux (fp32 master in mixed mode, bf16 Kahan compensation otherwise).
-STREAMS = {"mixed": ("p", "g", "m", "v", "master"), "kahan": ("p", "g", "m", "v", "c")}
+STREAMS = {"mixed": ("p", "g", "m", "v", "master"), "kahan": ("p", "g", "m", "v", "c"),
+           "split": ("p", "g", "m", "v", "r")}
 
 # Resident bytes per parameter of each stream layout (what one rank holds).
 RESIDENT_BYTES = {
     "mixed": {"p": 2, "g": 2, "master": 4, "m": 4, "v": 4},
     "kahan": {"p": 2, "g": 2, "m": 2, "v": 2, "c": 2},
     "bf16_naive": {"p": 2, "g": 2, "m": 2, "v": 2},
+    "split": {"p": 2, "g": 2, "m": 4, "v": 4, "r": 2},
 }
 
 # Bytes moved per parameter by one step: what is read plus what is written.
@@ -251,6 +275,7 @@ TRAFFIC_BYTES = {
     "mixed": {"read": {"g": 2, "master": 4, "m": 4, "v": 4}, "write": {"master": 4, "m": 4, "v": 4, "p": 2}},
     "kahan": {"read": {"g": 2, "p": 2, "m": 2, "v": 2, "c": 2}, "write": {"p": 2, "m": 2, "v": 2, "c": 2}},
     "check_f16": {"read": {"g": 2}, "write": {}},
+    "split": {"read": {"g": 2, "p": 2, "r": 2, "m": 4, "v": 4}, "write": {"p": 2, "r": 2, "m": 4, "v": 4}},
 }
 
 
