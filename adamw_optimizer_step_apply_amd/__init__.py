@@ -35,13 +35,19 @@ STREAM_PARAM, STREAM_GRAD, STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_AUX = range
 NUM_STREAMS = 5
 _STATUS = {0: "ADAMW_OK", 1: "ADAMW_E_INVALID", 2: "ADAMW_E_UNSUPPORTED", 3: "ADAMW_E_NOMEM", 4: "ADAMW_E_HIP"}
 
-EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_check_finite", "adamw_last_error",
-            "adamw_release_workspace", "adamw_abi_version", "adamw_plan_inspect", "adamw_set_chunk_elems")
+EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_amp", "adamw_check_finite",
+            "adamw_last_error", "adamw_release_workspace", "adamw_abi_version", "adamw_plan_inspect",
+            "adamw_set_chunk_elems")
 
 
 class adamw_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("inv_loss_scale", ctypes.c_float)]
+
+
+class adamw_loss_scaler(ctypes.Structure):
+    _fields_ = [("growth_factor", ctypes.c_float), ("backoff_factor", ctypes.c_float),
+                ("growth_interval", ctypes.c_int32)]
 
 
 class adamw_tensor_list(ctypes.Structure):
@@ -68,6 +74,10 @@ def _declare(_lib):
     _lib.adamw_multi_tensor_step.restype = ctypes.c_int
     _lib.adamw_multi_tensor_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list),
                                              ctypes.POINTER(adamw_hparams), _vp, _vp, _vp]
+    _lib.adamw_multi_tensor_step_amp.restype = ctypes.c_int
+    _lib.adamw_multi_tensor_step_amp.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list),
+                                                 ctypes.POINTER(adamw_hparams), _vp, _vp, _vp,
+                                                 ctypes.POINTER(adamw_loss_scaler), _vp]
     _lib.adamw_check_finite.restype = ctypes.c_int
     _lib.adamw_check_finite.argtypes = [ctypes.c_int, ctypes.POINTER(adamw_tensor_list), _vp, _vp]
     _lib.adamw_last_error.restype = ctypes.c_char_p
@@ -180,6 +190,37 @@ def adamw_multi_tensor_step(mode: int, p_dtype: int, tensors: TensorList, hp, d_
     h = _hp(hp)
     _check(_lib.adamw_multi_tensor_step(mode, p_dtype, ctypes.byref(tensors.c), ctypes.byref(h), _addr(d_step),
                                         _addr(d_found_inf), _stream(stream)))
+
+
+@dataclass
+class LossScaler:
+    """Dynamic loss-scaling rule (growth after growth_interval clean steps,
+    back-off on an inf/NaN gradient)."""
+    growth_factor: float = 2.0
+    backoff_factor: float = 0.5
+    growth_interval: int = 2000
+
+    def c(self) -> adamw_loss_scaler:
+        return adamw_loss_scaler(self.growth_factor, self.backoff_factor, int(self.growth_interval))
+
+
+def loss_scale_state(scale: float = 65536.0, device="cuda") -> torch.Tensor:
+    """A device adamw_loss_scale_state {float scale; int32 growth_tracker} as an
+    8-byte tensor (view it as float32 for the scale, int32 for the tracker)."""
+    t = torch.zeros(2, dtype=torch.float32, device=device)
+    t[0] = scale
+    return t
+
+
+def adamw_multi_tensor_step_amp(mode: int, p_dtype: int, tensors: TensorList, hp, d_step, d_found_inf,
+                                d_scale, scaler: LossScaler = None, stream=None) -> None:
+    """AdamW step that unscales by a device-resident dynamic loss scale and then
+    advances it from the overflow flag (C ABI adamw_multi_tensor_step_amp)."""
+    h = _hp(hp)
+    sc = (scaler or LossScaler()).c()
+    _check(_lib.adamw_multi_tensor_step_amp(mode, p_dtype, ctypes.byref(tensors.c), ctypes.byref(h), _addr(d_step),
+                                            _addr(d_found_inf), _addr(d_scale), ctypes.byref(sc),
+                                            _stream(stream)))
 
 
 def adamw_check_finite(g_dtype: int, grads: TensorList, d_found_inf, stream=None) -> None:

@@ -24,7 +24,8 @@
 namespace adamw {
 
 hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32_t* d_found_inf,
-                           LaunchScalars* d_scalars, hipStream_t stream);
+                           LaunchScalars* d_scalars, adamw_loss_scale_state* d_amp, const adamw_loss_scaler& scaler,
+                           hipStream_t stream);
 hipError_t launch_update(adamw_mode mode, adamw_dtype p_dtype, const DevSeg* segs, const DevChunk* chunks,
                          int64_t n_chunks, const LaunchScalars* d_scalars, hipStream_t stream);
 hipError_t launch_check(adamw_dtype g_dtype, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
@@ -205,10 +206,21 @@ adamw_status basic_list_check(const adamw_tensor_list* list)
     return ADAMW_OK;
 }
 
-adamw_status do_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, const adamw_hparams* hp,
-                     int32_t* d_step, const int32_t* d_found_inf, void* hip_stream)
+adamw_status check_scaler(const adamw_loss_scaler* sc)
 {
-    g_err.clear();
+    if (!sc) return fail(ADAMW_E_INVALID, "loss scaler is null");
+    if (!std::isfinite(sc->growth_factor) || !(sc->growth_factor >= 1.0f))
+        return fail(ADAMW_E_INVALID, "growth_factor must be finite and >= 1");
+    if (!(sc->backoff_factor > 0.0f && sc->backoff_factor <= 1.0f))
+        return fail(ADAMW_E_INVALID, "backoff_factor must lie in (0, 1]");
+    if (sc->growth_interval < 1) return fail(ADAMW_E_INVALID, "growth_interval must be >= 1");
+    return ADAMW_OK;
+}
+
+adamw_status do_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, const adamw_hparams* hp,
+                     int32_t* d_step, const int32_t* d_found_inf, void* hip_stream,
+                     adamw_loss_scale_state* d_amp = nullptr, const adamw_loss_scaler* scaler = nullptr)
+{
     std::string err;
     adamw_status st = check_mode(mode, p_dtype, false, err);
     if (st != ADAMW_OK) return fail(st, err);
@@ -233,7 +245,8 @@ adamw_status do_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_li
     }
     PlanSlot* plan = nullptr;
     if ((st = ensure_plan(*ws, mode, p_dtype, list, false, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
-    e = launch_prologue(*hp, d_step, d_found_inf, ws->scalars, stream);
+    const adamw_loss_scaler no_scaler{1.0f, 1.0f, 1};
+    e = launch_prologue(*hp, d_step, d_found_inf, ws->scalars, d_amp, scaler ? *scaler : no_scaler, stream);
     if (e != hipSuccess) return hip_fail("prologue launch", e);
     e = launch_update(mode, p_dtype, plan->segs(), plan->chunks(), plan->n_chunks, ws->scalars, stream);
     if (e != hipSuccess) return hip_fail("update launch", e);
@@ -251,7 +264,21 @@ adamw_status adamw_multi_tensor_step(adamw_mode mode, adamw_dtype p_dtype, const
                                      const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
                                      void* hip_stream)
 {
+    g_err.clear();
     return do_step(mode, p_dtype, list, hp, d_step, d_found_inf, hip_stream);
+}
+
+adamw_status adamw_multi_tensor_step_amp(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
+                                         const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
+                                         adamw_loss_scale_state* d_scale, const adamw_loss_scaler* scaler,
+                                         void* hip_stream)
+{
+    g_err.clear();
+    if (!d_found_inf) return fail(ADAMW_E_INVALID, "d_found_inf is required with a dynamic loss scale");
+    if (!d_scale || (uintptr_t)d_scale % 4) return fail(ADAMW_E_INVALID, "d_scale is null or not 4-byte aligned");
+    adamw_status st = check_scaler(scaler);
+    if (st != ADAMW_OK) return st;
+    return do_step(mode, p_dtype, list, hp, d_step, d_found_inf, hip_stream, d_scale, scaler);
 }
 
 adamw_status adamw_step(adamw_mode mode, adamw_dtype p_dtype, int64_t n, void* param, const void* grad,

@@ -148,7 +148,8 @@ __device__ __forceinline__ uint32_t split_bits(uint32_t w, uint32_t& r16)
 
 // ---------------------------------------------------------------------------
 // Prologue: one lane.  skip = *found_inf != 0; otherwise t = *step + 1, the
-// step's scalars, and *step = t.
+// step's scalars, and *step = t.  With a loss-scale state, the unscale factor
+// is 1/scale and the state advances by the dynamic loss-scaling rule.
 // ---------------------------------------------------------------------------
 
 __device__ double pow_sq(double b, int64_t t)
@@ -164,11 +165,33 @@ __device__ double pow_sq(double b, int64_t t)
 }
 
 __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, const int32_t* __restrict__ found_inf,
-                                LaunchScalars* __restrict__ out)
+                                LaunchScalars* __restrict__ out, adamw_loss_scale_state* __restrict__ amp,
+                                adamw_loss_scaler scaler)
 {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     LaunchScalars s{};
-    if (found_inf && *found_inf != 0) {
+    const bool skip = found_inf && *found_inf != 0;
+    float inv_scale = hp.inv_loss_scale;
+    if (amp) {
+        // this step unscales by the current scale; the scale for the next step
+        // follows from the flag
+        const float scale = amp->scale;
+        inv_scale = (float)(1.0 / (double)scale);
+        if (skip) {
+            amp->scale = scale * scaler.backoff_factor;
+            amp->growth_tracker = 0;
+        } else {
+            const int32_t run = amp->growth_tracker + 1;
+            if (run == scaler.growth_interval) {
+                const float grown = scale * scaler.growth_factor;
+                if (__builtin_isfinite(grown)) amp->scale = grown;
+                amp->growth_tracker = 0;
+            } else {
+                amp->growth_tracker = run;
+            }
+        }
+    }
+    if (skip) {
         s.skip = 1;
         *out = s;
         return;
@@ -188,7 +211,7 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
     s.beta1 = hp.beta1;
     s.beta2 = hp.beta2;
     s.eps = hp.eps;
-    s.inv_scale = hp.inv_loss_scale;
+    s.inv_scale = inv_scale;
     *out = s;
     *step = (int32_t)t;
 }
@@ -546,9 +569,11 @@ __global__ __launch_bounds__(kBlock) void check_kernel(const DevSeg* __restrict_
 // ---------------------------------------------------------------------------
 
 hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32_t* d_found_inf,
-                           LaunchScalars* d_scalars, hipStream_t stream)
+                           LaunchScalars* d_scalars, adamw_loss_scale_state* d_amp, const adamw_loss_scaler& scaler,
+                           hipStream_t stream)
 {
-    hipLaunchKernelGGL(prologue_kernel, dim3(1), dim3(64), 0, stream, hp, d_step, d_found_inf, d_scalars);
+    hipLaunchKernelGGL(prologue_kernel, dim3(1), dim3(64), 0, stream, hp, d_step, d_found_inf, d_scalars, d_amp,
+                       scaler);
     return hipGetLastError();
 }
 

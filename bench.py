@@ -224,7 +224,9 @@ def main():
         state[mode] = (arena, A.TensorList(numels, streams), torch.zeros(1, dtype=torch.int32, device=dev))
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     hp = A.HParams()
-    hp16 = A.HParams(inv_loss_scale=1.0 / wl.loss_scale)
+    # fp16 AMP keeps its loss scale on the device (growth 2, back-off 0.5, every 2000 clean steps)
+    scale_state = A.loss_scale_state(wl.loss_scale)
+    scaler = A.LossScaler(2.0, 0.5, 2000)
 
     def one(mode, ev=None):
         _, tl, ctr = state[mode]
@@ -234,7 +236,7 @@ def main():
             A.adamw_check_finite(A.F16, tl, flag, stream)
             if ev:
                 ev[1].record(stream)
-            A.adamw_multi_tensor_step(A.MIXED, A.F16, tl, hp16, ctr, flag, stream)
+            A.adamw_multi_tensor_step_amp(A.MIXED, A.F16, tl, hp, ctr, flag, scale_state, scaler, stream)
             if ev:
                 ev[2].record(stream)
             return
@@ -299,7 +301,8 @@ def main():
             traffic = t.get("traffic_bytes_per_launch", {}).get(dom)
     names = {"mixed": "mixed (bf16 p/g + fp32 master/m/v)", "kahan": "pure bf16 + bf16 Kahan compensation",
              "split": "mixed with the master split into bf16 param + int16 remainder",
-             "f16amp": "fp16-AMP overflow check + mixed fp16 step (loss scale 65536)"}
+             "f16amp": "fp16-AMP overflow check + mixed fp16 step with a device-resident dynamic loss scale "
+                       "(65536 to start)"}
     out = {
         "metric": "AdamW step Gparams/s + achieved HBM GB/s (% of peak), OPT-1.3B shape, 1 GPU",
         "value": round(value, 3),

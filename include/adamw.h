@@ -170,6 +170,41 @@ adamw_status adamw_multi_tensor_step(adamw_mode mode, adamw_dtype p_dtype, const
                                      const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
                                      void* hip_stream);
 
+/* Dynamic loss scaling state, in device memory owned by the caller (8 bytes,
+ * 4-byte aligned).  growth_tracker counts consecutive steps taken since the
+ * scale last changed and must start in [0, growth_interval). */
+typedef struct {
+    float scale;
+    int32_t growth_tracker;
+} adamw_loss_scale_state;
+
+/* Dynamic loss scaling rule (host values): after growth_interval consecutive
+ * steps without an inf/NaN gradient the scale is multiplied by growth_factor
+ * (kept unchanged if the product is not finite); a step with an inf/NaN gradient
+ * multiplies it by backoff_factor.  Either event resets the tracker.
+ * Requirements: growth_factor finite and >= 1; 0 < backoff_factor <= 1;
+ * growth_interval >= 1.  The pages show an fp16-amp run but not its scaler's
+ * constants; the usual choice is growth 2, backoff 0.5, interval 2000. */
+typedef struct {
+    float growth_factor;
+    float backoff_factor;
+    int32_t growth_interval;
+} adamw_loss_scaler;
+
+/* fp16-AMP step with a device-resident dynamic loss scale: as
+ * adamw_multi_tensor_step with d_found_inf required, except that the gradient
+ * multiplier is (float)(1 / (double)d_scale->scale) read on the device when the
+ * step runs (hp->inv_loss_scale is ignored), and that the same launch then
+ * advances *d_scale by the rule above using *d_found_inf -- whether or not the
+ * step itself was skipped.  No host synchronisation is involved.  Typical
+ * sequence per iteration: adamw_check_finite, then this call with the same flag
+ * (the opt-125m fp16-amp run on the page "[pure bf16 training] w/
+ * AnyPrecisionAdamW and Kahan summation"). */
+adamw_status adamw_multi_tensor_step_amp(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
+                                         const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
+                                         adamw_loss_scale_state* d_scale, const adamw_loss_scaler* scaler,
+                                         void* hip_stream);
+
 /* fp16-AMP overflow check: stores 0 to *d_found_inf (stream ordered), then 1
  * if any gradient element of the list (stream 1 only; shard range and
  * flat_mask bit 1 honoured) has an all-ones exponent field, i.e. is inf or NaN.

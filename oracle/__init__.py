@@ -77,6 +77,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                             _F, _F, _F, _F, _F, _F, _I64]),
         "oracle_split_make_n": (None, [_U32P, _U16P, _U16P, _I64]),
         "oracle_split_join_n": (None, [_U16P, _U16P, _U32P, _I64]),
+        "oracle_inv_scale": (_F, [_F]),
+        "oracle_update_loss_scale": (None, [ctypes.POINTER(_F), ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
+                                            _F, _F, ctypes.c_int32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -317,6 +320,44 @@ def step_list(mode: str, tensors: list, hp: HParams, step: int, *, p_is_f16=Fals
         else:
             raise ValueError(f"unknown mode {mode!r}")
     return t
+
+
+@dataclass
+class LossScale:
+    """Dynamic loss-scale state and rule (fp32 scale, int32 growth tracker)."""
+    scale: float = 65536.0
+    tracker: int = 0
+    growth: float = 2.0
+    backoff: float = 0.5
+    interval: int = 2000
+
+    def inv(self, lib=None) -> float:
+        lib = lib or load()
+        return float(lib.oracle_inv_scale(float(np.float32(self.scale))))
+
+    def update(self, found_inf: bool, lib=None):
+        lib = lib or load()
+        s = _F(float(np.float32(self.scale)))
+        t = ctypes.c_int32(int(self.tracker))
+        lib.oracle_update_loss_scale(ctypes.byref(s), ctypes.byref(t), int(bool(found_inf)),
+                                     float(np.float32(self.growth)), float(np.float32(self.backoff)),
+                                     int(self.interval))
+        self.scale, self.tracker = float(s.value), int(t.value)
+
+
+def amp_step_list(mode: str, tensors: list, hp: HParams, step: int, ls: LossScale, *, p_is_f16=True,
+                  shard_begin=0, shard_end=None, lib=None) -> int:
+    """fp16-AMP step with a dynamic loss scale: the overflow test over every
+    gradient of the list, the step (unless skipped) with the gradient multiplier
+    1/scale, then the scale update from the test's outcome.  Returns the new
+    step counter; ``ls`` is updated in place."""
+    lib = lib or load()
+    found = any(any_nonfinite(tt["g"], p_is_f16, lib) for tt in tensors)
+    hps = HParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, ls.inv(lib))
+    new_step = step if found else step_list(mode, tensors, hps, step, p_is_f16=p_is_f16,
+                                            shard_begin=shard_begin, shard_end=shard_end, lib=lib)
+    ls.update(found, lib)
+    return new_step
 
 
 def warmup_linear_lr(t: int, base_lr: float = 2e-4, warmup: int = 500) -> float:

@@ -170,6 +170,31 @@ int oracle_any_nonfinite_bf16(const uint16_t* g, int64_t n)
     return 0;
 }
 
+/* Dynamic loss scaling (fp16 AMP): a step with an inf/NaN gradient multiplies
+ * the scale by `backoff`; growth_interval consecutive clean steps multiply it
+ * by `growth`, unless that product is not finite; either event restarts the
+ * count.  The step itself unscales by 1/scale formed in double, rounded to
+ * float (exact for the power-of-two scales of the fp16-amp run). */
+float oracle_inv_scale(float scale) { return (float)(1.0 / (double)scale); }
+
+void oracle_update_loss_scale(float* scale, int32_t* tracker, int found_inf,
+                              float growth, float backoff, int32_t interval)
+{
+    if (found_inf) {
+        *scale = *scale * backoff;
+        *tracker = 0;
+        return;
+    }
+    int32_t run = *tracker + 1;
+    if (run == interval) {
+        float grown = *scale * growth;
+        if (isfinite(grown)) *scale = grown;
+        *tracker = 0;
+    } else {
+        *tracker = run;
+    }
+}
+
 /* ------------------------------------------------------------------------- */
 /* The element update.                                                        */
 /* ------------------------------------------------------------------------- */

@@ -73,6 +73,18 @@ def _tl(numels, base=FAKE, esz=(2, 2, 4, 4, 4), **kw):
                                        A.HParams(), FAKE, stream=0), "grad"),
     (lambda: A.adamw_step(A.MIXED, A.BF16, -1, FAKE, FAKE, FAKE, FAKE, FAKE, A.HParams(), FAKE, stream=0), "n < 0"),
     (lambda: A.adamw_step(A.MIXED, A.BF16, 5, FAKE, 0, FAKE, FAKE, FAKE, A.HParams(), FAKE, stream=0), "null"),
+    (lambda: A.adamw_multi_tensor_step_amp(A.MIXED, A.F16, _tl([10]), A.HParams(), FAKE, 0, FAKE, stream=0),
+     "d_found_inf"),
+    (lambda: A.adamw_multi_tensor_step_amp(A.MIXED, A.F16, _tl([10]), A.HParams(), FAKE, FAKE, 0, stream=0),
+     "d_scale"),
+    (lambda: A.adamw_multi_tensor_step_amp(A.MIXED, A.F16, _tl([10]), A.HParams(), FAKE, FAKE, FAKE,
+                                           A.LossScaler(0.5, 0.5, 10), stream=0), "growth_factor"),
+    (lambda: A.adamw_multi_tensor_step_amp(A.MIXED, A.F16, _tl([10]), A.HParams(), FAKE, FAKE, FAKE,
+                                           A.LossScaler(2.0, 0.0, 10), stream=0), "backoff_factor"),
+    (lambda: A.adamw_multi_tensor_step_amp(A.MIXED, A.F16, _tl([10]), A.HParams(), FAKE, FAKE, FAKE,
+                                           A.LossScaler(2.0, 0.5, 0), stream=0), "growth_interval"),
+    (lambda: A.adamw_multi_tensor_step(A.MIXED_SPLIT, A.F16, _tl([10], esz=(2, 2, 4, 4, 2)), A.HParams(), FAKE,
+                                       stream=0), "MIXED_SPLIT"),
     (lambda: A.adamw_check_finite(A.F32, _tl([10]), FAKE, stream=0), "g_dtype"),
     (lambda: A.adamw_check_finite(A.F16, _tl([10]), 0, stream=0), "d_found_inf"),
     (lambda: A.adamw_check_finite(A.F16, _tl([10, 3], shard_begin=0, shard_end=14), FAKE, stream=0), "shard"),

@@ -434,3 +434,38 @@ def test_split_master_tracks_mixed_master():
     pe, _ = oracle.split_make(wj)
     assert np.array_equal(to_np(sp.arena.bufs["p"]), pe)
     free()
+
+
+@pytest.mark.parametrize("scale0,interval", [(65536.0, 3), (3e38, 2)])
+def test_dynamic_loss_scale_sequence(scale0, interval):
+    """fp16 AMP with the device-resident loss scale: 12 iterations of check +
+    step, overflows planted at two seeded iterations.  After every iteration the
+    device scale, tracker and step counter equal the oracle's, and at the end every
+    buffer matches element by element.  The 3e38 start exercises a refused growth."""
+    case = Case("mixed", EDGE_SIZES, seed=1700, p_dtype="f16", loss_scale=65536.0, align_elems=3)
+    tl = case.tensor_list()
+    hg, ho = hp_pair()
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    state = A.loss_scale_state(scale0)
+    scaler = A.LossScaler(2.0, 0.5, interval)
+    ls = oracle.LossScale(scale=scale0, tracker=0, growth=2.0, backoff=0.5, interval=interval)
+    rng = np.random.default_rng(33)
+    bad_iters = set(int(x) for x in rng.choice(np.arange(1, 12), size=2, replace=False))
+    for it in range(12):
+        if it:
+            case.refill_grads(it)
+        if it in bad_iters:
+            i = int(rng.choice([j for j, n in enumerate(EDGE_SIZES) if n]))
+            case.arena.view("g", i)[int(rng.integers(0, EDGE_SIZES[i]))] = float("inf")
+            case.host["g"] = to_np(case.arena.bufs["g"])
+        A.adamw_check_finite(A.F16, tl, flag)
+        A.adamw_multi_tensor_step_amp(A.MIXED, A.F16, tl, hg, case.d_step, flag, state, scaler)
+        case.step = oracle.amp_step_list("mixed", case.oracle_tensors(), ho, case.step, ls)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == int(it in bad_iters)
+        assert np.float32(state[0].item()) == np.float32(ls.scale), (it, state[0].item(), ls.scale)
+        assert int(state.view(torch.int32)[1].item()) == ls.tracker, it
+        assert int(case.d_step.item()) == case.step, it
+    case.compare_all(f"amp-{scale0}")
+    assert case.step == 12 - len(bad_iters)
+    free()

@@ -43,6 +43,10 @@ MUTANTS = [
     ("split tie goes down", "hi = (w >> 16) + (low >= 0x8000u ? 1u : 0u);", "hi = (w >> 16) + (low > 0x8000u ? 1u : 0u);"),
     ("split truncates", "hi = (w >> 16) + (low >= 0x8000u ? 1u : 0u);", "hi = (w >> 16);"),
     ("remainder zero-extended", "int32_t rem = (int32_t)(int16_t)r;", "int32_t rem = (int32_t)r;"),
+    ("growth one step early", "if (run == interval) {", "if (run + 1 >= interval) {"),
+    ("backoff keeps tracker", "*scale = *scale * backoff;\n        *tracker = 0;", "*scale = *scale * backoff;"),
+    ("growth without finiteness test", "if (isfinite(grown)) *scale = grown;", "*scale = grown;"),
+    ("inverse scale in float", "return (float)(1.0 / (double)scale);", "return 1.0f / (scale * 1.0000001f);"),
     ("split decay dropped", "w = w * decay - step_size * u;\n        oracle_split_make", "w = w - step_size * u;\n        oracle_split_make"),
 ]
 
@@ -64,6 +68,12 @@ PINS = [
     (pins.test_f16_narrow_vs_numpy, ()),
     (pins.test_kahan_tracks_constant_tiny_updates, ()),
     (pins.test_zero_gradient_kahan_tracks_decay, ()),
+]
+AMP_PINS = [
+    (pins.test_loss_scale_rule_matches_torch, (2.0, 0.5, 3, 65536.0)),
+    (pins.test_loss_scale_rule_matches_torch, (2.0, 0.5, 2, 3e38)),
+    (pins.test_inv_scale, ()),
+    (pins.test_amp_step_skips_and_backs_off, ()),
 ]
 SPLIT_PINS = [
     (pins.test_split_step_equals_mixed_step, (pins.HParams(),)),
@@ -89,7 +99,10 @@ def test_mutant_is_killed(tmpdir_mut, name, orig, bad):
     open(csrc, "w").write(mutated)
     subprocess.run(["gcc", *CFLAGS, "-o", so, csrc, "-lm"], check=True)
     lib = _bind(ctypes.CDLL(so))
-    for pin, args in (SPLIT_PINS + PINS if name.startswith("split") or "remainder" in name else PINS + SPLIT_PINS):
+    amp = any(w in name for w in ("growth", "backoff", "inverse scale"))
+    split = name.startswith("split") or "remainder" in name
+    order = AMP_PINS + PINS + SPLIT_PINS if amp else SPLIT_PINS + PINS + AMP_PINS if split else PINS + SPLIT_PINS + AMP_PINS
+    for pin, args in order:
         try:
             pin(lib, *args)
         except AssertionError:

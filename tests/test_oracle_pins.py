@@ -629,3 +629,59 @@ def test_split_step_equals_mixed_step(olib, hp):
     assert np.array_equal(ms, mm) and np.array_equal(vs, vm)
     pe, _ = oracle.split_make(master, olib)
     assert np.array_equal(ps, pe)
+
+
+# ---------------------------------------------------------------------------
+# Dynamic loss scaling (fp16 AMP)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("growth,backoff,interval,scale0", [
+    (2.0, 0.5, 3, 65536.0), (2.0, 0.5, 1, 1.0), (1.5, 0.25, 4, 1000.0), (2.0, 0.5, 2, 3e38),
+    (2.0, 0.5, 5, 1e-30), (1.0, 1.0, 3, 7.0)])
+def test_loss_scale_rule_matches_torch(olib, growth, backoff, interval, scale0):
+    """The scale/tracker trajectory over a random overflow pattern equals torch's
+    own loss-scale update (torch._amp_update_scale_, the op behind GradScaler.update),
+    including the growth that would overflow fp32 and is refused."""
+    rng = np.random.default_rng(31)
+    flags = (rng.random(300) < 0.15).astype(int)
+    ls = oracle.LossScale(scale=scale0, tracker=0, growth=growth, backoff=backoff, interval=interval)
+    ts = torch.tensor([scale0], dtype=torch.float32)
+    tt = torch.tensor([0], dtype=torch.int32)
+    for f in flags:
+        ls.update(bool(f), olib)
+        torch._amp_update_scale_(ts, tt, torch.tensor([float(f)]), growth, backoff, interval)
+        assert np.float32(ls.scale) == np.float32(ts.item()) and ls.tracker == int(tt.item())
+
+
+def test_inv_scale(olib):
+    ls = oracle.LossScale()
+    for e in range(-20, 40):
+        ls.scale = float(2.0 ** e)
+        assert ls.inv(olib) == 2.0 ** -e
+    for x in (3.0, 1000.0, 12345.678):
+        ls.scale = float(np.float32(x))
+        assert ls.inv(olib) == float(np.float32(1.0 / np.float64(np.float32(x))))
+
+
+def test_amp_step_skips_and_backs_off(olib):
+    """An overflow leaves every buffer and the counter unchanged and halves the
+    scale; clean steps unscale by 1/scale, i.e. act like the bf16-equivalent step."""
+    rng = np.random.default_rng(32)
+    n = 4000
+    w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g = (rng.standard_normal(n) * 65.536).astype(np.float16).view(np.uint16)
+    t = [dict(p=w.astype(np.float16).view(np.uint16), g=g.copy(), master=w.copy(),
+              m=np.zeros(n, np.float32), v=np.zeros(n, np.float32))]
+    ref = [{k: a.copy() for k, a in t[0].items()}]
+    ls = oracle.LossScale(scale=65536.0, interval=2)
+    step = oracle.amp_step_list("mixed", t, HParams(), 0, ls, lib=olib)
+    assert step == 1 and ls.scale == 65536.0 and ls.tracker == 1
+    oracle.step_list("mixed", ref, HParams(inv_scale=1 / 65536), 0, p_is_f16=True, lib=olib)
+    for k in t[0]:
+        assert np.array_equal(t[0][k], ref[0][k])
+    t[0]["g"][17] = 0x7C00
+    before = {k: a.copy() for k, a in t[0].items()}
+    step = oracle.amp_step_list("mixed", t, HParams(), step, ls, lib=olib)
+    assert step == 1 and ls.scale == 32768.0 and ls.tracker == 0
+    for k in t[0]:
+        assert np.array_equal(t[0][k], before[k])
