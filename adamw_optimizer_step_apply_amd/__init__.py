@@ -35,7 +35,8 @@ STREAM_PARAM, STREAM_GRAD, STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_AUX = range
 NUM_STREAMS = 5
 _STATUS = {0: "ADAMW_OK", 1: "ADAMW_E_INVALID", 2: "ADAMW_E_UNSUPPORTED", 3: "ADAMW_E_NOMEM", 4: "ADAMW_E_HIP"}
 
-EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_amp", "adamw_check_finite",
+EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_amp", "adamw_pure_multi_tensor_step",
+            "adamw_check_finite",
             "adamw_last_error", "adamw_release_workspace", "adamw_abi_version", "adamw_plan_inspect",
             "adamw_set_chunk_elems")
 
@@ -43,6 +44,10 @@ EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_am
 class adamw_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("inv_loss_scale", ctypes.c_float)]
+
+
+class adamw_pure_precision(ctypes.Structure):
+    _fields_ = [("exp_avg", ctypes.c_int), ("exp_avg_sq", ctypes.c_int), ("kahan", ctypes.c_int32)]
 
 
 class adamw_loss_scaler(ctypes.Structure):
@@ -78,6 +83,10 @@ def _declare(_lib):
     _lib.adamw_multi_tensor_step_amp.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list),
                                                  ctypes.POINTER(adamw_hparams), _vp, _vp, _vp,
                                                  ctypes.POINTER(adamw_loss_scaler), _vp]
+    _lib.adamw_pure_multi_tensor_step.restype = ctypes.c_int
+    _lib.adamw_pure_multi_tensor_step.argtypes = [ctypes.POINTER(adamw_pure_precision),
+                                                  ctypes.POINTER(adamw_tensor_list), ctypes.POINTER(adamw_hparams),
+                                                  _vp, _vp, _vp]
     _lib.adamw_check_finite.restype = ctypes.c_int
     _lib.adamw_check_finite.argtypes = [ctypes.c_int, ctypes.POINTER(adamw_tensor_list), _vp, _vp]
     _lib.adamw_last_error.restype = ctypes.c_char_p
@@ -221,6 +230,27 @@ def adamw_multi_tensor_step_amp(mode: int, p_dtype: int, tensors: TensorList, hp
     _check(_lib.adamw_multi_tensor_step_amp(mode, p_dtype, ctypes.byref(tensors.c), ctypes.byref(h), _addr(d_step),
                                             _addr(d_found_inf), _addr(d_scale), ctypes.byref(sc),
                                             _stream(stream)))
+
+
+@dataclass
+class PurePrecision:
+    """State precisions of a pure-bf16 step: exp_avg / exp_avg_sq dtype (F32 or
+    BF16) and whether the aux stream is a bf16 Kahan compensation buffer."""
+    exp_avg: int = BF16
+    exp_avg_sq: int = BF16
+    kahan: bool = True
+
+    def c(self) -> adamw_pure_precision:
+        return adamw_pure_precision(int(self.exp_avg), int(self.exp_avg_sq), int(bool(self.kahan)))
+
+
+def adamw_pure_multi_tensor_step(prec: PurePrecision, tensors: TensorList, hp, d_step, d_found_inf=None,
+                                 stream=None) -> None:
+    """Pure-bf16 step with chosen state precisions (C ABI adamw_pure_multi_tensor_step)."""
+    h = _hp(hp)
+    pc = prec.c()
+    _check(_lib.adamw_pure_multi_tensor_step(ctypes.byref(pc), ctypes.byref(tensors.c), ctypes.byref(h),
+                                             _addr(d_step), _addr(d_found_inf), _stream(stream)))
 
 
 def adamw_check_finite(g_dtype: int, grads: TensorList, d_found_inf, stream=None) -> None:

@@ -26,8 +26,8 @@ namespace adamw {
 hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32_t* d_found_inf,
                            LaunchScalars* d_scalars, adamw_loss_scale_state* d_amp, const adamw_loss_scaler& scaler,
                            hipStream_t stream);
-hipError_t launch_update(adamw_mode mode, adamw_dtype p_dtype, const DevSeg* segs, const DevChunk* chunks,
-                         int64_t n_chunks, const LaunchScalars* d_scalars, hipStream_t stream);
+hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
+                         const LaunchScalars* d_scalars, hipStream_t stream);
 hipError_t launch_check(adamw_dtype g_dtype, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
                         int32_t* d_flag, hipStream_t stream);
 
@@ -109,11 +109,11 @@ adamw_status get_workspace(hipStream_t stream, StreamWorkspace** out)
 // Returns (in *out) a slot of `ws` holding the device plan of (mode, dtype,
 // list, for_check): a cached one if every input matches, else the least
 // recently used slot, re-planned and re-uploaded.
-adamw_status ensure_plan(StreamWorkspace& ws, adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
-                         bool for_check, int64_t chunk_elems, hipStream_t stream, PlanSlot** out)
+adamw_status ensure_plan(StreamWorkspace& ws, int64_t tag, const int esz[kStreams], const adamw_tensor_list* list,
+                         int64_t chunk_elems, hipStream_t stream, PlanSlot** out)
 {
     std::vector<int64_t> key;
-    plan_key(mode, p_dtype, list, for_check, chunk_elems, key);
+    plan_key(tag, esz, list, chunk_elems, key);
     auto& plans = ws.plans;
     for (size_t i = 0; i < plans.size(); ++i) {
         if (plans[i]->valid && plans[i]->key == key) {
@@ -130,7 +130,7 @@ adamw_status ensure_plan(StreamWorkspace& ws, adamw_mode mode, adamw_dtype p_dty
 
     Plan plan;
     std::string err;
-    adamw_status st = build_plan(mode, p_dtype, list, for_check, chunk_elems, &plan, err);
+    adamw_status st = build_plan(esz, list, chunk_elems, &plan, err);
     if (st != ADAMW_OK) return fail(st, err);
 
     const size_t seg_bytes = plan.segs.size() * sizeof(DevSeg);
@@ -217,13 +217,28 @@ adamw_status check_scaler(const adamw_loss_scaler* sc)
     return ADAMW_OK;
 }
 
-adamw_status do_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, const adamw_hparams* hp,
-                     int32_t* d_step, const int32_t* d_found_inf, void* hip_stream,
-                     adamw_loss_scale_state* d_amp = nullptr, const adamw_loss_scaler* scaler = nullptr)
+// What one step launches: the update kernel and its streams' element sizes.
+struct StepKind {
+    int kernel;
+    int esz[kStreams];
+};
+
+StepKind kind_of_mode(adamw_mode mode, adamw_dtype p_dtype)
 {
+    StepKind k{};
+    mode_esizes(mode, p_dtype, false, k.esz);
+    k.kernel = mode == ADAMW_PURE_KAHAN ? kKernelKahan
+             : mode == ADAMW_MIXED_SPLIT ? kKernelSplit
+             : p_dtype == ADAMW_F16 ? kKernelMixedF16 : kKernelMixedBf16;
+    return k;
+}
+
+adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const adamw_hparams* hp, int32_t* d_step,
+                     const int32_t* d_found_inf, void* hip_stream, adamw_loss_scale_state* d_amp = nullptr,
+                     const adamw_loss_scaler* scaler = nullptr)
+{
+    adamw_status st;
     std::string err;
-    adamw_status st = check_mode(mode, p_dtype, false, err);
-    if (st != ADAMW_OK) return fail(st, err);
     if ((st = check_hparams(hp)) != ADAMW_OK) return st;
     if (!d_step) return fail(ADAMW_E_INVALID, "d_step is null");
     if ((uintptr_t)d_step % 4 || (uintptr_t)d_found_inf % 4)
@@ -232,7 +247,7 @@ adamw_status do_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_li
 
     // the whole list is validated before the first HIP call
     const int64_t chunk_elems = g_chunk_elems;
-    st = build_plan(mode, p_dtype, list, false, chunk_elems, nullptr, err);
+    st = build_plan(kind.esz, list, chunk_elems, nullptr, err);
     if (st != ADAMW_OK) return fail(st, err);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     StreamWorkspace* ws = nullptr;
@@ -244,12 +259,21 @@ adamw_status do_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_li
         if (e != hipSuccess) { ws->scalars = nullptr; return fail(ADAMW_E_NOMEM, "hipMalloc of the scalar block failed"); }
     }
     PlanSlot* plan = nullptr;
-    if ((st = ensure_plan(*ws, mode, p_dtype, list, false, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
+    if ((st = ensure_plan(*ws, kind.kernel, kind.esz, list, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
     const adamw_loss_scaler no_scaler{1.0f, 1.0f, 1};
     e = launch_prologue(*hp, d_step, d_found_inf, ws->scalars, d_amp, scaler ? *scaler : no_scaler, stream);
     if (e != hipSuccess) return hip_fail("prologue launch", e);
-    e = launch_update(mode, p_dtype, plan->segs(), plan->chunks(), plan->n_chunks, ws->scalars, stream);
+    e = launch_update(kind.kernel, plan->segs(), plan->chunks(), plan->n_chunks, ws->scalars, stream);
     if (e != hipSuccess) return hip_fail("update launch", e);
+    return ADAMW_OK;
+}
+
+adamw_status mode_kind(adamw_mode mode, adamw_dtype p_dtype, StepKind* out)
+{
+    std::string err;
+    adamw_status st = check_mode(mode, p_dtype, false, err);
+    if (st != ADAMW_OK) return fail(st, err);
+    *out = kind_of_mode(mode, p_dtype);
     return ADAMW_OK;
 }
 
@@ -265,7 +289,30 @@ adamw_status adamw_multi_tensor_step(adamw_mode mode, adamw_dtype p_dtype, const
                                      void* hip_stream)
 {
     g_err.clear();
-    return do_step(mode, p_dtype, list, hp, d_step, d_found_inf, hip_stream);
+    StepKind kind;
+    adamw_status st = mode_kind(mode, p_dtype, &kind);
+    if (st != ADAMW_OK) return st;
+    return do_step(kind, list, hp, d_step, d_found_inf, hip_stream);
+}
+
+adamw_status adamw_pure_multi_tensor_step(const adamw_pure_precision* prec, const adamw_tensor_list* list,
+                                          const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
+                                          void* hip_stream)
+{
+    g_err.clear();
+    if (!prec) return fail(ADAMW_E_INVALID, "precision descriptor is null");
+    const bool ok_m = prec->exp_avg == ADAMW_F32 || prec->exp_avg == ADAMW_BF16;
+    const bool ok_v = prec->exp_avg_sq == ADAMW_F32 || prec->exp_avg_sq == ADAMW_BF16;
+    if (!ok_m || !ok_v) return fail(ADAMW_E_UNSUPPORTED, "exp_avg / exp_avg_sq dtype must be ADAMW_F32 or ADAMW_BF16");
+    const int m32 = prec->exp_avg == ADAMW_F32, v32 = prec->exp_avg_sq == ADAMW_F32, kahan = prec->kahan != 0;
+    StepKind kind{};
+    kind.kernel = kKernelPure + 4 * m32 + 2 * v32 + kahan;
+    kind.esz[ADAMW_STREAM_PARAM] = 2;
+    kind.esz[ADAMW_STREAM_GRAD] = 2;
+    kind.esz[ADAMW_STREAM_EXP_AVG] = m32 ? 4 : 2;
+    kind.esz[ADAMW_STREAM_EXP_AVG_SQ] = v32 ? 4 : 2;
+    kind.esz[ADAMW_STREAM_AUX] = kahan ? 2 : 0;
+    return do_step(kind, list, hp, d_step, d_found_inf, hip_stream);
 }
 
 adamw_status adamw_multi_tensor_step_amp(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
@@ -278,7 +325,9 @@ adamw_status adamw_multi_tensor_step_amp(adamw_mode mode, adamw_dtype p_dtype, c
     if (!d_scale || (uintptr_t)d_scale % 4) return fail(ADAMW_E_INVALID, "d_scale is null or not 4-byte aligned");
     adamw_status st = check_scaler(scaler);
     if (st != ADAMW_OK) return st;
-    return do_step(mode, p_dtype, list, hp, d_step, d_found_inf, hip_stream, d_scale, scaler);
+    StepKind kind;
+    if ((st = mode_kind(mode, p_dtype, &kind)) != ADAMW_OK) return st;
+    return do_step(kind, list, hp, d_step, d_found_inf, hip_stream, d_scale, scaler);
 }
 
 adamw_status adamw_step(adamw_mode mode, adamw_dtype p_dtype, int64_t n, void* param, const void* grad,
@@ -311,7 +360,10 @@ adamw_status adamw_step(adamw_mode mode, adamw_dtype p_dtype, int64_t n, void* p
     list.flat_mask = 0;
     if (n > 0 && (!param || !grad || !exp_avg || !exp_avg_sq || !aux))
         return fail(ADAMW_E_INVALID, "a required buffer pointer is null");
-    return do_step(mode, p_dtype, &list, hp, d_step, d_found_inf, hip_stream);
+    StepKind kind;
+    adamw_status st = mode_kind(mode, p_dtype, &kind);
+    if (st != ADAMW_OK) return st;
+    return do_step(kind, &list, hp, d_step, d_found_inf, hip_stream);
 }
 
 adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* grads, int32_t* d_found_inf,
@@ -323,16 +375,17 @@ adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* gr
     if (st != ADAMW_OK) return fail(st, err);
     if (!d_found_inf || (uintptr_t)d_found_inf % 4) return fail(ADAMW_E_INVALID, "d_found_inf is null or misaligned");
     if ((st = basic_list_check(grads)) != ADAMW_OK) return st;
-    const int64_t chunk_elems = g_chunk_elems;
-    st = build_plan(ADAMW_MIXED, g_dtype, grads, true, chunk_elems, nullptr, err);
+    const int64_t chunk_elems = g_chunk_elems * kCheckChunkMult;
+    int esz[kStreams];
+    mode_esizes(ADAMW_MIXED, g_dtype, true, esz);
+    st = build_plan(esz, grads, chunk_elems, nullptr, err);
     if (st != ADAMW_OK) return fail(st, err);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     StreamWorkspace* ws = nullptr;
     if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
     std::lock_guard<std::mutex> lk(ws->mu);
     PlanSlot* plan = nullptr;
-    if ((st = ensure_plan(*ws, ADAMW_MIXED, g_dtype, grads, true, chunk_elems, stream, &plan)) != ADAMW_OK)
-        return st;
+    if ((st = ensure_plan(*ws, -1, esz, grads, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
     hipError_t e = launch_check(g_dtype, plan->segs(), plan->chunks(), plan->n_chunks, d_found_inf, stream);
     if (e != hipSuccess) return hip_fail("check launch", e);
     return ADAMW_OK;
@@ -361,7 +414,11 @@ int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_ten
     g_err.clear();
     Plan plan;
     std::string err;
-    adamw_status st = build_plan(mode, p_dtype, list, for_check != 0, g_chunk_elems, &plan, err);
+    adamw_status st = check_mode(mode, p_dtype, for_check != 0, err);
+    int esz[kStreams];
+    mode_esizes(mode, p_dtype, for_check != 0, esz);
+    if (st == ADAMW_OK)
+        st = build_plan(esz, list, for_check ? g_chunk_elems * kCheckChunkMult : g_chunk_elems, &plan, err);
     if (st != ADAMW_OK) {
         g_err = err;
         return -1;

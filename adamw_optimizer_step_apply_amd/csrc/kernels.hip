@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "adamw.h"
 #include "layout.hpp"
 
@@ -297,8 +299,8 @@ __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
 #define ADAMW_WPE_ATTR
 #endif
 
-// MODE 0: mixed bf16, 1: mixed fp16, 2: pure bf16 + Kahan, 3: mixed bf16 with the
-// master split into param + int16 remainder
+// MODE 0: mixed bf16, 1: mixed fp16, 3: mixed bf16 with the master split into
+// param + int16 remainder
 template <int MODE>
 __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const DevSeg* __restrict__ segs,
                                                         const DevChunk* __restrict__ chunks,
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
 {
     if (sc->skip) return;
     constexpr bool F16 = (MODE == 1);   // MODE 3 uses bf16 param/grad
-    constexpr int NTM = ADAMW_NT_MIXED, NTK = ADAMW_NT_KAHAN;
+    constexpr int NTM = ADAMW_NT_MIXED;
     const Coef c = load_coef(sc);
     const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
     const DevSeg& sg = segs[ch.seg];
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
                 r[i] = (uint16_t)ri;
             }
         }
-    } else if constexpr (MODE != 2) {
+    } else {
         GLOBAL uint16_t* __restrict__ p = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_PARAM], off);
         const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
         GLOBAL float* __restrict__ m = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
@@ -440,73 +442,145 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
                 p[i] = narrow1<F16>(nw);
             }
         }
-    } else {
-        GLOBAL uint16_t* __restrict__ p = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_PARAM], off);
-        const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
-        GLOBAL uint16_t* __restrict__ m = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
-        GLOBAL uint16_t* __restrict__ v = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_EXP_AVG_SQ], off);
-        GLOBAL uint16_t* __restrict__ cc = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_AUX], off);
-        if (ch.n_kind & kVecBit) {
-            const uint32_t npack = n / kPack;
-            const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
-            GLOBAL u32x4* __restrict__ p4 = reinterpret_cast<GLOBAL u32x4*>(p);
-            GLOBAL u32x4* __restrict__ m4 = reinterpret_cast<GLOBAL u32x4*>(m);
-            GLOBAL u32x4* __restrict__ v4 = reinterpret_cast<GLOBAL u32x4*>(v);
-            GLOBAL u32x4* __restrict__ c4 = reinterpret_cast<GLOBAL u32x4*>(cc);
-            for (uint32_t k0 = tid; k0 < npack; k0 += kBlock * kUnroll) {
-                u32x4 G[kUnroll], P[kUnroll], M[kUnroll], V[kUnroll], C[kUnroll];
+    }
+}
+
+// Pure bf16 parameters with chosen state precisions: M32 / V32 = fp32 exp_avg /
+// exp_avg_sq (else bf16), KAHAN = bf16 compensation buffer in the aux stream
+// (else none: p' = round(p * decay - step_size * u)).  <false, false, true> is
+// the pure-bf16 Kahan mode.
+template <bool M32, bool V32, bool KAHAN>
+__global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_pure_kernel(const DevSeg* __restrict__ segs,
+                                                                            const DevChunk* __restrict__ chunks,
+                                                                            const LaunchScalars* __restrict__ sc)
+{
+    if (sc->skip) return;
+    constexpr int NT = ADAMW_NT_KAHAN;
+    const Coef c = load_coef(sc);
+    const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
+    const DevSeg& sg = segs[ch.seg];
+    const uint32_t n = ch.n_kind & kCountMask;
+    const uint64_t off = ch.off;
+    const uint32_t tid = threadIdx.x;
+    using MT = typename std::conditional<M32, float, uint16_t>::type;
+    using VT = typename std::conditional<V32, float, uint16_t>::type;
+    GLOBAL uint16_t* __restrict__ p = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_PARAM], off);
+    const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
+    GLOBAL MT* __restrict__ m = gptr<MT>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
+    GLOBAL VT* __restrict__ v = gptr<VT>(sg.ptr[ADAMW_STREAM_EXP_AVG_SQ], off);
+    GLOBAL uint16_t* __restrict__ cc = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_AUX], off);
+
+    if (ch.n_kind & kVecBit) {
+        const uint32_t npack = n / kPack;
+        const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
+        GLOBAL u32x4* __restrict__ p4 = reinterpret_cast<GLOBAL u32x4*>(p);
+        GLOBAL u32x4* __restrict__ c4 = reinterpret_cast<GLOBAL u32x4*>(cc);
+        // a pack of 8 moments is one dwordx4 in bf16, two in fp32
+        constexpr int MW = M32 ? 2 : 1, VW = V32 ? 2 : 1;
+        GLOBAL u32x4* __restrict__ m4 = reinterpret_cast<GLOBAL u32x4*>(m);
+        GLOBAL u32x4* __restrict__ v4 = reinterpret_cast<GLOBAL u32x4*>(v);
+        for (uint32_t k0 = tid; k0 < npack; k0 += kBlock * kUnroll) {
+            u32x4 G[kUnroll], P[kUnroll], C[kUnroll], M[kUnroll][MW], V[kUnroll][VW];
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const uint32_t k = k0 + u * kBlock;
-                    if (k < npack) {
-                        G[u] = ld<NTK>(g4 + k); P[u] = ld<NTK>(p4 + k); M[u] = ld<NTK>(m4 + k); V[u] = ld<NTK>(v4 + k);
-                        C[u] = ld<NTK>(c4 + k);
-                    }
+            for (int u = 0; u < kUnroll; ++u) {
+                const uint32_t k = k0 + u * kBlock;
+                if (k < npack) {
+                    G[u] = ld<NT>(g4 + k);
+                    P[u] = ld<NT>(p4 + k);
+#pragma unroll
+                    for (int q = 0; q < MW; ++q) M[u][q] = ld<NT>(m4 + MW * k + q);
+#pragma unroll
+                    for (int q = 0; q < VW; ++q) V[u][q] = ld<NT>(v4 + VW * k + q);
+                    if constexpr (KAHAN) C[u] = ld<NT>(c4 + k);
                 }
+            }
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const uint32_t k = k0 + u * kBlock;
-                    if (k < npack) {
-                        const uint32_t gw[4] = {G[u].x, G[u].y, G[u].z, G[u].w};
-                        const uint32_t pw[4] = {P[u].x, P[u].y, P[u].z, P[u].w};
-                        const uint32_t mw[4] = {M[u].x, M[u].y, M[u].z, M[u].w};
-                        const uint32_t vw[4] = {V[u].x, V[u].y, V[u].z, V[u].w};
-                        const uint32_t cw[4] = {C[u].x, C[u].y, C[u].z, C[u].w};
-                        uint32_t po[4], mo[4], vo[4], co[4];
+            for (int u = 0; u < kUnroll; ++u) {
+                const uint32_t k = k0 + u * kBlock;
+                if (k < npack) {
+                    const uint32_t* gw = reinterpret_cast<const uint32_t*>(&G[u]);
+                    const uint32_t* pw = reinterpret_cast<const uint32_t*>(&P[u]);
+                    const uint32_t* cw = reinterpret_cast<const uint32_t*>(&C[u]);
+                    uint32_t* mw = reinterpret_cast<uint32_t*>(M[u]);   // 4 (bf16) or 8 (fp32) words
+                    uint32_t* vw = reinterpret_cast<uint32_t*>(V[u]);
+                    uint32_t po[4], co[4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const f32x2 gg = widen2<false>(gw[j]);
-                            const f32x2 pp = widen2<false>(pw[j]);
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x2 gg = widen2<false>(gw[j]);
+                        const f32x2 pp = widen2<false>(pw[j]);
+                        float ma, mb, va, vb;
+                        if constexpr (M32) {
+                            ma = __uint_as_float(mw[2 * j]);
+                            mb = __uint_as_float(mw[2 * j + 1]);
+                        } else {
+                            const f32x2 t2 = widen2<false>(mw[j]);
+                            ma = t2.x;
+                            mb = t2.y;
+                        }
+                        if constexpr (V32) {
+                            va = __uint_as_float(vw[2 * j]);
+                            vb = __uint_as_float(vw[2 * j + 1]);
+                        } else {
+                            const f32x2 t2 = widen2<false>(vw[j]);
+                            va = t2.x;
+                            vb = t2.y;
+                        }
+                        if constexpr (KAHAN) {
                             const f32x2 cf = widen2<false>(cw[j]);
-                            const f32x2 m2 = widen2<false>(mw[j]);
-                            const f32x2 v2 = widen2<false>(vw[j]);
-                            float ma = m2.x, mb = m2.y, va = v2.x, vb = v2.y, sa, sb;
+                            float sa, sb;
                             const float ta = kahan_sum(gg.x, pp.x, cf.x, ma, va, c, sa);
                             const float tb = kahan_sum(gg.y, pp.y, cf.y, mb, vb, c, sb);
                             po[j] = narrow2<false>(ta, tb);
                             const f32x2 pn = widen2<false>(po[j]);
                             co[j] = narrow2<false>(sa - (pn.x - pp.x), sb - (pn.y - pp.y));
-                            mo[j] = narrow2<false>(ma, mb);
-                            vo[j] = narrow2<false>(va, vb);
+                        } else {
+                            float wa = pp.x, wb = pp.y;
+                            mixed_elem(gg.x, wa, ma, va, c);
+                            mixed_elem(gg.y, wb, mb, vb, c);
+                            po[j] = narrow2<false>(wa, wb);
                         }
-                        st<NTK>(p4 + k, u32x4{po[0], po[1], po[2], po[3]});
-                        st<NTK>(m4 + k, u32x4{mo[0], mo[1], mo[2], mo[3]});
-                        st<NTK>(v4 + k, u32x4{vo[0], vo[1], vo[2], vo[3]});
-                        st<NTK>(c4 + k, u32x4{co[0], co[1], co[2], co[3]});
+                        if constexpr (M32) {
+                            mw[2 * j] = __float_as_uint(ma);
+                            mw[2 * j + 1] = __float_as_uint(mb);
+                        } else {
+                            mw[j] = narrow2<false>(ma, mb);
+                        }
+                        if constexpr (V32) {
+                            vw[2 * j] = __float_as_uint(va);
+                            vw[2 * j + 1] = __float_as_uint(vb);
+                        } else {
+                            vw[j] = narrow2<false>(va, vb);
+                        }
                     }
+                    st<NT>(p4 + k, u32x4{po[0], po[1], po[2], po[3]});
+#pragma unroll
+                    for (int q = 0; q < MW; ++q) st<NT>(m4 + MW * k + q, M[u][q]);
+#pragma unroll
+                    for (int q = 0; q < VW; ++q) st<NT>(v4 + VW * k + q, V[u][q]);
+                    if constexpr (KAHAN) st<NT>(c4 + k, u32x4{co[0], co[1], co[2], co[3]});
                 }
             }
-        } else {
-            for (uint32_t i = tid; i < n; i += kBlock) {
-                const float pf = widen1<false>(p[i]);
-                float mi = widen1<false>(m[i]), vi = widen1<false>(v[i]), s;
-                const float tot = kahan_sum(widen1<false>(g[i]), pf, widen1<false>(cc[i]), mi, vi, c, s);
+        }
+    } else {
+        for (uint32_t i = tid; i < n; i += kBlock) {
+            const float pf = widen1<false>(p[i]);
+            float mi, vi;
+            if constexpr (M32) mi = m[i]; else mi = widen1<false>(m[i]);
+            if constexpr (V32) vi = v[i]; else vi = widen1<false>(v[i]);
+            const float gi = widen1<false>(g[i]);
+            if constexpr (KAHAN) {
+                float s;
+                const float tot = kahan_sum(gi, pf, widen1<false>(cc[i]), mi, vi, c, s);
                 const uint16_t pn = narrow1<false>(tot);
                 cc[i] = narrow1<false>(s - (widen1<false>(pn) - pf));
                 p[i] = pn;
-                m[i] = narrow1<false>(mi);
-                v[i] = narrow1<false>(vi);
+            } else {
+                float w = pf;
+                mixed_elem(gi, w, mi, vi, c);
+                p[i] = narrow1<false>(w);
             }
+            if constexpr (M32) m[i] = mi; else m[i] = narrow1<false>(mi);
+            if constexpr (V32) v[i] = vi; else v[i] = narrow1<false>(vi);
         }
     }
 }
@@ -589,19 +663,32 @@ hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32
 #define ADAMW_LDS_KAHAN 81920
 #endif
 
-hipError_t launch_update(adamw_mode mode, adamw_dtype p_dtype, const DevSeg* segs, const DevChunk* chunks,
-                         int64_t n_chunks, const LaunchScalars* d_scalars, hipStream_t stream)
+hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
+                         const LaunchScalars* d_scalars, hipStream_t stream)
 {
     if (n_chunks <= 0) return hipSuccess;
     const dim3 grid((unsigned)n_chunks), block(kBlock);
-    if (mode == ADAMW_PURE_KAHAN)
-        hipLaunchKernelGGL(update_kernel<2>, grid, block, ADAMW_LDS_KAHAN, stream, segs, chunks, d_scalars);
-    else if (mode == ADAMW_MIXED_SPLIT)
-        hipLaunchKernelGGL(update_kernel<3>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
-    else if (p_dtype == ADAMW_F16)
-        hipLaunchKernelGGL(update_kernel<1>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
-    else
+    switch (kernel) {
+    case kKernelMixedBf16:
         hipLaunchKernelGGL(update_kernel<0>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
+        break;
+    case kKernelMixedF16:
+        hipLaunchKernelGGL(update_kernel<1>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
+        break;
+    case kKernelSplit:
+        hipLaunchKernelGGL(update_kernel<3>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
+        break;
+#define ADAMW_PURE_CASE(M, V, K)                                                                          \
+    case kKernelPure + (M) * 4 + (V) * 2 + (K):                                                            \
+        hipLaunchKernelGGL((update_pure_kernel<M, V, K>), grid, block, ADAMW_LDS_KAHAN, stream, segs, chunks, \
+                           d_scalars);                                                                     \
+        break;
+        ADAMW_PURE_CASE(0, 0, 0) ADAMW_PURE_CASE(0, 0, 1) ADAMW_PURE_CASE(0, 1, 0) ADAMW_PURE_CASE(0, 1, 1)
+        ADAMW_PURE_CASE(1, 0, 0) ADAMW_PURE_CASE(1, 0, 1) ADAMW_PURE_CASE(1, 1, 0) ADAMW_PURE_CASE(1, 1, 1)
+#undef ADAMW_PURE_CASE
+    default:
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -28,6 +28,14 @@ constexpr int64_t kElemChunkElems = 4096;       // element chunk: 16 elements pe
 #endif
 constexpr int kCheckChunkMult = ADAMW_CHECK_CHUNK_MULT;
 
+// Update kernels, by launch id.  The pure-bf16 family adds
+// 4 * (fp32 exp_avg) + 2 * (fp32 exp_avg_sq) + (Kahan compensation).
+constexpr int kKernelMixedBf16 = 0;
+constexpr int kKernelMixedF16 = 1;
+constexpr int kKernelSplit = 3;
+constexpr int kKernelPure = 4;
+constexpr int kKernelKahan = kKernelPure + 1;   // bf16 moments + compensation
+
 // One segment: the device address of its element 0 in each stream (0 for a
 // stream the launch does not touch).
 struct alignas(64) DevSeg {

@@ -18,16 +18,17 @@
 
 namespace adamw {
 
-static bool stream_active(int s, bool for_check) { return for_check ? s == ADAMW_STREAM_GRAD : true; }
-
-int stream_esize(adamw_mode mode, adamw_dtype p_dtype, int s, bool for_check)
+void mode_esizes(adamw_mode mode, adamw_dtype p_dtype, bool for_check, int esz[kStreams])
 {
     (void)p_dtype;
-    if (!stream_active(s, for_check)) return 0;
-    if (for_check || s == ADAMW_STREAM_PARAM || s == ADAMW_STREAM_GRAD) return 2;
-    if (mode == ADAMW_MIXED) return 4;
-    if (mode == ADAMW_MIXED_SPLIT) return s == ADAMW_STREAM_AUX ? 2 : 4;
-    return 2;
+    for (int s = 0; s < kStreams; ++s) esz[s] = 0;
+    esz[ADAMW_STREAM_GRAD] = 2;
+    if (for_check) return;
+    esz[ADAMW_STREAM_PARAM] = 2;
+    const int state = mode == ADAMW_PURE_KAHAN ? 2 : 4;
+    esz[ADAMW_STREAM_EXP_AVG] = state;
+    esz[ADAMW_STREAM_EXP_AVG_SQ] = state;
+    esz[ADAMW_STREAM_AUX] = mode == ADAMW_MIXED ? 4 : 2;
 }
 
 adamw_status check_mode(adamw_mode mode, adamw_dtype p_dtype, bool for_check, std::string& err)
@@ -74,16 +75,14 @@ static void push_chunks(Plan& p, uint32_t seg, int64_t off, int64_t count, int64
     }
 }
 
-adamw_status build_plan(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, bool for_check,
-                        int64_t chunk_elems, Plan* outp, std::string& err)
+adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* list, int64_t chunk_elems, Plan* outp,
+                        std::string& err)
 {
     char buf[256];
     Plan scratch;
     Plan& out = outp ? *outp : scratch;   // validation only when outp is null
     out = Plan();
     const bool build = outp != nullptr;
-    adamw_status st = check_mode(mode, p_dtype, for_check, err);
-    if (st != ADAMW_OK) return st;
     if (!list) { err = "tensor list is null"; return ADAMW_E_INVALID; }
     const int64_t nt = list->n_tensors;
     if (nt < 0) { err = "n_tensors < 0"; return ADAMW_E_INVALID; }
@@ -113,7 +112,7 @@ adamw_status build_plan(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor
     int esz[kStreams];
     bool flat[kStreams];
     for (int s = 0; s < kStreams; ++s) {
-        esz[s] = stream_esize(mode, p_dtype, s, for_check);
+        esz[s] = esz_in[s];
         flat[s] = (list->flat_mask >> s) & 1u;
         if (!esz[s]) continue;
         bool needed = flat[s] ? (e > b) : (nt > 0);
@@ -132,7 +131,6 @@ adamw_status build_plan(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor
         }
     }
     if (chunk_elems < 2048 || chunk_elems % 2048) { err = "bad chunk size"; return ADAMW_E_INVALID; }
-    if (for_check) chunk_elems *= kCheckChunkMult;
 
     int64_t base = 0, nseg = 0;
     for (int64_t i = 0; i < nt; ++i) {
@@ -190,15 +188,14 @@ adamw_status build_plan(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor
     return ADAMW_OK;
 }
 
-void plan_key(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, bool for_check,
-              int64_t chunk_elems, std::vector<int64_t>& key)
+void plan_key(int64_t tag, const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems,
+              std::vector<int64_t>& key)
 {
     const int64_t nt = list->n_tensors;
     key.clear();
-    key.reserve(8 + (size_t)nt * 6);
-    key.push_back((int64_t)mode);
-    key.push_back((int64_t)p_dtype);
-    key.push_back(for_check ? 1 : 0);
+    key.reserve(12 + (size_t)nt * 6);
+    key.push_back(tag);
+    for (int s = 0; s < kStreams; ++s) key.push_back(esz[s]);
     key.push_back(chunk_elems);
     key.push_back(nt);
     key.push_back(list->shard_begin);
@@ -206,7 +203,7 @@ void plan_key(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* lis
     key.push_back((int64_t)list->flat_mask);
     for (int64_t i = 0; i < nt; ++i) key.push_back(list->numel[i]);
     for (int s = 0; s < kStreams; ++s) {
-        if (!stream_esize(mode, p_dtype, s, for_check) || !list->ptr[s]) {
+        if (!esz[s] || !list->ptr[s]) {
             key.push_back(-1);
             continue;
         }

@@ -26,19 +26,21 @@ struct Plan {
     int64_t total = 0;           // elements covered
 };
 
-// Element size in bytes of stream s for this mode/dtype (0 = stream unused).
-int stream_esize(adamw_mode mode, adamw_dtype p_dtype, int s, bool for_check);
-
 // Checks the mode/dtype pair.  Returns ADAMW_OK or an error with `err` set.
 adamw_status check_mode(adamw_mode mode, adamw_dtype p_dtype, bool for_check, std::string& err);
 
-// Validates the list and, if `out` is non-null, builds the plan into it.
-// No HIP call.
-adamw_status build_plan(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, bool for_check,
-                        int64_t chunk_elems, Plan* out, std::string& err);
+// Element sizes of the five streams for a step in `mode` (or, with for_check,
+// for the overflow check, which reads the gradient only); 0 = stream unused.
+void mode_esizes(adamw_mode mode, adamw_dtype p_dtype, bool for_check, int esz[kStreams]);
 
-// The exact inputs a plan depends on, for caching.
-void plan_key(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, bool for_check,
-              int64_t chunk_elems, std::vector<int64_t>& key);
+// Validates the list against per-stream element sizes `esz` (0 = stream
+// unused) and, if `out` is non-null, builds the plan with vector chunks of
+// `chunk_elems` elements.  No HIP call.
+adamw_status build_plan(const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems, Plan* out,
+                        std::string& err);
+
+// The exact inputs a plan depends on, for caching (`tag` distinguishes kernels).
+void plan_key(int64_t tag, const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems,
+              std::vector<int64_t>& key);
 
 }  // namespace adamw

@@ -134,7 +134,7 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
     import workloads
     arena = workloads.make_state(mode, numels, device, seed, align_elems=128, p_dtype=p_dtype,
                                  loss_scale=loss_scale)
-    keys = workloads.STREAMS[mode]
+    keys = workloads.streams_of(mode)
     streams = [[arena.view(k, i) for i in range(len(numels))] for k in keys]
     return arena, streams
 
@@ -214,6 +214,9 @@ def main():
         print(json.dumps({"probes_gb_s": probes(N, stream), "n": N}), flush=True)
         return
     modes = (args.modes or ("f16amp" if wl.p_dtype == "f16" else "mixed,kahan")).split(",")
+    for mode in modes:
+        if mode.startswith("pure"):
+            BYTES[mode] = workloads.pure_traffic(mode)
 
     state = {}
     for i, mode in enumerate(modes):
@@ -242,8 +245,13 @@ def main():
             return
         if ev:
             ev[0].record(stream)
-        code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
-        A.adamw_multi_tensor_step(code, A.BF16, tl, hp, ctr, None, stream)
+        if mode.startswith("pure"):
+            m32, v32, kahan = workloads.parse_pure(mode)
+            prec = A.PurePrecision(A.F32 if m32 else A.BF16, A.F32 if v32 else A.BF16, kahan)
+            A.adamw_pure_multi_tensor_step(prec, tl, hp, ctr, None, stream)
+        else:
+            code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
+            A.adamw_multi_tensor_step(code, A.BF16, tl, hp, ctr, None, stream)
         if ev:
             ev[2].record(stream)
 
@@ -303,6 +311,11 @@ def main():
              "split": "mixed with the master split into bf16 param + int16 remainder",
              "f16amp": "fp16-AMP overflow check + mixed fp16 step with a device-resident dynamic loss scale "
                        "(65536 to start)"}
+    for mode in modes:
+        if mode.startswith("pure") and mode not in names:
+            m32, v32, kahan = workloads.parse_pure(mode)
+            names[mode] = (f"pure bf16 params, {'fp32' if m32 else 'bf16'} exp_avg, {'fp32' if v32 else 'bf16'} "
+                           f"exp_avg_sq, {'bf16 Kahan compensation' if kahan else 'no compensation'}")
     out = {
         "metric": "AdamW step Gparams/s + achieved HBM GB/s (% of peak), OPT-1.3B shape, 1 GPU",
         "value": round(value, 3),

@@ -170,6 +170,27 @@ adamw_status adamw_multi_tensor_step(adamw_mode mode, adamw_dtype p_dtype, const
                                      const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
                                      void* hip_stream);
 
+/* State precisions of a pure-bf16 step (the AnyPrecisionAdamW knobs of
+ * "[pure bf16 training] w/ AnyPrecisionAdamW and Kahan summation":
+ * momentum_dtype, variance_dtype, use_kahan_summation with a bf16
+ * compensation buffer). */
+typedef struct {
+    adamw_dtype exp_avg;     /* ADAMW_F32 or ADAMW_BF16 */
+    adamw_dtype exp_avg_sq;  /* ADAMW_F32 or ADAMW_BF16 */
+    int32_t kahan;           /* nonzero: stream 4 (aux) is a bf16 compensation buffer; 0: aux is unused */
+} adamw_pure_precision;
+
+/* Pure-bf16 step with chosen state precisions: param and grad bf16, exp_avg and
+ * exp_avg_sq in the dtypes of *prec (fp32 moments are kept and used exactly;
+ * bf16 ones are widened, updated in fp32 and stored rounded to nearest even).
+ * With kahan: the ADAMW_PURE_KAHAN rule; without: p = round_bf16(p*(1 - lr*wd)
+ * - (lr/(1-beta1^t))*u).  {ADAMW_BF16, ADAMW_BF16, 1} is ADAMW_PURE_KAHAN.
+ * Everything else (list, shard, counter, skip flag, errors) as
+ * adamw_multi_tensor_step. */
+adamw_status adamw_pure_multi_tensor_step(const adamw_pure_precision* prec, const adamw_tensor_list* list,
+                                          const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
+                                          void* hip_stream);
+
 /* Dynamic loss scaling state, in device memory owned by the caller (8 bytes,
  * 4-byte aligned).  growth_tracker counts consecutive steps taken since the
  * scale last changed and must start in [0, growth_interval). */

@@ -78,6 +78,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "oracle_split_make_n": (None, [_U32P, _U16P, _U16P, _I64]),
         "oracle_split_join_n": (None, [_U16P, _U16P, _U32P, _I64]),
         "oracle_inv_scale": (_F, [_F]),
+        "oracle_adamw_pure": (None, [_I64, _U16P, _U16P, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_void_p, _F, _F, _F, _F, _F, _F, _I64]),
         "oracle_update_loss_scale": (None, [ctypes.POINTER(_F), ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
                                             _F, _F, ctypes.c_int32]),
     }
@@ -249,6 +251,24 @@ def adamw_mixed_split(p, g, r, m, v, hp: HParams, t: int, lib=None):
                                  lr, b1, b2, eps, wd, s, int(t))
 
 
+def adamw_pure(p, g, m, v, c, hp: HParams, t: int, lib=None):
+    """Pure bf16 step with chosen state precisions: m and v are float32 (fp32
+    state) or uint16 (bf16 bits) arrays; c is the bf16 compensation buffer or None
+    (no Kahan summation)."""
+    lib = lib or load()
+    n = p.size
+    for a in (p, g):
+        assert a.dtype == np.uint16 and a.flags.c_contiguous and a.size == n
+    for a in (m, v):
+        assert a.dtype in (np.float32, np.uint16) and a.flags.c_contiguous and a.size == n
+    if c is not None:
+        assert c.dtype == np.uint16 and c.flags.c_contiguous and c.size == n
+    lr, b1, b2, eps, wd, s = hp.f32()
+    lib.oracle_adamw_pure(n, p.reshape(-1), g.reshape(-1), m.ctypes.data, int(m.dtype == np.float32),
+                          v.ctypes.data, int(v.dtype == np.float32), None if c is None else c.ctypes.data,
+                          lr, b1, b2, eps, wd, s, int(t))
+
+
 def any_nonfinite(g16, is_f16: bool, lib=None) -> bool:
     """True iff any 16-bit gradient is inf or NaN (exponent field all ones)."""
     lib = lib or load()
@@ -290,7 +310,8 @@ def step_list(mode: str, tensors: list, hp: HParams, step: int, *, p_is_f16=Fals
     """Take one AdamW step over a tensor list; return the new step counter.
 
     ``tensors`` is a list of dicts of flat numpy arrays: mixed mode uses keys
-    ``p, g, master, m, v``; split mode ``p, g, r, m, v``; Kahan mode ``p, g, m, v, c``.  With
+    ``p, g, master, m, v``; split mode ``p, g, r, m, v``; Kahan mode ``p, g, m, v, c``;
+    a "pure..." mode ``p, g, m, v`` (m, v float32 or uint16) and ``c`` when compensated.  With
     ``check_overflow`` the step is skipped (nothing written, counter kept) when
     any gradient of the whole list is inf/NaN.  Only elements inside
     ``[shard_begin, shard_end)`` of the flat concatenation are updated.
@@ -312,6 +333,13 @@ def step_list(mode: str, tensors: list, hp: HParams, step: int, *, p_is_f16=Fals
             adamw_mixed_split(sl["p"], sl["g"], sl["r"], sl["m"], sl["v"], hp, t, lib)
             for k in ("p", "r", "m", "v"):
                 tt[k][lo:hi] = sl[k]
+        elif mode.startswith("pure"):
+            keys = ["p", "g", "m", "v"] + (["c"] if "c" in tt else [])
+            sl = {k: np.ascontiguousarray(tt[k][lo:hi]) for k in keys}
+            adamw_pure(sl["p"], sl["g"], sl["m"], sl["v"], sl.get("c"), hp, t, lib)
+            for k in keys:
+                if k != "g":
+                    tt[k][lo:hi] = sl[k]
         elif mode == KAHAN:
             sl = {k: np.ascontiguousarray(tt[k][lo:hi]) for k in ("p", "g", "m", "v", "c")}
             adamw_kahan(sl["p"], sl["g"], sl["m"], sl["v"], sl["c"], hp, t, lib)

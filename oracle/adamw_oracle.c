@@ -321,6 +321,44 @@ void oracle_split_make_n(const uint32_t* w, uint16_t* p, uint16_t* r, int64_t n)
 void oracle_split_join_n(const uint16_t* p, const uint16_t* r, uint32_t* w, int64_t n)
 { for (int64_t i = 0; i < n; ++i) w[i] = oracle_split_join(p[i], r[i]); }
 
+/* Pure bf16 parameters with separately chosen state precisions (the
+ * AnyPrecisionAdamW knobs of "[pure bf16 training] w/ AnyPrecisionAdamW and
+ * Kahan summation": momentum_dtype, variance_dtype, use_kahan_summation with a
+ * bf16 compensation buffer).  m_f32 / v_f32 select fp32 moments (float arrays)
+ * instead of bf16 ones (uint16 bit arrays); c == NULL means no compensation:
+ * then p' = round_bf16(p * (1 - lr*wd) - step_size * u).  With c, the Kahan rule
+ * of oracle_adamw_kahan. */
+void oracle_adamw_pure(int64_t n, uint16_t* p, const uint16_t* g, void* m, int m_f32, void* v, int v_f32,
+                       uint16_t* c, float lr, float beta1, float beta2, float eps, float wd,
+                       float inv_scale, int64_t t)
+{
+    float s[6];
+    oracle_scalars(t, lr, beta1, beta2, wd, s);
+    float step_size = s[0], rbc2 = s[1], decay = s[2], lrwd = s[3];
+    float* mf = (float*)m;
+    float* vf = (float*)v;
+    uint16_t* mh = (uint16_t*)m;
+    uint16_t* vh = (uint16_t*)v;
+    for (int64_t i = 0; i < n; ++i) {
+        float gi = oracle_bf16_to_f32(g[i]) * inv_scale;
+        float mi = m_f32 ? mf[i] : oracle_bf16_to_f32(mh[i]);
+        float vi = v_f32 ? vf[i] : oracle_bf16_to_f32(vh[i]);
+        float u = adam_moments(gi, &mi, &vi, beta1, beta2, s[4], s[5], rbc2, eps);
+        float pf = oracle_bf16_to_f32(p[i]);
+        if (c) {
+            float d = -(lrwd * pf) - step_size * u;
+            float sum = oracle_bf16_to_f32(c[i]) + d;
+            uint16_t pn = oracle_f32_to_bf16(pf + sum);
+            c[i] = oracle_f32_to_bf16(sum - (oracle_bf16_to_f32(pn) - pf));
+            p[i] = pn;
+        } else {
+            p[i] = oracle_f32_to_bf16(pf * decay - step_size * u);
+        }
+        if (m_f32) mf[i] = mi; else mh[i] = oracle_f32_to_bf16(mi);
+        if (v_f32) vf[i] = vi; else vh[i] = oracle_f32_to_bf16(vi);
+    }
+}
+
 /* Pure bf16 without compensation: the same step applied directly to bf16 p.
  * Used by the tests as the control that Kahan summation is measured against. */
 void oracle_adamw_bf16_naive(int64_t n, uint16_t* p, const uint16_t* g,

@@ -25,6 +25,18 @@ DT = {"bf16": A.BF16, "f16": A.F16}
 F32_KEYS = {"mixed": ("m", "v", "master"), "kahan": (), "split": ("m", "v")}
 
 
+def f32_keys(mode):
+    if mode.startswith("pure"):
+        m32, v32, _ = workloads.parse_pure(mode)
+        return tuple(k for k, f in (("m", m32), ("v", v32)) if f)
+    return F32_KEYS[mode]
+
+
+def pure_precision(mode):
+    m32, v32, kahan = workloads.parse_pure(mode)
+    return A.PurePrecision(A.F32 if m32 else A.BF16, A.F32 if v32 else A.BF16, kahan)
+
+
 def join_master(p: np.ndarray, r: np.ndarray) -> np.ndarray:
     """fp32 masters encoded by split (bf16 high half p, int16 remainder r)."""
     w = (p.astype(np.int64) << 16) + r.view(np.int16).astype(np.int64)
@@ -40,7 +52,7 @@ def compare_streams(label, mode, got: dict, ref: dict, keys, p_is_f16=False):
             stats.append(compare(f"{label}:master(p,r)", join_master(got["p"], got["r"]),
                                  join_master(ref["p"], ref["r"]), True))
             continue
-        stats.append(compare(f"{label}:{k}", got[k], ref[k], k in F32_KEYS[mode], p_is_f16))
+        stats.append(compare(f"{label}:{k}", got[k], ref[k], k in f32_keys(mode), p_is_f16))
     return stats
 REL_TOL = 2e-6
 ULP_TOL = 1
@@ -114,7 +126,7 @@ class Case:
                                           random_moments=random_moments)
         for k, s in (shifts or {}).items():
             shift_stream(self.arena, k, s)
-        self.keys = workloads.STREAMS[mode]
+        self.keys = workloads.streams_of(mode)
         self.host = {k: to_np(self.arena.bufs[k]) for k in self.keys}
         self.d_step = torch.zeros(1, dtype=torch.int32, device=device)
         self.step = 0
@@ -136,7 +148,10 @@ class Case:
 
     def gpu_step(self, hp: A.HParams, shard=(0, -1), found_inf=None, tl=None):
         tl = tl or self.tensor_list(*shard)
-        A.adamw_multi_tensor_step(MODE[self.mode], DT[self.p_dtype], tl, hp, self.d_step, found_inf)
+        if self.mode.startswith("pure"):
+            A.adamw_pure_multi_tensor_step(pure_precision(self.mode), tl, hp, self.d_step, found_inf)
+        else:
+            A.adamw_multi_tensor_step(MODE[self.mode], DT[self.p_dtype], tl, hp, self.d_step, found_inf)
 
     def oracle_step(self, hp: oracle.HParams, shard=(0, -1), check_overflow=False):
         self.step = oracle.step_list(self.mode, self.oracle_tensors(), hp, self.step,
@@ -195,7 +210,7 @@ class SampledCase:
         self.numels = [int(n) for n in numels]
         self.arena = workloads.make_state(mode, self.numels, device, seed, p_dtype=p_dtype, align_elems=128,
                                           loss_scale=loss_scale)
-        self.keys = workloads.STREAMS[mode]
+        self.keys = workloads.streams_of(mode)
         total = sum(self.numels)
         b, e = shard[0], (total if shard[1] < 0 else shard[1])
         self.shard = (b, shard[1])
@@ -236,6 +251,8 @@ class SampledCase:
                                p_is_f16=self.p_dtype == "f16")
         elif self.mode == "split":
             oracle.adamw_mixed_split(sub["p"], sub["g"], sub["r"], sub["m"], sub["v"], ho, t)
+        elif self.mode.startswith("pure"):
+            oracle.adamw_pure(sub["p"], sub["g"], sub["m"], sub["v"], sub.get("c"), ho, t)
         else:
             oracle.adamw_kahan(sub["p"], sub["g"], sub["m"], sub["v"], sub["c"], ho, t)
         for k in self.keys:

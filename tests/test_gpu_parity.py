@@ -469,3 +469,35 @@ def test_dynamic_loss_scale_sequence(scale0, interval):
     case.compare_all(f"amp-{scale0}")
     assert case.step == 12 - len(bad_iters)
     free()
+
+
+PURE_MODES = [f"pure-{m}-{v}-{k}" for m in ("f32", "bf16") for v in ("f32", "bf16") for k in ("k", "n")]
+
+
+@pytest.mark.parametrize("mode", PURE_MODES)
+@pytest.mark.parametrize("align", [128, 3])
+def test_pure_precision_matrix(mode, align):
+    """Every AnyPrecision combination (fp32/bf16 exp_avg and exp_avg_sq, Kahan on
+    or off) against the oracle on the edge sizes, from a random state, 4 steps."""
+    case = Case(mode, EDGE_SIZES, seed=1800 + align, align_elems=align, random_moments=True)
+    _run(case, 4, label=f"{mode}-a{align}")
+    free()
+
+
+def test_pure_bf16_kahan_equals_kahan_mode():
+    """{bf16, bf16, Kahan} through adamw_pure_multi_tensor_step is ADAMW_PURE_KAHAN."""
+    a = Case("kahan", [30000, 17, 4099], seed=1900, random_moments=True)
+    b = Case("pure-bf16-bf16-k", [30000, 17, 4099], seed=1900, random_moments=True)
+    for k in a.keys:
+        b.arena.bufs[k].copy_(a.arena.bufs[k])
+    hg, _ = hp_pair()
+    for s in range(3):
+        if s:
+            a.refill_grads(s)
+            b.arena.bufs["g"].copy_(a.arena.bufs["g"])
+        a.gpu_step(hg)
+        b.gpu_step(hg)
+    torch.cuda.synchronize()
+    for k in a.keys:
+        assert same_bits(a.arena.bufs[k], b.arena.bufs[k]), k
+    free()

@@ -685,3 +685,76 @@ def test_amp_step_skips_and_backs_off(olib):
     assert step == 1 and ls.scale == 32768.0 and ls.tracker == 0
     for k in t[0]:
         assert np.array_equal(t[0][k], before[k])
+
+
+# ---------------------------------------------------------------------------
+# AnyPrecision state dtypes (pure bf16 params)
+# ---------------------------------------------------------------------------
+
+def _pure_state(n, rng, m32, v32, kahan):
+    p = bf16_bits(rng.standard_normal(n) * 0.02)
+    m = np.zeros(n, np.float32) if m32 else np.zeros(n, np.uint16)
+    v = np.zeros(n, np.float32) if v32 else np.zeros(n, np.uint16)
+    c = np.zeros(n, np.uint16) if kahan else None
+    return p, m, v, c
+
+
+def test_pure_bf16_state_reduces_to_kahan_and_naive(olib):
+    """bf16 moments with compensation is the Kahan step; without it, the naive bf16 step."""
+    rng = np.random.default_rng(41)
+    n = 30_000
+    for kahan in (True, False):
+        p, m, v, c = _pure_state(n, rng, False, False, kahan)
+        p2, m2, v2, c2 = p.copy(), m.copy(), v.copy(), None if c is None else c.copy()
+        for t in range(1, 6):
+            g = bf16_bits(rng.standard_normal(n) * 1e-3)
+            oracle.adamw_pure(p, g, m, v, c, HParams(), t, lib=olib)
+            if kahan:
+                oracle.adamw_kahan(p2, g, m2, v2, c2, HParams(), t, lib=olib)
+            else:
+                oracle.adamw_bf16_naive(p2, g, m2, v2, HParams(), t, lib=olib)
+        assert np.array_equal(p, p2) and np.array_equal(m, m2) and np.array_equal(v, v2)
+        if kahan:
+            assert np.array_equal(c, c2)
+
+
+@pytest.mark.parametrize("m32,v32", [(True, True), (True, False), (False, True)])
+def test_pure_fp32_moments_follow_the_mixed_moments(olib, m32, v32):
+    """fp32 moments evolve exactly as the pinned mixed oracle's (the moment update
+    does not read the weight); bf16 ones are its fp32 values rounded at step 1.
+    Without compensation the new param is the rounding of the mixed step's
+    master when that master starts at the bf16 param."""
+    rng = np.random.default_rng(42)
+    n = 30_000
+    p, m, v, _ = _pure_state(n, rng, m32, v32, False)
+    w = bf16_val(p).copy()
+    mm, vm, p16 = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    g = bf16_bits(rng.standard_normal(n) * 1e-3)
+    oracle.adamw_pure(p, g, m, v, None, HParams(), 1, lib=olib)
+    oracle.adamw_mixed(p16, g, w, mm, vm, HParams(), 1, lib=olib)
+    assert np.array_equal(p, p16)
+    assert np.array_equal(m, mm) if m32 else np.array_equal(m, bf16_bits(mm))
+    assert np.array_equal(v, vm) if v32 else np.array_equal(v, bf16_bits(vm))
+    if m32 and v32:
+        for t in range(2, 8):
+            g = bf16_bits(rng.standard_normal(n) * 1e-3)
+            oracle.adamw_pure(p, g, m, v, None, HParams(), t, lib=olib)
+            w = bf16_val(p).copy()        # the mixed master restarted from the bf16 param
+            oracle.adamw_mixed(p16, g, w, mm, vm, HParams(), t, lib=olib)
+        assert np.array_equal(m, mm) and np.array_equal(v, vm)
+
+
+def test_pure_fp32_moments_kahan_tracks_tiny_updates(olib):
+    """Compensation with fp32 moments: 10,000 constant +1e-4 updates from 1.0 land
+    within 5% of the fp64 sum (naive bf16 stays at 1.0)."""
+    n, k = 64, 10_000
+    hp = HParams(lr=1e-4, weight_decay=0.0, eps=0.0)
+    p = bf16_bits(np.ones(n))
+    m, v, c = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    pn, mn, vn = p.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    g = bf16_bits(-np.ones(n))
+    for t in range(1, k + 1):
+        oracle.adamw_pure(p, g, m, v, c, hp, t, lib=olib)
+        oracle.adamw_pure(pn, g, mn, vn, None, hp, t, lib=olib)
+    got = bf16_val(p).astype(np.float64) + bf16_val(c)
+    assert np.all(np.abs(got - 2.0) <= 0.1) and np.all(bf16_val(pn) == 1.0)

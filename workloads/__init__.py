@@ -232,6 +232,19 @@ def make_state(mode, numels, device, seed, *, p_dtype="bf16", align_elems=128, l
         else:
             a.bufs["m"] = torch.zeros(total, dtype=torch.float32, device=device)
             a.bufs["v"] = torch.zeros(total, dtype=torch.float32, device=device)
+    elif mode.startswith("pure"):
+        m32, v32, kahan = parse_pure(mode)
+        a.bufs["p"] = master.to(torch.bfloat16)
+        del master
+        for k, f32 in (("m", m32), ("v", v32)):
+            x = normal(total, GRAD_STD, device, k, seed) if random_moments else \
+                torch.zeros(total, dtype=torch.float32, device=device)
+            if random_moments and k == "v":
+                x = x.square()
+            a.bufs[k] = x if f32 else x.to(torch.bfloat16)
+        if kahan:
+            a.bufs["c"] = (normal(total, 1e-6, device, "c", seed, dtype=torch.bfloat16) if random_moments else
+                           torch.zeros(total, dtype=torch.bfloat16, device=device))
     elif mode == "kahan":
         a.bufs["p"] = master.to(torch.bfloat16)
         del master
@@ -259,6 +272,27 @@ def refill_grads(arena: Arena, seed, step, *, p_dtype="bf16", loss_scale=1.0):
 # param, grad, exp_avg, exp_avg_sq, aux (fp32 master in mixed mode, bf16 Kahan compensation otherwise).
 STREAMS = {"mixed": ("p", "g", "m", "v", "master"), "kahan": ("p", "g", "m", "v", "c"),
            "split": ("p", "g", "m", "v", "r")}
+
+
+def parse_pure(mode: str):
+    """'pure-<m>-<v>-<k|n>' with m, v in {f32, bf16}: (fp32 exp_avg, fp32 exp_avg_sq, Kahan)."""
+    _, m, v, k = mode.split("-")
+    assert m in ("f32", "bf16") and v in ("f32", "bf16") and k in ("k", "n"), mode
+    return m == "f32", v == "f32", k == "k"
+
+
+def streams_of(mode: str):
+    """Buffer keys of a mode in the C ABI's stream order (param, grad, exp_avg, exp_avg_sq[, aux])."""
+    if mode.startswith("pure"):
+        return ("p", "g", "m", "v", "c") if parse_pure(mode)[2] else ("p", "g", "m", "v")
+    return STREAMS[mode]
+
+
+def pure_traffic(mode: str) -> int:
+    """Bytes moved per parameter by a pure-bf16 step of this precision."""
+    m32, v32, kahan = parse_pure(mode)
+    state = (4 if m32 else 2) + (4 if v32 else 2) + (2 if kahan else 0)
+    return (2 + 2 + state) + (2 + state)
 
 # Resident bytes per parameter of each stream layout (what one rank holds).
 RESIDENT_BYTES = {
