@@ -501,3 +501,79 @@ def test_pure_bf16_kahan_equals_kahan_mode():
     for k in a.keys:
         assert same_bits(a.arena.bufs[k], b.arena.bufs[k]), k
     free()
+
+
+def test_graph_capture_replay_matches_eager():
+    """The check + step sequence captured once in a HIP graph and replayed 6
+    times (with eager work and synchronisations between replays) leaves every
+    buffer, the counter and the flag bit-identical to 6 eager iterations.  The
+    capture stream is warmed up first so its workspace and plan already exist
+    (capture records kernel launches only: no allocation, copy or memset)."""
+    numels = [40000, 7, 4099, 1]
+    eager = Case("mixed", numels, seed=2200, p_dtype="f16", loss_scale=65536.0, random_moments=True)
+    graph = Case("mixed", numels, seed=2200, p_dtype="f16", loss_scale=65536.0, random_moments=True)
+    hg, _ = hp_pair(inv_scale=1.0 / 65536)
+    s = torch.cuda.Stream()
+    fe = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fg = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tle, tlg = eager.tensor_list(), graph.tensor_list()
+
+    def it_graph():
+        A.adamw_check_finite(A.F16, tlg, fg, s)
+        A.adamw_multi_tensor_step(A.MIXED, A.F16, tlg, hg, graph.d_step, fg, s)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):          # warm-up on the capture stream (plans, workspace)
+        it_graph()
+    s.synchronize()
+    A.adamw_check_finite(A.F16, tle, fe)
+    A.adamw_multi_tensor_step(A.MIXED, A.F16, tle, hg, eager.d_step, fe)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        it_graph()
+    for r in range(6):
+        g.replay()
+        A.adamw_check_finite(A.F16, tle, fe)
+        A.adamw_multi_tensor_step(A.MIXED, A.F16, tle, hg, eager.d_step, fe)
+        torch.cuda.synchronize()
+        junk = torch.randn(1000, device="cuda").sum()      # unrelated eager work between replays
+        del junk
+        assert int(graph.d_step.item()) == int(eager.d_step.item()) == r + 2
+        for k in eager.keys:
+            assert same_bits(graph.arena.bufs[k], eager.arena.bufs[k]), (r, k)
+    free()
+
+
+def test_concurrent_host_threads_on_own_streams():
+    """Four host threads, each stepping its own list on its own stream 5 times,
+    concurrently (the ctypes calls release the GIL); each result equals the oracle."""
+    import threading
+    hg, ho = hp_pair()
+    cases = [Case("mixed" if i % 2 else "kahan", [20000 + 13 * i, 9, 3000], seed=2300 + i) for i in range(4)]
+    streams = [torch.cuda.Stream() for _ in cases]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(c, st):
+        try:
+            for _ in range(5):
+                tl = c.tensor_list()
+                if c.mode == "mixed":
+                    A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl, hg, c.d_step, None, st)
+                else:
+                    A.adamw_multi_tensor_step(A.PURE_KAHAN, A.BF16, tl, hg, c.d_step, None, st)
+            st.synchronize()
+        except Exception as e:      # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(c, st)) for c, st in zip(cases, streams)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i, c in enumerate(cases):
+        for _ in range(5):
+            c.oracle_step(ho)
+        c.compare_all(f"thread-{i}")
+    free()
