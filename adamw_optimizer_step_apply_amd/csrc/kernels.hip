@@ -231,8 +231,8 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
 #ifndef ADAMW_NT_MIXED
 #define ADAMW_NT_MIXED 2
 #endif
-#ifndef ADAMW_NT_KAHAN
-#define ADAMW_NT_KAHAN 3
+#ifndef ADAMW_NT_PURE
+#define ADAMW_NT_PURE 3
 #endif
 #ifndef ADAMW_NT_CHECK
 #define ADAMW_NT_CHECK 1
@@ -302,7 +302,7 @@ __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
 // MODE 0: mixed bf16, 1: mixed fp16, 3: mixed bf16 with the master split into
 // param + int16 remainder
 template <int MODE>
-__global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const DevSeg* __restrict__ segs,
+__global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(const DevSeg* __restrict__ segs,
                                                         const DevChunk* __restrict__ chunks,
                                                         const LaunchScalars* __restrict__ sc)
 {
@@ -329,12 +329,12 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
             GLOBAL u32x4* __restrict__ r4 = reinterpret_cast<GLOBAL u32x4*>(r);
             GLOBAL f32x4* __restrict__ m4 = reinterpret_cast<GLOBAL f32x4*>(m);
             GLOBAL f32x4* __restrict__ v4 = reinterpret_cast<GLOBAL f32x4*>(v);
-            for (uint32_t k0 = tid; k0 < npack; k0 += kBlock * kUnroll) {
+            for (uint32_t k0 = tid; k0 < npack; k0 += kBlockMixed * kUnroll) {
                 u32x4 G[kUnroll], P[kUnroll], R[kUnroll];
                 f32x4 M[kUnroll][2], V[kUnroll][2];
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    const uint32_t k = k0 + u * kBlock;
+                    const uint32_t k = k0 + u * kBlockMixed;
                     if (k < npack) {
                         G[u] = ld<NTM>(g4 + k); P[u] = ld<NTM>(p4 + k); R[u] = ld<NTM>(r4 + k);
                         M[u][0] = ld<NTM>(m4 + 2 * k); M[u][1] = ld<NTM>(m4 + 2 * k + 1);
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
                 }
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    const uint32_t k = k0 + u * kBlock;
+                    const uint32_t k = k0 + u * kBlockMixed;
                     if (k < npack) {
                         float* mf = reinterpret_cast<float*>(M[u]);
                         float* vf = reinterpret_cast<float*>(V[u]);
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
                 }
             }
         } else {
-            for (uint32_t i = tid; i < n; i += kBlock) {
+            for (uint32_t i = tid; i < n; i += kBlockMixed) {
                 float wi = __uint_as_float(join_bits(p[i], r[i])), mi = m[i], vi = v[i];
                 mixed_elem(widen1<false>(g[i]), wi, mi, vi, c);
                 uint32_t ri;
@@ -396,12 +396,12 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
             GLOBAL f32x4* __restrict__ m4 = reinterpret_cast<GLOBAL f32x4*>(m);
             GLOBAL f32x4* __restrict__ v4 = reinterpret_cast<GLOBAL f32x4*>(v);
             GLOBAL f32x4* __restrict__ w4 = reinterpret_cast<GLOBAL f32x4*>(w);
-            for (uint32_t k0 = tid; k0 < npack; k0 += kBlock * kUnroll) {
+            for (uint32_t k0 = tid; k0 < npack; k0 += kBlockMixed * kUnroll) {
                 u32x4 G[kUnroll];
                 f32x4 M[kUnroll][2], V[kUnroll][2], W[kUnroll][2];
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    const uint32_t k = k0 + u * kBlock;
+                    const uint32_t k = k0 + u * kBlockMixed;
                     if (k < npack) {
                         G[u] = ld<NTM>(g4 + k);
                         W[u][0] = ld<NTM>(w4 + 2 * k); W[u][1] = ld<NTM>(w4 + 2 * k + 1);
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
                 }
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    const uint32_t k = k0 + u * kBlock;
+                    const uint32_t k = k0 + u * kBlockMixed;
                     if (k < npack) {
                         float* wf = reinterpret_cast<float*>(W[u]);
                         float* mf = reinterpret_cast<float*>(M[u]);
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
                 }
             }
         } else {
-            for (uint32_t i = tid; i < n; i += kBlock) {
+            for (uint32_t i = tid; i < n; i += kBlockMixed) {
                 float wi = w[i], mi = m[i], vi = v[i];
                 const float nw = mixed_elem(widen1<F16>(g[i]), wi, mi, vi, c);
                 w[i] = wi;
@@ -450,12 +450,12 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_kernel(const Dev
 // (else none: p' = round(p * decay - step_size * u)).  <false, false, true> is
 // the pure-bf16 Kahan mode.
 template <bool M32, bool V32, bool KAHAN>
-__global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_pure_kernel(const DevSeg* __restrict__ segs,
+__global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(const DevSeg* __restrict__ segs,
                                                                             const DevChunk* __restrict__ chunks,
                                                                             const LaunchScalars* __restrict__ sc)
 {
     if (sc->skip) return;
-    constexpr int NT = ADAMW_NT_KAHAN;
+    constexpr int NT = ADAMW_NT_PURE;
     const Coef c = load_coef(sc);
     const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
     const DevSeg& sg = segs[ch.seg];
@@ -479,11 +479,11 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_pure_kernel(cons
         constexpr int MW = M32 ? 2 : 1, VW = V32 ? 2 : 1;
         GLOBAL u32x4* __restrict__ m4 = reinterpret_cast<GLOBAL u32x4*>(m);
         GLOBAL u32x4* __restrict__ v4 = reinterpret_cast<GLOBAL u32x4*>(v);
-        for (uint32_t k0 = tid; k0 < npack; k0 += kBlock * kUnroll) {
+        for (uint32_t k0 = tid; k0 < npack; k0 += kBlockPure * kUnroll) {
             u32x4 G[kUnroll], P[kUnroll], C[kUnroll], M[kUnroll][MW], V[kUnroll][VW];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const uint32_t k = k0 + u * kBlock;
+                const uint32_t k = k0 + u * kBlockPure;
                 if (k < npack) {
                     G[u] = ld<NT>(g4 + k);
                     P[u] = ld<NT>(p4 + k);
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_pure_kernel(cons
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const uint32_t k = k0 + u * kBlock;
+                const uint32_t k = k0 + u * kBlockPure;
                 if (k < npack) {
                     const uint32_t* gw = reinterpret_cast<const uint32_t*>(&G[u]);
                     const uint32_t* pw = reinterpret_cast<const uint32_t*>(&P[u]);
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(kBlock) ADAMW_WPE_ATTR void update_pure_kernel(cons
             }
         }
     } else {
-        for (uint32_t i = tid; i < n; i += kBlock) {
+        for (uint32_t i = tid; i < n; i += kBlockPure) {
             const float pf = widen1<false>(p[i]);
             float mi, vi;
             if constexpr (M32) mi = m[i]; else mi = widen1<false>(m[i]);
@@ -604,7 +604,7 @@ __device__ __forceinline__ uint32_t nonfinite2(uint32_t w)
 }
 
 template <bool F16>
-__global__ __launch_bounds__(kBlock) void check_kernel(const DevSeg* __restrict__ segs,
+__global__ __launch_bounds__(kBlockCheck) void check_kernel(const DevSeg* __restrict__ segs,
                                                        const DevChunk* __restrict__ chunks,
                                                        int32_t* __restrict__ flag)
 {
@@ -618,11 +618,11 @@ __global__ __launch_bounds__(kBlock) void check_kernel(const DevSeg* __restrict_
         // its loads before testing any, so one pass covers the chunk
         const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
         const uint32_t npack = n / kPack;
-        for (uint32_t k0 = threadIdx.x; k0 < npack; k0 += kBlock * kCheckUnroll) {
+        for (uint32_t k0 = threadIdx.x; k0 < npack; k0 += kBlockCheck * kCheckUnroll) {
             u32x4 q[kCheckUnroll];
 #pragma unroll
             for (int u = 0; u < kCheckUnroll; ++u) {
-                const uint32_t k = k0 + u * kBlock;
+                const uint32_t k = k0 + u * kBlockCheck;
                 q[u] = k < npack ? ld<ADAMW_NT_CHECK>(g4 + k) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
@@ -631,7 +631,7 @@ __global__ __launch_bounds__(kBlock) void check_kernel(const DevSeg* __restrict_
                        nonfinite2<EXP>(q[u].w);
         }
     } else {
-        for (uint32_t i = threadIdx.x; i < n; i += kBlock) bad |= (uint32_t)((g[i] & EXP) == EXP);
+        for (uint32_t i = threadIdx.x; i < n; i += kBlockCheck) bad |= (uint32_t)((g[i] & EXP) == EXP);
     }
     // one atomic per wavefront that saw a non-finite value
     if (__any((int)bad) && (threadIdx.x % warpSize) == 0)
@@ -651,23 +651,24 @@ hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32
     return hipGetLastError();
 }
 
-// Occupancy cap, per mode: the update kernel uses no LDS, but reserving this
-// much per workgroup leaves room for only 160 KiB / bytes workgroups on a CU.
-// Measured on MI355X with the OPT-1.3B list, two resident workgroups per CU
-// (eight waves) stream faster than the register-limited five or six: fewer
-// concurrent streams keep more DRAM rows open.
+// Occupancy cap, per kernel family: the update kernels use no LDS, but
+// reserving this much per workgroup leaves room for only 160 KiB / bytes
+// workgroups on a CU.  Measured on MI355X with the OPT-1.3B list, one resident
+// workgroup per CU (8 waves mixed, 16 waves pure) streams faster than the
+// register-limited 20-24 waves: fewer concurrent address streams per CU keep
+// more DRAM rows open.
 #ifndef ADAMW_LDS_MIXED
-#define ADAMW_LDS_MIXED 81920
+#define ADAMW_LDS_MIXED 163840
 #endif
-#ifndef ADAMW_LDS_KAHAN
-#define ADAMW_LDS_KAHAN 81920
+#ifndef ADAMW_LDS_PURE
+#define ADAMW_LDS_PURE 163840
 #endif
 
 hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
                          const LaunchScalars* d_scalars, hipStream_t stream)
 {
     if (n_chunks <= 0) return hipSuccess;
-    const dim3 grid((unsigned)n_chunks), block(kBlock);
+    const dim3 grid((unsigned)n_chunks), block(kBlockMixed), block_pure(kBlockPure);
     switch (kernel) {
     case kKernelMixedBf16:
         hipLaunchKernelGGL(update_kernel<0>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
@@ -680,7 +681,7 @@ hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks,
         break;
 #define ADAMW_PURE_CASE(M, V, K)                                                                          \
     case kKernelPure + (M) * 4 + (V) * 2 + (K):                                                            \
-        hipLaunchKernelGGL((update_pure_kernel<M, V, K>), grid, block, ADAMW_LDS_KAHAN, stream, segs, chunks, \
+        hipLaunchKernelGGL((update_pure_kernel<M, V, K>), grid, block_pure, ADAMW_LDS_PURE, stream, segs, chunks, \
                            d_scalars);                                                                     \
         break;
         ADAMW_PURE_CASE(0, 0, 0) ADAMW_PURE_CASE(0, 0, 1) ADAMW_PURE_CASE(0, 1, 0) ADAMW_PURE_CASE(0, 1, 1)
@@ -698,7 +699,7 @@ hipError_t launch_check(adamw_dtype g_dtype, const DevSeg* segs, const DevChunk*
     hipLaunchKernelGGL(zero_flag_kernel, dim3(1), dim3(64), 0, stream, d_flag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_chunks <= 0) return e;
-    const dim3 grid((unsigned)n_chunks), block(kBlock);
+    const dim3 grid((unsigned)n_chunks), block(kBlockCheck);
     if (g_dtype == ADAMW_F16)
         hipLaunchKernelGGL(check_kernel<true>, grid, block, 0, stream, segs, chunks, d_flag);
     else

@@ -14,19 +14,27 @@
 namespace adamw {
 
 constexpr int kStreams = 5;            // param, grad, exp_avg, exp_avg_sq, aux
-constexpr int kBlock = 256;            // threads per workgroup: four wave64s
+// Threads per workgroup, per kernel family (measured on MI355X with the OPT-1.3B
+// list, one workgroup resident per CU): the mixed kernels stream best with 8
+// waves per CU, the VALU-heavier pure-bf16 family with 16; the overflow check
+// keeps 4-wave workgroups and full occupancy (it only reads).
+constexpr int kBlockMixed = 512;
+constexpr int kBlockPure = 1024;
+constexpr int kBlockCheck = 256;
 constexpr int kPack = 8;               // elements per lane per dwordx4 of a 16-bit stream
 constexpr uint32_t kVecBit = 0x80000000u;
 constexpr uint32_t kCountMask = 0x7fffffffu;
-constexpr int64_t kDefaultChunkElems = 2048;    // vector chunk: one pack per lane, one pass
-constexpr int64_t kElemChunkElems = 4096;       // element chunk: 16 elements per lane
-// The overflow check moves 2 B per element (the step 18-28 B): its chunks are
-// this many step chunks long, so a workgroup's fixed cost (two dependent table
+constexpr int64_t kElemChunkElems = 4096;       // element chunk
+// Default vector chunk of a kernel: one 8-element pack per lane, one pass.
+constexpr int64_t chunk_elems_for_block(int block) { return (int64_t)block * 8; }
+// The overflow check moves 2 B per element (the step 18-28 B): each lane reads
+// this many packs in one pass, so a workgroup's fixed cost (two dependent table
 // loads) is spread over as many bytes as a step workgroup moves.
 #ifndef ADAMW_CHECK_CHUNK_MULT
 #define ADAMW_CHECK_CHUNK_MULT 8
 #endif
 constexpr int kCheckChunkMult = ADAMW_CHECK_CHUNK_MULT;
+constexpr int64_t kCheckChunkElems = chunk_elems_for_block(kBlockCheck) * kCheckChunkMult;
 
 // Update kernels, by launch id.  The pure-bf16 family adds
 // 4 * (fp32 exp_avg) + 2 * (fp32 exp_avg_sq) + (Kahan compensation).

@@ -109,6 +109,10 @@ def test_valid_call_reaches_hip():
 # planner
 # ---------------------------------------------------------------------------
 
+# workgroup size x 8 of each kernel family
+DEFAULT_CHUNK = {A.MIXED: 4096, A.MIXED_SPLIT: 4096, A.PURE_KAHAN: 8192}
+
+
 def check_plan(rows, numels, b, e, ptrs, esz, chunk_elems):
     """Rows partition [b, e) in flat order; each row lies in one tensor; vector
     rows hold a multiple of 8 elements, 16-byte aligned in every stream."""
@@ -147,7 +151,7 @@ def test_plan_partitions_random_lists(seed):
         ptrs.append([base + int(o) * esz[s] + 256 * i for i, o in enumerate(offs)])
     tl = A.TensorList(numels, ptrs, b, e if rng.random() < 0.8 or e != total else -1)
     rows = A.adamw_plan_inspect(mode, A.BF16, tl)
-    check_plan(rows, numels, b, e, ptrs, esz, A.adamw_set_chunk_elems(0))
+    check_plan(rows, numels, b, e, ptrs, esz, DEFAULT_CHUNK[mode])
     if seed % 3 == 0:
         # all streams at one phase: at most 2 element rows per segment
         segs = {}
@@ -171,7 +175,7 @@ def test_plan_bert_shards():
         b, e = wl.shard(r)
         tl = A.TensorList(numels, ptrs, b, e)
         rows = A.adamw_plan_inspect(A.MIXED, A.BF16, tl)
-        check_plan(rows, numels, b, e, ptrs, esz, A.adamw_set_chunk_elems(0))
+        check_plan(rows, numels, b, e, ptrs, esz, DEFAULT_CHUNK[A.MIXED])
         nseg.append(len({row[5] for row in rows}))
     assert nseg[0] == 1 and all(n > 1 for n in nseg[1:])
 
@@ -196,8 +200,11 @@ def test_chunk_size_knob():
             A.adamw_set_chunk_elems(1000)
     finally:
         A.adamw_set_chunk_elems(0)
+    assert A.adamw_set_chunk_elems(0) == 0
     rows = A.adamw_plan_inspect(A.MIXED, A.BF16, tl)
-    assert max(r[2] for r in rows) == A.adamw_set_chunk_elems(0) == 2048
+    assert max(r[2] for r in rows) == 4096
+    rows = A.adamw_plan_inspect(A.PURE_KAHAN, A.BF16, _tl(numels, esz=(2, 2, 2, 2, 2)))
+    assert max(r[2] for r in rows) == 8192
 
 
 C_PROGRAM = r"""
