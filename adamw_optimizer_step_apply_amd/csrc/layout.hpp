@@ -14,12 +14,20 @@
 namespace adamw {
 
 constexpr int kStreams = 5;            // param, grad, exp_avg, exp_avg_sq, aux
-// Threads per workgroup, per kernel family (measured on MI355X with the OPT-1.3B
-// list, one workgroup resident per CU): the mixed kernels stream best with 8
-// waves per CU, the VALU-heavier pure-bf16 family with 16; the overflow check
-// keeps 4-wave workgroups and full occupancy (it only reads).
-constexpr int kBlockMixed = 512;
-constexpr int kBlockPure = 1024;
+// Threads per workgroup, per kernel family, with the occupancy caps in
+// kernels.hip: the mixed kernels run 256-lane workgroups, two per CU (8 waves);
+// the VALU-heavier pure-bf16 family 1024-lane workgroups, one per CU (16 waves);
+// the overflow check 256-lane workgroups at full occupancy (it only reads).
+// Chosen by interleaved A/B runs on three MI355X boxes (OPT-1.3B list): the
+// candidate shapes differed by at most ~3%, less than the spread between boxes.
+#ifndef ADAMW_BLOCK_MIXED
+#define ADAMW_BLOCK_MIXED 256
+#endif
+#ifndef ADAMW_BLOCK_PURE
+#define ADAMW_BLOCK_PURE 1024
+#endif
+constexpr int kBlockMixed = ADAMW_BLOCK_MIXED;
+constexpr int kBlockPure = ADAMW_BLOCK_PURE;
 constexpr int kBlockCheck = 256;
 constexpr int kPack = 8;               // elements per lane per dwordx4 of a 16-bit stream
 constexpr uint32_t kVecBit = 0x80000000u;

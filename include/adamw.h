@@ -260,7 +260,7 @@ int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_ten
 
 /* Tuning knob: elements per vector chunk (one workgroup's share), a multiple
  * of 2048 in [2048, 1<<22], for every kernel (the overflow check uses 8x it);
- * 0 restores the built-in per-kernel defaults (workgroup size x 8: 4096 for the
+ * 0 restores the built-in per-kernel defaults (workgroup size x 8: 2048 for the
  * mixed kernels, 8192 for the pure-bf16 family, 16384 for the check).  Affects
  * plans built after the call.  Returns the value now in force (0 = defaults),
  * or -1 if rejected. */
