@@ -87,7 +87,8 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
     const int64_t nt = list->n_tensors;
     if (nt < 0) { err = "n_tensors < 0"; return ADAMW_E_INVALID; }
     if (nt > 0 && !list->numel) { err = "numel array is null"; return ADAMW_E_INVALID; }
-    if (list->flat_mask >> kStreams) { err = "flat_mask has bits above stream 4"; return ADAMW_E_INVALID; }
+    if (list->flat_mask & ~(0x1fu | ADAMW_BLOCKED_STATE)) { err = "flat_mask has unknown bits"; return ADAMW_E_INVALID; }
+    const bool blocked = (list->flat_mask & ADAMW_BLOCKED_STATE) != 0;
 
     int64_t total = 0;
     for (int64_t i = 0; i < nt; ++i) {
@@ -111,10 +112,31 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
 
     int esz[kStreams];
     bool flat[kStreams];
+    // blocked state: exp_avg, exp_avg_sq and aux share one flat buffer of the
+    // shard in blocks of kStateBlock elements, [exp_avg][exp_avg_sq][aux] each
+    int64_t soff[kStreams] = {0, 0, 0, 0, 0}, block_bytes = 0;
+    uintptr_t state_base = 0;
+    if (blocked) {
+        int64_t acc = 0;
+        for (int s = ADAMW_STREAM_EXP_AVG; s <= ADAMW_STREAM_AUX; ++s) {
+            soff[s] = acc;
+            acc += kStateBlock * esz_in[s];
+        }
+        block_bytes = acc;
+        if (e > b) {
+            if (!list->ptr[ADAMW_STREAM_EXP_AVG] || !list->ptr[ADAMW_STREAM_EXP_AVG][0] ||
+                (uintptr_t)list->ptr[ADAMW_STREAM_EXP_AVG][0] % 16u) {
+                err = "blocked state buffer (ptr[2][0]) is null or not 16-byte aligned";
+                return ADAMW_E_INVALID;
+            }
+            state_base = (uintptr_t)list->ptr[ADAMW_STREAM_EXP_AVG][0];
+        }
+    }
     for (int s = 0; s < kStreams; ++s) {
         esz[s] = esz_in[s];
         flat[s] = (list->flat_mask >> s) & 1u;
         if (!esz[s]) continue;
+        if (blocked && s >= ADAMW_STREAM_EXP_AVG) continue;
         bool needed = flat[s] ? (e > b) : (nt > 0);
         if (needed && !list->ptr[s]) {
             snprintf(buf, sizeof buf, "pointer array of stream %s is null", kStreamName[s]);
@@ -137,14 +159,24 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
         const int64_t n = list->numel[i];
         const int64_t lo = b > base ? b : base;
         const int64_t hi = e < base + n ? e : base + n;
-        if (lo < hi) {
-            SegInfo si{i, lo - base, lo, hi - lo};
+        // a blocked state splits the piece at block boundaries (relative to b)
+        for (int64_t plo = lo; plo < hi;) {
+            int64_t phi = hi;
+            if (blocked) {
+                const int64_t next = b + ((plo - b) / kStateBlock + 1) * kStateBlock;
+                if (next < phi) phi = next;
+            }
+            SegInfo si{i, plo - base, plo, phi - plo};
             DevSeg d{};
             for (int s = 0; s < kStreams; ++s) {
                 if (!esz[s]) continue;
                 uintptr_t a;
-                if (flat[s]) {
-                    a = (uintptr_t)list->ptr[s][0] + (uintptr_t)((lo - b) * esz[s]);
+                if (blocked && s >= ADAMW_STREAM_EXP_AVG) {
+                    const int64_t rel = plo - b;
+                    a = state_base + (uintptr_t)((rel / kStateBlock) * block_bytes + soff[s] +
+                                                 (rel % kStateBlock) * esz[s]);
+                } else if (flat[s]) {
+                    a = (uintptr_t)list->ptr[s][0] + (uintptr_t)((plo - b) * esz[s]);
                 } else {
                     uintptr_t t0 = (uintptr_t)list->ptr[s][i];
                     if (!t0 || t0 % (uintptr_t)esz[s]) {
@@ -153,13 +185,14 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
                         err = buf;
                         return ADAMW_E_INVALID;
                     }
-                    a = t0 + (uintptr_t)((lo - base) * esz[s]);
+                    a = t0 + (uintptr_t)((plo - base) * esz[s]);
                 }
                 d.ptr[s] = (uint64_t)a;
             }
+            plo = phi;
             if (nseg >= (int64_t)UINT32_MAX) { err = "too many segments"; return ADAMW_E_INVALID; }
             const uint32_t seg = (uint32_t)nseg++;
-            if (!build) { base += n; continue; }
+            if (!build) continue;
             out.segs.push_back(d);
             out.info.push_back(si);
 
@@ -202,12 +235,13 @@ void plan_key(int64_t tag, const int esz[kStreams], const adamw_tensor_list* lis
     key.push_back(list->shard_end);
     key.push_back((int64_t)list->flat_mask);
     for (int64_t i = 0; i < nt; ++i) key.push_back(list->numel[i]);
+    const bool blocked = (list->flat_mask & ADAMW_BLOCKED_STATE) != 0;
     for (int s = 0; s < kStreams; ++s) {
-        if (!esz[s] || !list->ptr[s]) {
+        if (!esz[s] || !list->ptr[s] || (blocked && s > ADAMW_STREAM_EXP_AVG)) {
             key.push_back(-1);
             continue;
         }
-        if ((list->flat_mask >> s) & 1u) {
+        if (((list->flat_mask >> s) & 1u) || (blocked && s == ADAMW_STREAM_EXP_AVG)) {
             key.push_back((int64_t)(uintptr_t)list->ptr[s][0]);
         } else {
             for (int64_t i = 0; i < nt; ++i) key.push_back((int64_t)(uintptr_t)list->ptr[s][i]);

@@ -131,11 +131,32 @@ def probes(n, stream):
 
 
 def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
+    """Per-tensor buffers for every stream; a "-blocked" mode instead keeps
+    exp_avg / exp_avg_sq / aux in one blocked flat buffer of the whole list
+    (the optimizer-owned layout; param and grad stay per tensor)."""
+    import torch
+
     import workloads
-    arena = workloads.make_state(mode, numels, device, seed, align_elems=128, p_dtype=p_dtype,
+    base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
+    arena = workloads.make_state(base, numels, device, seed, align_elems=128, p_dtype=p_dtype,
                                  loss_scale=loss_scale)
-    keys = workloads.streams_of(mode)
+    keys = workloads.streams_of(base)
     streams = [[arena.view(k, i) for i in range(len(numels))] for k in keys]
+    if base != mode:
+        import adamw_optimizer_step_apply_amd as A
+        B = A.STATE_BLOCK
+        n = sum(numels)
+        nb = -(-n // B)
+        cols = []
+        for k in keys[2:]:
+            src = arena.bufs[k]
+            flat = torch.cat([arena.view(k, i) for i in range(len(numels))])
+            flat = torch.cat([flat, torch.zeros(nb * B - n, dtype=src.dtype, device=device)])
+            cols.append(flat.view(nb, B).view(torch.uint8))
+            del arena.bufs[k]
+        arena.bufs["blocked"] = torch.cat(cols, dim=1).contiguous()
+        del cols
+        streams = streams[:2] + [[arena.bufs["blocked"]], None, None]
     return arena, streams
 
 
@@ -215,8 +236,11 @@ def main():
         return
     modes = (args.modes or ("f16amp" if wl.p_dtype == "f16" else "mixed,kahan")).split(",")
     for mode in modes:
-        if mode.startswith("pure"):
-            BYTES[mode] = workloads.pure_traffic(mode)
+        base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
+        if base.startswith("pure"):
+            BYTES[mode] = workloads.pure_traffic(base)
+        elif base != mode:
+            BYTES[mode] = BYTES[base]
 
     state = {}
     for i, mode in enumerate(modes):
@@ -224,7 +248,8 @@ def main():
             arena, streams = make_mode_state("mixed", numels, dev, 100 + i, p_dtype="f16", loss_scale=wl.loss_scale)
         else:
             arena, streams = make_mode_state(mode, numels, dev, seed=100 + i)
-        state[mode] = (arena, A.TensorList(numels, streams), torch.zeros(1, dtype=torch.int32, device=dev))
+        flags = A.BLOCKED_STATE if mode.endswith("-blocked") else 0
+        state[mode] = (arena, A.TensorList(numels, streams, 0, -1, flags), torch.zeros(1, dtype=torch.int32, device=dev))
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     hp = A.HParams()
     # fp16 AMP keeps its loss scale on the device (growth 2, back-off 0.5, every 2000 clean steps)
@@ -245,12 +270,13 @@ def main():
             return
         if ev:
             ev[0].record(stream)
-        if mode.startswith("pure"):
-            m32, v32, kahan = workloads.parse_pure(mode)
+        base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
+        if base.startswith("pure"):
+            m32, v32, kahan = workloads.parse_pure(base)
             prec = A.PurePrecision(A.F32 if m32 else A.BF16, A.F32 if v32 else A.BF16, kahan)
             A.adamw_pure_multi_tensor_step(prec, tl, hp, ctr, None, stream)
         else:
-            code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
+            code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[base]
             A.adamw_multi_tensor_step(code, A.BF16, tl, hp, ctr, None, stream)
         if ev:
             ev[2].record(stream)
@@ -312,10 +338,13 @@ def main():
              "f16amp": "fp16-AMP overflow check + mixed fp16 step with a device-resident dynamic loss scale "
                        "(65536 to start)"}
     for mode in modes:
-        if mode.startswith("pure") and mode not in names:
-            m32, v32, kahan = workloads.parse_pure(mode)
-            names[mode] = (f"pure bf16 params, {'fp32' if m32 else 'bf16'} exp_avg, {'fp32' if v32 else 'bf16'} "
+        base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
+        if base.startswith("pure") and base not in names:
+            m32, v32, kahan = workloads.parse_pure(base)
+            names[base] = (f"pure bf16 params, {'fp32' if m32 else 'bf16'} exp_avg, {'fp32' if v32 else 'bf16'} "
                            f"exp_avg_sq, {'bf16 Kahan compensation' if kahan else 'no compensation'}")
+        if base != mode:
+            names[mode] = names[base] + ", state in one blocked buffer"
     out = {
         "metric": "AdamW step Gparams/s + achieved HBM GB/s (% of peak), OPT-1.3B shape, 1 GPU",
         "value": round(value, 3),

@@ -141,7 +141,22 @@ typedef struct {
  *                         elements holding this rank's share, element 0 being
  *                         flat position shard_begin (e.g. a reduce-scattered
  *                         gradient shard, or ZeRO-sharded master/m/v).
+ *   flat_mask & ADAMW_BLOCKED_STATE: see above.
  * numel is a host array of n_tensors element counts (each >= 0). */
+/* flat_mask bit: the blocked state layout.  exp_avg, exp_avg_sq and aux share
+ * ONE flat buffer of the shard, ptr[2][0] (16-byte aligned; ptr[3], ptr[4] and
+ * flat_mask bits 2-4 are ignored), made of ceil((shard_end - shard_begin) /
+ * ADAMW_STATE_BLOCK) blocks.  Block k holds the state of the shard's elements
+ * [k*B, (k+1)*B), B = ADAMW_STATE_BLOCK, stream after stream:
+ *     [exp_avg x B][exp_avg_sq x B][aux x B]
+ * each in its stream's dtype (an unused aux stream takes no room); the last
+ * block is padded to B.  For optimizer-owned ZeRO state: the step's per-element
+ * state traffic becomes one contiguous region per workgroup instead of three
+ * separate streams (fewer concurrently open DRAM rows; measured faster on
+ * MI355X).  param and grad keep their own layout. */
+#define ADAMW_BLOCKED_STATE (1u << 8)
+#define ADAMW_STATE_BLOCK 2048
+
 typedef struct {
     int64_t n_tensors;
     const int64_t* numel;

@@ -270,3 +270,40 @@ class SampledCase:
                 assert np.array_equal(got[k][out], self.initial[k][out]), f"{label}:{k} changed outside the shard"
         log_stats(stats)
         return stats
+
+
+STATE_KEYS = ("m", "v")
+
+
+def blocked_state_keys(case) -> tuple:
+    """The state streams (exp_avg, exp_avg_sq[, aux]) of a case, in block order."""
+    return tuple(case.keys[2:])
+
+
+def build_blocked(case, b, e) -> torch.Tensor:
+    """The blocked state buffer of the shard [b, e) of a tightly packed case
+    (arena index == flat index): per block of STATE_BLOCK elements, each state
+    stream's values one after another, as raw bytes."""
+    B = A.STATE_BLOCK
+    L = e - b
+    nb = -(-L // B)
+    cols = []
+    for k in blocked_state_keys(case):
+        x = case.arena.bufs[k][b:e]
+        pad = torch.zeros(nb * B - L, dtype=x.dtype, device=x.device)
+        cols.append(torch.cat([x, pad]).view(nb, B).view(torch.uint8))
+    return torch.cat(cols, dim=1).contiguous()
+
+
+def unpack_blocked(case, blocked: torch.Tensor, b, e) -> dict:
+    """Per-stream host arrays (flat order, length e - b) from a blocked buffer."""
+    B = A.STATE_BLOCK
+    L = e - b
+    out, col = {}, 0
+    for k in blocked_state_keys(case):
+        dt = case.arena.bufs[k].dtype
+        nbytes = B * torch.empty(0, dtype=dt).element_size()
+        part = blocked[:, col:col + nbytes].contiguous().view(dt).reshape(-1)[:L]
+        out[k] = to_np(part)
+        col += nbytes
+    return out

@@ -256,3 +256,34 @@ def test_header_is_plain_c_and_library_callable_from_c(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert r.stdout.startswith("ok")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_blocked_state_never_straddles_a_block(seed):
+    """With the blocked state layout every chunk lies inside one state block
+    (block k = shard elements [k*B, (k+1)*B)), and the rows still partition the shard."""
+    rng = np.random.default_rng(100 + seed)
+    numels = [int(x) for x in rng.choice([1, 7, 8, 100, 2047, 2048, 2049, 5000, 20000], size=rng.integers(1, 12))]
+    total = sum(numels)
+    b = int(rng.integers(0, total))
+    e = int(rng.integers(b + 1, total + 1))
+    esz = (2, 2, 4, 4, 4)
+    offs = np.concatenate([[0], np.cumsum(numels)[:-1]])
+    ptrs = [[FAKE + s * (1 << 36) + int(o) * esz[s] for o in offs] for s in range(2)]
+    ptrs += [[FAKE + 7 * (1 << 36)], None, None]
+    tl = A.TensorList(numels, ptrs, b, e, flat_mask=A.BLOCKED_STATE)
+    rows = A.adamw_plan_inspect(A.MIXED, A.BF16, tl)
+    pos = b
+    for (t, off, n, vec, flat, seg) in rows:
+        assert flat == pos
+        assert (flat - b) // A.STATE_BLOCK == (flat + n - 1 - b) // A.STATE_BLOCK
+        pos += n
+    assert pos == e
+
+
+def test_blocked_state_needs_aligned_buffer():
+    numels = [100]
+    ptrs = [[FAKE], [FAKE + (1 << 36)], [FAKE + 2 * (1 << 36) + 8], None, None]
+    with pytest.raises(A.AdamWError, match="blocked"):
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, A.TensorList(numels, ptrs, 0, -1, A.BLOCKED_STATE),
+                                  A.HParams(), FAKE, stream=0)

@@ -577,3 +577,43 @@ def test_concurrent_host_threads_on_own_streams():
             c.oracle_step(ho)
         c.compare_all(f"thread-{i}")
     free()
+
+
+@pytest.mark.parametrize("mode", ["mixed", "kahan", "split", "pure-f32-bf16-n", "pure-f32-f32-k"])
+@pytest.mark.parametrize("shard", [(0, None), (37, 60013), (4096, 4096 * 3 + 13)], ids=["all", "odd", "aligned"])
+def test_blocked_state_layout(mode, shard):
+    """exp_avg / exp_avg_sq / aux in one blocked buffer of the shard (2,048-element
+    blocks, stream after stream), param and grad per tensor: 3 steps against the
+    oracle run on the ordinary per-stream arrays."""
+    from gpu_util import build_blocked, unpack_blocked, pure_precision
+    numels = [30000, 7, 4099, 2048, 40000, 1]
+    case = Case(mode, numels, seed=2400, align_elems=1, random_moments=True)
+    total = sum(numels)
+    b, e = shard[0], shard[1] if shard[1] is not None else total
+    blocked = build_blocked(case, b, e)
+    streams = [[case.arena.view("p", i) for i in range(len(numels))],
+               [case.arena.view("g", i) for i in range(len(numels))], [blocked], None, None]
+    tl = A.TensorList(numels, streams, b, e, flat_mask=A.BLOCKED_STATE)
+    hg, ho = hp_pair()
+    for s in range(3):
+        if s:
+            case.refill_grads(s)
+        if mode.startswith("pure"):
+            A.adamw_pure_multi_tensor_step(pure_precision(mode), tl, hg, case.d_step)
+        else:
+            code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
+            A.adamw_multi_tensor_step(code, A.BF16, tl, hg, case.d_step)
+        case.oracle_step(ho, shard=(b, e))
+    torch.cuda.synchronize()
+    assert int(case.d_step.item()) == case.step == 3
+    got = unpack_blocked(case, blocked, b, e)
+    got["p"] = to_np(case.arena.bufs["p"])[b:e]
+    ref = {k: case.host[k][b:e] for k in case.keys}
+    keys = [k for k in case.keys if k != "g"]
+    from gpu_util import compare_streams
+    stats = compare_streams(f"blocked-{mode}", mode, got, ref, keys)
+    print(stats)
+    # the params outside the shard are untouched
+    hp_all = to_np(case.arena.bufs["p"])
+    assert np.array_equal(hp_all[:b], case.host["p"][:b]) and np.array_equal(hp_all[e:], case.host["p"][e:])
+    free()
