@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=160_000_000,
                     help="elements of the list the oracle steps once per mode")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE and WRITE_SIZE over this bench, then over --calib-copy); needs no GPU")
     ap.add_argument("--chunk-elems", type=int, default=0)
     ap.add_argument("--interleave", action="store_true",
                     help="alternate the modes every step instead of timing them as consecutive phases")
@@ -63,13 +66,66 @@ def calib_copy():
     """A plain copy of 4 GiB, three times: FETCH_SIZE / WRITE_SIZE of this kernel
     against the known 4 GiB per direction give the counters' scale."""
     import torch
-    n = 1 << 30
+    n = CALIB_COPY_BYTES // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes_each_way": n * 4, "launches": 3}), flush=True)
+
+
+CALIB_COPY_BYTES = 4 << 30
+# the kernel each timed mode launches, as rocprofv3 names it (a substring of the symbol)
+KERNEL_OF = {"mixed": "update_kernel<0>", "split": "update_kernel<3>",
+             "kahan": "update_pure_kernel<false, false, true>", "f16amp": "update_kernel<1>",
+             "check": "check_kernel"}
+
+
+def _pmc_values(path, counter, kernel):
+    import csv
+    with open(path) as f:
+        return [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+
+
+def write_traffic(wl_name, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    """HBM bytes per launch of each timed kernel from two rocprofv3 --pmc passes
+    (FETCH_SIZE, WRITE_SIZE: KiB per dispatch), each scaled by what the same
+    counter reads for the plain copy of --calib-copy (CALIB_COPY_BYTES each way)."""
+    import workloads
+    n = workloads.get(wl_name).total
+    scale = {}
+    for counter, path in (("FETCH_SIZE", cal_fetch_csv), ("WRITE_SIZE", cal_write_csv)):
+        vals = _pmc_values(path, counter, "copyBuffer")
+        if not vals:
+            raise SystemExit(f"no copy dispatches with {counter} in {path}")
+        scale[counter] = sum(vals) / len(vals) * 1024 / CALIB_COPY_BYTES
+    traffic, alg, per_param, raw = {}, {}, {}, {}
+    for mode, kernel in KERNEL_OF.items():
+        fv = _pmc_values(fetch_csv, "FETCH_SIZE", kernel)
+        wv = _pmc_values(write_csv, "WRITE_SIZE", kernel)
+        if not fv or not wv:
+            continue
+        rd = sum(fv) / len(fv) * 1024 / scale["FETCH_SIZE"]
+        wr = sum(wv) / len(wv) * 1024 / scale["WRITE_SIZE"]
+        traffic[mode] = round(rd + wr)
+        alg[mode] = BYTES[mode] * n
+        per_param[mode] = {"read": round(rd / n, 4), "write": round(wr / n, 4)}
+        raw[mode] = {"kernel": kernel, "FETCH_SIZE_KiB": fv, "WRITE_SIZE_KiB": wv}
+    if not traffic:
+        raise SystemExit("no timed kernel found in the counter files")
+    out = {"about": f"HBM bytes per launch on the {wl_name} list from two rocprofv3 --pmc passes (FETCH_SIZE, "
+                    "then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a plain "
+                    f"{CALIB_COPY_BYTES >> 30} GiB device copy (bench.py --calib-copy).",
+           "kernel_source_sha": _kernel_sha(),
+           "counter_scale": {k: round(v, 6) for k, v in scale.items()},
+           "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": alg,
+           "per_param": per_param, "raw": raw}
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl_name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({"wrote": path, "per_param": per_param, "counter_scale": out["counter_scale"]}), flush=True)
 
 
 def _time_launches(fn, reps, stream):
@@ -212,9 +268,12 @@ def cpu_baseline(numels, sample, modes):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the step runs on one rank's share; a run on "
-              f"{args.gpus} GPUs is not part of this build.", file=sys.stderr)
+        print("bench.py measures one GPU: the step runs on one rank's share; runs on "
+              f"{args.gpus} GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:
+        write_traffic(args.workload, *args.traffic_from)
+        return
     import torch
 
     if args.calib_copy:
@@ -388,8 +447,9 @@ def main():
 def _kernel_sha():
     import hashlib
     h = hashlib.sha256()
-    for f in ("kernels.hip", "plan.cpp", "layout.hpp"):
-        with open(os.path.join(ROOT, "adamw_optimizer_step_apply_amd", "csrc", f), "rb") as fh:
+    for f in ("adamw_optimizer_step_apply_amd/csrc/kernels.hip", "adamw_optimizer_step_apply_amd/csrc/plan.cpp",
+              "adamw_optimizer_step_apply_amd/csrc/layout.hpp", "include/adamw.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

@@ -153,9 +153,11 @@ typedef struct {
  * block is padded to B.  For optimizer-owned ZeRO state: the step's per-element
  * state traffic becomes one contiguous region per workgroup instead of three
  * separate streams (fewer concurrently open DRAM rows; measured faster on
- * MI355X).  param and grad keep their own layout. */
+ * MI355X).  param and grad keep their own layout.  B equals the largest default
+ * chunk of the update kernels, so splitting work at block edges never leaves a
+ * workgroup's lanes idle. */
 #define ADAMW_BLOCKED_STATE (1u << 8)
-#define ADAMW_STATE_BLOCK 2048
+#define ADAMW_STATE_BLOCK 8192
 
 typedef struct {
     int64_t n_tensors;

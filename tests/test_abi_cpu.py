@@ -263,7 +263,7 @@ def test_plan_blocked_state_never_straddles_a_block(seed):
     """With the blocked state layout every chunk lies inside one state block
     (block k = shard elements [k*B, (k+1)*B)), and the rows still partition the shard."""
     rng = np.random.default_rng(100 + seed)
-    numels = [int(x) for x in rng.choice([1, 7, 8, 100, 2047, 2048, 2049, 5000, 20000], size=rng.integers(1, 12))]
+    numels = [int(x) for x in rng.choice([1, 7, 8, 100, 2047, 2048, 2049, 5000, 8191, 8192, 8193, 20000, 40000], size=rng.integers(1, 12))]
     total = sum(numels)
     b = int(rng.integers(0, total))
     e = int(rng.integers(b + 1, total + 1))

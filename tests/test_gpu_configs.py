@@ -89,6 +89,51 @@ def test_opt13b_full_size_10_steps(mode):
     free()
 
 
+@pytest.mark.parametrize("mode", ["mixed", "kahan", "split"])
+def test_opt13b_full_size_blocked_state(mode):
+    """OPT-1.3B list with exp_avg / exp_avg_sq / aux in one blocked buffer of the
+    whole list (bench.py's "-blocked" modes), 3 steps; the sampled elements are
+    read back out of their blocks and compared with the oracle."""
+    wl = workloads.get("opt_1_3b")
+    case = SampledCase(mode, wl.numels, seed={"mixed": 4101, "kahan": 4102, "split": 4103}[mode])
+    B, n = A.STATE_BLOCK, sum(wl.numels)
+    nb = -(-n // B)
+    state = case.keys[2:]
+    cols = []
+    for k in state:
+        flat = torch.cat([case.arena.view(k, i) for i in range(len(wl.numels))])
+        flat = torch.cat([flat, torch.zeros(nb * B - n, dtype=flat.dtype, device=flat.device)])
+        cols.append(flat.view(nb, B).view(torch.uint8))
+        del flat
+    blocked = torch.cat(cols, dim=1).contiguous()
+    del cols
+    streams = [[case.arena.view(k, i) for i in range(len(wl.numels))] for k in case.keys[:2]]
+    tl = A.TensorList(wl.numels, streams + [[blocked], None, None], 0, -1, A.BLOCKED_STATE)
+    hg, ho = hp_pair()
+    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
+    for s in range(3):
+        if s:
+            case.refill_grads(s)
+        A.adamw_multi_tensor_step(code, A.BF16, tl, hg, case.d_step)
+        case.oracle_step(ho)
+    torch.cuda.synchronize()
+    flat_idx = torch.from_numpy(case.flat).to(blocked.device)
+    blk, off = flat_idx // B, flat_idx % B
+    col = 0
+    for k in state:
+        dt = case.arena.bufs[k].dtype
+        width = B * torch.empty(0, dtype=dt).element_size()
+        view = blocked[:, col:col + width].contiguous().view(dt)
+        # the per-tensor arena copy of this stream was not stepped: put the blocked
+        # values of the sampled elements there so the usual comparison reads them
+        case.arena.bufs[k][case.idx] = view[blk, off]
+        col += width
+        del view
+    _print(case.compare_all(f"opt13b-{mode}-blocked"))
+    del case, tl, blocked
+    free()
+
+
 def _host_any_nonfinite(g: torch.Tensor, block=1 << 28) -> bool:
     for i in range(0, g.numel(), block):
         if oracle.any_nonfinite(to_np(g[i:i + block]), True):

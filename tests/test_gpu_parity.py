@@ -582,7 +582,7 @@ def test_concurrent_host_threads_on_own_streams():
 @pytest.mark.parametrize("mode", ["mixed", "kahan", "split", "pure-f32-bf16-n", "pure-f32-f32-k"])
 @pytest.mark.parametrize("shard", [(0, None), (37, 60013), (4096, 4096 * 3 + 13)], ids=["all", "odd", "aligned"])
 def test_blocked_state_layout(mode, shard):
-    """exp_avg / exp_avg_sq / aux in one blocked buffer of the shard (2,048-element
+    """exp_avg / exp_avg_sq / aux in one blocked buffer of the shard (8,192-element
     blocks, stream after stream), param and grad per tensor: 3 steps against the
     oracle run on the ordinary per-stream arrays."""
     from gpu_util import build_blocked, unpack_blocked, pure_precision
