@@ -88,7 +88,10 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
     if (nt < 0) { err = "n_tensors < 0"; return ADAMW_E_INVALID; }
     if (nt > 0 && !list->numel) { err = "numel array is null"; return ADAMW_E_INVALID; }
     if (list->flat_mask & ~(0x1fu | ADAMW_BLOCKED_STATE)) { err = "flat_mask has unknown bits"; return ADAMW_E_INVALID; }
-    const bool blocked = (list->flat_mask & ADAMW_BLOCKED_STATE) != 0;
+    // the blocked layout concerns the state streams only: a plan that reads
+    // none of them (the overflow check) ignores it
+    const bool blocked = (list->flat_mask & ADAMW_BLOCKED_STATE) != 0 &&
+                         (esz_in[ADAMW_STREAM_EXP_AVG] || esz_in[ADAMW_STREAM_EXP_AVG_SQ] || esz_in[ADAMW_STREAM_AUX]);
 
     int64_t total = 0;
     for (int64_t i = 0; i < nt; ++i) {

@@ -1,28 +1,34 @@
 """Throughput of the fused AdamW step on one MI355X, OPT-1.3B-shaped.
 
 One bench step is the whole hot path over the OPT-1.3B parameter list (386
-tensors, 1,315,753,984 parameters, each tensor its own allocation-aligned
-buffer) in both of its modes: a mixed-precision step (bf16 param/grad + fp32
-master, exp_avg, exp_avg_sq) and a pure-bf16 step with bf16 Kahan compensation,
-each one call of adamw_multi_tensor_step (prologue + one update-kernel launch).
-The timed region runs K mixed steps then K Kahan steps (two consecutive phases,
-as two training runs would); --interleave alternates them instead.  Inputs
-are synthetic and seeded (master ~ N(0, 0.02), grads ~ N(0, 1e-3), moments 0) and
-already resident in HBM when the timed region starts; the gradient buffers are
-reused across steps.
+tensors, 1,315,753,984 parameters; params and grads each tensor its own
+allocation-aligned buffer) in both of its modes: a mixed-precision step (bf16
+param/grad + fp32 master, exp_avg, exp_avg_sq) and a pure-bf16 step with bf16
+Kahan compensation, each one call of adamw_multi_tensor_step (prologue + one
+update-kernel launch).  The optimizer owns its state, as a ZeRO shard's
+optimizer does, and keeps it in the blocked layout (exp_avg, exp_avg_sq and
+master or compensation interleaved per block of one buffer); the same steps on
+per-tensor state buffers are timed after the headline region and reported as
+per_tensor_state.  The timed region runs K mixed steps then K Kahan steps (two
+consecutive phases, as two training runs would); --interleave alternates them
+instead.  Inputs are synthetic and seeded (master ~ N(0, 0.02), grads ~
+N(0, 1e-3), moments 0) and already resident in HBM when the timed region
+starts; the gradient buffers are reused across steps.
 
 value = parameter updates per second over the timed steps (2 x N per step, one
 per mode), in Gparam/s.  Alongside it: per-mode Gparam/s and algorithmic HBM
-GB/s (28 B/param mixed, 18 B/param Kahan), the roofline of the dominant kernel
-(the mixed update) from HIP events recorded on the launch stream, the same-mix
-ceiling measured by bench_probe.hip, and the CPU oracle timed on a bounded
-sample on the host cores.
+GB/s (28 B/param mixed, 18 B/param Kahan), the time of each mode's first call
+(plan build + chunk-table upload), the roofline of the dominant kernel (the
+mixed update) from HIP events recorded on the launch stream, the same-mix
+ceilings measured by bench_probe.hip, and the CPU oracle timed on a bounded
+sample on the host cores (one thread, and one thread per range on all cores).
 
 Usage:
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-probe]
-  python bench.py --workload ragged_10k --modes f16amp   (overflow check + fp16 step, 10k tensors)
+  python bench.py --workload ragged_10k                  (overflow check + fp16 step, 10k tensors)
   python bench.py --probe-only                            (memory ceilings only)
   python bench.py --calib-copy                            (plain 4 GiB copy, to scale rocprofv3 byte counters)
+  python bench.py --traffic-from F.csv W.csv CF.csv CW.csv (rocprofv3 counters -> profiles/traffic_<workload>.json)
 """
 from __future__ import annotations
 
@@ -46,11 +52,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="opt_1_3b")
-    ap.add_argument("--modes", default=None, help="comma list of mixed,kahan,f16amp")
+    ap.add_argument("--modes", default=None,
+                    help="comma list of mixed, kahan, split, pure-<m>-<v>-<k|n>, f16amp, each optionally -blocked")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-probe", action="store_true", help="skip the same-mix ceiling probes")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the per-tensor-state timing that follows a blocked-state headline")
     ap.add_argument("--probe-only", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=160_000_000,
+    ap.add_argument("--cpu-sample", type=int, default=256_000_000,
                     help="elements of the list the oracle steps once per mode")
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
@@ -89,12 +98,21 @@ def _pmc_values(path, counter, kernel):
                 if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
 
 
-def write_traffic(wl_name, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+def write_traffic(wl_name, modes, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     """HBM bytes per launch of each timed kernel from two rocprofv3 --pmc passes
-    (FETCH_SIZE, WRITE_SIZE: KiB per dispatch), each scaled by what the same
-    counter reads for the plain copy of --calib-copy (CALIB_COPY_BYTES each way)."""
+    (FETCH_SIZE, WRITE_SIZE: KiB per dispatch) over a bench run of `modes`,
+    each scaled by what the same counter reads for the plain copy of
+    --calib-copy (CALIB_COPY_BYTES each way)."""
     import workloads
     n = workloads.get(wl_name).total
+    kernels = {}
+    for mode in modes:
+        base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
+        kernels[mode] = KERNEL_OF[base]
+        if base == "f16amp":
+            kernels["check"] = KERNEL_OF["check"]
+    if len(set(kernels.values())) != len(kernels):
+        raise SystemExit("two of the modes launch the same kernel: profile them in separate runs")
     scale = {}
     for counter, path in (("FETCH_SIZE", cal_fetch_csv), ("WRITE_SIZE", cal_write_csv)):
         vals = _pmc_values(path, counter, "copyBuffer")
@@ -102,7 +120,7 @@ def write_traffic(wl_name, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
             raise SystemExit(f"no copy dispatches with {counter} in {path}")
         scale[counter] = sum(vals) / len(vals) * 1024 / CALIB_COPY_BYTES
     traffic, alg, per_param, raw = {}, {}, {}, {}
-    for mode, kernel in KERNEL_OF.items():
+    for mode, kernel in kernels.items():
         fv = _pmc_values(fetch_csv, "FETCH_SIZE", kernel)
         wv = _pmc_values(write_csv, "WRITE_SIZE", kernel)
         if not fv or not wv:
@@ -110,7 +128,7 @@ def write_traffic(wl_name, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
         rd = sum(fv) / len(fv) * 1024 / scale["FETCH_SIZE"]
         wr = sum(wv) / len(wv) * 1024 / scale["WRITE_SIZE"]
         traffic[mode] = round(rd + wr)
-        alg[mode] = BYTES[mode] * n
+        alg[mode] = BYTES[mode[:-len("-blocked")] if mode.endswith("-blocked") else mode] * n
         per_param[mode] = {"read": round(rd / n, 4), "write": round(wr / n, 4)}
         raw[mode] = {"kernel": kernel, "FETCH_SIZE_KiB": fv, "WRITE_SIZE_KiB": wv}
     if not traffic:
@@ -126,6 +144,19 @@ def write_traffic(wl_name, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps({"wrote": path, "per_param": per_param, "counter_scale": out["counter_scale"]}), flush=True)
+
+
+def default_modes(args):
+    """The modes one bench step runs: both modes of the OPT-1.3B list with their
+    state in the blocked layout, or the fp16-AMP step on an fp16 workload."""
+    import workloads
+    if args.modes:
+        return args.modes
+    # The ragged fp16 list keeps per-tensor state: its lengths are arbitrary, so
+    # most tensors start at flat positions that are not multiples of 8, where a
+    # blocked state's addresses never share 16-byte alignment with the tensor's
+    # own param and grad buffers and the planner falls back to element chunks.
+    return "f16amp" if workloads.get(args.workload).p_dtype == "f16" else "mixed-blocked,kahan-blocked"
 
 
 def _time_launches(fn, reps, stream):
@@ -168,6 +199,13 @@ def probes(n, stream):
     w, m, v = (torch.ones(n, dtype=torch.float32, device=dev) for _ in range(3))
     run(0, [g, w, m, v, p], n, 28 * n, "mixed_mix")
     del w, m, v
+    nb = -(-n // 8192)                            # whole blocks of the blocked state layout
+    blk = torch.ones(nb * 8192 * 3, dtype=torch.float32, device=dev)
+    run(6, [g, blk, p], n, 28 * n, "mixed_blocked_mix")
+    del blk
+    blk = torch.ones(nb * 8192 * 3, dtype=torch.bfloat16, device=dev)
+    run(7, [g, p, blk], n, 18 * n, "kahan_blocked_mix")
+    del blk
     r16 = torch.ones(n, dtype=torch.bfloat16, device=dev)
     m32, v32 = (torch.ones(n, dtype=torch.float32, device=dev) for _ in range(2))
     run(5, [g, p, r16, m32, v32], n, 26 * n, "split_mix")
@@ -217,52 +255,101 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
 
 
 def cpu_baseline(numels, sample, modes):
-    """The oracle as it is (one host thread), one step per mode over the first
-    `sample` elements of the list; scaled to param-updates/s of the bench step."""
+    """The oracle as it is, one step per mode over the first `sample` elements
+    of the list, scaled to param-updates/s of the bench step: on one host
+    thread (value), and with the sample cut into equal ranges stepped by one
+    host thread each (all_cores; the oracle's C loops release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
 
     import oracle
     import workloads
+    modes = [m[:-len("-blocked")] if m.endswith("-blocked") else m for m in modes]
     n = min(sample, sum(numels))
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
     hp = oracle.HParams()
-    secs = {}
     w = workloads.normal(n, workloads.INIT_STD, "cpu", "master", 7).numpy()
-    if "f16amp" in modes:
+    f16 = "f16amp" in modes
+    if f16:
         g = workloads.grads(n, "cpu", 7, 0, dtype=torch.float16, scale=65536.0).view(torch.int16).numpy().view(np.uint16)
-        hp16 = oracle.HParams(inv_scale=1.0 / 65536)
-        p16, m, v = np.zeros(n, np.uint16), np.zeros(n, np.float32), np.zeros(n, np.float32)
-        t0 = time.perf_counter()
-        assert not oracle.any_nonfinite(g, True)
-        oracle.adamw_mixed(p16, g, w, m, v, hp16, 1, p_is_f16=True)
-        secs["f16amp"] = time.perf_counter() - t0
+        hp = oracle.HParams(inv_scale=1.0 / 65536)
     else:
         g = workloads.grads(n, "cpu", 7, 0, dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-        if "mixed" in modes:
-            p16, m, v = np.zeros(n, np.uint16), np.zeros(n, np.float32), np.zeros(n, np.float32)
-            wm = w.copy()
-            t0 = time.perf_counter()
-            oracle.adamw_mixed(p16, g, wm, m, v, hp, 1)
-            secs["mixed"] = time.perf_counter() - t0
-            del m, v
-        if "split" in modes:
+
+    def zeros(dt):
+        return np.full(n, 0, dt)       # written now, so no first-touch page faults land in the timed call
+
+    def state(mode):
+        if mode in ("mixed", "f16amp"):
+            return (zeros(np.uint16), g, w.copy(), zeros(np.float32), zeros(np.float32))
+        if mode == "split":
             ps, rs = oracle.split_make(w)
-            ms_, vs_ = np.zeros(n, np.float32), np.zeros(n, np.float32)
+            return (ps, g, rs, zeros(np.float32), zeros(np.float32))
+        return (oracle.f32_to_bf16(w), g, zeros(np.uint16), zeros(np.uint16), zeros(np.uint16))
+
+    def step(mode, bufs, lo, hi):
+        s = [x[lo:hi] for x in bufs]
+        if mode == "f16amp":
+            assert not oracle.any_nonfinite(s[1], True)
+            oracle.adamw_mixed(s[0], s[1], s[2], s[3], s[4], hp, 1, p_is_f16=True)
+        elif mode == "mixed":
+            oracle.adamw_mixed(s[0], s[1], s[2], s[3], s[4], hp, 1)
+        elif mode == "split":
+            oracle.adamw_mixed_split(s[0], s[1], s[2], s[3], s[4], hp, 1)
+        else:
+            oracle.adamw_kahan(s[0], s[1], s[3], s[4], s[2], hp, 1)
+
+    secs, secs_mt = {}, {}
+    cuts = [n * i // threads for i in range(threads + 1)]
+    with ThreadPoolExecutor(threads) as pool:
+        for mode in [m for m in ("f16amp", "mixed", "split", "kahan") if m in modes]:
+            bufs = state(mode)
             t0 = time.perf_counter()
-            oracle.adamw_mixed_split(ps, g, rs, ms_, vs_, hp, 1)
-            secs["split"] = time.perf_counter() - t0
-            del ms_, vs_, ps, rs
-        if "kahan" in modes:
-            pk = oracle.f32_to_bf16(w)
-            mk, vk, ck = (np.zeros(n, np.uint16) for _ in range(3))
+            step(mode, bufs, 0, n)
+            secs[mode] = time.perf_counter() - t0
+            bufs = state(mode)
             t0 = time.perf_counter()
-            oracle.adamw_kahan(pk, g, mk, vk, ck, hp, 1)
-            secs["kahan"] = time.perf_counter() - t0
-    per_param = sum(s / n for s in secs.values())
-    return {"value": round(len(secs) / per_param / 1e9, 4), "unit": "Gparam/s", "cores": 1, "kind": "oracle",
+            list(pool.map(lambda i: step(mode, bufs, cuts[i], cuts[i + 1]), range(threads)))
+            secs_mt[mode] = time.perf_counter() - t0
+            del bufs
+
+    def rate(d):
+        return round(len(d) / sum(s / n for s in d.values()) / 1e9, 4)
+    return {"value": rate(secs), "unit": "Gparam/s", "cores": 1, "kind": "oracle",
             "sample": f"one step per mode ({', '.join(secs)}) over the first {n:,} parameters of the list, "
                       f"host-resident, 1 thread: " + " + ".join(f"{s:.2f} s" for s in secs.values()),
+            "all_cores": {"value": rate(secs_mt), "unit": "Gparam/s", "cores": threads,
+                          "sample": f"the same, cut into {threads} ranges on {threads} threads: "
+                                    + " + ".join(f"{s:.2f} s" for s in secs_mt.values())},
             "host_cpus": os.cpu_count()}
+
+
+def _per_mode(modes, ev, K, N, first_ms):
+    per_mode = {}
+    for mode in modes:
+        if mode.startswith("f16amp"):
+            chk = [a.elapsed_time(b) for a, b, _ in ev[mode]]
+            upd = [b.elapsed_time(c) for _, b, c in ev[mode]]
+            c_avg = sum(chk) / K
+            per_mode["check" + mode[len("f16amp"):]] = {"ms_avg": round(c_avg, 4), "gb_s": round(N * 2 / (c_avg * 1e-3) / 1e9, 1),
+                                 "frac_of_hbm_peak": round(N * 2 / (c_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "bytes_per_param": 2}
+            ms = upd
+        else:
+            ms = [a.elapsed_time(c) for a, _, c in ev[mode]]
+        avg = sum(ms) / len(ms)
+        key = mode + "_step" if mode.startswith("f16amp") else mode
+        per_mode[key] = {
+            "ms_avg": round(avg, 4), "ms_median": round(sorted(ms)[len(ms) // 2], 4), "ms_min": round(min(ms), 4),
+            "gparam_s": round(N / (avg * 1e-3) / 1e9, 2),
+            "gb_s": round(N * BYTES[mode] / (avg * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(N * BYTES[mode] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_param": BYTES[mode],
+            "first_call_ms": round(first_ms[mode], 3),
+        }
+    return per_mode
 
 
 def main():
@@ -272,7 +359,7 @@ def main():
               f"{args.gpus} GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
     if args.traffic_from:
-        write_traffic(args.workload, *args.traffic_from)
+        write_traffic(args.workload, default_modes(args).split(","), *args.traffic_from)
         return
     import torch
 
@@ -293,8 +380,10 @@ def main():
     if args.probe_only:
         print(json.dumps({"probes_gb_s": probes(N, stream), "n": N}), flush=True)
         return
-    modes = (args.modes or ("f16amp" if wl.p_dtype == "f16" else "mixed,kahan")).split(",")
-    for mode in modes:
+    modes = default_modes(args).split(",")
+    # the same steps on per-tensor state buffers, timed after the headline region
+    compare = [] if args.no_compare else [m[:-len("-blocked")] for m in modes if m.endswith("-blocked")]
+    for mode in modes + compare:
         base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
         if base.startswith("pure"):
             BYTES[mode] = workloads.pure_traffic(base)
@@ -302,9 +391,10 @@ def main():
             BYTES[mode] = BYTES[base]
 
     state = {}
-    for i, mode in enumerate(modes):
-        if mode == "f16amp":
-            arena, streams = make_mode_state("mixed", numels, dev, 100 + i, p_dtype="f16", loss_scale=wl.loss_scale)
+    for i, mode in enumerate(modes + compare):
+        if mode.startswith("f16amp"):
+            arena, streams = make_mode_state("mixed" + mode[len("f16amp"):], numels, dev, 100 + i, p_dtype="f16",
+                                             loss_scale=wl.loss_scale)
         else:
             arena, streams = make_mode_state(mode, numels, dev, seed=100 + i)
         flags = A.BLOCKED_STATE if mode.endswith("-blocked") else 0
@@ -317,7 +407,7 @@ def main():
 
     def one(mode, ev=None):
         _, tl, ctr = state[mode]
-        if mode == "f16amp":
+        if mode.startswith("f16amp"):
             if ev:
                 ev[0].record(stream)
             A.adamw_check_finite(A.F16, tl, flag, stream)
@@ -340,8 +430,16 @@ def main():
         if ev:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        for mode in modes:
+    # the first call of each mode builds its plan and uploads the chunk table
+    first_ms = {}
+    for mode in modes + compare:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        one(mode)
+        torch.cuda.synchronize()
+        first_ms[mode] = (time.perf_counter() - t0) * 1e3
+    for _ in range(args.warmup - 1):
+        for mode in modes + compare:
             one(mode)
     torch.cuda.synchronize()
 
@@ -350,40 +448,26 @@ def main():
     # training configurations, and a real loop runs one of them.  --interleave
     # alternates them every step instead.
     K = args.steps
-    ev = {m: [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)] for m in modes}
-    order = [(s, m) for s in range(K) for m in modes] if args.interleave else [(s, m) for m in modes for s in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s, mode in order:
-        one(mode, ev[mode][s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
-    per_mode = {}
-    for mode in modes:
-        if mode == "f16amp":
-            chk = [a.elapsed_time(b) for a, b, _ in ev[mode]]
-            upd = [b.elapsed_time(c) for _, b, c in ev[mode]]
-            c_avg = sum(chk) / K
-            per_mode["check"] = {"ms_avg": round(c_avg, 4), "gb_s": round(N * 2 / (c_avg * 1e-3) / 1e9, 1),
-                                 "frac_of_hbm_peak": round(N * 2 / (c_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                 "bytes_per_param": 2}
-            ms = upd
-        else:
-            ms = [a.elapsed_time(c) for a, _, c in ev[mode]]
-        avg = sum(ms) / len(ms)
-        key = "f16amp_step" if mode == "f16amp" else mode
-        per_mode[key] = {
-            "ms_avg": round(avg, 4), "ms_min": round(min(ms), 4),
-            "gparam_s": round(N / (avg * 1e-3) / 1e9, 2),
-            "gb_s": round(N * BYTES[mode] / (avg * 1e-3) / 1e9, 1),
-            "frac_of_hbm_peak": round(N * BYTES[mode] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_param": BYTES[mode],
-        }
+    def timed(ms_):
+        ev = {m: [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)] for m in ms_}
+        order = [(s, m) for s in range(K) for m in ms_] if args.interleave else [(s, m) for m in ms_ for s in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s, mode in order:
+            one(mode, ev[mode][s])
+        torch.cuda.synchronize()
+        return ev, time.perf_counter() - t0
+
+    ev, wall = timed(modes)
+    per_mode = _per_mode(modes, ev, K, N, first_ms)
+    if compare:
+        ev_c, _ = timed(compare)
+        per_tensor = _per_mode(compare, ev_c, K, N, first_ms)
     ms_step = wall / K * 1e3
     value = len(modes) * N / (wall / K) / 1e9
     dom = modes[0]
-    dom_key = "f16amp_step" if dom == "f16amp" else dom
+    dom_key = dom + "_step" if dom.startswith("f16amp") else dom
     achieved = per_mode[dom_key]["gb_s"]
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
@@ -403,7 +487,8 @@ def main():
             names[base] = (f"pure bf16 params, {'fp32' if m32 else 'bf16'} exp_avg, {'fp32' if v32 else 'bf16'} "
                            f"exp_avg_sq, {'bf16 Kahan compensation' if kahan else 'no compensation'}")
         if base != mode:
-            names[mode] = names[base] + ", state in one blocked buffer"
+            names[mode] = (names[base] + f", exp_avg/exp_avg_sq/{'master' if base == 'mixed' else 'aux'} "
+                           f"interleaved per {A.STATE_BLOCK}-element block of one optimizer-owned buffer")
     out = {
         "metric": "AdamW step Gparams/s + achieved HBM GB/s (% of peak), OPT-1.3B shape, 1 GPU",
         "value": round(value, 3),
@@ -425,6 +510,7 @@ def main():
                    "hparams": {"lr": hp.lr, "beta1": hp.beta1, "beta2": hp.beta2, "eps": hp.eps,
                                "weight_decay": hp.weight_decay}},
         "per_mode": per_mode,
+        **({"per_tensor_state": per_tensor} if compare else {}),
         "roofline": {"bound": "hbm", "kernel": f"update_kernel ({dom})", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
@@ -435,10 +521,14 @@ def main():
         torch.cuda.empty_cache()
         pr = probes(N, stream)
         out["ceilings_gb_s"] = pr
-        for mode, key in (("mixed", "mixed_mix"), ("kahan", "kahan_mix"), ("f16amp_step", "mixed_mix"),
-                          ("split", "split_mix")):
-            if mode in per_mode:
-                per_mode[mode]["frac_of_same_mix_probe"] = round(per_mode[mode]["gb_s"] / pr[key], 4)
+        probe_of = {"mixed": "mixed_mix", "kahan": "kahan_mix", "f16amp_step": "mixed_mix", "split": "split_mix",
+                    "mixed-blocked": "mixed_blocked_mix", "kahan-blocked": "kahan_blocked_mix",
+                    "f16amp-blocked_step": "mixed_blocked_mix"}
+        for table in (per_mode, per_tensor if compare else {}):
+            for mode, row in table.items():
+                key = probe_of.get(mode)
+                if key:
+                    row["frac_of_same_mix_probe"] = round(row["gb_s"] / pr[key], 4)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(numels, args.cpu_sample, modes)
     print(json.dumps(out), flush=True)

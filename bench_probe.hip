@@ -1,4 +1,4 @@
-// bench_probe.hip -- memory-system ceilings for bench.py --probe (gfx950).
+// bench_probe.hip -- memory-system ceilings for bench.py's probes (gfx950).
 //
 // Kernels that move exactly the bytes of the fused AdamW step's streams, in the
 // same launch shape as the library's update kernel (256 lanes, one 8-element
@@ -73,6 +73,53 @@ __global__ __launch_bounds__(256) void kahan_mix(const GLOBAL u32x4* g, GLOBAL u
     __builtin_nontemporal_store(f ^ a, c + k);
 }
 
+// The blocked state layout: per block of kBlock elements, the state streams one
+// after another ([m][v][w] fp32 for the mixed mix, [m][v][c] bf16 for Kahan);
+// g and p keep their own buffers.  Pack k (elements 8k..8k+7) lies in block
+// k / (kBlock / 8) at pack offset k % (kBlock / 8).
+constexpr uint64_t kBlock = 8192;
+constexpr uint64_t kPacksPerBlock = kBlock / 8;
+
+__global__ __launch_bounds__(256) void mixed_blocked_mix(const GLOBAL u32x4* g, GLOBAL f32x4* s, GLOBAL u32x4* p,
+                                                         uint64_t npack)
+{
+    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    if (k >= npack) return;
+    // one block of fp32 state = 3 x kBlock floats = 3 x kBlock / 4 f32x4
+    const uint64_t base = (k / kPacksPerBlock) * (3 * kBlock / 4) + 2 * (k % kPacksPerBlock);
+    GLOBAL f32x4* m = s + base;
+    GLOBAL f32x4* v = m + kBlock / 4;
+    GLOBAL f32x4* w = v + kBlock / 4;
+    const u32x4 gv = g[k];
+    const f32x4 w0 = w[0], w1 = w[1], m0 = m[0], m1 = m[1], v0 = v[0], v1 = v[1];
+    const f32x4 a = w0 + m0, b = w1 + v1;
+    __builtin_nontemporal_store(a, w);
+    __builtin_nontemporal_store(b, w + 1);
+    __builtin_nontemporal_store(m1, m);
+    __builtin_nontemporal_store(m0, m + 1);
+    __builtin_nontemporal_store(v1, v);
+    __builtin_nontemporal_store(v0, v + 1);
+    __builtin_nontemporal_store(gv ^ __builtin_bit_cast(u32x4, a), p + k);
+}
+
+__global__ __launch_bounds__(256) void kahan_blocked_mix(const GLOBAL u32x4* g, GLOBAL u32x4* p, GLOBAL u32x4* s,
+                                                         uint64_t npack)
+{
+    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    if (k >= npack) return;
+    // one block of bf16 state = 3 x kBlock halves = 3 x kBlock / 8 u32x4
+    GLOBAL u32x4* m = s + (k / kPacksPerBlock) * (3 * kBlock / 8) + (k % kPacksPerBlock);
+    GLOBAL u32x4* v = m + kBlock / 8;
+    GLOBAL u32x4* c = v + kBlock / 8;
+    const u32x4 a = __builtin_nontemporal_load(g + k), b = __builtin_nontemporal_load(p + k);
+    const u32x4 d = __builtin_nontemporal_load(m), e = __builtin_nontemporal_load(v);
+    const u32x4 f = __builtin_nontemporal_load(c);
+    __builtin_nontemporal_store(a ^ b, p + k);
+    __builtin_nontemporal_store(d ^ a, m);
+    __builtin_nontemporal_store(e ^ a, v);
+    __builtin_nontemporal_store(f ^ a, c);
+}
+
 __global__ __launch_bounds__(256) void copy_mix(const GLOBAL f32x4* src, GLOBAL f32x4* dst, uint64_t n4)
 {
     const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
@@ -98,14 +145,16 @@ constexpr size_t kLds = 81920;   // two resident workgroups per CU, as the updat
 
 }  // namespace
 
-// kind: 0 mixed, 1 Kahan, 5 split master (n elements); 2 copy, 3 read, 4 write (n floats).
-// a..e: the buffers of the kind, in the order of the kernel's parameters.
+// kind: 0 mixed, 1 Kahan, 5 split master, 6 mixed with blocked state, 7 Kahan with
+// blocked state (n elements); 2 copy, 3 read, 4 write (n floats).
+// a..e: the buffers of the kind, in the order of the kernel's parameters; a
+// blocked state buffer holds ceil(n / 8192) whole blocks.
 // n must be a multiple of 8.  Returns the hipError_t of the launch.
 extern "C" int probe_launch(int kind, void* a, void* b, void* c, void* d, void* e, uint64_t n, void* stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (n % 8) return (int)hipErrorInvalidValue;
-    const uint64_t items = (kind <= 1 || kind == 5) ? n / 8 : n / 4;
+    const uint64_t items = (kind <= 1 || kind >= 5) ? n / 8 : n / 4;
     const uint64_t grid = (items + 255) / 256;
     if (grid == 0 || grid > 0x7fffffffull) return (int)hipErrorInvalidValue;
     switch (kind) {
@@ -120,6 +169,14 @@ extern "C" int probe_launch(int kind, void* a, void* b, void* c, void* d, void* 
     case 5:
         hipLaunchKernelGGL(split_mix, dim3((unsigned)grid), dim3(256), kLds, s, (const GLOBAL u32x4*)a,
                            (GLOBAL u32x4*)b, (GLOBAL u32x4*)c, (GLOBAL f32x4*)d, (GLOBAL f32x4*)e, items);
+        break;
+    case 6:
+        hipLaunchKernelGGL(mixed_blocked_mix, dim3((unsigned)grid), dim3(256), kLds, s, (const GLOBAL u32x4*)a,
+                           (GLOBAL f32x4*)b, (GLOBAL u32x4*)c, items);
+        break;
+    case 7:
+        hipLaunchKernelGGL(kahan_blocked_mix, dim3((unsigned)grid), dim3(256), kLds, s, (const GLOBAL u32x4*)a,
+                           (GLOBAL u32x4*)b, (GLOBAL u32x4*)c, items);
         break;
     case 2:
         hipLaunchKernelGGL(copy_mix, dim3((unsigned)grid), dim3(256), 0, s, (const GLOBAL f32x4*)a,

@@ -281,6 +281,19 @@ def test_plan_blocked_state_never_straddles_a_block(seed):
     assert pos == e
 
 
+def test_check_plan_ignores_blocked_bit():
+    """The overflow check reads only grads: with the blocked bit its plan is the
+    plan without it (no splits at state-block edges), and it needs no state buffer."""
+    numels = [30000, 7, 20000, 1, 40000]
+    offs = np.concatenate([[0], np.cumsum(numels)[:-1]])
+    g = [FAKE + (1 << 36) + int(o) * 2 for o in offs]
+    plain = A.adamw_plan_inspect(A.MIXED, A.F16, A.TensorList(numels, [None, g, None, None, None]), True)
+    blocked = A.adamw_plan_inspect(A.MIXED, A.F16, A.TensorList(numels, [None, g, None, None, None],
+                                                                flat_mask=A.BLOCKED_STATE), True)
+    assert blocked == plain
+    assert max(r[2] for r in plain) > A.STATE_BLOCK
+
+
 def test_blocked_state_needs_aligned_buffer():
     numels = [100]
     ptrs = [[FAKE], [FAKE + (1 << 36)], [FAKE + 2 * (1 << 36) + 8], None, None]

@@ -471,6 +471,47 @@ def test_dynamic_loss_scale_sequence(scale0, interval):
     free()
 
 
+def test_blocked_state_fp16_amp_sequence():
+    """fp16 AMP (check + step with the device-resident loss scale) with
+    exp_avg / exp_avg_sq / master in the blocked layout: 8 iterations, an overflow
+    planted at two of them; the scale, tracker and step counter after every
+    iteration, and every element at the end, against the oracle."""
+    from gpu_util import build_blocked, compare_streams, unpack_blocked
+    numels = [30000, 7, 4099, 2048, 40000, 1, 9000]
+    case = Case("mixed", numels, seed=2500, p_dtype="f16", loss_scale=65536.0, align_elems=1)
+    total = sum(numels)
+    blocked = build_blocked(case, 0, total)
+    streams = [[case.arena.view("p", i) for i in range(len(numels))],
+               [case.arena.view("g", i) for i in range(len(numels))], [blocked], None, None]
+    tl = A.TensorList(numels, streams, 0, -1, flat_mask=A.BLOCKED_STATE)
+    hg, ho = hp_pair()
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    state = A.loss_scale_state(65536.0)
+    scaler = A.LossScaler(2.0, 0.5, 3)
+    ls = oracle.LossScale(scale=65536.0, tracker=0, growth=2.0, backoff=0.5, interval=3)
+    bad = {2, 5}
+    for it in range(8):
+        if it:
+            case.refill_grads(it)
+        if it in bad:
+            case.arena.view("g", 4)[1234 * it] = float("inf") if it == 2 else float("nan")
+            case.host["g"] = to_np(case.arena.bufs["g"])
+        A.adamw_check_finite(A.F16, tl, flag)
+        A.adamw_multi_tensor_step_amp(A.MIXED, A.F16, tl, hg, case.d_step, flag, state, scaler)
+        case.step = oracle.amp_step_list("mixed", case.oracle_tensors(), ho, case.step, ls)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == int(it in bad), it
+        assert np.float32(state[0].item()) == np.float32(ls.scale), (it, state[0].item(), ls.scale)
+        assert int(state.view(torch.int32)[1].item()) == ls.tracker, it
+        assert int(case.d_step.item()) == case.step, it
+    assert case.step == 6
+    got = unpack_blocked(case, blocked, 0, total)
+    got["p"] = to_np(case.arena.bufs["p"])
+    keys = [k for k in case.keys if k != "g"]
+    print(compare_streams("blocked-amp", "mixed", got, {k: case.host[k] for k in case.keys}, keys, True))
+    free()
+
+
 PURE_MODES = [f"pure-{m}-{v}-{k}" for m in ("f32", "bf16") for v in ("f32", "bf16") for k in ("k", "n")]
 
 
