@@ -654,14 +654,14 @@ hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32
 // Occupancy cap, per kernel family: the update kernels use no LDS, but
 // reserving this much per workgroup leaves room for only 160 KiB / bytes
 // workgroups on a CU.  Measured on MI355X with the OPT-1.3B list, 8 waves per CU
-// (mixed: two 256-lane workgroups) and 16 (pure: one 1024-lane workgroup) stream
-// faster than the register-limited 20-24 waves: fewer concurrent address
+// (mixed: two 256-lane workgroups) and 16 (pure: four 256-lane workgroups)
+// stream faster than the register-limited 20-32 waves: fewer concurrent address
 // streams per CU keep more DRAM rows open.
 #ifndef ADAMW_LDS_MIXED
 #define ADAMW_LDS_MIXED 81920
 #endif
 #ifndef ADAMW_LDS_PURE
-#define ADAMW_LDS_PURE 163840
+#define ADAMW_LDS_PURE 40960
 #endif
 
 hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,

@@ -18,15 +18,17 @@ namespace adamw {
 constexpr int kStreams = 5;            // param, grad, exp_avg, exp_avg_sq, aux
 // Threads per workgroup, per kernel family, with the occupancy caps in
 // kernels.hip: the mixed kernels run 256-lane workgroups, two per CU (8 waves);
-// the VALU-heavier pure-bf16 family 1024-lane workgroups, one per CU (16 waves);
+// the VALU-heavier pure-bf16 family 256-lane workgroups, four per CU (16 waves);
 // the overflow check 256-lane workgroups at full occupancy (it only reads).
-// Chosen by interleaved A/B runs on three MI355X boxes (OPT-1.3B list): the
-// candidate shapes differed by at most ~3%, less than the spread between boxes.
+// Chosen by interleaved A/B runs on MI355X (OPT-1.3B list, state in the blocked
+// layout and per tensor): for the pure family 256 x 4 and 512 x 2 beat 1024 x 1
+// by 5% on blocked state and tie with it per tensor; for the mixed family
+// 256 x 2 leads every other shape by 3% or more on blocked state.
 #ifndef ADAMW_BLOCK_MIXED
 #define ADAMW_BLOCK_MIXED 256
 #endif
 #ifndef ADAMW_BLOCK_PURE
-#define ADAMW_BLOCK_PURE 1024
+#define ADAMW_BLOCK_PURE 256
 #endif
 constexpr int kBlockMixed = ADAMW_BLOCK_MIXED;
 constexpr int kBlockPure = ADAMW_BLOCK_PURE;

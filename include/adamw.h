@@ -154,8 +154,8 @@ typedef struct {
  * state traffic becomes one contiguous region per workgroup instead of three
  * separate streams (fewer concurrently open DRAM rows; measured faster on
  * MI355X).  param and grad keep their own layout (adamw_check_finite, which
- * reads only grads, ignores the bit).  B equals the largest default
- * chunk of the update kernels, so splitting work at block edges never leaves a
+ * reads only grads, ignores the bit).  B is a multiple of every update
+ * kernel's default chunk, so splitting work at block edges never leaves a
  * workgroup's lanes idle.  The 16-byte vector path needs an element's state
  * address and its param/grad addresses to share their alignment: with
  * per-tensor param/grad buffers that start 16-byte aligned, a tensor whose
@@ -285,7 +285,7 @@ int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_ten
 /* Tuning knob: elements per vector chunk (one workgroup's share), a multiple
  * of 2048 in [2048, 1<<22], for every kernel (the overflow check uses 8x it);
  * 0 restores the built-in per-kernel defaults (workgroup size x 8: 2048 for the
- * mixed kernels, 8192 for the pure-bf16 family, 16384 for the check).  Affects
+ * update kernels, 16384 for the check).  Affects
  * plans built after the call.  Returns the value now in force (0 = defaults),
  * or -1 if rejected. */
 int64_t adamw_set_chunk_elems(int64_t elems);

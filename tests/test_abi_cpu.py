@@ -110,7 +110,7 @@ def test_valid_call_reaches_hip():
 # ---------------------------------------------------------------------------
 
 # workgroup size x 8 of each kernel family
-DEFAULT_CHUNK = {A.MIXED: 2048, A.MIXED_SPLIT: 2048, A.PURE_KAHAN: 8192}
+DEFAULT_CHUNK = {A.MIXED: 2048, A.MIXED_SPLIT: 2048, A.PURE_KAHAN: 2048}
 
 
 def check_plan(rows, numels, b, e, ptrs, esz, chunk_elems):
@@ -204,7 +204,7 @@ def test_chunk_size_knob():
     rows = A.adamw_plan_inspect(A.MIXED, A.BF16, tl)
     assert max(r[2] for r in rows) == 2048
     rows = A.adamw_plan_inspect(A.PURE_KAHAN, A.BF16, _tl(numels, esz=(2, 2, 2, 2, 2)))
-    assert max(r[2] for r in rows) == 8192
+    assert max(r[2] for r in rows) == 2048
 
 
 C_PROGRAM = r"""
