@@ -471,6 +471,45 @@ def test_dynamic_loss_scale_sequence(scale0, interval):
     free()
 
 
+@pytest.mark.parametrize("mode", ["mixed", "kahan", "split"])
+@pytest.mark.parametrize("rank", [0, 1, 2, 3])
+@pytest.mark.parametrize("flat_param", [False, True], ids=["param-per-tensor", "param-flat"])
+def test_zero_layout_flat_grad_blocked_state(mode, rank, flat_param):
+    """A ZeRO rank's layout: the reduce-scattered gradient as one flat shard
+    buffer, exp_avg / exp_avg_sq / aux in the blocked layout of the shard, params
+    per tensor (or, as after an all-gather into a flat buffer, flat too); 3 steps
+    of rank r's quarter of the list against the oracle."""
+    from gpu_util import build_blocked, compare_streams, unpack_blocked
+    numels = [30592 * 8, 768, 2048 * 3, 8, 4099, 3 * 768, 40000, 1]
+    total = sum(numels)
+    b, e = rank * total // 4, (rank + 1) * total // 4
+    case = Case(mode, numels, seed=2600 + rank, align_elems=1, random_moments=True)
+    blocked = build_blocked(case, b, e)
+    g_flat = case.arena.bufs["g"][b:e].clone()
+    p_flat = case.arena.bufs["p"][b:e].clone()
+    p_stream = [p_flat] if flat_param else [case.arena.view("p", i) for i in range(len(numels))]
+    mask = A.BLOCKED_STATE | 0b10 | (0b1 if flat_param else 0)
+    tl = A.TensorList(numels, [p_stream, [g_flat], [blocked], None, None], b, e, flat_mask=mask)
+    hg, ho = hp_pair()
+    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
+    for s in range(3):
+        if s:
+            case.refill_grads(s)
+            g_flat.copy_(case.arena.bufs["g"][b:e])
+        A.adamw_multi_tensor_step(code, A.BF16, tl, hg, case.d_step)
+        case.oracle_step(ho, shard=(b, e))
+    torch.cuda.synchronize()
+    assert int(case.d_step.item()) == case.step == 3
+    got = unpack_blocked(case, blocked, b, e)
+    got["p"] = to_np(p_flat) if flat_param else to_np(case.arena.bufs["p"])[b:e]
+    ref = {k: case.host[k][b:e] for k in case.keys}
+    print(compare_streams(f"zero-{mode}-r{rank}", mode, got, ref, [k for k in case.keys if k != "g"]))
+    if not flat_param:
+        hp_all = to_np(case.arena.bufs["p"])
+        assert np.array_equal(hp_all[:b], case.host["p"][:b]) and np.array_equal(hp_all[e:], case.host["p"][e:])
+    free()
+
+
 def test_blocked_state_fp16_amp_sequence():
     """fp16 AMP (check + step with the device-resident loss scale) with
     exp_avg / exp_avg_sq / master in the blocked layout: 8 iterations, an overflow
