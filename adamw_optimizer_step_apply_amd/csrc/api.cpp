@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <map>
 #include <memory>
@@ -92,7 +93,7 @@ struct StreamWorkspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, uintptr_t>, std::unique_ptr<StreamWorkspace>> g_ws;
-int64_t g_chunk_elems = 0;   // 0: each kernel's own default (its workgroup size x 8)
+std::atomic<int64_t> g_chunk_elems{0};   // 0: each kernel's own default (its workgroup size x 8)
 
 adamw_status get_workspace(hipStream_t stream, StreamWorkspace** out)
 {
@@ -227,7 +228,14 @@ int kernel_block(int kernel) { return kernel >= kKernelPure ? kBlockPure : kBloc
 
 int64_t chunk_elems_of(int kernel)
 {
-    return g_chunk_elems ? g_chunk_elems : chunk_elems_for_block(kernel_block(kernel));
+    const int64_t c = g_chunk_elems.load(std::memory_order_relaxed);
+    return c ? c : chunk_elems_for_block(kernel_block(kernel));
+}
+
+int64_t check_chunk_elems()
+{
+    const int64_t c = g_chunk_elems.load(std::memory_order_relaxed);
+    return c ? c * kCheckChunkMult : kCheckChunkElems;
 }
 
 StepKind kind_of_mode(adamw_mode mode, adamw_dtype p_dtype)
@@ -382,7 +390,7 @@ adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* gr
     if (st != ADAMW_OK) return fail(st, err);
     if (!d_found_inf || (uintptr_t)d_found_inf % 4) return fail(ADAMW_E_INVALID, "d_found_inf is null or misaligned");
     if ((st = basic_list_check(grads)) != ADAMW_OK) return st;
-    const int64_t chunk_elems = g_chunk_elems ? g_chunk_elems * kCheckChunkMult : kCheckChunkElems;
+    const int64_t chunk_elems = check_chunk_elems();
     int esz[kStreams];
     mode_esizes(ADAMW_MIXED, g_dtype, true, esz);
     st = build_plan(esz, grads, chunk_elems, nullptr, err);
@@ -424,7 +432,7 @@ int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_ten
     adamw_status st = check_mode(mode, p_dtype, for_check != 0, err);
     int esz[kStreams];
     mode_esizes(mode, p_dtype, for_check != 0, esz);
-    const int64_t chunk = for_check ? (g_chunk_elems ? g_chunk_elems * kCheckChunkMult : kCheckChunkElems)
+    const int64_t chunk = for_check ? check_chunk_elems()
                                     : chunk_elems_of(st == ADAMW_OK ? kind_of_mode(mode, p_dtype).kernel : 0);
     if (st == ADAMW_OK) st = build_plan(esz, list, chunk, &plan, err);
     if (st != ADAMW_OK) {
@@ -449,8 +457,7 @@ int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_ten
 int64_t adamw_set_chunk_elems(int64_t elems)
 {
     if (elems != 0 && (elems < 2048 || elems > (INT64_C(1) << 22) || elems % 2048)) return -1;
-    std::lock_guard<std::mutex> lk(g_mu);
-    g_chunk_elems = elems;
+    g_chunk_elems.store(elems, std::memory_order_relaxed);
     return elems;
 }
 

@@ -535,12 +535,19 @@ def main():
 
 
 def _kernel_sha():
+    """Hash of the code that decides a launch's HBM traffic (kernels, planner,
+    layout constants), comments and blank lines left out, so that a recorded
+    counter summary stays valid across edits of the documentation alone."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("adamw_optimizer_step_apply_amd/csrc/kernels.hip", "adamw_optimizer_step_apply_amd/csrc/plan.cpp",
               "adamw_optimizer_step_apply_amd/csrc/layout.hpp", "include/adamw.h"):
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update("\n".join(ln.rstrip() for ln in src.splitlines() if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 

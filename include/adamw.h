@@ -265,7 +265,8 @@ adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* gr
 const char* adamw_last_error(void);
 
 /* Frees every workspace the library holds (all devices and streams).  The
- * caller must make sure no enqueued step is still running. */
+ * caller must make sure no enqueued step is still running and that no other
+ * thread is inside a library call. */
 void adamw_release_workspace(void);
 
 /* ADAMW_ABI_VERSION of the built library. */
