@@ -34,6 +34,7 @@ MIXED, PURE_KAHAN, MIXED_SPLIT = 0, 1, 2
 STREAM_PARAM, STREAM_GRAD, STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_AUX = range(5)
 BLOCKED_STATE = 1 << 8        # flat_mask bit: exp_avg / exp_avg_sq / aux in one blocked buffer
 STATE_BLOCK = 8192            # elements per block of that buffer
+FLAT_PAD8 = 1 << 9            # flat_mask bit: every tensor starts at a multiple of 8 in the flat index
 NUM_STREAMS = 5
 _STATUS = {0: "ADAMW_OK", 1: "ADAMW_E_INVALID", 2: "ADAMW_E_UNSUPPORTED", 3: "ADAMW_E_NOMEM", 4: "ADAMW_E_HIP"}
 

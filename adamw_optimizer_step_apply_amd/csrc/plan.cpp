@@ -87,7 +87,12 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
     const int64_t nt = list->n_tensors;
     if (nt < 0) { err = "n_tensors < 0"; return ADAMW_E_INVALID; }
     if (nt > 0 && !list->numel) { err = "numel array is null"; return ADAMW_E_INVALID; }
-    if (list->flat_mask & ~(0x1fu | ADAMW_BLOCKED_STATE)) { err = "flat_mask has unknown bits"; return ADAMW_E_INVALID; }
+    if (list->flat_mask & ~(0x1fu | ADAMW_BLOCKED_STATE | ADAMW_FLAT_PAD8)) {
+        err = "flat_mask has unknown bits";
+        return ADAMW_E_INVALID;
+    }
+    // the padded flat index: every tensor starts at a multiple of 8
+    const int64_t flat_align = (list->flat_mask & ADAMW_FLAT_PAD8) ? 8 : 1;
     // the blocked layout concerns the state streams only: a plan that reads
     // none of them (the overflow check) ignores it
     const bool blocked = (list->flat_mask & ADAMW_BLOCKED_STATE) != 0 &&
@@ -102,7 +107,7 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
             return ADAMW_E_INVALID;
         }
         if (n > (INT64_C(1) << 56) || total > (INT64_C(1) << 56)) { err = "list too large"; return ADAMW_E_INVALID; }
-        total += n;
+        total += (n + flat_align - 1) / flat_align * flat_align;
     }
     const int64_t b = list->shard_begin;
     const int64_t e = list->shard_end < 0 ? total : list->shard_end;
@@ -217,7 +222,7 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
                 push_chunks(out, seg, head + body, cnt - head - body, kElemChunkElems, false);
             }
         }
-        base += n;
+        base += (n + flat_align - 1) / flat_align * flat_align;
     }
     if (out.chunks.size() > (size_t)INT32_MAX) { err = "too many chunks for one launch"; return ADAMW_E_INVALID; }
     out.total = e - b;

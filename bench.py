@@ -147,16 +147,14 @@ def write_traffic(wl_name, modes, fetch_csv, write_csv, cal_fetch_csv, cal_write
 
 
 def default_modes(args):
-    """The modes one bench step runs: both modes of the OPT-1.3B list with their
-    state in the blocked layout, or the fp16-AMP step on an fp16 workload."""
+    """The modes one bench step runs: both modes of the OPT-1.3B list, or the
+    fp16-AMP step on an fp16 workload, with their state in the blocked layout."""
     import workloads
     if args.modes:
         return args.modes
-    # The ragged fp16 list keeps per-tensor state: its lengths are arbitrary, so
-    # most tensors start at flat positions that are not multiples of 8, where a
-    # blocked state's addresses never share 16-byte alignment with the tensor's
-    # own param and grad buffers and the planner falls back to element chunks.
-    return "f16amp" if workloads.get(args.workload).p_dtype == "f16" else "mixed-blocked,kahan-blocked"
+    # Blocked state in the padded flat index (every tensor at a multiple of 8),
+    # so that the ragged fp16 list's arbitrary lengths keep the vector path.
+    return "f16amp-blocked" if workloads.get(args.workload).p_dtype == "f16" else "mixed-blocked,kahan-blocked"
 
 
 def _time_launches(fn, reps, stream):
@@ -227,7 +225,8 @@ def probes(n, stream):
 def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
     """Per-tensor buffers for every stream; a "-blocked" mode instead keeps
     exp_avg / exp_avg_sq / aux in one blocked flat buffer of the whole list
-    (the optimizer-owned layout; param and grad stay per tensor)."""
+    (the optimizer-owned layout; param and grad stay per tensor), indexed by
+    the padded flat index (every tensor at a multiple of 8 elements)."""
     import torch
 
     import workloads
@@ -239,15 +238,19 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
     if base != mode:
         import adamw_optimizer_step_apply_amd as A
         B = A.STATE_BLOCK
-        n = sum(numels)
+        n = sum(-(-m // 8) * 8 for m in numels)     # padded flat index
         nb = -(-n // B)
         cols = []
         for k in keys[2:]:
             src = arena.bufs[k]
-            flat = torch.cat([arena.view(k, i) for i in range(len(numels))])
-            flat = torch.cat([flat, torch.zeros(nb * B - n, dtype=src.dtype, device=device)])
-            cols.append(flat.view(nb, B).view(torch.uint8))
-            del arena.bufs[k]
+            parts = []
+            for i, m in enumerate(numels):
+                parts.append(arena.view(k, i))
+                if m % 8:
+                    parts.append(torch.zeros(8 - m % 8, dtype=src.dtype, device=device))
+            parts.append(torch.zeros(nb * B - n, dtype=src.dtype, device=device))
+            cols.append(torch.cat(parts).view(nb, B).view(torch.uint8))
+            del arena.bufs[k], parts
         arena.bufs["blocked"] = torch.cat(cols, dim=1).contiguous()
         del cols
         streams = streams[:2] + [[arena.bufs["blocked"]], None, None]
@@ -397,7 +400,7 @@ def main():
                                              loss_scale=wl.loss_scale)
         else:
             arena, streams = make_mode_state(mode, numels, dev, seed=100 + i)
-        flags = A.BLOCKED_STATE if mode.endswith("-blocked") else 0
+        flags = (A.BLOCKED_STATE | A.FLAT_PAD8) if mode.endswith("-blocked") else 0
         state[mode] = (arena, A.TensorList(numels, streams, 0, -1, flags), torch.zeros(1, dtype=torch.int32, device=dev))
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     hp = A.HParams()

@@ -141,7 +141,7 @@ typedef struct {
  *                         elements holding this rank's share, element 0 being
  *                         flat position shard_begin (e.g. a reduce-scattered
  *                         gradient shard, or ZeRO-sharded master/m/v).
- *   flat_mask & ADAMW_BLOCKED_STATE: see above.
+ *   flat_mask & ADAMW_BLOCKED_STATE, flat_mask & ADAMW_FLAT_PAD8: see below.
  * numel is a host array of n_tensors element counts (each >= 0). */
 /* flat_mask bit: the blocked state layout.  exp_avg, exp_avg_sq and aux share
  * ONE flat buffer of the shard, ptr[2][0] (16-byte aligned; ptr[3], ptr[4] and
@@ -165,6 +165,16 @@ typedef struct {
  * are multiples of 8. */
 #define ADAMW_BLOCKED_STATE (1u << 8)
 #define ADAMW_STATE_BLOCK 8192
+/* flat_mask bit: the padded flat index.  The list's flat concatenation places
+ * every tensor at a multiple of 8 elements: tensor i starts at the sum over
+ * j < i of numel[j] rounded up to a multiple of 8, and the gaps hold no
+ * element (nothing reads or writes them).  shard_begin and shard_end, flat
+ * shard buffers and the blocked state are all indexed in this padded space,
+ * as in ZeRO implementations that pad each tensor inside their flat buffers;
+ * shard_end may reach the padded total.  With per-tensor buffers that start
+ * 16-byte aligned and a shard_begin that is a multiple of 8, every tensor of
+ * any length keeps the 16-byte vector path in every layout. */
+#define ADAMW_FLAT_PAD8 (1u << 9)
 
 typedef struct {
     int64_t n_tensors;

@@ -286,13 +286,21 @@ KAHAN = "kahan"
 SPLIT = "split"
 
 
-def shard_pieces(numels, shard_begin: int = 0, shard_end: int | None = None):
+def _place(n: int, flat_align: int) -> int:
+    """Room a tensor of n elements takes in the flat concatenation."""
+    return -(-n // flat_align) * flat_align
+
+
+def shard_pieces(numels, shard_begin: int = 0, shard_end: int | None = None, flat_align: int = 1):
     """Intersect the list's flat concatenation with ``[shard_begin, shard_end)``.
 
-    Yields ``(tensor_index, lo, hi, flat_lo)``: elements ``lo..hi`` of that
-    tensor, which sit at flat position ``flat_lo`` of the concatenation.
+    The concatenation places the tensors in list order, each starting at a
+    multiple of ``flat_align`` elements (1: back to back; 8: the padded flat
+    index, whose gaps hold no element).  Yields ``(tensor_index, lo, hi,
+    flat_lo)``: elements ``lo..hi`` of that tensor, which sit at flat position
+    ``flat_lo`` of the concatenation.
     """
-    total = int(sum(int(n) for n in numels))
+    total = int(sum(_place(int(n), flat_align) for n in numels))
     if shard_end is None or shard_end < 0:
         shard_end = total
     base = 0
@@ -302,11 +310,11 @@ def shard_pieces(numels, shard_begin: int = 0, shard_end: int | None = None):
         hi = min(shard_end, base + n)
         if lo < hi:
             yield i, lo - base, hi - base, lo
-        base += n
+        base += _place(n, flat_align)
 
 
 def step_list(mode: str, tensors: list, hp: HParams, step: int, *, p_is_f16=False,
-              check_overflow=False, shard_begin=0, shard_end=None, lib=None) -> int:
+              check_overflow=False, shard_begin=0, shard_end=None, flat_align=1, lib=None) -> int:
     """Take one AdamW step over a tensor list; return the new step counter.
 
     ``tensors`` is a list of dicts of flat numpy arrays: mixed mode uses keys
@@ -314,14 +322,15 @@ def step_list(mode: str, tensors: list, hp: HParams, step: int, *, p_is_f16=Fals
     a "pure..." mode ``p, g, m, v`` (m, v float32 or uint16) and ``c`` when compensated.  With
     ``check_overflow`` the step is skipped (nothing written, counter kept) when
     any gradient of the whole list is inf/NaN.  Only elements inside
-    ``[shard_begin, shard_end)`` of the flat concatenation are updated.
+    ``[shard_begin, shard_end)`` of the flat concatenation (tensors placed at
+    multiples of ``flat_align``, see shard_pieces) are updated.
     """
     lib = lib or load()
     if check_overflow and any(any_nonfinite(tt["g"], p_is_f16, lib) for tt in tensors):
         return step
     t = step + 1
     numels = [tt["g"].size for tt in tensors]
-    for i, lo, hi, _ in shard_pieces(numels, shard_begin, shard_end):
+    for i, lo, hi, _ in shard_pieces(numels, shard_begin, shard_end, flat_align):
         tt = tensors[i]
         if mode == MIXED:
             sl = {k: np.ascontiguousarray(tt[k][lo:hi]) for k in ("p", "g", "master", "m", "v")}
@@ -374,7 +383,7 @@ class LossScale:
 
 
 def amp_step_list(mode: str, tensors: list, hp: HParams, step: int, ls: LossScale, *, p_is_f16=True,
-                  shard_begin=0, shard_end=None, lib=None) -> int:
+                  shard_begin=0, shard_end=None, flat_align=1, lib=None) -> int:
     """fp16-AMP step with a dynamic loss scale: the overflow test over every
     gradient of the list, the step (unless skipped) with the gradient multiplier
     1/scale, then the scale update from the test's outcome.  Returns the new
@@ -383,7 +392,8 @@ def amp_step_list(mode: str, tensors: list, hp: HParams, step: int, ls: LossScal
     found = any(any_nonfinite(tt["g"], p_is_f16, lib) for tt in tensors)
     hps = HParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, ls.inv(lib))
     new_step = step if found else step_list(mode, tensors, hps, step, p_is_f16=p_is_f16,
-                                            shard_begin=shard_begin, shard_end=shard_end, lib=lib)
+                                            shard_begin=shard_begin, shard_end=shard_end,
+                                            flat_align=flat_align, lib=lib)
     ls.update(found, lib)
     return new_step
 

@@ -153,10 +153,10 @@ class Case:
         else:
             A.adamw_multi_tensor_step(MODE[self.mode], DT[self.p_dtype], tl, hp, self.d_step, found_inf)
 
-    def oracle_step(self, hp: oracle.HParams, shard=(0, -1), check_overflow=False):
+    def oracle_step(self, hp: oracle.HParams, shard=(0, -1), check_overflow=False, flat_align=1):
         self.step = oracle.step_list(self.mode, self.oracle_tensors(), hp, self.step,
                                      p_is_f16=self.p_dtype == "f16", check_overflow=check_overflow,
-                                     shard_begin=shard[0], shard_end=shard[1])
+                                     shard_begin=shard[0], shard_end=shard[1], flat_align=flat_align)
 
     def compare_all(self, label=""):
         torch.cuda.synchronize()
@@ -293,6 +293,47 @@ def build_blocked(case, b, e) -> torch.Tensor:
         pad = torch.zeros(nb * B - L, dtype=x.dtype, device=x.device)
         cols.append(torch.cat([x, pad]).view(nb, B).view(torch.uint8))
     return torch.cat(cols, dim=1).contiguous()
+
+
+def padded_starts(numels) -> np.ndarray:
+    """Each tensor's start in the padded flat index (multiples of 8), plus the total."""
+    return np.concatenate([[0], np.cumsum([-(-int(n) // 8) * 8 for n in numels])]).astype(np.int64)
+
+
+def build_blocked_padded(arena, keys, numels) -> torch.Tensor:
+    """The blocked state buffer of a whole list in the padded flat index, from
+    the per-tensor state views of an arena (any alignment)."""
+    B = A.STATE_BLOCK
+    total = int(padded_starts(numels)[-1])
+    nb = -(-total // B)
+    cols = []
+    for k in keys:
+        dt = arena.bufs[k].dtype
+        parts = []
+        for i, n in enumerate(numels):
+            parts.append(arena.view(k, i))
+            if n % 8:
+                parts.append(torch.zeros(8 - n % 8, dtype=dt, device=arena.bufs[k].device))
+        parts.append(torch.zeros(nb * B - total, dtype=dt, device=arena.bufs[k].device))
+        cols.append(torch.cat(parts).view(nb, B).view(torch.uint8))
+        del parts
+    out = torch.cat(cols, dim=1).contiguous()
+    del cols
+    return out
+
+
+def blocked_gather(blocked: torch.Tensor, dtypes: dict, pos: torch.Tensor) -> dict:
+    """Values at flat positions `pos` (device int64) of each state stream of a
+    whole-list blocked buffer; `dtypes` maps the streams, in block order, to
+    their torch dtypes."""
+    B = A.STATE_BLOCK
+    blk, off = pos // B, pos % B
+    out, col = {}, 0
+    for k, dt in dtypes.items():
+        width = B * torch.empty(0, dtype=dt).element_size()
+        out[k] = blocked[:, col:col + width].contiguous().view(dt)[blk, off]
+        col += width
+    return out
 
 
 def unpack_blocked(case, blocked: torch.Tensor, b, e) -> dict:

@@ -281,6 +281,40 @@ def test_plan_blocked_state_never_straddles_a_block(seed):
     assert pos == e
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_plan_padded_flat_index(seed):
+    """ADAMW_FLAT_PAD8: tensors sit at multiples of 8 in the flat index.  The rows
+    cover exactly the real elements of [b, e) in that padded space (written out
+    slot by slot here); with 16-byte aligned per-tensor param/grad buffers, a
+    blocked state and a shard start that is a multiple of 8, the only element
+    rows are the last numel % 8 elements of a tensor or the shard's end."""
+    rng = np.random.default_rng(500 + seed)
+    numels = [int(x) for x in rng.choice([0, 1, 3, 7, 9, 100, 2049, 8191, 8193, 16391, 40001], size=rng.integers(1, 14))]
+    slots = []
+    for i, n in enumerate(numels):
+        slots += [(i, j) for j in range(n)]
+        slots += [None] * (-len(slots) % 8)
+    total = len(slots)
+    b = int(rng.integers(0, total // 8 + 1)) * 8 if seed % 2 == 0 else int(rng.integers(0, total + 1))
+    e = int(rng.integers(b, total + 1))
+    esz = (2, 2, 4, 4, 4)
+    ptrs = [[FAKE + s * (1 << 36) + (1 << 20) * i for i in range(len(numels))] for s in range(2)]
+    ptrs += [[FAKE + 7 * (1 << 36)], None, None]
+    tl = A.TensorList(numels, ptrs, b, e, flat_mask=A.BLOCKED_STATE | A.FLAT_PAD8)
+    rows = A.adamw_plan_inspect(A.MIXED, A.BF16, tl)
+    covered = []
+    for (t, off, n, vec, flat, seg) in rows:
+        assert slots[flat] == (t, off)
+        assert (flat - b) // A.STATE_BLOCK == (flat + n - 1 - b) // A.STATE_BLOCK
+        covered += [(t, off + j) for j in range(n)]
+        if seed % 2 == 0 and not vec:
+            assert n < 8 and (off + n == numels[t] or flat + n == e), (t, off, n, numels[t])
+    assert covered == [sl for sl in slots[b:e] if sl is not None]
+    with pytest.raises(A.AdamWError, match="shard range"):
+        A.adamw_plan_inspect(A.MIXED, A.BF16, A.TensorList(numels, ptrs, 0, total + 1,
+                                                          flat_mask=A.BLOCKED_STATE | A.FLAT_PAD8))
+
+
 def test_check_plan_ignores_blocked_bit():
     """The overflow check reads only grads: with the blocked bit its plan is the
     plan without it (no splits at state-block edges), and it needs no state buffer."""

@@ -9,7 +9,8 @@ import torch
 import adamw_optimizer_step_apply_amd as A
 import oracle
 import workloads
-from gpu_util import Case, SampledCase, free, hp_pair, same_bits, to_np
+from gpu_util import (Case, SampledCase, blocked_gather, build_blocked_padded, free, hp_pair, padded_starts,
+                      same_bits, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,7 +109,7 @@ def test_opt13b_full_size_blocked_state(mode):
     blocked = torch.cat(cols, dim=1).contiguous()
     del cols
     streams = [[case.arena.view(k, i) for i in range(len(wl.numels))] for k in case.keys[:2]]
-    tl = A.TensorList(wl.numels, streams + [[blocked], None, None], 0, -1, A.BLOCKED_STATE)
+    tl = A.TensorList(wl.numels, streams + [[blocked], None, None], 0, -1, A.BLOCKED_STATE | A.FLAT_PAD8)
     hg, ho = hp_pair()
     code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
     for s in range(3):
@@ -180,4 +181,44 @@ def test_ragged_10k_fp16_overflow_skip():
             del before
     _print(case.compare_all("ragged10k"))
     del case, tl
+    free()
+
+
+def test_ragged_10k_fp16_blocked_padded_state():
+    """The 10,000-tensor fp16 list in the launch configuration bench.py times for
+    it: exp_avg / exp_avg_sq / master in the blocked layout of the padded flat
+    index (every tensor at a multiple of 8), params and grads per tensor.  Check
+    + step for 3 steps, an overflow planted in the second (skipped: nothing
+    written, counter kept); sampled elements against the oracle."""
+    wl = workloads.get("ragged_10k")
+    scale = wl.loss_scale
+    case = SampledCase("mixed", wl.numels, seed=5101, p_dtype="f16", loss_scale=scale, n_random=1 << 21)
+    state = case.keys[2:]
+    blocked = build_blocked_padded(case.arena, state, wl.numels)
+    streams = [[case.arena.view(k, i) for i in range(len(wl.numels))] for k in case.keys[:2]]
+    tl = A.TensorList(wl.numels, streams + [[blocked], None, None], 0, -1, A.BLOCKED_STATE | A.FLAT_PAD8)
+    hg, ho = hp_pair(inv_scale=1.0 / scale)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    starts = np.concatenate([[0], np.cumsum(wl.numels)]).astype(np.int64)
+    tens = np.searchsorted(starts, case.flat, side="right") - 1
+    pos = torch.from_numpy(padded_starts(wl.numels)[tens] + (case.flat - starts[tens])).to("cuda")
+    t_inj = int(np.argmax(wl.numels))
+    for s in range(3):
+        if s:
+            case.refill_grads(s)
+        if s == 1:
+            case.arena.view("g", t_inj)[12345] = float("inf")
+        A.adamw_check_finite(A.F16, tl, flag)
+        A.adamw_multi_tensor_step(A.MIXED, A.F16, tl, hg, case.d_step, flag)
+        case.oracle_step(ho, skip=(s == 1))
+        torch.cuda.synchronize()
+        assert int(flag.item()) == int(s == 1), s
+    assert case.step == 2
+    got = blocked_gather(blocked, {k: case.arena.bufs[k].dtype for k in state}, pos)
+    for k in state:
+        # the per-tensor arena copy of this stream was not stepped: put the blocked
+        # values of the sampled elements there so the usual comparison reads them
+        case.arena.bufs[k][case.idx] = got[k]
+    _print(case.compare_all("ragged10k-blocked"))
+    del case, tl, blocked, got
     free()

@@ -520,6 +520,27 @@ def test_shard_pieces_brute_force():
         assert got == [(owner[f], local[f]) for f in range(b, e)]
 
 
+def test_shard_pieces_padded_flat_index_brute_force():
+    """The padded flat index: each tensor's elements followed by empty slots up
+    to the next multiple of 8, written out one slot at a time."""
+    rng = np.random.default_rng(16)
+    for _ in range(300):
+        numels = list(rng.integers(0, 20, size=rng.integers(1, 8)))
+        slots = []                      # (tensor, element) or None for a gap
+        for i, n in enumerate(numels):
+            slots += [(i, j) for j in range(n)]
+            while len(slots) % 8:
+                slots.append(None)
+        total = len(slots)
+        b = int(rng.integers(0, total + 1))
+        e = int(rng.integers(b, total + 1))
+        got = []
+        for i, lo, hi, flo in oracle.shard_pieces(numels, b, e, flat_align=8):
+            assert slots[flo] == (i, lo)
+            got += [(i, j) for j in range(lo, hi)]
+        assert got == [sl for sl in slots[b:e] if sl is not None]
+
+
 def test_shard_union_equals_full_step(olib):
     """The single-GPU form of the pages' ZeRO on/off comparison (same losses in
     the A40/A100 tables): four rank shards stepped one after another equal one
