@@ -231,11 +231,15 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
 
     import workloads
     base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
-    arena = workloads.make_state(base, numels, device, seed, align_elems=128, p_dtype=p_dtype,
+    blocked = base != mode
+    # blocked: tensors at multiples of 8 in every arena, so that a state arena
+    # is already the padded flat concatenation (the same offsets as 128 when all
+    # lengths are multiples of 128, as in the OPT and BERT lists)
+    arena = workloads.make_state(base, numels, device, seed, align_elems=8 if blocked else 128, p_dtype=p_dtype,
                                  loss_scale=loss_scale)
     keys = workloads.streams_of(base)
     streams = [[arena.view(k, i) for i in range(len(numels))] for k in keys]
-    if base != mode:
+    if blocked:
         import adamw_optimizer_step_apply_amd as A
         B = A.STATE_BLOCK
         n = sum(-(-m // 8) * 8 for m in numels)     # padded flat index
@@ -243,14 +247,9 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
         cols = []
         for k in keys[2:]:
             src = arena.bufs[k]
-            parts = []
-            for i, m in enumerate(numels):
-                parts.append(arena.view(k, i))
-                if m % 8:
-                    parts.append(torch.zeros(8 - m % 8, dtype=src.dtype, device=device))
-            parts.append(torch.zeros(nb * B - n, dtype=src.dtype, device=device))
-            cols.append(torch.cat(parts).view(nb, B).view(torch.uint8))
-            del arena.bufs[k], parts
+            flat = torch.cat([src, torch.zeros(nb * B - src.numel(), dtype=src.dtype, device=device)])
+            cols.append(flat.view(nb, B).view(torch.uint8))
+            del arena.bufs[k], src, flat
         arena.bufs["blocked"] = torch.cat(cols, dim=1).contiguous()
         del cols
         streams = streams[:2] + [[arena.bufs["blocked"]], None, None]

@@ -205,11 +205,11 @@ class SampledCase:
     ZeRO shard [b, e): samples outside it must come back unchanged."""
 
     def __init__(self, mode, numels, seed, *, p_dtype="bf16", loss_scale=1.0, n_random=1 << 21,
-                 shard=(0, -1), device="cuda"):
+                 shard=(0, -1), align_elems=128, device="cuda"):
         self.mode, self.p_dtype, self.seed, self.loss_scale = mode, p_dtype, seed, loss_scale
         self.numels = [int(n) for n in numels]
-        self.arena = workloads.make_state(mode, self.numels, device, seed, p_dtype=p_dtype, align_elems=128,
-                                          loss_scale=loss_scale)
+        self.arena = workloads.make_state(mode, self.numels, device, seed, p_dtype=p_dtype,
+                                          align_elems=align_elems, loss_scale=loss_scale)
         self.keys = workloads.streams_of(mode)
         total = sum(self.numels)
         b, e = shard[0], (total if shard[1] < 0 else shard[1])
@@ -302,21 +302,18 @@ def padded_starts(numels) -> np.ndarray:
 
 def build_blocked_padded(arena, keys, numels) -> torch.Tensor:
     """The blocked state buffer of a whole list in the padded flat index, from
-    the per-tensor state views of an arena (any alignment)."""
+    an arena whose tensors already sit at their padded positions (aligned to 8
+    elements, or to any multiple of 8 when every length is one)."""
     B = A.STATE_BLOCK
-    total = int(padded_starts(numels)[-1])
-    nb = -(-total // B)
+    starts = padded_starts(numels)
+    assert list(arena.offsets) == [int(x) for x in starts[:-1]], "arena is not in the padded flat index"
+    nb = -(-int(starts[-1]) // B)
     cols = []
     for k in keys:
-        dt = arena.bufs[k].dtype
-        parts = []
-        for i, n in enumerate(numels):
-            parts.append(arena.view(k, i))
-            if n % 8:
-                parts.append(torch.zeros(8 - n % 8, dtype=dt, device=arena.bufs[k].device))
-        parts.append(torch.zeros(nb * B - total, dtype=dt, device=arena.bufs[k].device))
-        cols.append(torch.cat(parts).view(nb, B).view(torch.uint8))
-        del parts
+        src = arena.bufs[k]
+        flat = torch.cat([src, torch.zeros(nb * B - src.numel(), dtype=src.dtype, device=src.device)])
+        cols.append(flat.view(nb, B).view(torch.uint8))
+        del flat
     out = torch.cat(cols, dim=1).contiguous()
     del cols
     return out

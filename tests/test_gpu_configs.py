@@ -97,17 +97,8 @@ def test_opt13b_full_size_blocked_state(mode):
     read back out of their blocks and compared with the oracle."""
     wl = workloads.get("opt_1_3b")
     case = SampledCase(mode, wl.numels, seed={"mixed": 4101, "kahan": 4102, "split": 4103}[mode])
-    B, n = A.STATE_BLOCK, sum(wl.numels)
-    nb = -(-n // B)
     state = case.keys[2:]
-    cols = []
-    for k in state:
-        flat = torch.cat([case.arena.view(k, i) for i in range(len(wl.numels))])
-        flat = torch.cat([flat, torch.zeros(nb * B - n, dtype=flat.dtype, device=flat.device)])
-        cols.append(flat.view(nb, B).view(torch.uint8))
-        del flat
-    blocked = torch.cat(cols, dim=1).contiguous()
-    del cols
+    blocked = build_blocked_padded(case.arena, state, wl.numels)
     streams = [[case.arena.view(k, i) for i in range(len(wl.numels))] for k in case.keys[:2]]
     tl = A.TensorList(wl.numels, streams + [[blocked], None, None], 0, -1, A.BLOCKED_STATE | A.FLAT_PAD8)
     hg, ho = hp_pair()
@@ -118,18 +109,13 @@ def test_opt13b_full_size_blocked_state(mode):
         A.adamw_multi_tensor_step(code, A.BF16, tl, hg, case.d_step)
         case.oracle_step(ho)
     torch.cuda.synchronize()
-    flat_idx = torch.from_numpy(case.flat).to(blocked.device)
-    blk, off = flat_idx // B, flat_idx % B
-    col = 0
+    # every OPT-1.3B length is a multiple of 8: the padded flat index is the plain one
+    got = blocked_gather(blocked, {k: case.arena.bufs[k].dtype for k in state},
+                         torch.from_numpy(case.flat).to(blocked.device))
     for k in state:
-        dt = case.arena.bufs[k].dtype
-        width = B * torch.empty(0, dtype=dt).element_size()
-        view = blocked[:, col:col + width].contiguous().view(dt)
         # the per-tensor arena copy of this stream was not stepped: put the blocked
         # values of the sampled elements there so the usual comparison reads them
-        case.arena.bufs[k][case.idx] = view[blk, off]
-        col += width
-        del view
+        case.arena.bufs[k][case.idx] = got[k]
     _print(case.compare_all(f"opt13b-{mode}-blocked"))
     del case, tl, blocked
     free()
@@ -192,7 +178,8 @@ def test_ragged_10k_fp16_blocked_padded_state():
     written, counter kept); sampled elements against the oracle."""
     wl = workloads.get("ragged_10k")
     scale = wl.loss_scale
-    case = SampledCase("mixed", wl.numels, seed=5101, p_dtype="f16", loss_scale=scale, n_random=1 << 21)
+    case = SampledCase("mixed", wl.numels, seed=5101, p_dtype="f16", loss_scale=scale, n_random=1 << 21,
+                       align_elems=8)
     state = case.keys[2:]
     blocked = build_blocked_padded(case.arena, state, wl.numels)
     streams = [[case.arena.view(k, i) for i in range(len(wl.numels))] for k in case.keys[:2]]
