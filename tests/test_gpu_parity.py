@@ -407,6 +407,45 @@ def test_plan_cache_eviction_cycle():
     free()
 
 
+@pytest.mark.parametrize("mode", ["mixed", "kahan", "split", "pure-f32-bf16-k"])
+def test_chunk_size_does_not_change_results(mode):
+    """The same step at every legal kind of chunk size (the smallest, a middle
+    one, one larger than most tensors, the largest) gives the default's bytes:
+    the chunking decides only which workgroup does an element."""
+    numels = [70001, 9, 4099, 2048, 300000, 17]
+    ref = Case(mode, numels, seed=2700, align_elems=3, random_moments=True)
+    hg, _ = hp_pair()
+    ref.gpu_step(hg)
+    try:
+        for chunk in (2048, 6144, 262144, 1 << 22):
+            c = Case(mode, numels, seed=2700, align_elems=3, random_moments=True)
+            assert A.adamw_set_chunk_elems(chunk) == chunk
+            c.gpu_step(hg)
+            torch.cuda.synchronize()
+            for k in c.keys:
+                assert same_bits(c.arena.bufs[k], ref.arena.bufs[k]), (chunk, k)
+            del c
+    finally:
+        A.adamw_set_chunk_elems(0)
+    free()
+
+
+def test_release_workspace_then_continue():
+    """adamw_release_workspace between steps (after a synchronisation): the next
+    call rebuilds its workspace and plan, and the run continues exactly."""
+    case = Case("mixed", [5000, 70000, 13], seed=2800, random_moments=True)
+    hg, ho = hp_pair()
+    for s in range(4):
+        if s:
+            case.refill_grads(s)
+        case.gpu_step(hg)
+        case.oracle_step(ho)
+        torch.cuda.synchronize()
+        A.adamw_release_workspace()
+    case.compare_all("release")
+    free()
+
+
 def test_split_master_tracks_mixed_master():
     """The split kernel on (p, r) and the mixed kernel on the fp32 master they
     encode stay bit-identical in the master and the moments over 10 steps; the
