@@ -86,6 +86,7 @@ struct PlanSlot {
 constexpr size_t kPlansPerStream = 8;
 
 struct StreamWorkspace {
+    int device = 0;                     // the stream's device: the workspace lives there
     LaunchScalars* scalars = nullptr;   // device, kScalarsBytes
     std::vector<std::unique_ptr<PlanSlot>> plans;
     std::mutex mu;                      // one call at a time per stream
@@ -95,17 +96,42 @@ std::mutex g_mu;
 std::map<std::pair<int, uintptr_t>, std::unique_ptr<StreamWorkspace>> g_ws;
 std::atomic<int64_t> g_chunk_elems{0};   // 0: each kernel's own default (its workgroup size x 8)
 
+// The workspace of a stream, on the stream's own device (the null stream
+// belongs to the calling thread's current device).
 adamw_status get_workspace(hipStream_t stream, StreamWorkspace** out)
 {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(stream ? "hipStreamGetDevice" : "hipGetDevice", e);
     std::lock_guard<std::mutex> lk(g_mu);
     auto& ws = g_ws[{dev, (uintptr_t)stream}];
-    if (!ws) ws.reset(new StreamWorkspace());
+    if (!ws) {
+        ws.reset(new StreamWorkspace());
+        ws->device = dev;
+    }
     *out = ws.get();
     return ADAMW_OK;
 }
+
+// Makes `dev` the current device for the lifetime of the guard (allocations
+// and launches of a call then land on its stream's device).
+class DeviceGuard {
+public:
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev_) == hipSuccess && prev_ != dev && hipSetDevice(dev) == hipSuccess) switched_ = true;
+    }
+    ~DeviceGuard()
+    {
+        if (switched_) (void)hipSetDevice(prev_);
+    }
+    DeviceGuard(const DeviceGuard&) = delete;
+    DeviceGuard& operator=(const DeviceGuard&) = delete;
+
+private:
+    int prev_ = 0;
+    bool switched_ = false;
+};
 
 // Returns (in *out) a slot of `ws` holding the device plan of (mode, dtype,
 // list, for_check): a cached one if every input matches, else the least
@@ -268,6 +294,7 @@ adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const 
     StreamWorkspace* ws = nullptr;
     if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
     std::lock_guard<std::mutex> lk(ws->mu);
+    DeviceGuard dg(ws->device);
     hipError_t e;
     if (!ws->scalars) {
         e = hipMalloc(reinterpret_cast<void**>(&ws->scalars), kScalarsBytes);
@@ -399,6 +426,7 @@ adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* gr
     StreamWorkspace* ws = nullptr;
     if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
     std::lock_guard<std::mutex> lk(ws->mu);
+    DeviceGuard dg(ws->device);
     PlanSlot* plan = nullptr;
     if ((st = ensure_plan(*ws, -1, esz, grads, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
     hipError_t e = launch_check(g_dtype, plan->segs(), plan->chunks(), plan->n_chunks, d_found_inf, stream);

@@ -64,10 +64,12 @@
  *
  * Ownership and execution.  The caller owns every tensor, d_step, d_found_inf
  * and the stream; the library never frees or reallocates them.  All work is
- * enqueued on hip_stream (a hipStream_t; NULL = the null stream) and the call
- * returns without synchronising.  The library owns only a small device
- * workspace per (device, stream) holding the launch scalars and the chunk
- * table, grown on demand and kept until adamw_release_workspace().  The host
+ * enqueued on hip_stream (a hipStream_t; NULL = the null stream of the calling
+ * thread's current device) and the call returns without synchronising.  Every
+ * buffer must live on the stream's device.  The library owns only a small
+ * device workspace per (device, stream), on the stream's device, holding the
+ * launch scalars and the chunk table, grown on demand and kept until
+ * adamw_release_workspace().  The host
  * arrays inside adamw_tensor_list are read during the call only.
  *
  * Errors.  Arguments are validated before anything is enqueued; on an error
