@@ -86,15 +86,21 @@ def compare(name: str, got: np.ndarray, ref: np.ndarray, is_f32: bool, p_is_f16:
     diff_bits = int(np.count_nonzero(gb[ok] != rb[ok]))
     stats = {"stream": name, "n": int(got.size), "bit_mismatches": diff_bits}
     if is_f32:
-        g64, r64 = got[ok].astype(np.float64), ref[ok].astype(np.float64)
+        # an infinity on either side must be the same infinity; the relative bar
+        # covers the pairs that are both finite
+        inf = np.isinf(got[ok]) | np.isinf(ref[ok])
+        assert np.array_equal(gb[ok][inf], rb[ok][inf]), f"{name}: infinities differ"
+        g64, r64 = got[ok][~inf].astype(np.float64), ref[ok][~inf].astype(np.float64)
         zero = r64 == 0
         assert np.all(g64[zero] == 0), f"{name}: nonzero where the oracle is 0"
         nz = ~zero
-        rel = np.abs(g64[nz] - r64[nz]) / np.abs(r64[nz]) if nz.any() else np.zeros(1)
-        rel = rel[np.isfinite(rel)] if rel.size else np.zeros(1)
+        rel = np.abs(g64[nz] - r64[nz]) / np.abs(r64[nz])
         stats["max_rel"] = float(rel.max()) if rel.size else 0.0
         assert stats["max_rel"] <= REL_TOL, f"{name}: max relative error {stats['max_rel']:.3e} > {REL_TOL}"
     else:
+        mag = (0x7C00 if p_is_f16 else 0x7F80)
+        inf = ((got[ok] & 0x7FFF) == mag) | ((ref[ok] & 0x7FFF) == mag)
+        assert np.array_equal(got[ok][inf], ref[ok][inf]), f"{name}: infinities differ"
         d = np.abs(ordered16(got[ok]) - ordered16(ref[ok]))
         stats["max_ulp"] = int(d.max()) if d.size else 0
         assert stats["max_ulp"] <= ULP_TOL, f"{name}: {stats['max_ulp']} ulp apart"
