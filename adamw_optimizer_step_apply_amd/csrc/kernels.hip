@@ -4,8 +4,9 @@
 // no reuse, so there is nothing to stage in LDS and no contraction for the
 // matrix cores.  The kernels are shaped for HBM: every lane moves whole 16-byte
 // words (8 elements of a 16-bit stream, 4 of an fp32 stream), consecutive lanes
-// touch consecutive words, and each lane keeps two packs of loads in flight
-// before it computes.  The math is fp32 in registers.
+// touch consecutive words, and each lane issues all loads of its 8-element pack
+// (one to two 16-byte words per stream) before it computes.  The math is fp32
+// in registers.
 //
 // Kernels:
 //   prologue_kernel      one lane: reads the skip flag and the step counter,
@@ -222,9 +223,10 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
 // Update kernel
 // ---------------------------------------------------------------------------
 
-// Packs each lane loads before computing (memory-level parallelism), and the
-// cache policy of the streaming accesses per mode: bit 0 = non-temporal loads,
-// bit 1 = non-temporal stores (every element is touched exactly once per step).
+// Packs each lane loads before computing (1: one pack, all a workgroup's chunk
+// in one pass; 2 was measured slower), and the cache policy of the streaming
+// accesses per mode: bit 0 = non-temporal loads, bit 1 = non-temporal stores
+// (every element is touched exactly once per step).
 #ifndef ADAMW_UNROLL
 #define ADAMW_UNROLL 1
 #endif
