@@ -4,9 +4,11 @@ planner partitions lists and shards correctly (through adamw_plan_inspect)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
+import torch
 
 import adamw_optimizer_step_apply_amd as A
 
@@ -33,6 +35,72 @@ def test_abi_version():
     src = open(HEADER).read()
     v = int(re.search(r"#define ADAMW_ABI_VERSION (\d+)", src).group(1))
     assert A.adamw_abi_version() == v
+
+
+def test_binding_constants_match_the_header():
+    """The binding restates the header's enums and layout constants: they must agree."""
+    src = open(HEADER).read()
+
+    def define(name):
+        m = re.search(rf"#define {name} \(?(\d+)u?(?: << (\d+)\))?", src)
+        return int(m.group(1)) << int(m.group(2) or 0)
+
+    assert define("ADAMW_BLOCKED_STATE") == A.BLOCKED_STATE
+    assert define("ADAMW_FLAT_PAD8") == A.FLAT_PAD8
+    assert define("ADAMW_STATE_BLOCK") == A.STATE_BLOCK
+    for name, value in (("ADAMW_OK", A.OK), ("ADAMW_E_INVALID", A.E_INVALID), ("ADAMW_E_UNSUPPORTED", A.E_UNSUPPORTED),
+                        ("ADAMW_E_NOMEM", A.E_NOMEM), ("ADAMW_E_HIP", A.E_HIP), ("ADAMW_F32", A.F32),
+                        ("ADAMW_BF16", A.BF16), ("ADAMW_F16", A.F16), ("ADAMW_MIXED", A.MIXED),
+                        ("ADAMW_PURE_KAHAN", A.PURE_KAHAN), ("ADAMW_MIXED_SPLIT", A.MIXED_SPLIT),
+                        ("ADAMW_STREAM_PARAM", A.STREAM_PARAM), ("ADAMW_STREAM_GRAD", A.STREAM_GRAD),
+                        ("ADAMW_STREAM_EXP_AVG", A.STREAM_EXP_AVG), ("ADAMW_STREAM_EXP_AVG_SQ", A.STREAM_EXP_AVG_SQ),
+                        ("ADAMW_STREAM_AUX", A.STREAM_AUX), ("ADAMW_NUM_STREAMS", A.NUM_STREAMS)):
+        assert int(re.search(rf"\b{name} = (\d+)", src).group(1)) == value, name
+
+
+LAYOUT_PROGRAM = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "adamw.h"
+#define F(T, m) printf(#T "." #m " %zu\n", offsetof(T, m))
+int main(void)
+{
+    printf("adamw_hparams %zu\n", sizeof(adamw_hparams));
+    F(adamw_hparams, lr); F(adamw_hparams, beta1); F(adamw_hparams, beta2); F(adamw_hparams, eps);
+    F(adamw_hparams, weight_decay); F(adamw_hparams, inv_loss_scale);
+    printf("adamw_pure_precision %zu\n", sizeof(adamw_pure_precision));
+    F(adamw_pure_precision, exp_avg); F(adamw_pure_precision, exp_avg_sq); F(adamw_pure_precision, kahan);
+    printf("adamw_loss_scaler %zu\n", sizeof(adamw_loss_scaler));
+    F(adamw_loss_scaler, growth_factor); F(adamw_loss_scaler, backoff_factor); F(adamw_loss_scaler, growth_interval);
+    printf("adamw_tensor_list %zu\n", sizeof(adamw_tensor_list));
+    F(adamw_tensor_list, n_tensors); F(adamw_tensor_list, numel); F(adamw_tensor_list, ptr);
+    F(adamw_tensor_list, shard_begin); F(adamw_tensor_list, shard_end); F(adamw_tensor_list, flat_mask);
+    printf("adamw_loss_scale_state %zu\n", sizeof(adamw_loss_scale_state));
+    F(adamw_loss_scale_state, scale); F(adamw_loss_scale_state, growth_tracker);
+    return 0;
+}
+"""
+
+
+def test_binding_structs_match_the_c_layout(tmp_path):
+    """Sizes and field offsets of the binding's ctypes structures equal the C
+    compiler's for the header (a mismatch would pass garbage across the ABI)."""
+    src = tmp_path / "layout.c"
+    src.write_text(LAYOUT_PROGRAM)
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    c = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                               check=True).stdout.splitlines())
+    c = {k: int(v) for k, v in c.items()}
+    for cls in (A.adamw_hparams, A.adamw_pure_precision, A.adamw_loss_scaler, A.adamw_tensor_list):
+        assert ctypes.sizeof(cls) == c[cls.__name__], cls.__name__
+        for name, _ in cls._fields_:
+            assert getattr(cls, name).offset == c[f"{cls.__name__}.{name}"], (cls.__name__, name)
+    # the device-resident loss-scale state: fp32 scale, then int32 tracker
+    assert c["adamw_loss_scale_state"] == 8 and c["adamw_loss_scale_state.scale"] == 0
+    assert c["adamw_loss_scale_state.growth_tracker"] == 4
+    st = A.loss_scale_state(1024.0, device="cpu")
+    assert st.numel() * st.element_size() == 8 and float(st[0]) == 1024.0 and int(st.view(torch.int32)[1]) == 0
 
 
 FAKE = 0x7f0000000000     # never dereferenced: validation fails before any HIP call
