@@ -93,8 +93,8 @@ def test_opt13b_full_size_10_steps(mode):
 @pytest.mark.parametrize("mode", ["mixed", "kahan", "split"])
 def test_opt13b_full_size_blocked_state(mode):
     """OPT-1.3B list with exp_avg / exp_avg_sq / aux in one blocked buffer of the
-    whole list (bench.py's "-blocked" modes), 3 steps; the sampled elements are
-    read back out of their blocks and compared with the oracle."""
+    whole list (bench.py's "-blocked" modes), the workload's 10 steps; the sampled
+    elements are read back out of their blocks and compared with the oracle."""
     wl = workloads.get("opt_1_3b")
     case = SampledCase(mode, wl.numels, seed={"mixed": 4101, "kahan": 4102, "split": 4103}[mode])
     state = case.keys[2:]
@@ -103,7 +103,7 @@ def test_opt13b_full_size_blocked_state(mode):
     tl = A.TensorList(wl.numels, streams + [[blocked], None, None], 0, -1, A.BLOCKED_STATE | A.FLAT_PAD8)
     hg, ho = hp_pair()
     code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
-    for s in range(3):
+    for s in range(wl.steps):
         if s:
             case.refill_grads(s)
         A.adamw_multi_tensor_step(code, A.BF16, tl, hg, case.d_step)
