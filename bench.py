@@ -325,7 +325,18 @@ def cpu_baseline(numels, sample, modes):
             "all_cores": {"value": rate(secs_mt), "unit": "Gparam/s", "cores": threads,
                           "sample": f"the same, cut into {threads} ranges on {threads} threads: "
                                     + " + ".join(f"{s:.2f} s" for s in secs_mt.values())},
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "host_cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _per_mode(modes, ev, K, N, first_ms):
