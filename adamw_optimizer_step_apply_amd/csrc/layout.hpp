@@ -37,7 +37,8 @@ constexpr int kPack = 8;               // elements per lane per dwordx4 of a 16-
 constexpr uint32_t kVecBit = 0x80000000u;
 constexpr uint32_t kCountMask = 0x7fffffffu;
 constexpr int64_t kElemChunkElems = 4096;       // element chunk
-constexpr int64_t kStateBlock = ADAMW_STATE_BLOCK;   // elements per block of a blocked state buffer
+// bytes of the largest state sub-stream in one block of a blocked state buffer
+constexpr int64_t kStateBlockBytes = ADAMW_STATE_BLOCK_BYTES;
 // Default vector chunk of a kernel: one 8-element pack per lane, one pass.
 constexpr int64_t chunk_elems_for_block(int block) { return (int64_t)block * 8; }
 // The overflow check moves 2 B per element (the step 18-28 B): each lane reads

@@ -121,14 +121,18 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
     int esz[kStreams];
     bool flat[kStreams];
     // blocked state: exp_avg, exp_avg_sq and aux share one flat buffer of the
-    // shard in blocks of kStateBlock elements, [exp_avg][exp_avg_sq][aux] each
-    int64_t soff[kStreams] = {0, 0, 0, 0, 0}, block_bytes = 0;
+    // shard in blocks of state_block elements, [exp_avg][exp_avg_sq][aux] each;
+    // the largest sub-stream of a block spans kStateBlockBytes
+    int64_t soff[kStreams] = {0, 0, 0, 0, 0}, block_bytes = 0, state_block = 1;
     uintptr_t state_base = 0;
     if (blocked) {
+        int max_esz = 0;
+        for (int s = ADAMW_STREAM_EXP_AVG; s <= ADAMW_STREAM_AUX; ++s) max_esz = esz_in[s] > max_esz ? esz_in[s] : max_esz;
+        state_block = kStateBlockBytes / max_esz;
         int64_t acc = 0;
         for (int s = ADAMW_STREAM_EXP_AVG; s <= ADAMW_STREAM_AUX; ++s) {
             soff[s] = acc;
-            acc += kStateBlock * esz_in[s];
+            acc += state_block * esz_in[s];
         }
         block_bytes = acc;
         if (e > b) {
@@ -171,7 +175,7 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
         for (int64_t plo = lo; plo < hi;) {
             int64_t phi = hi;
             if (blocked) {
-                const int64_t next = b + ((plo - b) / kStateBlock + 1) * kStateBlock;
+                const int64_t next = b + ((plo - b) / state_block + 1) * state_block;
                 if (next < phi) phi = next;
             }
             SegInfo si{i, plo - base, plo, phi - plo};
@@ -181,8 +185,8 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
                 uintptr_t a;
                 if (blocked && s >= ADAMW_STREAM_EXP_AVG) {
                     const int64_t rel = plo - b;
-                    a = state_base + (uintptr_t)((rel / kStateBlock) * block_bytes + soff[s] +
-                                                 (rel % kStateBlock) * esz[s]);
+                    a = state_base + (uintptr_t)((rel / state_block) * block_bytes + soff[s] +
+                                                 (rel % state_block) * esz[s]);
                 } else if (flat[s]) {
                     a = (uintptr_t)list->ptr[s][0] + (uintptr_t)((plo - b) * esz[s]);
                 } else {

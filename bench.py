@@ -241,7 +241,7 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
     streams = [[arena.view(k, i) for i in range(len(numels))] for k in keys]
     if blocked:
         import adamw_optimizer_step_apply_amd as A
-        B = A.STATE_BLOCK
+        B = A.state_block(max(arena.bufs[k].element_size() for k in keys[2:]))
         n = sum(-(-m // 8) * 8 for m in numels)     # padded flat index
         nb = -(-n // B)
         cols = []
@@ -501,7 +501,8 @@ def main():
                            f"exp_avg_sq, {'bf16 Kahan compensation' if kahan else 'no compensation'}")
         if base != mode:
             names[mode] = (names[base] + f", exp_avg/exp_avg_sq/{'master' if base == 'mixed' else 'aux'} "
-                           f"interleaved per {A.STATE_BLOCK}-element block of one optimizer-owned buffer")
+                           "interleaved per block of one optimizer-owned buffer (32 KiB per block of the widest "
+                           "state stream)")
     out = {
         "metric": "AdamW step Gparams/s + achieved HBM GB/s (% of peak), OPT-1.3B shape, 1 GPU",
         "value": round(value, 3),

@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define ADAMW_ABI_VERSION 1
+#define ADAMW_ABI_VERSION 2
 
 typedef enum {
     ADAMW_OK = 0,
@@ -147,26 +147,31 @@ typedef struct {
  * numel is a host array of n_tensors element counts (each >= 0). */
 /* flat_mask bit: the blocked state layout.  exp_avg, exp_avg_sq and aux share
  * ONE flat buffer of the shard, ptr[2][0] (16-byte aligned; ptr[3], ptr[4] and
- * flat_mask bits 2-4 are ignored), made of ceil((shard_end - shard_begin) /
- * ADAMW_STATE_BLOCK) blocks.  Block k holds the state of the shard's elements
- * [k*B, (k+1)*B), B = ADAMW_STATE_BLOCK, stream after stream:
+ * flat_mask bits 2-4 are ignored), made of ceil((shard_end - shard_begin) / B)
+ * blocks of B elements, B = ADAMW_STATE_BLOCK_ELEMS(largest element size in
+ * bytes among the step's state streams): 8192 when any of them is fp32 (the
+ * mixed and split modes, fp32 AnyPrecision moments), 16384 when all are 16-bit
+ * (ADAMW_PURE_KAHAN, bf16 AnyPrecision moments).  Block k holds the state of
+ * the shard's elements [k*B, (k+1)*B), stream after stream:
  *     [exp_avg x B][exp_avg_sq x B][aux x B]
  * each in its stream's dtype (an unused aux stream takes no room); the last
  * block is padded to B.  For optimizer-owned ZeRO state: the step's per-element
  * state traffic becomes one contiguous region per workgroup instead of three
  * separate streams (fewer concurrently open DRAM rows; measured faster on
- * MI355X).  param and grad keep their own layout (adamw_check_finite, which
- * reads only grads, ignores the bit).  B is a multiple of every update
- * kernel's default chunk, so splitting work at block edges never leaves a
- * workgroup's lanes idle.  The 16-byte vector path needs an element's state
- * address and its param/grad addresses to share their alignment: with
- * per-tensor param/grad buffers that start 16-byte aligned, a tensor whose
- * flat start is not a multiple of 8 elements runs element-wise (correct, but
- * slower: on 10,000 tensors of random lengths the mixed fp16 step fell from 5.6
- * to 4.2 TB/s on MI355X), so give such lists tensor lengths, or padding, that
- * are multiples of 8. */
+ * MI355X, and fastest when the largest sub-stream of a block spans 32 KiB).
+ * param and grad keep their own layout (adamw_check_finite, which reads only
+ * grads, ignores the bit).  B is a multiple of every update kernel's default
+ * chunk, so splitting work at block edges never leaves a workgroup's lanes
+ * idle.  The 16-byte vector path needs an element's state address and its
+ * param/grad addresses to share their alignment: with per-tensor param/grad
+ * buffers that start 16-byte aligned, a tensor whose flat start is not a
+ * multiple of 8 elements runs element-wise (correct, but slower: on 10,000
+ * tensors of random lengths the mixed fp16 step fell from 5.6 to 4.2 TB/s on
+ * MI355X), so give such lists tensor lengths, or padding, that are multiples
+ * of 8 (see ADAMW_FLAT_PAD8). */
 #define ADAMW_BLOCKED_STATE (1u << 8)
-#define ADAMW_STATE_BLOCK 8192
+#define ADAMW_STATE_BLOCK_BYTES 32768
+#define ADAMW_STATE_BLOCK_ELEMS(max_state_elem_bytes) (ADAMW_STATE_BLOCK_BYTES / (max_state_elem_bytes))
 /* flat_mask bit: the padded flat index.  The list's flat concatenation places
  * every tensor at a multiple of 8 elements: tensor i starts at the sum over
  * j < i of numel[j] rounded up to a multiple of 8, and the gaps hold no

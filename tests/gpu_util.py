@@ -286,11 +286,16 @@ def blocked_state_keys(case) -> tuple:
     return tuple(case.keys[2:])
 
 
+def state_block_of(dtypes) -> int:
+    """Elements per block of a blocked state buffer with state streams of these dtypes."""
+    return A.state_block(max(torch.empty(0, dtype=dt).element_size() for dt in dtypes))
+
+
 def build_blocked(case, b, e) -> torch.Tensor:
     """The blocked state buffer of the shard [b, e) of a tightly packed case
-    (arena index == flat index): per block of STATE_BLOCK elements, each state
-    stream's values one after another, as raw bytes."""
-    B = A.STATE_BLOCK
+    (arena index == flat index): per block of B elements (32 KiB of the widest
+    state stream), each state stream's values one after another, as raw bytes."""
+    B = state_block_of([case.arena.bufs[k].dtype for k in blocked_state_keys(case)])
     L = e - b
     nb = -(-L // B)
     cols = []
@@ -310,7 +315,7 @@ def build_blocked_padded(arena, keys, numels) -> torch.Tensor:
     """The blocked state buffer of a whole list in the padded flat index, from
     an arena whose tensors already sit at their padded positions (aligned to 8
     elements, or to any multiple of 8 when every length is one)."""
-    B = A.STATE_BLOCK
+    B = state_block_of([arena.bufs[k].dtype for k in keys])
     starts = padded_starts(numels)
     assert list(arena.offsets) == [int(x) for x in starts[:-1]], "arena is not in the padded flat index"
     nb = -(-int(starts[-1]) // B)
@@ -329,7 +334,7 @@ def blocked_gather(blocked: torch.Tensor, dtypes: dict, pos: torch.Tensor) -> di
     """Values at flat positions `pos` (device int64) of each state stream of a
     whole-list blocked buffer; `dtypes` maps the streams, in block order, to
     their torch dtypes."""
-    B = A.STATE_BLOCK
+    B = state_block_of(list(dtypes.values()))
     blk, off = pos // B, pos % B
     out, col = {}, 0
     for k, dt in dtypes.items():
@@ -341,7 +346,7 @@ def blocked_gather(blocked: torch.Tensor, dtypes: dict, pos: torch.Tensor) -> di
 
 def unpack_blocked(case, blocked: torch.Tensor, b, e) -> dict:
     """Per-stream host arrays (flat order, length e - b) from a blocked buffer."""
-    B = A.STATE_BLOCK
+    B = state_block_of([case.arena.bufs[k].dtype for k in blocked_state_keys(case)])
     L = e - b
     out, col = {}, 0
     for k in blocked_state_keys(case):

@@ -47,7 +47,8 @@ def test_binding_constants_match_the_header():
 
     assert define("ADAMW_BLOCKED_STATE") == A.BLOCKED_STATE
     assert define("ADAMW_FLAT_PAD8") == A.FLAT_PAD8
-    assert define("ADAMW_STATE_BLOCK") == A.STATE_BLOCK
+    assert define("ADAMW_STATE_BLOCK_BYTES") == A.STATE_BLOCK_BYTES
+    assert A.state_block(4) == 8192 and A.state_block(2) == 16384
     for name, value in (("ADAMW_OK", A.OK), ("ADAMW_E_INVALID", A.E_INVALID), ("ADAMW_E_UNSUPPORTED", A.E_UNSUPPORTED),
                         ("ADAMW_E_NOMEM", A.E_NOMEM), ("ADAMW_E_HIP", A.E_HIP), ("ADAMW_F32", A.F32),
                         ("ADAMW_BF16", A.BF16), ("ADAMW_F16", A.F16), ("ADAMW_MIXED", A.MIXED),
@@ -344,7 +345,7 @@ def test_plan_blocked_state_never_straddles_a_block(seed):
     pos = b
     for (t, off, n, vec, flat, seg) in rows:
         assert flat == pos
-        assert (flat - b) // A.STATE_BLOCK == (flat + n - 1 - b) // A.STATE_BLOCK
+        assert (flat - b) // A.state_block(4) == (flat + n - 1 - b) // A.state_block(4)
         pos += n
     assert pos == e
 
@@ -373,7 +374,7 @@ def test_plan_padded_flat_index(seed):
     covered = []
     for (t, off, n, vec, flat, seg) in rows:
         assert slots[flat] == (t, off)
-        assert (flat - b) // A.STATE_BLOCK == (flat + n - 1 - b) // A.STATE_BLOCK
+        assert (flat - b) // A.state_block(4) == (flat + n - 1 - b) // A.state_block(4)
         covered += [(t, off + j) for j in range(n)]
         if seed % 2 == 0 and not vec:
             assert n < 8 and (off + n == numels[t] or flat + n == e), (t, off, n, numels[t])
@@ -393,7 +394,28 @@ def test_check_plan_ignores_blocked_bit():
     blocked = A.adamw_plan_inspect(A.MIXED, A.F16, A.TensorList(numels, [None, g, None, None, None],
                                                                 flat_mask=A.BLOCKED_STATE), True)
     assert blocked == plain
-    assert max(r[2] for r in plain) > A.STATE_BLOCK
+    assert max(r[2] for r in plain) > A.state_block(4)
+
+
+@pytest.mark.parametrize("mode,esz,block", [(A.MIXED, (2, 2, 4, 4, 4), 8192), (A.PURE_KAHAN, (2, 2, 2, 2, 2), 16384)])
+def test_blocked_state_block_follows_the_widest_state_stream(mode, esz, block):
+    """B = 32 KiB / (widest state element): the segments of a blocked plan are
+    exactly the pieces of the list cut at tensor edges and at multiples of B
+    from the shard start, and no more."""
+    rng = np.random.default_rng(7)
+    numels = [int(x) for x in rng.integers(1, 60000, size=9)]
+    total = sum(numels)
+    b, e = 12345, total - 777
+    offs = np.concatenate([[0], np.cumsum(numels)[:-1]])
+    ptrs = [[FAKE + s * (1 << 36) + int(o) * esz[s] for o in offs] for s in range(2)]
+    ptrs += [[FAKE + 7 * (1 << 36)], None, None]
+    rows = A.adamw_plan_inspect(mode, A.BF16, A.TensorList(numels, ptrs, b, e, flat_mask=A.BLOCKED_STATE))
+    starts = set(int(x) for x in np.concatenate([[0], np.cumsum(numels)]))
+    cuts = {x for x in starts if b < x < e} | {x for x in range(b + block, e, block)}
+    want_segments = len(cuts) + 1
+    assert len({r[5] for r in rows}) == want_segments
+    for (t, off, n, vec, flat, seg) in rows:
+        assert (flat - b) // block == (flat + n - 1 - b) // block
 
 
 def test_blocked_state_needs_aligned_buffer():
