@@ -197,11 +197,13 @@ def probes(n, stream):
     w, m, v = (torch.ones(n, dtype=torch.float32, device=dev) for _ in range(3))
     run(0, [g, w, m, v, p], n, 28 * n, "mixed_mix")
     del w, m, v
-    nb = -(-n // 8192)                            # whole blocks of the blocked state layout
+    # whole blocks of the blocked state layout: 32 KiB per state stream and block
+    nb = -(-n // 8192)
     blk = torch.ones(nb * 8192 * 3, dtype=torch.float32, device=dev)
     run(6, [g, blk, p], n, 28 * n, "mixed_blocked_mix")
     del blk
-    blk = torch.ones(nb * 8192 * 3, dtype=torch.bfloat16, device=dev)
+    nb = -(-n // 16384)
+    blk = torch.ones(nb * 16384 * 3, dtype=torch.bfloat16, device=dev)
     run(7, [g, p, blk], n, 18 * n, "kahan_blocked_mix")
     del blk
     r16 = torch.ones(n, dtype=torch.bfloat16, device=dev)

@@ -73,12 +73,15 @@ __global__ __launch_bounds__(256) void kahan_mix(const GLOBAL u32x4* g, GLOBAL u
     __builtin_nontemporal_store(f ^ a, c + k);
 }
 
-// The blocked state layout: per block of kBlock elements, the state streams one
-// after another ([m][v][w] fp32 for the mixed mix, [m][v][c] bf16 for Kahan);
-// g and p keep their own buffers.  Pack k (elements 8k..8k+7) lies in block
-// k / (kBlock / 8) at pack offset k % (kBlock / 8).
-constexpr uint64_t kBlock = 8192;
+// The blocked state layout: per block, the state streams one after another
+// ([m][v][w] fp32 for the mixed mix, [m][v][c] bf16 for Kahan), each spanning
+// 32 KiB as in the library (8192 fp32 / 16384 bf16 elements); g and p keep their
+// own buffers.  Pack k (elements 8k..8k+7) lies in block k / (kBlock / 8) at
+// pack offset k % (kBlock / 8).
+constexpr uint64_t kBlock = 8192;            // fp32 state
 constexpr uint64_t kPacksPerBlock = kBlock / 8;
+constexpr uint64_t kBlock16 = 16384;         // 16-bit state
+constexpr uint64_t kPacksPerBlock16 = kBlock16 / 8;
 
 __global__ __launch_bounds__(256) void mixed_blocked_mix(const GLOBAL u32x4* g, GLOBAL f32x4* s, GLOBAL u32x4* p,
                                                          uint64_t npack)
@@ -107,10 +110,10 @@ __global__ __launch_bounds__(256) void kahan_blocked_mix(const GLOBAL u32x4* g, 
 {
     const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
     if (k >= npack) return;
-    // one block of bf16 state = 3 x kBlock halves = 3 x kBlock / 8 u32x4
-    GLOBAL u32x4* m = s + (k / kPacksPerBlock) * (3 * kBlock / 8) + (k % kPacksPerBlock);
-    GLOBAL u32x4* v = m + kBlock / 8;
-    GLOBAL u32x4* c = v + kBlock / 8;
+    // one block of bf16 state = 3 x kBlock16 halves = 3 x kBlock16 / 8 u32x4
+    GLOBAL u32x4* m = s + (k / kPacksPerBlock16) * (3 * kBlock16 / 8) + (k % kPacksPerBlock16);
+    GLOBAL u32x4* v = m + kBlock16 / 8;
+    GLOBAL u32x4* c = v + kBlock16 / 8;
     const u32x4 a = __builtin_nontemporal_load(g + k), b = __builtin_nontemporal_load(p + k);
     const u32x4 d = __builtin_nontemporal_load(m), e = __builtin_nontemporal_load(v);
     const u32x4 f = __builtin_nontemporal_load(c);
@@ -148,7 +151,8 @@ constexpr size_t kLds = 81920;   // two resident workgroups per CU, as the updat
 // kind: 0 mixed, 1 Kahan, 5 split master, 6 mixed with blocked state, 7 Kahan with
 // blocked state (n elements); 2 copy, 3 read, 4 write (n floats).
 // a..e: the buffers of the kind, in the order of the kernel's parameters; a
-// blocked state buffer holds ceil(n / 8192) whole blocks.
+// blocked state buffer holds whole blocks: ceil(n / 8192) of them for kind 6,
+// ceil(n / 16384) for kind 7.
 // n must be a multiple of 8.  Returns the hipError_t of the launch.
 extern "C" int probe_launch(int kind, void* a, void* b, void* c, void* d, void* e, uint64_t n, void* stream)
 {
