@@ -134,8 +134,11 @@ private:
 };
 
 // Returns (in *out) a slot of `ws` holding the device plan of (mode, dtype,
-// list, for_check): a cached one if every input matches, else the least
-// recently used slot, re-planned and re-uploaded.
+// list, for_check): a cached one if every input matches (the key holds every
+// input the plan depends on, so a hit was validated when it was built), else
+// the list is validated and planned, and the least recently used slot takes
+// the new plan.  An invalid list returns its error before any HIP call and
+// leaves the cache as it was.
 adamw_status ensure_plan(StreamWorkspace& ws, int64_t tag, const int esz[kStreams], const adamw_tensor_list* list,
                          int64_t chunk_elems, hipStream_t stream, PlanSlot** out)
 {
@@ -149,16 +152,16 @@ adamw_status ensure_plan(StreamWorkspace& ws, int64_t tag, const int esz[kStream
             return ADAMW_OK;
         }
     }
+    Plan plan;
+    std::string err;
+    adamw_status st = build_plan(esz, list, chunk_elems, &plan, err);
+    if (st != ADAMW_OK) return fail(st, err);
+
     if (plans.size() < kPlansPerStream) plans.emplace_back(new PlanSlot());
     std::rotate(plans.begin(), plans.end() - 1, plans.end());   // LRU slot to the front
     PlanSlot& slot = *plans.front();
     slot.valid = false;
     *out = &slot;
-
-    Plan plan;
-    std::string err;
-    adamw_status st = build_plan(esz, list, chunk_elems, &plan, err);
-    if (st != ADAMW_OK) return fail(st, err);
 
     const size_t seg_bytes = plan.segs.size() * sizeof(DevSeg);
     const size_t bytes = seg_bytes + plan.chunks.size() * sizeof(DevChunk);
@@ -207,6 +210,48 @@ adamw_status ensure_plan(StreamWorkspace& ws, int64_t tag, const int esz[kStream
     slot.n_chunks = (int64_t)plan.chunks.size();
     slot.key.swap(key);
     slot.valid = true;
+    return ADAMW_OK;
+}
+
+// Keys of the lists validated most recently (full keys, not hashes).  A call
+// whose key is here skips the validation walk, which for a blocked-state list
+// of 10^5-10^6 pieces costs milliseconds of host time per call; a new key is
+// validated before any HIP call.
+constexpr size_t kValidatedKeys = 16;
+std::mutex g_validated_mu;
+std::vector<std::vector<int64_t>> g_validated;   // most recent first
+
+bool validated_before(const std::vector<int64_t>& key)
+{
+    std::lock_guard<std::mutex> lk(g_validated_mu);
+    for (size_t i = 0; i < g_validated.size(); ++i) {
+        if (g_validated[i] == key) {
+            std::rotate(g_validated.begin(), g_validated.begin() + (ptrdiff_t)i,
+                        g_validated.begin() + (ptrdiff_t)i + 1);
+            return true;
+        }
+    }
+    return false;
+}
+
+void remember_validated(const std::vector<int64_t>& key)
+{
+    std::lock_guard<std::mutex> lk(g_validated_mu);
+    if (g_validated.size() >= kValidatedKeys) g_validated.pop_back();
+    g_validated.insert(g_validated.begin(), key);
+}
+
+// Validates the list for a plan of `tag` (unless the same key passed before),
+// with no HIP call.
+adamw_status validate_list(int64_t tag, const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems)
+{
+    std::vector<int64_t> key;
+    plan_key(tag, esz, list, chunk_elems, key);
+    if (validated_before(key)) return ADAMW_OK;
+    std::string err;
+    adamw_status st = build_plan(esz, list, chunk_elems, nullptr, err);
+    if (st != ADAMW_OK) return fail(st, err);
+    remember_validated(key);
     return ADAMW_OK;
 }
 
@@ -279,7 +324,6 @@ adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const 
                      const adamw_loss_scaler* scaler = nullptr)
 {
     adamw_status st;
-    std::string err;
     if ((st = check_hparams(hp)) != ADAMW_OK) return st;
     if (!d_step) return fail(ADAMW_E_INVALID, "d_step is null");
     if ((uintptr_t)d_step % 4 || (uintptr_t)d_found_inf % 4)
@@ -288,8 +332,7 @@ adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const 
 
     // the whole list is validated before the first HIP call
     const int64_t chunk_elems = chunk_elems_of(kind.kernel);
-    st = build_plan(kind.esz, list, chunk_elems, nullptr, err);
-    if (st != ADAMW_OK) return fail(st, err);
+    if ((st = validate_list(kind.kernel, kind.esz, list, chunk_elems)) != ADAMW_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     StreamWorkspace* ws = nullptr;
     if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
@@ -420,8 +463,7 @@ adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* gr
     const int64_t chunk_elems = check_chunk_elems();
     int esz[kStreams];
     mode_esizes(ADAMW_MIXED, g_dtype, true, esz);
-    st = build_plan(esz, grads, chunk_elems, nullptr, err);
-    if (st != ADAMW_OK) return fail(st, err);
+    if ((st = validate_list(-1, esz, grads, chunk_elems)) != ADAMW_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     StreamWorkspace* ws = nullptr;
     if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
