@@ -418,6 +418,28 @@ def test_blocked_state_block_follows_the_widest_state_stream(mode, esz, block):
         assert (flat - b) // block == (flat + n - 1 - b) // block
 
 
+def test_validation_is_not_skipped_for_a_changed_list():
+    """A list validated once is not walked again on the next call, but any change
+    (one pointer, one size, the shard, the mode) is validated afresh: errors in a
+    list that differs from a validated one in a single field are still caught
+    before any HIP call."""
+    numels = [5000, 70, 4099]
+    esz = (2, 2, 4, 4, 4)
+    offs = np.concatenate([[0], np.cumsum(numels)[:-1]])
+    ptrs = [[FAKE + s * (1 << 36) + int(o) * esz[s] for o in offs] for s in range(5)]
+    for _ in range(2):
+        with pytest.raises(A.AdamWError) as e:          # valid: passes validation, then needs a GPU
+            A.adamw_multi_tensor_step(A.MIXED, A.BF16, A.TensorList(numels, ptrs), A.HParams(), FAKE, stream=0)
+        assert e.value.status in (A.E_HIP, A.E_NOMEM), e.value
+    bad = [list(p) for p in ptrs]
+    bad[2][1] += 2                                      # exp_avg of tensor 1 misaligned for fp32
+    with pytest.raises(A.AdamWError, match="aligned"):
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, A.TensorList(numels, bad), A.HParams(), FAKE, stream=0)
+    with pytest.raises(A.AdamWError, match="shard"):
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, A.TensorList(numels, ptrs, 0, sum(numels) + 1),
+                                  A.HParams(), FAKE, stream=0)
+
+
 def test_blocked_state_needs_aligned_buffer():
     numels = [100]
     ptrs = [[FAKE], [FAKE + (1 << 36)], [FAKE + 2 * (1 << 36) + 8], None, None]
