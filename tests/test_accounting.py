@@ -61,3 +61,15 @@ def test_step_traffic_per_param():
     assert workloads.traffic_per_param("mixed") == 28
     assert workloads.traffic_per_param("kahan") == 18
     assert workloads.traffic_per_param("mixed") + workloads.traffic_per_param("check_f16") == 30
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py times one GPU's share; asked for more it exits with a message and
+    touches no GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=root, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
