@@ -736,3 +736,51 @@ def test_blocked_state_layout(mode, shard):
     hp_all = to_np(case.arena.bufs["p"])
     assert np.array_equal(hp_all[:b], case.host["p"][:b]) and np.array_equal(hp_all[e:], case.host["p"][e:])
     free()
+
+
+def test_mixed_step_tracks_torch_adamw():
+    """A user-facing cross-check against torch.optim.AdamW on the GPU (fp32 params,
+    gradients that are exact bf16 values): after 5 steps the fp32 master and the
+    moments agree with PyTorch's to a few units in the last place.  torch orders
+    the operations differently (moments by lerp, sqrt(v)/sqrt(1-b2^t)), so this is
+    not the bitwise bar of the oracle comparisons."""
+    torch.manual_seed(11)
+    shapes = [(513, 77), (4099,), (64, 64, 3)]
+    ref = [torch.randn(s, device="cuda") * 0.02 for s in shapes]
+    hp = dict(lr=2e-4, betas=(0.9, 0.95), eps=1e-8, weight_decay=0.1)
+    tparams = [torch.nn.Parameter(w.clone()) for w in ref]
+    opt = torch.optim.AdamW(tparams, foreach=False, **hp)
+    master = [w.clone() for w in ref]
+    p16 = [w.to(torch.bfloat16) for w in ref]
+    m = [torch.zeros_like(w) for w in ref]
+    v = [torch.zeros_like(w) for w in ref]
+    g16 = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    tl = A.TensorList([w.numel() for w in ref], [p16, g16, m, v, master])
+    step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hg = A.HParams(lr=hp["lr"], beta1=0.9, beta2=0.95, eps=hp["eps"], weight_decay=hp["weight_decay"])
+    gmax = [torch.zeros_like(w) for w in ref]
+    for _ in range(5):
+        for i, (g, tp) in enumerate(zip(g16, tparams)):
+            g.copy_((torch.randn_like(tp) * 1e-3).to(torch.bfloat16))
+            tp.grad = g.float()
+            gmax[i] = torch.maximum(gmax[i], tp.grad.abs())
+        opt.step()
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl, hg, step)
+    torch.cuda.synchronize()
+    # Bounds relative to the terms each quantity is formed from (a result near 0 can
+    # come from cancelling terms): the master moves by at most lr * |u| <= 2 lr per
+    # step; exp_avg is a decaying sum of gradients; exp_avg_sq of squares (no
+    # cancellation).  8 units in the last place of those magnitudes.
+    ulp = 8 * 2.0 ** -23
+    for i, tp in enumerate(tparams):
+        st = opt.state[tp]
+        w_t, m_t, v_t = tp.detach(), st["exp_avg"], st["exp_avg_sq"]
+        checks = (("master", master[i], w_t, ref[i].abs() + w_t.abs() + 10 * hp["lr"]),
+                  ("exp_avg", m[i], m_t, m_t.abs() + gmax[i]),
+                  ("exp_avg_sq", v[i], v_t, v_t.abs()))
+        for name, ours, theirs, scale in checks:
+            diff = (ours - theirs).abs()
+            assert bool((diff <= ulp * scale).all()), (i, name, float((diff / scale).max()))
+        assert torch.equal(p16[i], master[i].to(torch.bfloat16))
+    assert int(step.item()) == 5
+    free()
