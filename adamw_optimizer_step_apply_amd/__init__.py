@@ -33,7 +33,10 @@ F32, BF16, F16 = 0, 1, 2
 MIXED, PURE_KAHAN, MIXED_SPLIT = 0, 1, 2
 STREAM_PARAM, STREAM_GRAD, STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_AUX = range(5)
 BLOCKED_STATE = 1 << 8        # flat_mask bit: exp_avg / exp_avg_sq / aux in one blocked buffer
-STATE_BLOCK_BYTES = 32768     # bytes of the widest state stream in one block of that buffer
+FLAT_PAD8 = 1 << 9            # flat_mask bit: every tensor starts at a multiple of 8 in the flat index
+STATE_BLOCK_BYTES = 32768     # bytes of the widest state stream in one block of a blocked buffer
+NUM_STREAMS = 5
+_STATUS = {0: "ADAMW_OK", 1: "ADAMW_E_INVALID", 2: "ADAMW_E_UNSUPPORTED", 3: "ADAMW_E_NOMEM", 4: "ADAMW_E_HIP"}
 
 
 def state_block(max_state_elem_bytes: int) -> int:
@@ -41,9 +44,7 @@ def state_block(max_state_elem_bytes: int) -> int:
     has elements of `max_state_elem_bytes` bytes (ADAMW_STATE_BLOCK_ELEMS):
     8192 with an fp32 state stream, 16384 when all state is 16-bit."""
     return STATE_BLOCK_BYTES // int(max_state_elem_bytes)
-FLAT_PAD8 = 1 << 9            # flat_mask bit: every tensor starts at a multiple of 8 in the flat index
-NUM_STREAMS = 5
-_STATUS = {0: "ADAMW_OK", 1: "ADAMW_E_INVALID", 2: "ADAMW_E_UNSUPPORTED", 3: "ADAMW_E_NOMEM", 4: "ADAMW_E_HIP"}
+
 
 EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_amp", "adamw_pure_multi_tensor_step",
             "adamw_check_finite",
