@@ -23,7 +23,7 @@ constexpr int kStreams = 5;            // param, grad, exp_avg, exp_avg_sq, aux
 // Chosen by interleaved A/B runs on MI355X (OPT-1.3B list, state in the blocked
 // layout and per tensor): for the pure family 256 x 4 and 512 x 2 beat 1024 x 1
 // by 5% on blocked state and tie with it per tensor; for the mixed family
-// 256 x 2 leads every other shape by 3% or more on blocked state.
+// 256 x 2 leads every other shape tried, by 0-10% on blocked state.
 #ifndef ADAMW_BLOCK_MIXED
 #define ADAMW_BLOCK_MIXED 256
 #endif
@@ -49,6 +49,11 @@ constexpr int64_t chunk_elems_for_block(int block) { return (int64_t)block * 8; 
 #endif
 constexpr int kCheckChunkMult = ADAMW_CHECK_CHUNK_MULT;
 constexpr int64_t kCheckChunkElems = chunk_elems_for_block(kBlockCheck) * kCheckChunkMult;
+// A launch's grid counts at most 2^32 - 1 lanes: the chunk limit of one plan
+// follows from the widest workgroup.
+constexpr int kMaxBlock = kBlockMixed > kBlockPure ? (kBlockMixed > kBlockCheck ? kBlockMixed : kBlockCheck)
+                                                   : (kBlockPure > kBlockCheck ? kBlockPure : kBlockCheck);
+constexpr int64_t kMaxChunks = (int64_t)UINT32_MAX / kMaxBlock;
 
 // Update kernels, by launch id.  The pure-bf16 family adds
 // 4 * (fp32 exp_avg) + 2 * (fp32 exp_avg_sq) + (Kahan compensation).

@@ -11,7 +11,8 @@
 //
 // The head is the smallest count h < 8 that brings every stream's address to a
 // 16-byte boundary at the same element; if no such h exists (streams misaligned
-// relative to each other) the whole segment is cut into element chunks.
+// relative to each other), or no whole 8-element pack follows it, the whole
+// segment is cut into element chunks.
 #include "plan.hpp"
 
 #include <stdio.h>
@@ -61,8 +62,13 @@ adamw_status check_mode(adamw_mode mode, adamw_dtype p_dtype, bool for_check, st
 
 static const char* kStreamName[kStreams] = {"param", "grad", "exp_avg", "exp_avg_sq", "aux"};
 
-static void push_chunks(Plan& p, uint32_t seg, int64_t off, int64_t count, int64_t per, bool vec)
+// Appends the chunks of `count` elements from `off` (at most `per` each) to the
+// plan when `build`, and counts them in `n_chunks` either way.
+static void push_chunks(Plan& p, bool build, int64_t& n_chunks, uint32_t seg, int64_t off, int64_t count, int64_t per,
+                        bool vec)
 {
+    n_chunks += (count + per - 1) / per;
+    if (!build) return;
     while (count > 0) {
         int64_t n = count < per ? count : per;
         DevChunk c;
@@ -166,7 +172,7 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
     }
     if (chunk_elems < 2048 || chunk_elems % 2048) { err = "bad chunk size"; return ADAMW_E_INVALID; }
 
-    int64_t base = 0, nseg = 0;
+    int64_t base = 0, nseg = 0, n_chunks = 0;
     for (int64_t i = 0; i < nt; ++i) {
         const int64_t n = list->numel[i];
         const int64_t lo = b > base ? b : base;
@@ -204,9 +210,10 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
             plo = phi;
             if (nseg >= (int64_t)UINT32_MAX) { err = "too many segments"; return ADAMW_E_INVALID; }
             const uint32_t seg = (uint32_t)nseg++;
-            if (!build) continue;
-            out.segs.push_back(d);
-            out.info.push_back(si);
+            if (build) {
+                out.segs.push_back(d);
+                out.info.push_back(si);
+            }
 
             // head peel: smallest h in [0, 8) aligning every active stream to 16 bytes
             int head = -1;
@@ -217,18 +224,26 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
                 if (ok) head = h;
             }
             const int64_t cnt = si.count;
-            if (head < 0 || head >= cnt) {
-                push_chunks(out, seg, 0, cnt, kElemChunkElems, false);
+            // no full pack after the head: one element pass over the piece
+            if (head < 0 || cnt - head < kPack) {
+                push_chunks(out, build, n_chunks, seg, 0, cnt, kElemChunkElems, false);
             } else {
                 const int64_t body = (cnt - head) / kPack * kPack;
-                push_chunks(out, seg, 0, head, kElemChunkElems, false);
-                push_chunks(out, seg, head, body, chunk_elems, true);
-                push_chunks(out, seg, head + body, cnt - head - body, kElemChunkElems, false);
+                push_chunks(out, build, n_chunks, seg, 0, head, kElemChunkElems, false);
+                push_chunks(out, build, n_chunks, seg, head, body, chunk_elems, true);
+                push_chunks(out, build, n_chunks, seg, head + body, cnt - head - body, kElemChunkElems, false);
+            }
+            if (n_chunks > kMaxChunks) {
+                snprintf(buf, sizeof buf,
+                         "more than %lld chunks in one launch (a grid holds at most 2^32 - 1 lanes): "
+                         "split the list or raise the chunk size",
+                         (long long)kMaxChunks);
+                err = buf;
+                return ADAMW_E_INVALID;
             }
         }
         base += (n + flat_align - 1) / flat_align * flat_align;
     }
-    if (out.chunks.size() > (size_t)INT32_MAX) { err = "too many chunks for one launch"; return ADAMW_E_INVALID; }
     out.total = e - b;
     return ADAMW_OK;
 }

@@ -75,7 +75,10 @@
  * Errors.  Arguments are validated before anything is enqueued; on an error
  * nothing is enqueued, no buffer is touched, and adamw_last_error() describes
  * it.  A HIP failure while enqueuing returns ADAMW_E_HIP.  Faults inside a
- * kernel surface at the caller's next synchronisation.
+ * kernel surface at the caller's next synchronisation.  One launch's grid
+ * holds at most 2^32 - 1 lanes, so a plan of more than 16,777,215 chunks
+ * (256-lane workgroups: about 34e9 elements at the default chunk, or that
+ * many tensors of under 8 elements) is rejected with ADAMW_E_INVALID.
  *
  * Concurrency.  Calls may come from several host threads.  Calls on different
  * streams run independently (each stream has its own workspace); two calls

@@ -446,3 +446,34 @@ def test_blocked_state_needs_aligned_buffer():
     with pytest.raises(A.AdamWError, match="blocked"):
         A.adamw_multi_tensor_step(A.MIXED, A.BF16, A.TensorList(numels, ptrs, 0, -1, A.BLOCKED_STATE),
                                   A.HParams(), FAKE, stream=0)
+
+
+def test_plan_beyond_the_grid_limit_is_rejected():
+    """A launch's grid holds at most 2^32 - 1 lanes: with 256-lane workgroups a
+    plan may have at most 16,777,215 chunks.  One flat shard of exactly that
+    many 2048-element chunks is counted without building the table and passes
+    validation (then needs a GPU); one chunk more is rejected before any HIP call."""
+    limit = (2 ** 32 - 1) // 256
+    for n_chunks, ok in ((limit, True), (limit + 1, False)):
+        n = n_chunks * 2048
+        ptrs = [[FAKE + s * (1 << 40)] for s in range(5)]
+        tl = A.TensorList([n], ptrs, 0, -1, 0x1f)
+        with pytest.raises(A.AdamWError) as e:
+            A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl, A.HParams(), FAKE, stream=0)
+        if ok:
+            assert e.value.status in (A.E_HIP, A.E_NOMEM), e.value
+        else:
+            assert e.value.status == A.E_INVALID and "chunks in one launch" in str(e.value), e.value
+
+
+def test_many_tiny_tensors_count_one_chunk_each():
+    """Tensors shorter than a pack run as one element chunk each, so the chunk
+    count of a list of tiny tensors is its length (planner count = inspected rows)."""
+    numels = [1, 3, 7, 2, 5] * 40
+    offs = np.concatenate([[0], np.cumsum(numels)[:-1]])
+    esz = (2, 2, 4, 4, 4)
+    ptrs = [[FAKE + s * (1 << 36) + int(o) * esz[s] for o in offs] for s in range(5)]
+    rows = A.adamw_plan_inspect(A.MIXED, A.BF16, A.TensorList(numels, ptrs))
+    assert len(rows) == len(numels)
+    assert all(r[3] == 0 for r in rows)
+    assert [r[2] for r in rows] == numels
