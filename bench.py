@@ -7,9 +7,9 @@ param/grad + fp32 master, exp_avg, exp_avg_sq) and a pure-bf16 step with bf16
 Kahan compensation, each one call of adamw_multi_tensor_step (prologue + one
 update-kernel launch).  The optimizer owns its state, as a ZeRO shard's
 optimizer does, and keeps it in the blocked layout (exp_avg, exp_avg_sq and
-master or compensation interleaved per block of one buffer); the same steps on
-per-tensor state buffers are timed after the headline region and reported as
-per_tensor_state.  The timed region runs K mixed steps then K Kahan steps (two
+master or compensation interleaved per block of one buffer); with --compare the
+same steps on per-tensor state buffers are timed after the headline region and
+reported as per_tensor_state.  The timed region runs K mixed steps then K Kahan steps (two
 consecutive phases, as two training runs would); --interleave alternates them
 instead.  Inputs are synthetic and seeded (master ~ N(0, 0.02), grads ~
 N(0, 1e-3), moments 0) and already resident in HBM when the timed region
@@ -24,7 +24,7 @@ ceilings measured by bench_probe.hip, and the CPU oracle timed on a bounded
 sample on the host cores (one thread, and one thread per range on all cores).
 
 Usage:
-  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-probe]
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-probe] [--compare]
   python bench.py --workload ragged_10k                  (overflow check + fp16 step, 10k tensors)
   python bench.py --probe-only                            (memory ceilings only)
   python bench.py --calib-copy                            (plain 4 GiB copy, to scale rocprofv3 byte counters)
@@ -56,8 +56,11 @@ def parse():
                     help="comma list of mixed, kahan, split, pure-<m>-<v>-<k|n>, f16amp, each optionally -blocked")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-probe", action="store_true", help="skip the same-mix ceiling probes")
-    ap.add_argument("--no-compare", action="store_true",
-                    help="skip the per-tensor-state timing that follows a blocked-state headline")
+    ap.add_argument("--compare", action="store_true",
+                    help="after a blocked-state headline, also time the same steps on per-tensor state "
+                         "(per_tensor_state); off by default, so that each update kernel in a profile of the "
+                         "default run serves the headline layout only")
+    ap.add_argument("--no-compare", action="store_true", help="the default (no per-tensor-state timing)")
     ap.add_argument("--probe-only", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256_000_000,
                     help="elements of the list the oracle steps once per mode")
@@ -396,8 +399,9 @@ def main():
         print(json.dumps({"probes_gb_s": probes(N, stream), "n": N}), flush=True)
         return
     modes = default_modes(args).split(",")
-    # the same steps on per-tensor state buffers, timed after the headline region
-    compare = [] if args.no_compare else [m[:-len("-blocked")] for m in modes if m.endswith("-blocked")]
+    # with --compare, the same steps on per-tensor state buffers, timed after the headline region
+    compare = [m[:-len("-blocked")] for m in modes if m.endswith("-blocked")] if args.compare and not args.no_compare \
+        else []
     for mode in modes + compare:
         base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
         if base.startswith("pure"):
