@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libadamw_amd.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m adamw_optimizer_step_apply_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python adamw_optimizer_step_apply_amd/build.py` "
                       "(or __graft_entry__.build())")
 
 _lib = None
@@ -49,7 +49,7 @@ def state_block(max_state_elem_bytes: int) -> int:
 EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_amp", "adamw_pure_multi_tensor_step",
             "adamw_check_finite",
             "adamw_last_error", "adamw_release_workspace", "adamw_abi_version", "adamw_plan_inspect",
-            "adamw_set_chunk_elems")
+            "adamw_set_chunk_elems", "adamw_set_single_launch_max_chunks")
 
 
 class adamw_hparams(ctypes.Structure):
@@ -111,6 +111,8 @@ def _declare(_lib):
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
     _lib.adamw_set_chunk_elems.restype = ctypes.c_int64
     _lib.adamw_set_chunk_elems.argtypes = [ctypes.c_int64]
+    _lib.adamw_set_single_launch_max_chunks.restype = ctypes.c_int64
+    _lib.adamw_set_single_launch_max_chunks.argtypes = [ctypes.c_int64]
 
 
 _load(LIB_PATH)
@@ -297,6 +299,12 @@ def adamw_set_chunk_elems(elems: int) -> int:
     if r < 0:
         raise AdamWError(E_INVALID, f"chunk size {elems} rejected")
     return r
+
+
+def adamw_set_single_launch_max_chunks(max_chunks: int) -> int:
+    """Largest plan (in chunks) that runs as one launch; 0 = always prologue +
+    update kernel, < 0 = the default.  Returns the value now in force."""
+    return _lib.adamw_set_single_launch_max_chunks(int(max_chunks))
 
 
 def library_path() -> str:

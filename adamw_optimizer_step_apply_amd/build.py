@@ -1,8 +1,10 @@
 """Build the gfx950 shared library ``libadamw_amd.so`` in-tree with hipcc.
 
-Usage: ``python -m adamw_optimizer_step_apply_amd.build`` (also run by
-``__graft_entry__.build()``).  The library is written next to this file so
-that it travels with the source tree.
+Usage: ``python adamw_optimizer_step_apply_amd/build.py`` (also run by
+``__graft_entry__.build()``).  Run it as a script, not with ``-m``: importing
+it as a submodule would first run the package's ``__init__``, which loads the
+library this builds.  The library is written next to this file so that it
+travels with the source tree.
 """
 from __future__ import annotations
 

@@ -2,6 +2,7 @@
 // per-(device, stream) workspace, and the launch sequence
 //   [check: zero flag -> check kernel]   (adamw_check_finite)
 //   [step:  prologue  -> update kernel]  (adamw_step / adamw_multi_tensor_step)
+//   [step:  update kernel alone]         (the same, for plans of a few chunks)
 // Nothing here synchronises with the device except when a workspace has to
 // grow (the old buffer may still be read by work queued on its stream).
 #include <hip/hip_runtime.h>
@@ -28,7 +29,8 @@ hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32
                            LaunchScalars* d_scalars, adamw_loss_scale_state* d_amp, const adamw_loss_scaler& scaler,
                            hipStream_t stream);
 hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
-                         const LaunchScalars* d_scalars, hipStream_t stream);
+                         const LaunchScalars* d_scalars, const FusedStep* fused, hipStream_t stream);
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
 hipError_t launch_check(adamw_dtype g_dtype, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
                         int32_t* d_flag, hipStream_t stream);
 
@@ -87,7 +89,7 @@ constexpr size_t kPlansPerStream = 8;
 
 struct StreamWorkspace {
     int device = 0;                     // the stream's device: the workspace lives there
-    LaunchScalars* scalars = nullptr;   // device, kScalarsBytes
+    LaunchScalars* scalars = nullptr;   // device, kWorkspaceBytes: scalars, then the completion counters
     std::vector<std::unique_ptr<PlanSlot>> plans;
     std::mutex mu;                      // one call at a time per stream
 };
@@ -95,6 +97,9 @@ struct StreamWorkspace {
 std::mutex g_mu;
 std::map<std::pair<int, uintptr_t>, std::unique_ptr<StreamWorkspace>> g_ws;
 std::atomic<int64_t> g_chunk_elems{0};   // 0: each kernel's own default (its workgroup size x 8)
+// Plans of at most this many chunks run as one launch (the update kernel forms
+// the step's scalars itself) instead of prologue + update kernel.
+std::atomic<int64_t> g_single_launch_max_chunks{kSingleLaunchMaxChunks};
 
 // The workspace of a stream, on the stream's own device (the null stream
 // belongs to the calling thread's current device).
@@ -339,16 +344,36 @@ adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const 
     std::lock_guard<std::mutex> lk(ws->mu);
     DeviceGuard dg(ws->device);
     hipError_t e;
+    uint32_t* done = nullptr;
     if (!ws->scalars) {
-        e = hipMalloc(reinterpret_cast<void**>(&ws->scalars), kScalarsBytes);
+        e = hipMalloc(reinterpret_cast<void**>(&ws->scalars), kWorkspaceBytes);
         if (e != hipSuccess) { ws->scalars = nullptr; return fail(ADAMW_E_NOMEM, "hipMalloc of the scalar block failed"); }
+        // the single-launch form's counts of finished workgroups start at zero
+        // (and every such launch leaves them at zero)
+        done = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws->scalars) + kDoneOffset);
+        e = launch_zero_words(done, kDoneWords, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(ws->scalars);
+            ws->scalars = nullptr;
+            return hip_fail("workspace initialisation", e);
+        }
     }
+    done = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws->scalars) + kDoneOffset);
     PlanSlot* plan = nullptr;
     if ((st = ensure_plan(*ws, kind.kernel, kind.esz, list, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
+    // Small plans: one launch.  The dynamic loss scale, and an empty plan (whose
+    // step still advances the counter), keep the prologue kernel.
+    const int64_t single_max = g_single_launch_max_chunks.load(std::memory_order_relaxed);
+    if (!d_amp && plan->n_chunks > 0 && plan->n_chunks <= single_max) {
+        const FusedStep fs{*hp, d_step, d_found_inf, done};
+        e = launch_update(kind.kernel, plan->segs(), plan->chunks(), plan->n_chunks, nullptr, &fs, stream);
+        if (e != hipSuccess) return hip_fail("update launch", e);
+        return ADAMW_OK;
+    }
     const adamw_loss_scaler no_scaler{1.0f, 1.0f, 1};
     e = launch_prologue(*hp, d_step, d_found_inf, ws->scalars, d_amp, scaler ? *scaler : no_scaler, stream);
     if (e != hipSuccess) return hip_fail("prologue launch", e);
-    e = launch_update(kind.kernel, plan->segs(), plan->chunks(), plan->n_chunks, ws->scalars, stream);
+    e = launch_update(kind.kernel, plan->segs(), plan->chunks(), plan->n_chunks, ws->scalars, nullptr, stream);
     if (e != hipSuccess) return hip_fail("update launch", e);
     return ADAMW_OK;
 }
@@ -522,6 +547,13 @@ int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_ten
         r[5] = (int64_t)c.seg;
     }
     return n;
+}
+
+int64_t adamw_set_single_launch_max_chunks(int64_t max_chunks)
+{
+    const int64_t v = max_chunks < 0 ? kSingleLaunchMaxChunks : max_chunks;
+    g_single_launch_max_chunks.store(v, std::memory_order_relaxed);
+    return v;
 }
 
 int64_t adamw_set_chunk_elems(int64_t elems)

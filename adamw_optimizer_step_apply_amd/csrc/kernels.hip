@@ -11,7 +11,11 @@
 // Kernels:
 //   prologue_kernel      one lane: reads the skip flag and the step counter,
 //                        forms the step's scalars in binary64, advances the counter
-//   update_kernel<MODE>  one workgroup per chunk: the AdamW element update
+//   update_kernel<MODE, FUSED> / update_pure_kernel<M32, V32, KAHAN, FUSED>
+//                        one workgroup per chunk: the AdamW element update;
+//                        FUSED: without a prologue, for small plans (each
+//                        workgroup forms the scalars, the last one advances
+//                        the counter)
 //   zero_flag_kernel /
 //   check_kernel<F16>    the fp16-AMP overflow test (any inf/NaN gradient)
 //
@@ -167,6 +171,27 @@ __device__ double pow_sq(double b, int64_t t)
     return r;
 }
 
+// The scalars of step t: binary64 from +, -, *, / only, each rounded once to
+// binary32.  The prologue kernel and the single-launch form share this code.
+__device__ __forceinline__ Coef step_coef(const adamw_hparams& hp, int64_t t, float inv_scale)
+{
+    const double lr = (double)hp.lr, wd = (double)hp.weight_decay;
+    const double b1t = pow_sq((double)hp.beta1, t);
+    const double b2t = pow_sq((double)hp.beta2, t);
+    Coef c;
+    c.step_size = (float)(lr / (1.0 - b1t));
+    c.rbc2 = (float)(1.0 / (1.0 - b2t));
+    c.decay = (float)(1.0 - lr * wd);
+    c.lrwd = (float)(lr * wd);
+    c.omb1 = 1.0f - hp.beta1;
+    c.omb2 = 1.0f - hp.beta2;
+    c.beta1 = hp.beta1;
+    c.beta2 = hp.beta2;
+    c.eps = hp.eps;
+    c.inv_scale = inv_scale;
+    return c;
+}
+
 __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, const int32_t* __restrict__ found_inf,
                                 LaunchScalars* __restrict__ out, adamw_loss_scale_state* __restrict__ amp,
                                 adamw_loss_scaler scaler)
@@ -200,21 +225,19 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
         return;
     }
     const int64_t t = (int64_t)*step + 1;
-    const double lr = (double)hp.lr, wd = (double)hp.weight_decay;
-    const double b1t = pow_sq((double)hp.beta1, t);
-    const double b2t = pow_sq((double)hp.beta2, t);
+    const Coef c = step_coef(hp, t, inv_scale);
     s.skip = 0;
     s.t = (int32_t)t;
-    s.step_size = (float)(lr / (1.0 - b1t));
-    s.rbc2 = (float)(1.0 / (1.0 - b2t));
-    s.decay = (float)(1.0 - lr * wd);
-    s.lrwd = (float)(lr * wd);
-    s.omb1 = 1.0f - hp.beta1;
-    s.omb2 = 1.0f - hp.beta2;
-    s.beta1 = hp.beta1;
-    s.beta2 = hp.beta2;
-    s.eps = hp.eps;
-    s.inv_scale = inv_scale;
+    s.step_size = c.step_size;
+    s.rbc2 = c.rbc2;
+    s.decay = c.decay;
+    s.lrwd = c.lrwd;
+    s.omb1 = c.omb1;
+    s.omb2 = c.omb2;
+    s.beta1 = c.beta1;
+    s.beta2 = c.beta2;
+    s.eps = c.eps;
+    s.inv_scale = c.inv_scale;
     *out = s;
     *step = (int32_t)t;
 }
@@ -298,6 +321,63 @@ __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
     return c;
 }
 
+// Start of a step in an update kernel.  Two-launch form: the prologue kernel
+// has written the skip flag and the scalars.  Single launch: the workgroup
+// reads the flag and the counter itself; its scalars are formed by
+// fused_coef once its data loads are in flight.  Returns false on a skipped
+// step (uniform over the grid: nothing is written, the counter is kept).
+template <bool FUSED>
+__device__ __forceinline__ bool begin_step(const LaunchScalars* sc, const FusedStep& fs, Coef& c, int32_t& t)
+{
+    if constexpr (FUSED) {
+        if (fs.found_inf && *fs.found_inf != 0) return false;
+        t = *fs.step + 1;
+    } else {
+        if (sc->skip) return false;
+        c = load_coef(sc);
+    }
+    return true;
+}
+
+template <bool FUSED>
+__device__ __forceinline__ void fused_coef(const FusedStep& fs, int32_t t, Coef& c)
+{
+    if constexpr (FUSED) c = step_coef(fs.hp, t, fs.hp.inv_loss_scale);
+}
+
+// End of a single-launch step: once every wave of this workgroup is past its
+// read of the counter, one lane counts the workgroup in its first-level
+// counter (b % kDoneLanes); the workgroup completing a first-level count rearms
+// it and counts once in the second level, and the one completing that stores
+// the new step counter and rearms it.  Spreading the count over separate lines
+// keeps the same-address atomics, which the memory side serialises, to about
+// nb / kDoneLanes + kDoneLanes per launch.  The counts order nothing but those
+// reads (whose values every wave has consumed before the barrier), so the
+// atomics are relaxed: acquire-release ones at device scope would write back
+// and invalidate the XCD's L2 in every workgroup.
+template <bool FUSED>
+__device__ __forceinline__ void end_step(const FusedStep& fs, int32_t t)
+{
+    if constexpr (FUSED) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t nb = gridDim.x, b = blockIdx.x;
+            const uint32_t lanes = nb < (uint32_t)kDoneLanes ? nb : (uint32_t)kDoneLanes;
+            const uint32_t j = b % lanes;
+            const uint32_t in_lane = nb / lanes + (j < nb % lanes ? 1u : 0u);
+            uint32_t* first = fs.done + (size_t)j * kDoneStrideWords;
+            uint32_t* second = fs.done + (size_t)kDoneLanes * kDoneStrideWords;
+            if (__hip_atomic_fetch_add(first, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_lane - 1) {
+                __hip_atomic_store(first, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (__hip_atomic_fetch_add(second, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == lanes - 1) {
+                    __hip_atomic_store(fs.step, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(second, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    }
+}
+
 #ifndef ADAMW_WPE
 #define ADAMW_WPE 0
 #endif
@@ -309,16 +389,17 @@ __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
 
 // MODE 0: mixed bf16, 1: mixed fp16, 3: mixed bf16 with the master split into
 // param + int16 remainder
-template <int MODE>
+template <int MODE, bool FUSED>
 __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(const DevSeg* __restrict__ segs,
                                                         const DevChunk* __restrict__ chunks,
-                                                        const LaunchScalars* __restrict__ sc)
+                                                        const LaunchScalars* __restrict__ sc, FusedStep fs)
 {
-    if (sc->skip) return;
+    Coef c{};
+    int32_t t = 0;
+    if (!begin_step<FUSED>(sc, fs, c, t)) return;
     constexpr bool F16 = (MODE == 1);   // MODE 3 uses bf16 param/grad
     constexpr int NTM = ADAMW_NT_MIXED;
     constexpr int NTG = ADAMW_NT_MIXED | (ADAMW_NT_MIXED_GRAD ? 1 : 0);   // the gradient's loads
-    const Coef c = load_coef(sc);
     const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
     const DevSeg& sg = segs[ch.seg];
     const uint32_t n = ch.n_kind & kCountMask;
@@ -350,6 +431,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
                         V[u][0] = ld<NTM>(v4 + 2 * k); V[u][1] = ld<NTM>(v4 + 2 * k + 1);
                     }
                 }
+                fused_coef<FUSED>(fs, t, c);   // while the loads are in flight
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const uint32_t k = k0 + u * kBlockMixed;
@@ -381,6 +463,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
                 }
             }
         } else {
+            fused_coef<FUSED>(fs, t, c);
             for (uint32_t i = tid; i < n; i += kBlockMixed) {
                 float wi = __uint_as_float(join_bits(p[i], r[i])), mi = m[i], vi = v[i];
                 mixed_elem(widen1<false>(g[i]), wi, mi, vi, c);
@@ -418,6 +501,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
                         V[u][0] = ld<NTM>(v4 + 2 * k); V[u][1] = ld<NTM>(v4 + 2 * k + 1);
                     }
                 }
+                fused_coef<FUSED>(fs, t, c);   // while the loads are in flight
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const uint32_t k = k0 + u * kBlockMixed;
@@ -442,6 +526,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
                 }
             }
         } else {
+            fused_coef<FUSED>(fs, t, c);
             for (uint32_t i = tid; i < n; i += kBlockMixed) {
                 float wi = w[i], mi = m[i], vi = v[i];
                 const float nw = mixed_elem(widen1<F16>(g[i]), wi, mi, vi, c);
@@ -452,20 +537,23 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
             }
         }
     }
+    end_step<FUSED>(fs, t);
 }
 
 // Pure bf16 parameters with chosen state precisions: M32 / V32 = fp32 exp_avg /
 // exp_avg_sq (else bf16), KAHAN = bf16 compensation buffer in the aux stream
 // (else none: p' = round(p * decay - step_size * u)).  <false, false, true> is
 // the pure-bf16 Kahan mode.
-template <bool M32, bool V32, bool KAHAN>
+template <bool M32, bool V32, bool KAHAN, bool FUSED>
 __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(const DevSeg* __restrict__ segs,
                                                                             const DevChunk* __restrict__ chunks,
-                                                                            const LaunchScalars* __restrict__ sc)
+                                                                            const LaunchScalars* __restrict__ sc,
+                                                                            FusedStep fs)
 {
-    if (sc->skip) return;
+    Coef c{};
+    int32_t t = 0;
+    if (!begin_step<FUSED>(sc, fs, c, t)) return;
     constexpr int NT = ADAMW_NT_PURE;
-    const Coef c = load_coef(sc);
     const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
     const DevSeg& sg = segs[ch.seg];
     const uint32_t n = ch.n_kind & kCountMask;
@@ -503,6 +591,7 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
                     if constexpr (KAHAN) C[u] = ld<NT>(c4 + k);
                 }
             }
+            fused_coef<FUSED>(fs, t, c);   // while the loads are in flight
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const uint32_t k = k0 + u * kBlockPure;
@@ -571,6 +660,7 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
             }
         }
     } else {
+        fused_coef<FUSED>(fs, t, c);
         for (uint32_t i = tid; i < n; i += kBlockPure) {
             const float pf = widen1<false>(p[i]);
             float mi, vi;
@@ -592,6 +682,7 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
             if constexpr (V32) v[i] = vi; else v[i] = narrow1<false>(vi);
         }
     }
+    end_step<FUSED>(fs, t);
 }
 
 // ---------------------------------------------------------------------------
@@ -673,25 +764,27 @@ hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32
 #define ADAMW_LDS_PURE 40960
 #endif
 
-hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
-                         const LaunchScalars* d_scalars, hipStream_t stream)
+// Two-launch form (fused == nullptr): the update kernel reads the prologue's
+// scalars at d_scalars.  Single launch: the kernel forms them from *fused.
+template <bool FUSED>
+static hipError_t launch_update_as(int kernel, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
+                                   const LaunchScalars* d_scalars, const FusedStep& fs, hipStream_t stream)
 {
-    if (n_chunks <= 0) return hipSuccess;
     const dim3 grid((unsigned)n_chunks), block(kBlockMixed), block_pure(kBlockPure);
     switch (kernel) {
     case kKernelMixedBf16:
-        hipLaunchKernelGGL(update_kernel<0>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
+        hipLaunchKernelGGL((update_kernel<0, FUSED>), grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars, fs);
         break;
     case kKernelMixedF16:
-        hipLaunchKernelGGL(update_kernel<1>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
+        hipLaunchKernelGGL((update_kernel<1, FUSED>), grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars, fs);
         break;
     case kKernelSplit:
-        hipLaunchKernelGGL(update_kernel<3>, grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars);
+        hipLaunchKernelGGL((update_kernel<3, FUSED>), grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars, fs);
         break;
 #define ADAMW_PURE_CASE(M, V, K)                                                                          \
     case kKernelPure + (M) * 4 + (V) * 2 + (K):                                                            \
-        hipLaunchKernelGGL((update_pure_kernel<M, V, K>), grid, block_pure, ADAMW_LDS_PURE, stream, segs, chunks, \
-                           d_scalars);                                                                     \
+        hipLaunchKernelGGL((update_pure_kernel<M, V, K, FUSED>), grid, block_pure, ADAMW_LDS_PURE, stream, segs, \
+                           chunks, d_scalars, fs);                                                         \
         break;
         ADAMW_PURE_CASE(0, 0, 0) ADAMW_PURE_CASE(0, 0, 1) ADAMW_PURE_CASE(0, 1, 0) ADAMW_PURE_CASE(0, 1, 1)
         ADAMW_PURE_CASE(1, 0, 0) ADAMW_PURE_CASE(1, 0, 1) ADAMW_PURE_CASE(1, 1, 0) ADAMW_PURE_CASE(1, 1, 1)
@@ -699,6 +792,27 @@ hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks,
     default:
         return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
+                         const LaunchScalars* d_scalars, const FusedStep* fused, hipStream_t stream)
+{
+    if (n_chunks <= 0) return hipSuccess;
+    if (fused) return launch_update_as<true>(kernel, segs, chunks, n_chunks, nullptr, *fused, stream);
+    return launch_update_as<false>(kernel, segs, chunks, n_chunks, d_scalars, FusedStep{}, stream);
+}
+
+__global__ void zero_words_kernel(uint32_t* __restrict__ p, int64_t n)
+{
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// Zeroes n 32-bit words (a fill kernel rather than a memset, so that it may
+// sit in a captured graph).
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream)
+{
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, stream, p, n);
     return hipGetLastError();
 }
 

@@ -477,3 +477,15 @@ def test_many_tiny_tensors_count_one_chunk_each():
     assert len(rows) == len(numels)
     assert all(r[3] == 0 for r in rows)
     assert [r[2] for r in rows] == numels
+
+
+def test_single_launch_limit_knob():
+    """The single-launch limit: any value >= 0 is taken as given, a negative one
+    restores the default (4096 chunks), and the call needs no GPU."""
+    try:
+        assert A.adamw_set_single_launch_max_chunks(0) == 0
+        assert A.adamw_set_single_launch_max_chunks(123) == 123
+        assert A.adamw_set_single_launch_max_chunks(-1) == 4096
+        assert A.adamw_set_single_launch_max_chunks(-7) == 4096
+    finally:
+        A.adamw_set_single_launch_max_chunks(-1)

@@ -1,0 +1,129 @@
+"""GPU: the two launch forms of a step give the same bits.  Plans of at most
+adamw_set_single_launch_max_chunks chunks run as one launch of the update
+kernel, which forms the step's scalars in every workgroup and lets the last
+workgroup advance the counter; larger plans run the prologue kernel first.
+Every element, the counter and the skip behaviour must not depend on the form,
+and both must match the oracle."""
+import pytest
+import torch
+
+import adamw_optimizer_step_apply_amd as A
+from gpu_util import Case, free, hp_pair, same_bits
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [0, 1, 7, 8, 9, 2047, 2048, 2049, 16385, 100_003, 3, 40_000]
+
+
+@pytest.fixture
+def single_launch_limit():
+    """Sets the single-launch limit for one test and restores the default."""
+    def set_limit(n):
+        return A.adamw_set_single_launch_max_chunks(n)
+    yield set_limit
+    A.adamw_set_single_launch_max_chunks(-1)
+
+
+def _plan_chunks(case: Case) -> int:
+    """Chunks of the case's plan (mixed, kahan and split lists)."""
+    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[case.mode]
+    dt = A.F16 if case.p_dtype == "f16" else A.BF16
+    return len(A.adamw_plan_inspect(code, dt, case.tensor_list()))
+
+
+@pytest.mark.parametrize("mode,p_dtype", [("mixed", "bf16"), ("mixed", "f16"), ("kahan", "bf16"), ("split", "bf16"),
+                                          ("pure-f32-f32-k", "bf16"), ("pure-bf16-f32-n", "bf16")])
+def test_forms_are_bit_identical_and_match_the_oracle(mode, p_dtype, single_launch_limit):
+    """The same list stepped 4 times in each form (one copy each), a skipped step
+    in the middle: every buffer and the counter bitwise equal between the forms,
+    and the single-launch copy within the bar of the oracle."""
+    scale = 65536.0 if p_dtype == "f16" else 1.0
+    kw = dict(p_dtype=p_dtype, align_elems=3, loss_scale=scale, random_moments=True)
+    one, two = Case(mode, SIZES, seed=911, **kw), Case(mode, SIZES, seed=911, **kw)
+    if not mode.startswith("pure"):
+        assert 0 < _plan_chunks(one) <= 4096
+    hg, ho = hp_pair(inv_scale=1.0 / scale)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for s in range(5):
+        if s:
+            one.refill_grads(s)
+            two.refill_grads(s)
+        flag.fill_(1 if s == 2 else 0)
+        single_launch_limit(-1)
+        one.gpu_step(hg, found_inf=flag)
+        single_launch_limit(0)
+        two.gpu_step(hg, found_inf=flag)
+        if s != 2:
+            one.oracle_step(ho)
+    torch.cuda.synchronize()
+    assert int(one.d_step.item()) == int(two.d_step.item()) == 4
+    for k in one.keys:
+        assert same_bits(one.arena.bufs[k], two.arena.bufs[k]), f"{mode}: stream {k} differs between the forms"
+    one.compare_all(f"single-launch-{mode}-{p_dtype}")
+    free()
+
+
+@pytest.mark.parametrize("extra", [0, 1])
+def test_limit_boundary(extra, single_launch_limit):
+    """A plan of exactly the limit runs as one launch; one chunk more takes the
+    prologue.  Both match the oracle over 3 steps."""
+    case = Case("mixed", SIZES, seed=912, align_elems=3, random_moments=True)
+    k = _plan_chunks(case)
+    single_launch_limit(k - extra)
+    hg, ho = hp_pair()
+    for s in range(3):
+        if s:
+            case.refill_grads(s)
+        case.gpu_step(hg)
+        case.oracle_step(ho)
+    case.compare_all(f"boundary-{extra}")
+    free()
+
+
+def test_forms_alternate_on_one_stream(single_launch_limit):
+    """Two lists on one stream, stepped in turn while the form changes every
+    call: the single-launch completion count must be back at zero after each
+    launch, and each counter must advance once per step."""
+    a = Case("mixed", SIZES, seed=913, random_moments=True)
+    b = Case("kahan", [5000, 70, 4099, 1], seed=914, random_moments=True)
+    hg, ho = hp_pair()
+    for s in range(8):
+        for i, case in enumerate((a, b)):
+            if s:
+                case.refill_grads(s)
+            single_launch_limit(-1 if (s + i) % 2 == 0 else 0)
+            case.gpu_step(hg)
+            case.oracle_step(ho)
+    a.compare_all("alternate-mixed")
+    b.compare_all("alternate-kahan")
+    free()
+
+
+def test_single_launch_graph_replays(single_launch_limit):
+    """A single-launch step captured in a HIP graph and replayed 5 times, with
+    eager work between the replays, equals 5 eager steps bit for bit."""
+    single_launch_limit(-1)
+    numels = [5000, 70, 4099, 1, 20000]
+    eager, graphed = Case("mixed", numels, seed=915), Case("mixed", numels, seed=915)
+    hg, _ = hp_pair()
+    tl_e, tl_g = eager.tensor_list(), graphed.tensor_list()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        # one warm-up call on the capture stream builds its workspace and plan
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl_g, hg, graphed.d_step, None, s)
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl_e, hg, eager.d_step, None, s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl_g, hg, graphed.d_step, None, s)
+    for r in range(5):
+        g.replay()
+        with torch.cuda.stream(s):
+            A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl_e, hg, eager.d_step, None, s)
+        torch.cuda.synchronize()
+        _ = torch.ones(1 << 20, device="cuda").sum().item()   # unrelated eager work between replays
+        assert int(graphed.d_step.item()) == int(eager.d_step.item()) == r + 2
+        for k in eager.keys:
+            assert same_bits(graphed.arena.bufs[k], eager.arena.bufs[k]), (r, k)
+    del g
+    free()
