@@ -89,16 +89,27 @@ def calib_copy():
 
 CALIB_COPY_BYTES = 4 << 30
 # the kernel each timed mode launches, as rocprofv3 names it (a substring of the symbol)
-KERNEL_OF = {"mixed": "update_kernel<0>", "split": "update_kernel<3>",
-             "kahan": "update_pure_kernel<false, false, true>", "f16amp": "update_kernel<1>",
+# the timed kernel of each mode, as a prefix of its name in rocprofv3 output (the
+# last template argument, the launch form, is left open)
+KERNEL_OF = {"mixed": "update_kernel<0,", "split": "update_kernel<3,",
+             "kahan": "update_pure_kernel<false, false, true,", "f16amp": "update_kernel<1,",
              "check": "check_kernel"}
 
 
-def _pmc_values(path, counter, kernel):
+def _pmc_rows(path, counter, kernel):
     import csv
     with open(path) as f:
-        return [float(r["Counter_Value"]) for r in csv.DictReader(f)
-                if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+        return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+
+
+def _pmc_values(path, counter, kernel):
+    return [float(r["Counter_Value"]) for r in _pmc_rows(path, counter, kernel)]
+
+
+def _kernel_name(path, counter, kernel):
+    """The full kernel name (without its argument list) matched by `kernel`."""
+    names = {r["Kernel_Name"].split("(")[0].replace("void ", "") for r in _pmc_rows(path, counter, kernel)}
+    return " / ".join(sorted(names))
 
 
 def write_traffic(wl_name, modes, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
@@ -133,7 +144,8 @@ def write_traffic(wl_name, modes, fetch_csv, write_csv, cal_fetch_csv, cal_write
         traffic[mode] = round(rd + wr)
         alg[mode] = BYTES[mode[:-len("-blocked")] if mode.endswith("-blocked") else mode] * n
         per_param[mode] = {"read": round(rd / n, 4), "write": round(wr / n, 4)}
-        raw[mode] = {"kernel": kernel, "FETCH_SIZE_KiB": fv, "WRITE_SIZE_KiB": wv}
+        raw[mode] = {"kernel": _kernel_name(fetch_csv, "FETCH_SIZE", kernel), "FETCH_SIZE_KiB": fv,
+                     "WRITE_SIZE_KiB": wv}
     if not traffic:
         raise SystemExit("no timed kernel found in the counter files")
     out = {"about": f"HBM bytes per launch on the {wl_name} list from two rocprofv3 --pmc passes (FETCH_SIZE, "
