@@ -68,9 +68,15 @@
  * thread's current device) and the call returns without synchronising.  Every
  * buffer must live on the stream's device.  The library owns only a small
  * device workspace per (device, stream), on the stream's device, holding the
- * launch scalars and the chunk table, grown on demand and kept until
- * adamw_release_workspace().  The host
- * arrays inside adamw_tensor_list are read during the call only.
+ * launch scalars, the single-launch completion counters (about 8.7 KB) and the
+ * chunk table, grown on demand and kept until adamw_release_workspace().  The
+ * host arrays inside adamw_tensor_list are read during the call only.
+ *
+ * HIP graphs.  After one call on a stream with a given list (which allocates
+ * the workspace and uploads the list's chunk table), the same call captured on
+ * that stream records kernel launches only: no allocation, copy or memset.
+ * A captured step may be replayed any number of times; it reads the workspace,
+ * so adamw_release_workspace() must not run while such a graph is in use.
  *
  * Errors.  Arguments are validated before anything is enqueued; on an error
  * nothing is enqueued, no buffer is touched, and adamw_last_error() describes
