@@ -327,11 +327,11 @@ __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
 // fused_coef once its data loads are in flight.  Returns false on a skipped
 // step (uniform over the grid: nothing is written, the counter is kept).
 template <bool FUSED>
-__device__ __forceinline__ bool begin_step(const LaunchScalars* sc, const FusedStep& fs, Coef& c, int32_t& t)
+__device__ __forceinline__ bool begin_step(const LaunchScalars* sc, const FusedStep& fs, Coef& c, int64_t& t)
 {
     if constexpr (FUSED) {
         if (fs.found_inf && *fs.found_inf != 0) return false;
-        t = *fs.step + 1;
+        t = (int64_t)*fs.step + 1;   // as the prologue: no int32 overflow in the scalars
     } else {
         if (sc->skip) return false;
         c = load_coef(sc);
@@ -340,7 +340,7 @@ __device__ __forceinline__ bool begin_step(const LaunchScalars* sc, const FusedS
 }
 
 template <bool FUSED>
-__device__ __forceinline__ void fused_coef(const FusedStep& fs, int32_t t, Coef& c)
+__device__ __forceinline__ void fused_coef(const FusedStep& fs, int64_t t, Coef& c)
 {
     if constexpr (FUSED) c = step_coef(fs.hp, t, fs.hp.inv_loss_scale);
 }
@@ -356,7 +356,7 @@ __device__ __forceinline__ void fused_coef(const FusedStep& fs, int32_t t, Coef&
 // atomics are relaxed: acquire-release ones at device scope would write back
 // and invalidate the XCD's L2 in every workgroup.
 template <bool FUSED>
-__device__ __forceinline__ void end_step(const FusedStep& fs, int32_t t)
+__device__ __forceinline__ void end_step(const FusedStep& fs, int64_t t)
 {
     if constexpr (FUSED) {
         __syncthreads();
@@ -370,7 +370,7 @@ __device__ __forceinline__ void end_step(const FusedStep& fs, int32_t t)
             if (__hip_atomic_fetch_add(first, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_lane - 1) {
                 __hip_atomic_store(first, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (__hip_atomic_fetch_add(second, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == lanes - 1) {
-                    __hip_atomic_store(fs.step, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(fs.step, (int32_t)t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     __hip_atomic_store(second, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
                                                         const LaunchScalars* __restrict__ sc, FusedStep fs)
 {
     Coef c{};
-    int32_t t = 0;
+    int64_t t = 0;
     if (!begin_step<FUSED>(sc, fs, c, t)) return;
     constexpr bool F16 = (MODE == 1);   // MODE 3 uses bf16 param/grad
     constexpr int NTM = ADAMW_NT_MIXED;
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
                                                                             FusedStep fs)
 {
     Coef c{};
-    int32_t t = 0;
+    int64_t t = 0;
     if (!begin_step<FUSED>(sc, fs, c, t)) return;
     constexpr int NT = ADAMW_NT_PURE;
     const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];

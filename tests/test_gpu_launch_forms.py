@@ -127,3 +127,30 @@ def test_single_launch_graph_replays(single_launch_limit):
             assert same_bits(graphed.arena.bufs[k], eager.arena.bufs[k]), (r, k)
     del g
     free()
+
+
+@pytest.mark.parametrize("start", [999_999, 2**31 - 3])
+def test_forms_agree_at_large_step_counts(start, single_launch_limit):
+    """Resuming at a large step counter: both forms form the same scalars (the
+    bias corrections are then 1 to within fp32) and store the same counter,
+    and both match the oracle, for 2 steps."""
+    one, two = (Case("mixed", SIZES, seed=916, random_moments=True) for _ in range(2))
+    for c in (one, two):
+        c.d_step.fill_(start)
+        c.step = start
+    hg, ho = hp_pair()
+    for s in range(2):
+        if s:
+            one.refill_grads(s)
+            two.refill_grads(s)
+        single_launch_limit(-1)
+        one.gpu_step(hg)
+        single_launch_limit(0)
+        two.gpu_step(hg)
+        one.oracle_step(ho)
+        two.oracle_step(ho)
+    one.compare_all(f"large-step-single-{start}")
+    two.compare_all(f"large-step-two-{start}")
+    for k in one.keys:
+        assert same_bits(one.arena.bufs[k], two.arena.bufs[k]), k
+    free()
