@@ -75,8 +75,12 @@
  * HIP graphs.  After one call on a stream with a given list (which allocates
  * the workspace and uploads the list's chunk table), the same call captured on
  * that stream records kernel launches only: no allocation, copy or memset.
- * A captured step may be replayed any number of times; it reads the workspace,
- * so adamw_release_workspace() must not run while such a graph is in use.
+ * A captured step may be replayed any number of times.  It uses the capture
+ * stream's workspace (launch scalars, completion counters, chunk table), so
+ * adamw_release_workspace() must not run while such a graph is in use, and a
+ * replay must not overlap other work that uses that workspace: steps enqueued
+ * on the capture stream, or replays of other graphs captured on it.  Replaying
+ * on the capture stream itself keeps all of these in stream order.
  *
  * Errors.  Arguments are validated before anything is enqueued; on an error
  * nothing is enqueued, no buffer is touched, and adamw_last_error() describes
