@@ -1,8 +1,9 @@
 // api.cpp -- the C ABI declared in include/adamw.h: validation, plan caching,
 // per-(device, stream) workspace, and the launch sequence
 //   [check: zero flag -> check kernel]   (adamw_check_finite)
-//   [step:  prologue  -> update kernel]  (adamw_step / adamw_multi_tensor_step)
-//   [step:  update kernel alone]         (the same, for plans of a few chunks)
+//   [step:  prologue  -> update kernel]  (adamw_step / adamw_multi_tensor_step[_amp])
+//   small plans (up to a few thousand chunks): the check kernel alone, the
+//   update kernel alone
 // Nothing here synchronises with the device except when a workspace has to
 // grow (the old buffer may still be read by work queued on its stream).
 #include <hip/hip_runtime.h>
@@ -32,7 +33,7 @@ hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks,
                          const LaunchScalars* d_scalars, const FusedStep* fused, hipStream_t stream);
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
 hipError_t launch_check(adamw_dtype g_dtype, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
-                        int32_t* d_flag, hipStream_t stream);
+                        int32_t* d_flag, uint32_t* done, bool fused, hipStream_t stream);
 
 namespace {
 
@@ -294,6 +295,31 @@ adamw_status check_scaler(const adamw_loss_scaler* sc)
     return ADAMW_OK;
 }
 
+// The stream's 256-byte scalar block and the single-launch completion counters
+// after it, allocated on first use (the counters start at zero, and every
+// single launch leaves them at zero).  Returns the counters in *done.
+adamw_status ensure_workspace_block(StreamWorkspace& ws, hipStream_t stream, uint32_t** done)
+{
+    if (!ws.scalars) {
+        hipError_t e = hipMalloc(reinterpret_cast<void**>(&ws.scalars), kWorkspaceBytes);
+        if (e != hipSuccess) { ws.scalars = nullptr; return fail(ADAMW_E_NOMEM, "hipMalloc of the scalar block failed"); }
+        uint32_t* d = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws.scalars) + kDoneOffset);
+        e = launch_zero_words(d, kDoneWords, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(ws.scalars);
+            ws.scalars = nullptr;
+            return hip_fail("workspace initialisation", e);
+        }
+    }
+    *done = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws.scalars) + kDoneOffset);
+    return ADAMW_OK;
+}
+
+bool single_launch(int64_t n_chunks)
+{
+    return n_chunks > 0 && n_chunks <= g_single_launch_max_chunks.load(std::memory_order_relaxed);
+}
+
 // What one step launches: the update kernel and its streams' element sizes.
 struct StepKind {
     int kernel;
@@ -345,27 +371,13 @@ adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const 
     DeviceGuard dg(ws->device);
     hipError_t e;
     uint32_t* done = nullptr;
-    if (!ws->scalars) {
-        e = hipMalloc(reinterpret_cast<void**>(&ws->scalars), kWorkspaceBytes);
-        if (e != hipSuccess) { ws->scalars = nullptr; return fail(ADAMW_E_NOMEM, "hipMalloc of the scalar block failed"); }
-        // the single-launch form's counts of finished workgroups start at zero
-        // (and every such launch leaves them at zero)
-        done = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws->scalars) + kDoneOffset);
-        e = launch_zero_words(done, kDoneWords, stream);
-        if (e != hipSuccess) {
-            (void)hipFree(ws->scalars);
-            ws->scalars = nullptr;
-            return hip_fail("workspace initialisation", e);
-        }
-    }
-    done = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws->scalars) + kDoneOffset);
+    if ((st = ensure_workspace_block(*ws, stream, &done)) != ADAMW_OK) return st;
     PlanSlot* plan = nullptr;
     if ((st = ensure_plan(*ws, kind.kernel, kind.esz, list, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
-    // Small plans: one launch.  The dynamic loss scale, and an empty plan (whose
-    // step still advances the counter), keep the prologue kernel.
-    const int64_t single_max = g_single_launch_max_chunks.load(std::memory_order_relaxed);
-    if (!d_amp && plan->n_chunks > 0 && plan->n_chunks <= single_max) {
-        const FusedStep fs{*hp, d_step, d_found_inf, done};
+    // Small plans: one launch.  An empty plan, whose step still advances the
+    // counter (and the loss scale), keeps the prologue kernel.
+    if (single_launch(plan->n_chunks)) {
+        const FusedStep fs{*hp, d_step, d_found_inf, done, d_amp, scaler ? *scaler : adamw_loss_scaler{1.0f, 1.0f, 1}};
         e = launch_update(kind.kernel, plan->segs(), plan->chunks(), plan->n_chunks, nullptr, &fs, stream);
         if (e != hipSuccess) return hip_fail("update launch", e);
         return ADAMW_OK;
@@ -494,9 +506,12 @@ adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* gr
     if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
     std::lock_guard<std::mutex> lk(ws->mu);
     DeviceGuard dg(ws->device);
+    uint32_t* done = nullptr;
+    if ((st = ensure_workspace_block(*ws, stream, &done)) != ADAMW_OK) return st;
     PlanSlot* plan = nullptr;
     if ((st = ensure_plan(*ws, -1, esz, grads, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
-    hipError_t e = launch_check(g_dtype, plan->segs(), plan->chunks(), plan->n_chunks, d_found_inf, stream);
+    hipError_t e = launch_check(g_dtype, plan->segs(), plan->chunks(), plan->n_chunks, d_found_inf, done,
+                                single_launch(plan->n_chunks), stream);
     if (e != hipSuccess) return hip_fail("check launch", e);
     return ADAMW_OK;
 }

@@ -17,7 +17,8 @@
 //                        workgroup forms the scalars, the last one advances
 //                        the counter)
 //   zero_flag_kernel /
-//   check_kernel<F16>    the fp16-AMP overflow test (any inf/NaN gradient)
+//   check_kernel<F16, FUSED>  the fp16-AMP overflow test (any inf/NaN gradient);
+//                        FUSED: one launch that also sets the flag to 0 or 1
 //
 // Element rule (the AdamW of Loshchilov & Hutter, Algorithm 2, with Adam's bias
 // correction from Kingma & Ba, Algorithm 1; named on the pages "Distributed
@@ -192,6 +193,28 @@ __device__ __forceinline__ Coef step_coef(const adamw_hparams& hp, int64_t t, fl
     return c;
 }
 
+// The dynamic loss-scaling rule, applied once per step after the step's
+// unscale factor 1/scale has been read: back off on an overflow, grow after
+// growth_interval clean steps in a row (a growth that would overflow binary32
+// is refused).  One lane of the grid runs it.
+__device__ __forceinline__ void advance_loss_scale(adamw_loss_scale_state* amp, const adamw_loss_scaler& scaler,
+                                                   float scale, bool skip)
+{
+    if (skip) {
+        amp->scale = scale * scaler.backoff_factor;
+        amp->growth_tracker = 0;
+    } else {
+        const int32_t run = amp->growth_tracker + 1;
+        if (run == scaler.growth_interval) {
+            const float grown = scale * scaler.growth_factor;
+            if (__builtin_isfinite(grown)) amp->scale = grown;
+            amp->growth_tracker = 0;
+        } else {
+            amp->growth_tracker = run;
+        }
+    }
+}
+
 __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, const int32_t* __restrict__ found_inf,
                                 LaunchScalars* __restrict__ out, adamw_loss_scale_state* __restrict__ amp,
                                 adamw_loss_scaler scaler)
@@ -205,19 +228,7 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
         // follows from the flag
         const float scale = amp->scale;
         inv_scale = (float)(1.0 / (double)scale);
-        if (skip) {
-            amp->scale = scale * scaler.backoff_factor;
-            amp->growth_tracker = 0;
-        } else {
-            const int32_t run = amp->growth_tracker + 1;
-            if (run == scaler.growth_interval) {
-                const float grown = scale * scaler.growth_factor;
-                if (__builtin_isfinite(grown)) amp->scale = grown;
-                amp->growth_tracker = 0;
-            } else {
-                amp->growth_tracker = run;
-            }
-        }
+        advance_loss_scale(amp, scaler, scale, skip);
     }
     if (skip) {
         s.skip = 1;
@@ -323,15 +334,27 @@ __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
 
 // Start of a step in an update kernel.  Two-launch form: the prologue kernel
 // has written the skip flag and the scalars.  Single launch: the workgroup
-// reads the flag and the counter itself; its scalars are formed by
-// fused_coef once its data loads are in flight.  Returns false on a skipped
-// step (uniform over the grid: nothing is written, the counter is kept).
+// reads the flag, the counter and (with a dynamic loss scale) the scale
+// itself; its scalars are formed by fused_coef once its data loads are in
+// flight.  Returns false on a skipped step (uniform over the grid: nothing is
+// written, the counter is kept; workgroup 0 backs the loss scale off).
 template <bool FUSED>
-__device__ __forceinline__ bool begin_step(const LaunchScalars* sc, const FusedStep& fs, Coef& c, int64_t& t)
+__device__ __forceinline__ bool begin_step(const LaunchScalars* sc, const FusedStep& fs, Coef& c, int64_t& t,
+                                           float& scale)
 {
     if constexpr (FUSED) {
-        if (fs.found_inf && *fs.found_inf != 0) return false;
-        t = (int64_t)*fs.step + 1;   // as the prologue: no int32 overflow in the scalars
+        // All three reads come before the one store a workgroup may make here,
+        // so that the compiler can issue them as scalar loads (a store ahead of
+        // a load in the kernel would turn it into a vector load with a full
+        // wait before the data loads start).
+        const int32_t flag = fs.found_inf ? *fs.found_inf : 0;
+        const int32_t step = *fs.step;
+        scale = fs.amp ? fs.amp->scale : 0.0f;
+        if (flag != 0) {
+            if (fs.amp && blockIdx.x == 0 && threadIdx.x == 0) advance_loss_scale(fs.amp, fs.scaler, scale, true);
+            return false;
+        }
+        t = (int64_t)step + 1;   // as the prologue: no int32 overflow in the scalars
     } else {
         if (sc->skip) return false;
         c = load_coef(sc);
@@ -340,40 +363,80 @@ __device__ __forceinline__ bool begin_step(const LaunchScalars* sc, const FusedS
 }
 
 template <bool FUSED>
-__device__ __forceinline__ void fused_coef(const FusedStep& fs, int64_t t, Coef& c)
+__device__ __forceinline__ void fused_coef(const FusedStep& fs, int64_t t, float scale, Coef& c)
 {
-    if constexpr (FUSED) c = step_coef(fs.hp, t, fs.hp.inv_loss_scale);
+    if constexpr (FUSED) c = step_coef(fs.hp, t, fs.amp ? (float)(1.0 / (double)scale) : fs.hp.inv_loss_scale);
+}
+
+// The grid's completion count, shared by the single-launch kernels.  Each
+// workgroup counts itself in a first-level counter (b % kDoneLanes); the
+// workgroup completing a first-level count rearms it and counts once in the
+// second level, and the one completing that rearms it and returns true.
+// Spreading the count over separate 256-byte lines keeps the same-address
+// atomics, which the memory side serialises, to about nb / kDoneLanes +
+// kDoneLanes per launch.  The counts order nothing but reads that every wave
+// has consumed before the workgroup's barrier, so the atomics are relaxed:
+// acquire-release ones at device scope would write back and invalidate the
+// XCD's L2 in every workgroup.
+struct DoneLane {
+    uint32_t lanes, j, in_lane;
+};
+
+__device__ __forceinline__ DoneLane done_lane()
+{
+    const uint32_t nb = gridDim.x, b = blockIdx.x;
+    const uint32_t lanes = nb < (uint32_t)kDoneLanes ? nb : (uint32_t)kDoneLanes;
+    const uint32_t j = b % lanes;
+    return DoneLane{lanes, j, nb / lanes + (j < nb % lanes ? 1u : 0u)};
+}
+
+// The count alone, on 32-bit words (the low words of the counter lines).
+__device__ __forceinline__ bool grid_done(uint32_t* done)
+{
+    const DoneLane d = done_lane();
+    uint32_t* first = done + (size_t)d.j * kDoneStrideWords;
+    uint32_t* second = done + (size_t)kDoneLanes * kDoneStrideWords;
+    if (__hip_atomic_fetch_add(first, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != d.in_lane - 1) return false;
+    __hip_atomic_store(first, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_fetch_add(second, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != d.lanes - 1) return false;
+    __hip_atomic_store(second, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
+// The count with a 0/1 verdict per workgroup, on 64-bit words: the count in the
+// low half and the number of raised verdicts in the high half, so the verdicts
+// travel in the atomics' own values.  The completer gets the number of lanes
+// with a raised verdict in *lanes_hit.  Both forms leave every counter word at
+// zero, so the update and check kernels of one stream share the lines.
+__device__ __forceinline__ bool grid_done_verdict(uint32_t* done, uint32_t verdict, uint32_t* lanes_hit)
+{
+    const DoneLane d = done_lane();
+    uint64_t* first = reinterpret_cast<uint64_t*>(done + (size_t)d.j * kDoneStrideWords);
+    uint64_t* second = reinterpret_cast<uint64_t*>(done + (size_t)kDoneLanes * kDoneStrideWords);
+    const uint64_t prev = __hip_atomic_fetch_add(first, 1ull + ((uint64_t)verdict << 32), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)prev != d.in_lane - 1) return false;
+    __hip_atomic_store(first, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hit = ((prev >> 32) + verdict) != 0 ? 1ull : 0ull;
+    const uint64_t prev2 = __hip_atomic_fetch_add(second, 1ull + (hit << 32), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)prev2 != d.lanes - 1) return false;
+    __hip_atomic_store(second, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lanes_hit = (uint32_t)(prev2 >> 32) + (uint32_t)hit;
+    return true;
 }
 
 // End of a single-launch step: once every wave of this workgroup is past its
-// read of the counter, one lane counts the workgroup in its first-level
-// counter (b % kDoneLanes); the workgroup completing a first-level count rearms
-// it and counts once in the second level, and the one completing that stores
-// the new step counter and rearms it.  Spreading the count over separate lines
-// keeps the same-address atomics, which the memory side serialises, to about
-// nb / kDoneLanes + kDoneLanes per launch.  The counts order nothing but those
-// reads (whose values every wave has consumed before the barrier), so the
-// atomics are relaxed: acquire-release ones at device scope would write back
-// and invalidate the XCD's L2 in every workgroup.
+// reads of the counter and the loss scale, one lane counts the workgroup; the
+// last one of the grid stores the new counter and advances the loss scale.
 template <bool FUSED>
-__device__ __forceinline__ void end_step(const FusedStep& fs, int64_t t)
+__device__ __forceinline__ void end_step(const FusedStep& fs, int64_t t, float scale)
 {
     if constexpr (FUSED) {
         __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t nb = gridDim.x, b = blockIdx.x;
-            const uint32_t lanes = nb < (uint32_t)kDoneLanes ? nb : (uint32_t)kDoneLanes;
-            const uint32_t j = b % lanes;
-            const uint32_t in_lane = nb / lanes + (j < nb % lanes ? 1u : 0u);
-            uint32_t* first = fs.done + (size_t)j * kDoneStrideWords;
-            uint32_t* second = fs.done + (size_t)kDoneLanes * kDoneStrideWords;
-            if (__hip_atomic_fetch_add(first, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_lane - 1) {
-                __hip_atomic_store(first, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (__hip_atomic_fetch_add(second, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == lanes - 1) {
-                    __hip_atomic_store(fs.step, (int32_t)t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(second, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
+        if (threadIdx.x == 0 && grid_done(fs.done)) {
+            __hip_atomic_store(fs.step, (int32_t)t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (fs.amp) advance_loss_scale(fs.amp, fs.scaler, scale, false);
         }
     }
 }
@@ -396,7 +459,8 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
 {
     Coef c{};
     int64_t t = 0;
-    if (!begin_step<FUSED>(sc, fs, c, t)) return;
+    float scale = 0.0f;
+    if (!begin_step<FUSED>(sc, fs, c, t, scale)) return;
     constexpr bool F16 = (MODE == 1);   // MODE 3 uses bf16 param/grad
     constexpr int NTM = ADAMW_NT_MIXED;
     constexpr int NTG = ADAMW_NT_MIXED | (ADAMW_NT_MIXED_GRAD ? 1 : 0);   // the gradient's loads
@@ -431,7 +495,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
                         V[u][0] = ld<NTM>(v4 + 2 * k); V[u][1] = ld<NTM>(v4 + 2 * k + 1);
                     }
                 }
-                fused_coef<FUSED>(fs, t, c);   // while the loads are in flight
+                fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const uint32_t k = k0 + u * kBlockMixed;
@@ -463,7 +527,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
                 }
             }
         } else {
-            fused_coef<FUSED>(fs, t, c);
+            fused_coef<FUSED>(fs, t, scale, c);
             for (uint32_t i = tid; i < n; i += kBlockMixed) {
                 float wi = __uint_as_float(join_bits(p[i], r[i])), mi = m[i], vi = v[i];
                 mixed_elem(widen1<false>(g[i]), wi, mi, vi, c);
@@ -501,7 +565,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
                         V[u][0] = ld<NTM>(v4 + 2 * k); V[u][1] = ld<NTM>(v4 + 2 * k + 1);
                     }
                 }
-                fused_coef<FUSED>(fs, t, c);   // while the loads are in flight
+                fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const uint32_t k = k0 + u * kBlockMixed;
@@ -526,7 +590,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
                 }
             }
         } else {
-            fused_coef<FUSED>(fs, t, c);
+            fused_coef<FUSED>(fs, t, scale, c);
             for (uint32_t i = tid; i < n; i += kBlockMixed) {
                 float wi = w[i], mi = m[i], vi = v[i];
                 const float nw = mixed_elem(widen1<F16>(g[i]), wi, mi, vi, c);
@@ -537,7 +601,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
             }
         }
     }
-    end_step<FUSED>(fs, t);
+    end_step<FUSED>(fs, t, scale);
 }
 
 // Pure bf16 parameters with chosen state precisions: M32 / V32 = fp32 exp_avg /
@@ -552,7 +616,8 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
 {
     Coef c{};
     int64_t t = 0;
-    if (!begin_step<FUSED>(sc, fs, c, t)) return;
+    float scale = 0.0f;
+    if (!begin_step<FUSED>(sc, fs, c, t, scale)) return;
     constexpr int NT = ADAMW_NT_PURE;
     const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
     const DevSeg& sg = segs[ch.seg];
@@ -591,7 +656,7 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
                     if constexpr (KAHAN) C[u] = ld<NT>(c4 + k);
                 }
             }
-            fused_coef<FUSED>(fs, t, c);   // while the loads are in flight
+            fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const uint32_t k = k0 + u * kBlockPure;
@@ -660,7 +725,7 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
             }
         }
     } else {
-        fused_coef<FUSED>(fs, t, c);
+        fused_coef<FUSED>(fs, t, scale, c);
         for (uint32_t i = tid; i < n; i += kBlockPure) {
             const float pf = widen1<false>(p[i]);
             float mi, vi;
@@ -682,7 +747,7 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
             if constexpr (V32) v[i] = vi; else v[i] = narrow1<false>(vi);
         }
     }
-    end_step<FUSED>(fs, t);
+    end_step<FUSED>(fs, t, scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -703,10 +768,13 @@ __device__ __forceinline__ uint32_t nonfinite2(uint32_t w)
     return (uint32_t)((x & 0xffffu) == 0) | (uint32_t)((x >> 16) == 0);
 }
 
-template <bool F16>
+// FUSED: a single launch that also replaces the zeroing of the flag: the
+// workgroups count themselves with their verdicts (grid_done_verdict), and the last
+// one stores the flag, 1 if any workgroup saw a non-finite value, else 0.
+template <bool F16, bool FUSED>
 __global__ __launch_bounds__(kBlockCheck) void check_kernel(const DevSeg* __restrict__ segs,
                                                        const DevChunk* __restrict__ chunks,
-                                                       int32_t* __restrict__ flag)
+                                                       int32_t* __restrict__ flag, uint32_t* __restrict__ done)
 {
     constexpr uint32_t EXP = F16 ? 0x7c00u : 0x7f80u;
     const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
@@ -733,9 +801,16 @@ __global__ __launch_bounds__(kBlockCheck) void check_kernel(const DevSeg* __rest
     } else {
         for (uint32_t i = threadIdx.x; i < n; i += kBlockCheck) bad |= (uint32_t)((g[i] & EXP) == EXP);
     }
-    // one atomic per wavefront that saw a non-finite value
-    if (__any((int)bad) && (threadIdx.x % warpSize) == 0)
-        __hip_atomic_fetch_or(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (FUSED) {
+        const int any = __syncthreads_or((int)bad);
+        uint32_t hit = 0;
+        if (threadIdx.x == 0 && grid_done_verdict(done, any ? 1u : 0u, &hit))
+            __hip_atomic_store(flag, hit ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        // one atomic per wavefront that saw a non-finite value
+        if (__any((int)bad) && (threadIdx.x % warpSize) == 0)
+            __hip_atomic_fetch_or(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -816,17 +891,26 @@ hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream)
     return hipGetLastError();
 }
 
+// fused: one launch of the check (it stores the flag itself, through the
+// completion counters at done); else zero the flag, then the check ORs into it.
 hipError_t launch_check(adamw_dtype g_dtype, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
-                        int32_t* d_flag, hipStream_t stream)
+                        int32_t* d_flag, uint32_t* done, bool fused, hipStream_t stream)
 {
+    const dim3 grid((unsigned)(n_chunks > 0 ? n_chunks : 1)), block(kBlockCheck);
+    if (fused && n_chunks > 0) {
+        if (g_dtype == ADAMW_F16)
+            hipLaunchKernelGGL((check_kernel<true, true>), grid, block, 0, stream, segs, chunks, d_flag, done);
+        else
+            hipLaunchKernelGGL((check_kernel<false, true>), grid, block, 0, stream, segs, chunks, d_flag, done);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(zero_flag_kernel, dim3(1), dim3(64), 0, stream, d_flag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_chunks <= 0) return e;
-    const dim3 grid((unsigned)n_chunks), block(kBlockCheck);
     if (g_dtype == ADAMW_F16)
-        hipLaunchKernelGGL(check_kernel<true>, grid, block, 0, stream, segs, chunks, d_flag);
+        hipLaunchKernelGGL((check_kernel<true, false>), grid, block, 0, stream, segs, chunks, d_flag, nullptr);
     else
-        hipLaunchKernelGGL(check_kernel<false>, grid, block, 0, stream, segs, chunks, d_flag);
+        hipLaunchKernelGGL((check_kernel<false, false>), grid, block, 0, stream, segs, chunks, d_flag, nullptr);
     return hipGetLastError();
 }
 

@@ -120,6 +120,8 @@ struct FusedStep {
     int32_t* step;              // the caller's step counter
     const int32_t* found_inf;   // nullable skip flag
     uint32_t* done;             // the finished-workgroup counters (kDoneLanes + 1 lines)
+    adamw_loss_scale_state* amp;   // nullable: the device-resident dynamic loss scale
+    adamw_loss_scaler scaler;      // its rule (with amp)
 };
 
 }  // namespace adamw

@@ -315,14 +315,17 @@ int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_ten
 
 /* Launch form.  A step whose plan has at most max_chunks chunks (default
  * 4096, about 8.4e6 elements in 2048-element chunks) runs as ONE kernel
- * launch: every workgroup reads *d_found_inf and *d_step itself, forms the
- * step's scalars (the same binary64 formulas, so the same bits), and the last
- * workgroup to finish stores t into *d_step.  Larger plans, empty lists and
- * adamw_multi_tensor_step_amp run a one-lane prologue kernel first.  The
- * results are bit-identical either way; the single launch saves one kernel
- * launch and its dependency, which dominate steps of a few million elements.
- * max_chunks: 0 = always two launches, < 0 = restore the default.  Affects
- * later calls on every stream.  Returns the value now in force. */
+ * launch: every workgroup reads *d_found_inf, *d_step and the loss scale
+ * itself, forms the step's scalars (the same binary64 formulas, so the same
+ * bits), and the last workgroup to finish stores t into *d_step and advances
+ * the loss scale.  Larger plans and empty lists run a one-lane prologue kernel
+ * first.  Likewise adamw_check_finite over a plan of at most max_chunks of its
+ * chunks is one launch whose last workgroup stores the flag, instead of a
+ * zeroing kernel and the check.  The results are bit-identical either way; the
+ * single launch saves a kernel launch and its dependency, which dominate
+ * steps of a few million elements.  max_chunks: 0 = always two launches,
+ * < 0 = restore the default.  Affects later calls on every stream.  Returns
+ * the value now in force. */
 int64_t adamw_set_single_launch_max_chunks(int64_t max_chunks);
 
 /* Tuning knob: elements per vector chunk (one workgroup's share), a multiple

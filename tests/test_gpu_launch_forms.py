@@ -154,3 +154,83 @@ def test_forms_agree_at_large_step_counts(start, single_launch_limit):
     for k in one.keys:
         assert same_bits(one.arena.bufs[k], two.arena.bufs[k]), k
     free()
+
+
+@pytest.mark.parametrize("g_dtype", ["f16", "bf16"])
+def test_check_forms_agree(g_dtype, single_launch_limit):
+    """The overflow check in one launch (the last workgroup stores the flag)
+    and in two (zero the flag, then OR into it): the same flag as the oracle's
+    scan for clean gradients and for one planted inf/NaN at seeded positions,
+    with the flag holding a stale value before every call."""
+    import numpy as np
+    import oracle
+    from gpu_util import to_np
+    is16 = g_dtype == "f16"
+    case = Case("mixed", SIZES, seed=917, p_dtype=g_dtype, align_elems=3, loss_scale=65536.0 if is16 else 1.0)
+    tl = case.tensor_list()
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(918)
+    bad_bits = (0x7C00, 0xFC00, 0x7E00) if is16 else (0x7F80, 0xFF80, 0x7FC0)
+    nonempty = [i for i, n in enumerate(SIZES) if n]
+    for trial in range(12):
+        planted = None
+        if trial % 3:
+            i = int(rng.choice(nonempty))
+            e = int(rng.integers(0, SIZES[i]))
+            view = case.arena.view("g", i).view(torch.int16)
+            planted = (view, e, int(view[e].item()))
+            view[e] = int(np.int16(np.uint16(bad_bits[trial % 3]).view(np.int16)))
+        want = oracle.any_nonfinite(to_np(case.arena.bufs["g"]), is16)
+        got = []
+        for lim in (-1, 0):
+            single_launch_limit(lim)
+            flag.fill_(7)
+            A.adamw_check_finite(A.F16 if is16 else A.BF16, tl, flag)
+            torch.cuda.synchronize()
+            got.append(int(flag.item()))
+        assert got == [int(want)] * 2, (trial, got, want)
+        if planted:
+            planted[0][planted[1]] = planted[2]
+    free()
+
+
+def test_amp_sequence_forms_agree(single_launch_limit):
+    """fp16 AMP with the device-resident loss scale, 10 iterations of check +
+    step with overflows planted at two of them, run in one launch each and in
+    two launches each on identical copies: flag, scale, tracker, counter after
+    every iteration and every buffer at the end are bitwise equal, and the
+    single-launch copy matches the oracle."""
+    import numpy as np
+    import oracle
+    one = Case("mixed", SIZES, seed=919, p_dtype="f16", loss_scale=65536.0, align_elems=3)
+    two = Case("mixed", SIZES, seed=919, p_dtype="f16", loss_scale=65536.0, align_elems=3)
+    hg, ho = hp_pair()
+    scaler = A.LossScaler(2.0, 0.5, 3)
+    ls = oracle.LossScale(scale=65536.0, tracker=0, growth=2.0, backoff=0.5, interval=3)
+    runs = []
+    for case, lim in ((one, -1), (two, 0)):
+        runs.append((case, lim, case.tensor_list(), torch.zeros(1, dtype=torch.int32, device="cuda"),
+                     A.loss_scale_state(65536.0)))
+    bad_iters = {3, 7}
+    for it in range(10):
+        for case, lim, tl, flag, state in runs:
+            if it:
+                case.refill_grads(it)
+            if it in bad_iters:
+                case.arena.view("g", 9)[12345 % SIZES[9]] = float("inf")
+            single_launch_limit(lim)
+            A.adamw_check_finite(A.F16, tl, flag)
+            A.adamw_multi_tensor_step_amp(A.MIXED, A.F16, tl, hg, case.d_step, flag, state, scaler)
+        from gpu_util import to_np
+        one.host["g"] = to_np(one.arena.bufs["g"])
+        one.step = oracle.amp_step_list("mixed", one.oracle_tensors(), ho, one.step, ls)
+        torch.cuda.synchronize()
+        (_, _, _, f1, s1), (_, _, _, f2, s2) = runs
+        assert int(f1.item()) == int(f2.item()) == int(it in bad_iters), it
+        assert same_bits(s1, s2), (it, s1.tolist(), s2.tolist())
+        assert np.float32(s1[0].item()) == np.float32(ls.scale) and int(s1.view(torch.int32)[1].item()) == ls.tracker
+        assert int(one.d_step.item()) == int(two.d_step.item()) == one.step, it
+    for k in one.keys:
+        assert same_bits(one.arena.bufs[k], two.arena.bufs[k]), k
+    one.compare_all("amp-single-launch")
+    free()
