@@ -207,11 +207,12 @@ class SampledCase:
     elements (with the same per-step scalars) is exact for them.
 
     Samples: the first and last 8 elements of every tensor, plus ``n_random``
-    uniform positions of the flat list; optionally restricted bookkeeping for a
+    uniform positions of the flat list and the flat positions in ``extra``;
+    optionally restricted bookkeeping for a
     ZeRO shard [b, e): samples outside it must come back unchanged."""
 
     def __init__(self, mode, numels, seed, *, p_dtype="bf16", loss_scale=1.0, n_random=1 << 21,
-                 shard=(0, -1), align_elems=128, device="cuda"):
+                 shard=(0, -1), align_elems=128, device="cuda", extra=()):
         self.mode, self.p_dtype, self.seed, self.loss_scale = mode, p_dtype, seed, loss_scale
         self.numels = [int(n) for n in numels]
         self.arena = workloads.make_state(mode, self.numels, device, seed, p_dtype=p_dtype,
@@ -222,7 +223,8 @@ class SampledCase:
         self.shard = (b, shard[1])
         starts = np.concatenate([[0], np.cumsum(self.numels)]).astype(np.int64)
         rng = np.random.default_rng(np.random.SeedSequence([seed, 77]))
-        flat = [rng.integers(0, total, size=n_random, dtype=np.int64)]
+        flat = [rng.integers(0, total, size=n_random, dtype=np.int64),
+                np.asarray([x for x in extra if 0 <= x < total], dtype=np.int64)]
         for i, n in enumerate(self.numels):
             k = min(8, n)
             flat.append(starts[i] + np.arange(k))

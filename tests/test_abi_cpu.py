@@ -489,3 +489,45 @@ def test_single_launch_limit_knob():
         assert A.adamw_set_single_launch_max_chunks(-7) == 4096
     finally:
         A.adamw_set_single_launch_max_chunks(-1)
+
+
+def _plan_rows(mode, tl):
+    """adamw_plan_inspect's rows as an (n, 6) int64 array (for plans of millions of chunks)."""
+    lib = A._lib
+    n = lib.adamw_plan_inspect(mode, A.BF16, ctypes.byref(tl.c), 0, None, 0)
+    assert n >= 0, A.adamw_last_error()
+    buf = (ctypes.c_int64 * (6 * max(n, 1)))()
+    assert lib.adamw_plan_inspect(mode, A.BF16, ctypes.byref(tl.c), 0, buf, n) == n
+    return np.frombuffer(buf, dtype=np.int64, count=6 * n).reshape(n, 6)
+
+
+@pytest.mark.parametrize("mode", [A.MIXED, A.PURE_KAHAN])
+@pytest.mark.parametrize("shard", [(0, -1), (2 ** 31 + 5, 2 ** 32 + 100), (2 ** 32 - 3, 2 ** 32 + 6157 + 40)])
+def test_plan_beyond_32_bit_offsets(shard, mode):
+    """One tensor longer than 2^32 elements (a ragged tail of 5 after the last
+    pack) and a short one behind it: the plan covers the range exactly, with
+    64-bit offsets inside the tensor, whole 2,048-element vector chunks between
+    the peeled ends, and every row inside its tensor (the layout of the GPU test
+    at this size: arenas with tensors at 128-element offsets)."""
+    big = 2 ** 32 + 6157
+    numels = [big, 1000]
+    esz = (2, 2, 4, 4, 4) if mode == A.MIXED else (2, 2, 2, 2, 2)
+    offs = [0, -(-big // 128) * 128]
+    ptrs = [[FAKE + s * (1 << 40) + o * esz[s] for o in offs] for s in range(5)]
+    total = sum(numels)
+    b, e = shard[0], (total if shard[1] < 0 else shard[1])
+    rows = _plan_rows(mode, A.TensorList(numels, ptrs, *shard))
+    t, off, n, vec, flat, _ = rows.T
+    starts = np.array([0, big], dtype=np.int64)
+    assert flat[0] == b and np.array_equal(flat[1:], flat[:-1] + n[:-1]) and flat[-1] + n[-1] == e
+    assert (n > 0).all() and np.array_equal(starts[t] + off, flat)
+    assert (off + n <= np.array(numels, dtype=np.int64)[t]).all()
+    assert off.max() > 2 ** 32 if e > 2 ** 32 else True
+    v = vec == 1
+    assert (n[v] % 8 == 0).all() and (n[v] <= 2048).all() and (n[~v] <= 4096).all()
+    for s in range(5):
+        base = np.array([ptrs[s][0], ptrs[s][1]], dtype=np.int64)
+        assert ((base[t[v]] + off[v] * esz[s]) % 16 == 0).all()
+    # inside the big tensor, only its peeled ends run element-wise
+    big_rows = t == 0
+    assert (~v[big_rows]).sum() <= 2 and (n[big_rows & v] == 2048).sum() >= (min(e, big) - b) // 2048 - 2

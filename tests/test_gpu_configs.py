@@ -121,6 +121,37 @@ def test_opt13b_full_size_blocked_state(mode):
     free()
 
 
+BIG = 2 ** 32 + 6157     # one tensor past 2^32 elements, with a ragged tail of 5 after its last pack
+
+
+@pytest.mark.parametrize("mode,shard", [("mixed", (0, -1)), ("mixed", (2 ** 31 + 5, 2 ** 32 + 100)),
+                                        ("kahan", (0, -1))])
+def test_single_tensor_beyond_32_bit_offsets(mode, shard):
+    """The largest sizes: a tensor of 4,294,973,453 elements (68.7 GB of mixed
+    state) and a short tensor behind it, whole or through a shard that starts
+    at an unaligned position past 2^31 and ends past 2^32.  Two steps; the
+    oracle follows 2M uniform samples plus every element within 24 of 2^31,
+    2^32, the shard edges and the tensor ends."""
+    numels = [BIG, 1000]
+    total = sum(numels)
+    b, e = shard[0], (total if shard[1] < 0 else shard[1])
+    marks = [2 ** 31, 2 ** 32, b, e, BIG - 5, BIG]
+    extra = sorted({x + d for x in marks for d in range(-24, 24)})
+    _print(f"beyond-2^32 {mode} shard={shard}: allocating")
+    case = SampledCase(mode, numels, seed=4301 if mode == "mixed" else 4302, shard=shard, extra=extra)
+    tl = case.tensor_list()
+    hg, ho = hp_pair()
+    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN}[mode]
+    for s in range(2):
+        if s:
+            case.refill_grads(s)
+        A.adamw_multi_tensor_step(code, A.BF16, tl, hg, case.d_step)
+        case.oracle_step(ho)
+    _print(case.compare_all(f"beyond-2^32-{mode}-{shard}"))
+    del case, tl
+    free()
+
+
 def _host_any_nonfinite(g: torch.Tensor, block=1 << 28) -> bool:
     for i in range(0, g.numel(), block):
         if oracle.any_nonfinite(to_np(g[i:i + block]), True):
