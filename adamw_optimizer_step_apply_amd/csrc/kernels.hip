@@ -300,16 +300,12 @@ __device__ __forceinline__ void st(GLOBAL T* p, T v)
 #endif
 constexpr int kUnroll = ADAMW_UNROLL;
 
-// Workgroup -> chunk.  The dispatcher hands workgroup b to XCD b % 8 (the
-// MI355X has 8 XCDs).  With the swizzle, XCD x walks one contiguous run of
-// chunks, so the workgroups in flight on an XCD stream neighbouring addresses.
-// The map is a bijection on [0, nb) for any nb: XCD x owns q + (x < r) chunks,
-// q = nb / 8, r = nb % 8.
+// Workgroup -> chunk: with the swizzle, xcd_chunk (layout.hpp), under which
+// each XCD walks one contiguous run of chunks.
 __device__ __forceinline__ uint32_t chunk_index(uint32_t b, uint32_t nb)
 {
 #if ADAMW_XCD_SWIZZLE
-    const uint32_t q = nb >> 3, r = nb & 7u, x = b & 7u, j = b >> 3;
-    return x * q + (x < r ? x : r) + j;
+    return xcd_chunk(b, nb);
 #else
     (void)nb;
     return b;

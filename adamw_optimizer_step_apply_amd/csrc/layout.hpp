@@ -55,6 +55,18 @@ constexpr int kMaxBlock = kBlockMixed > kBlockPure ? (kBlockMixed > kBlockCheck 
                                                    : (kBlockPure > kBlockCheck ? kBlockPure : kBlockCheck);
 constexpr int64_t kMaxChunks = (int64_t)UINT32_MAX / kMaxBlock;
 
+// Workgroup b of a grid of nb -> the chunk it processes.  The dispatcher hands
+// workgroup b to XCD b % 8 (the MI355X has 8 XCDs, each with its own L2); this
+// map lets XCD x walk one contiguous run of chunks, so the workgroups in flight
+// on an XCD stream neighbouring addresses.  XCD x receives the q + (x < r)
+// workgroups b = 8j + x < nb (q = nb / 8, r = nb % 8) and owns as many chunks,
+// starting at x*q + min(x, r): a bijection on [0, nb) for every nb.  Plain
+// constexpr code, so that the kernels and a host-side test share it.
+constexpr uint32_t xcd_chunk(uint32_t b, uint32_t nb)
+{
+    return (b & 7u) * (nb >> 3) + ((b & 7u) < (nb & 7u) ? (b & 7u) : (nb & 7u)) + (b >> 3);
+}
+
 // Update kernels, by launch id.  The pure-bf16 family adds
 // 4 * (fp32 exp_avg) + 2 * (fp32 exp_avg_sq) + (Kahan compensation).
 constexpr int kKernelMixedBf16 = 0;

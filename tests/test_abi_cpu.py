@@ -531,3 +531,49 @@ def test_plan_beyond_32_bit_offsets(shard, mode):
     # inside the big tensor, only its peeled ends run element-wise
     big_rows = t == 0
     assert (~v[big_rows]).sum() <= 2 and (n[big_rows & v] == 2048).sum() >= (min(e, big) - b) // 2048 - 2
+
+
+XCD_MAP_PROGRAM = r"""
+#include <stdio.h>
+#include <vector>
+#include "layout.hpp"
+// every grid size up to 20000 and a few large ones (the OPT-1.3B plan, the grid
+// limit): each workgroup lands in [0, nb), every chunk is taken exactly once,
+// and the workgroups of one XCD (b % 8) take one contiguous run in b order
+static int check(uint32_t nb) {
+    std::vector<unsigned char> seen(nb, 0);
+    long last[8];
+    for (int x = 0; x < 8; ++x) last[x] = -1;
+    for (uint32_t b = 0; b < nb; ++b) {
+        const uint32_t c = adamw::xcd_chunk(b, nb);
+        if (c >= nb || seen[c]) return 1;
+        seen[c] = 1;
+        const int x = (int)(b & 7u);
+        if (last[x] >= 0 && (long)c != last[x] + 1) return 2;
+        last[x] = (long)c;
+    }
+    return 0;
+}
+int main() {
+    for (uint32_t nb = 1; nb <= 20000; ++nb)
+        if (int e = check(nb)) { printf("nb=%u err=%d\n", nb, e); return 1; }
+    const uint32_t big[] = {642458u, 1283467u, 16777215u};
+    for (uint32_t nb : big)
+        if (int e = check(nb)) { printf("nb=%u err=%d\n", nb, e); return 1; }
+    printf("ok\n");
+    return 0;
+}
+"""
+
+
+def test_xcd_chunk_map_is_a_bijection(tmp_path):
+    """The workgroup -> chunk map the update and check kernels use (constexpr in
+    layout.hpp, compiled here by the host compiler from the same header)."""
+    src = tmp_path / "xcd.cpp"
+    src.write_text(XCD_MAP_PROGRAM)
+    exe = tmp_path / "xcd"
+    subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    "-I", os.path.join(ROOT, "adamw_optimizer_step_apply_amd", "csrc"), str(src), "-o", str(exe)],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), (r.returncode, r.stdout, r.stderr)
