@@ -34,22 +34,15 @@ MIXED, PURE_KAHAN, MIXED_SPLIT = 0, 1, 2
 STREAM_PARAM, STREAM_GRAD, STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_AUX = range(5)
 BLOCKED_STATE = 1 << 8        # flat_mask bit: exp_avg / exp_avg_sq / aux in one blocked buffer
 FLAT_PAD8 = 1 << 9            # flat_mask bit: every tensor starts at a multiple of 8 in the flat index
-STATE_BLOCK_BYTES = 32768     # bytes of the widest state stream in one block of a blocked buffer
+STATE_BLOCK_ELEMS = 16384     # elements per block of a blocked state buffer (ADAMW_STATE_BLOCK_ELEMS)
 NUM_STREAMS = 5
 _STATUS = {0: "ADAMW_OK", 1: "ADAMW_E_INVALID", 2: "ADAMW_E_UNSUPPORTED", 3: "ADAMW_E_NOMEM", 4: "ADAMW_E_HIP"}
-
-
-def state_block(max_state_elem_bytes: int) -> int:
-    """Elements per block of a blocked state buffer whose widest state stream
-    has elements of `max_state_elem_bytes` bytes (ADAMW_STATE_BLOCK_ELEMS):
-    8192 with an fp32 state stream, 16384 when all state is 16-bit."""
-    return STATE_BLOCK_BYTES // int(max_state_elem_bytes)
 
 
 EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_amp", "adamw_pure_multi_tensor_step",
             "adamw_check_finite",
             "adamw_last_error", "adamw_release_workspace", "adamw_abi_version", "adamw_plan_inspect",
-            "adamw_set_chunk_elems", "adamw_set_single_launch_max_chunks")
+            "adamw_set_chunk_elems", "adamw_set_single_launch_max_workgroups")
 
 
 class adamw_hparams(ctypes.Structure):
@@ -111,8 +104,8 @@ def _declare(_lib):
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
     _lib.adamw_set_chunk_elems.restype = ctypes.c_int64
     _lib.adamw_set_chunk_elems.argtypes = [ctypes.c_int64]
-    _lib.adamw_set_single_launch_max_chunks.restype = ctypes.c_int64
-    _lib.adamw_set_single_launch_max_chunks.argtypes = [ctypes.c_int64]
+    _lib.adamw_set_single_launch_max_workgroups.restype = ctypes.c_int64
+    _lib.adamw_set_single_launch_max_workgroups.argtypes = [ctypes.c_int64]
 
 
 _load(LIB_PATH)
@@ -301,10 +294,11 @@ def adamw_set_chunk_elems(elems: int) -> int:
     return r
 
 
-def adamw_set_single_launch_max_chunks(max_chunks: int) -> int:
-    """Largest plan (in chunks) that runs as one launch; 0 = always prologue +
-    update kernel, < 0 = the default.  Returns the value now in force."""
-    return _lib.adamw_set_single_launch_max_chunks(int(max_chunks))
+def adamw_set_single_launch_max_workgroups(max_workgroups: int) -> int:
+    """Largest grid (in workgroups: 8 per chunk of a step, 1 per check chunk)
+    that runs as one launch; 0 = always two launches, < 0 = the default.
+    Returns the value now in force."""
+    return _lib.adamw_set_single_launch_max_workgroups(int(max_workgroups))
 
 
 def library_path() -> str:

@@ -97,10 +97,14 @@ struct StreamWorkspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, uintptr_t>, std::unique_ptr<StreamWorkspace>> g_ws;
-std::atomic<int64_t> g_chunk_elems{0};   // 0: each kernel's own default (its workgroup size x 8)
-// Plans of at most this many chunks run as one launch (the update kernel forms
-// the step's scalars itself) instead of prologue + update kernel.
-std::atomic<int64_t> g_single_launch_max_chunks{kSingleLaunchMaxChunks};
+std::atomic<int64_t> g_chunk_elems{0};   // 0: each kernel's own default chunk
+// Grids of at most this many workgroups run as one launch (the update kernel
+// forms the step's scalars itself) instead of prologue + update kernel.
+std::atomic<int64_t> g_single_launch_max_workgroups{kSingleLaunchMaxWorkgroups};
+
+// The chunk limit of a plan for `tag` (an update kernel id, or -1 for the
+// overflow check): the grid of one launch holds at most 2^32 - 1 lanes.
+int64_t max_chunks_of(int64_t tag) { return tag < 0 ? kMaxCheckChunks : kMaxUpdateChunks; }
 
 // The workspace of a stream, on the stream's own device (the null stream
 // belongs to the calling thread's current device).
@@ -160,7 +164,7 @@ adamw_status ensure_plan(StreamWorkspace& ws, int64_t tag, const int esz[kStream
     }
     Plan plan;
     std::string err;
-    adamw_status st = build_plan(esz, list, chunk_elems, &plan, err);
+    adamw_status st = build_plan(esz, list, chunk_elems, max_chunks_of(tag), &plan, err);
     if (st != ADAMW_OK) return fail(st, err);
 
     if (plans.size() < kPlansPerStream) plans.emplace_back(new PlanSlot());
@@ -255,7 +259,7 @@ adamw_status validate_list(int64_t tag, const int esz[kStreams], const adamw_ten
     plan_key(tag, esz, list, chunk_elems, key);
     if (validated_before(key)) return ADAMW_OK;
     std::string err;
-    adamw_status st = build_plan(esz, list, chunk_elems, nullptr, err);
+    adamw_status st = build_plan(esz, list, chunk_elems, max_chunks_of(tag), nullptr, err);
     if (st != ADAMW_OK) return fail(st, err);
     remember_validated(key);
     return ADAMW_OK;
@@ -315,9 +319,10 @@ adamw_status ensure_workspace_block(StreamWorkspace& ws, hipStream_t stream, uin
     return ADAMW_OK;
 }
 
-bool single_launch(int64_t n_chunks)
+// Whether a grid of n_workgroups (> 0) runs as one launch.
+bool single_launch(int64_t n_workgroups)
 {
-    return n_chunks > 0 && n_chunks <= g_single_launch_max_chunks.load(std::memory_order_relaxed);
+    return n_workgroups > 0 && n_workgroups <= g_single_launch_max_workgroups.load(std::memory_order_relaxed);
 }
 
 // What one step launches: the update kernel and its streams' element sizes.
@@ -331,13 +336,13 @@ int kernel_block(int kernel) { return kernel >= kKernelPure ? kBlockPure : kBloc
 int64_t chunk_elems_of(int kernel)
 {
     const int64_t c = g_chunk_elems.load(std::memory_order_relaxed);
-    return c ? c : chunk_elems_for_block(kernel_block(kernel));
+    return c ? c : update_chunk_elems(kernel_block(kernel));
 }
 
 int64_t check_chunk_elems()
 {
     const int64_t c = g_chunk_elems.load(std::memory_order_relaxed);
-    return c ? c * kCheckChunkMult : kCheckChunkElems;
+    return c ? c : kCheckChunkElems;
 }
 
 StepKind kind_of_mode(adamw_mode mode, adamw_dtype p_dtype)
@@ -376,7 +381,7 @@ adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const 
     if ((st = ensure_plan(*ws, kind.kernel, kind.esz, list, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
     // Small plans: one launch.  An empty plan, whose step still advances the
     // counter (and the loss scale), keeps the prologue kernel.
-    if (single_launch(plan->n_chunks)) {
+    if (single_launch(plan->n_chunks * kXcdParts)) {
         const FusedStep fs{*hp, d_step, d_found_inf, done, d_amp, scaler ? *scaler : adamw_loss_scaler{1.0f, 1.0f, 1}};
         e = launch_update(kind.kernel, plan->segs(), plan->chunks(), plan->n_chunks, nullptr, &fs, stream);
         if (e != hipSuccess) return hip_fail("update launch", e);
@@ -544,7 +549,7 @@ int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_ten
     mode_esizes(mode, p_dtype, for_check != 0, esz);
     const int64_t chunk = for_check ? check_chunk_elems()
                                     : chunk_elems_of(st == ADAMW_OK ? kind_of_mode(mode, p_dtype).kernel : 0);
-    if (st == ADAMW_OK) st = build_plan(esz, list, chunk, &plan, err);
+    if (st == ADAMW_OK) st = build_plan(esz, list, chunk, for_check ? kMaxCheckChunks : kMaxUpdateChunks, &plan, err);
     if (st != ADAMW_OK) {
         g_err = err;
         return -1;
@@ -564,10 +569,10 @@ int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_ten
     return n;
 }
 
-int64_t adamw_set_single_launch_max_chunks(int64_t max_chunks)
+int64_t adamw_set_single_launch_max_workgroups(int64_t max_workgroups)
 {
-    const int64_t v = max_chunks < 0 ? kSingleLaunchMaxChunks : max_chunks;
-    g_single_launch_max_chunks.store(v, std::memory_order_relaxed);
+    const int64_t v = max_workgroups < 0 ? kSingleLaunchMaxWorkgroups : max_workgroups;
+    g_single_launch_max_workgroups.store(v, std::memory_order_relaxed);
     return v;
 }
 

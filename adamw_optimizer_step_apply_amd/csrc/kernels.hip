@@ -12,7 +12,9 @@
 //   prologue_kernel      one lane: reads the skip flag and the step counter,
 //                        forms the step's scalars in binary64, advances the counter
 //   update_kernel<MODE, FUSED> / update_pure_kernel<M32, V32, KAHAN, FUSED>
-//                        one workgroup per chunk: the AdamW element update;
+//                        eight workgroups per chunk, one on each XCD, the chunk
+//                        interleaved between them in 1 KiB tiles: the AdamW
+//                        element update;
 //                        FUSED: without a prologue, for small plans (each
 //                        workgroup forms the scalars, the last one advances
 //                        the counter)
@@ -257,13 +259,9 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
 // Update kernel
 // ---------------------------------------------------------------------------
 
-// Packs each lane loads before computing (1: one pack, all a workgroup's chunk
-// in one pass; 2 was measured slower), and the cache policy of the streaming
-// accesses per mode: bit 0 = non-temporal loads, bit 1 = non-temporal stores
-// (every element is touched exactly once per step).
-#ifndef ADAMW_UNROLL
-#define ADAMW_UNROLL 1
-#endif
+// The cache policy of the streaming accesses per mode: bit 0 = non-temporal
+// loads, bit 1 = non-temporal stores (every element is touched exactly once
+// per step).
 #ifndef ADAMW_NT_MIXED
 #define ADAMW_NT_MIXED 2
 #endif
@@ -295,21 +293,19 @@ __device__ __forceinline__ void st(GLOBAL T* p, T v)
     else *p = v;
 }
 
-#ifndef ADAMW_XCD_SWIZZLE
-#define ADAMW_XCD_SWIZZLE 1
-#endif
-constexpr int kUnroll = ADAMW_UNROLL;
+// The overflow check's workgroup -> chunk map: xcd_chunk (layout.hpp), under
+// which each XCD walks one contiguous run of chunks.
+__device__ __forceinline__ uint32_t chunk_index(uint32_t b, uint32_t nb) { return xcd_chunk(b, nb); }
 
-// Workgroup -> chunk: with the swizzle, xcd_chunk (layout.hpp), under which
-// each XCD walks one contiguous run of chunks.
-__device__ __forceinline__ uint32_t chunk_index(uint32_t b, uint32_t nb)
+// An update kernel's chunk is processed by kXcdParts consecutive workgroups,
+// part = blockIdx.x % kXcdParts running on XCD `part`; lane tid takes the pack
+// tile_pack(tid, part, P) (layout.hpp) of every kXcdParts * BLOCK packs of the
+// chunk.  Element-wise chunks go to the parts in strides of the workgroup size.
+template <int P, int BLOCK>
+__device__ __forceinline__ uint32_t first_pack(uint32_t tid, uint32_t part)
 {
-#if ADAMW_XCD_SWIZZLE
-    return xcd_chunk(b, nb);
-#else
-    (void)nb;
-    return b;
-#endif
+    static_assert(BLOCK % P == 0, "a workgroup covers whole tiles");
+    return tile_pack(tid, part, P);
 }
 
 __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
@@ -460,7 +456,10 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
     constexpr bool F16 = (MODE == 1);   // MODE 3 uses bf16 param/grad
     constexpr int NTM = ADAMW_NT_MIXED;
     constexpr int NTG = ADAMW_NT_MIXED | (ADAMW_NT_MIXED_GRAD ? 1 : 0);   // the gradient's loads
-    const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
+    constexpr int P = tile_packs(4);   // every mixed-family mode keeps fp32 moments
+    constexpr uint32_t kStride = kXcdParts * kBlockMixed;
+    const uint32_t part = blockIdx.x % kXcdParts;
+    const DevChunk ch = chunks[blockIdx.x / kXcdParts];
     const DevSeg& sg = segs[ch.seg];
     const uint32_t n = ch.n_kind & kCountMask;
     const uint64_t off = ch.off;
@@ -479,52 +478,38 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
             GLOBAL u32x4* __restrict__ r4 = reinterpret_cast<GLOBAL u32x4*>(r);
             GLOBAL f32x4* __restrict__ m4 = reinterpret_cast<GLOBAL f32x4*>(m);
             GLOBAL f32x4* __restrict__ v4 = reinterpret_cast<GLOBAL f32x4*>(v);
-            for (uint32_t k0 = tid; k0 < npack; k0 += kBlockMixed * kUnroll) {
-                u32x4 G[kUnroll], P[kUnroll], R[kUnroll];
-                f32x4 M[kUnroll][2], V[kUnroll][2];
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const uint32_t k = k0 + u * kBlockMixed;
-                    if (k < npack) {
-                        G[u] = ld<NTG>(g4 + k); P[u] = ld<NTM>(p4 + k); R[u] = ld<NTM>(r4 + k);
-                        M[u][0] = ld<NTM>(m4 + 2 * k); M[u][1] = ld<NTM>(m4 + 2 * k + 1);
-                        V[u][0] = ld<NTM>(v4 + 2 * k); V[u][1] = ld<NTM>(v4 + 2 * k + 1);
-                    }
-                }
+            for (uint32_t k = first_pack<P, kBlockMixed>(tid, part); k < npack; k += kStride) {
+                const u32x4 G = ld<NTG>(g4 + k), Pv = ld<NTM>(p4 + k), R = ld<NTM>(r4 + k);
+                f32x4 M[2] = {ld<NTM>(m4 + 2 * k), ld<NTM>(m4 + 2 * k + 1)};
+                f32x4 V[2] = {ld<NTM>(v4 + 2 * k), ld<NTM>(v4 + 2 * k + 1)};
                 fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
+                float* mf = reinterpret_cast<float*>(M);
+                float* vf = reinterpret_cast<float*>(V);
+                const uint32_t gw[4] = {G.x, G.y, G.z, G.w};
+                const uint32_t pw[4] = {Pv.x, Pv.y, Pv.z, Pv.w};
+                const uint32_t rw[4] = {R.x, R.y, R.z, R.w};
+                uint32_t po[4], ro[4];
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const uint32_t k = k0 + u * kBlockMixed;
-                    if (k < npack) {
-                        float* mf = reinterpret_cast<float*>(M[u]);
-                        float* vf = reinterpret_cast<float*>(V[u]);
-                        const uint32_t gw[4] = {G[u].x, G[u].y, G[u].z, G[u].w};
-                        const uint32_t pw[4] = {P[u].x, P[u].y, P[u].z, P[u].w};
-                        const uint32_t rw[4] = {R[u].x, R[u].y, R[u].z, R[u].w};
-                        uint32_t po[4], ro[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const f32x2 gg = widen2<false>(gw[j]);
-                            float wa = __uint_as_float(join_bits(pw[j] & 0xffffu, rw[j] & 0xffffu));
-                            float wb = __uint_as_float(join_bits(pw[j] >> 16, rw[j] >> 16));
-                            mixed_elem(gg.x, wa, mf[2 * j], vf[2 * j], c);
-                            mixed_elem(gg.y, wb, mf[2 * j + 1], vf[2 * j + 1], c);
-                            uint32_t ra, rb;
-                            const uint32_t pa = split_bits(__float_as_uint(wa), ra);
-                            const uint32_t pb = split_bits(__float_as_uint(wb), rb);
-                            po[j] = pa | (pb << 16);
-                            ro[j] = ra | (rb << 16);
-                        }
-                        st<NTM>(m4 + 2 * k, M[u][0]); st<NTM>(m4 + 2 * k + 1, M[u][1]);
-                        st<NTM>(v4 + 2 * k, V[u][0]); st<NTM>(v4 + 2 * k + 1, V[u][1]);
-                        st<NTM>(p4 + k, u32x4{po[0], po[1], po[2], po[3]});
-                        st<NTM>(r4 + k, u32x4{ro[0], ro[1], ro[2], ro[3]});
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const f32x2 gg = widen2<false>(gw[j]);
+                    float wa = __uint_as_float(join_bits(pw[j] & 0xffffu, rw[j] & 0xffffu));
+                    float wb = __uint_as_float(join_bits(pw[j] >> 16, rw[j] >> 16));
+                    mixed_elem(gg.x, wa, mf[2 * j], vf[2 * j], c);
+                    mixed_elem(gg.y, wb, mf[2 * j + 1], vf[2 * j + 1], c);
+                    uint32_t ra, rb;
+                    const uint32_t pa = split_bits(__float_as_uint(wa), ra);
+                    const uint32_t pb = split_bits(__float_as_uint(wb), rb);
+                    po[j] = pa | (pb << 16);
+                    ro[j] = ra | (rb << 16);
                 }
+                st<NTM>(m4 + 2 * k, M[0]); st<NTM>(m4 + 2 * k + 1, M[1]);
+                st<NTM>(v4 + 2 * k, V[0]); st<NTM>(v4 + 2 * k + 1, V[1]);
+                st<NTM>(p4 + k, u32x4{po[0], po[1], po[2], po[3]});
+                st<NTM>(r4 + k, u32x4{ro[0], ro[1], ro[2], ro[3]});
             }
         } else {
             fused_coef<FUSED>(fs, t, scale, c);
-            for (uint32_t i = tid; i < n; i += kBlockMixed) {
+            for (uint32_t i = part * kBlockMixed + tid; i < n; i += kStride) {
                 float wi = __uint_as_float(join_bits(p[i], r[i])), mi = m[i], vi = v[i];
                 mixed_elem(widen1<false>(g[i]), wi, mi, vi, c);
                 uint32_t ri;
@@ -548,46 +533,32 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
             GLOBAL f32x4* __restrict__ m4 = reinterpret_cast<GLOBAL f32x4*>(m);
             GLOBAL f32x4* __restrict__ v4 = reinterpret_cast<GLOBAL f32x4*>(v);
             GLOBAL f32x4* __restrict__ w4 = reinterpret_cast<GLOBAL f32x4*>(w);
-            for (uint32_t k0 = tid; k0 < npack; k0 += kBlockMixed * kUnroll) {
-                u32x4 G[kUnroll];
-                f32x4 M[kUnroll][2], V[kUnroll][2], W[kUnroll][2];
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const uint32_t k = k0 + u * kBlockMixed;
-                    if (k < npack) {
-                        G[u] = ld<NTG>(g4 + k);
-                        W[u][0] = ld<NTM>(w4 + 2 * k); W[u][1] = ld<NTM>(w4 + 2 * k + 1);
-                        M[u][0] = ld<NTM>(m4 + 2 * k); M[u][1] = ld<NTM>(m4 + 2 * k + 1);
-                        V[u][0] = ld<NTM>(v4 + 2 * k); V[u][1] = ld<NTM>(v4 + 2 * k + 1);
-                    }
-                }
+            for (uint32_t k = first_pack<P, kBlockMixed>(tid, part); k < npack; k += kStride) {
+                const u32x4 G = ld<NTG>(g4 + k);
+                f32x4 W[2] = {ld<NTM>(w4 + 2 * k), ld<NTM>(w4 + 2 * k + 1)};
+                f32x4 M[2] = {ld<NTM>(m4 + 2 * k), ld<NTM>(m4 + 2 * k + 1)};
+                f32x4 V[2] = {ld<NTM>(v4 + 2 * k), ld<NTM>(v4 + 2 * k + 1)};
                 fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
+                float* wf = reinterpret_cast<float*>(W);
+                float* mf = reinterpret_cast<float*>(M);
+                float* vf = reinterpret_cast<float*>(V);
+                const uint32_t gw[4] = {G.x, G.y, G.z, G.w};
+                uint32_t pw[4];
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const uint32_t k = k0 + u * kBlockMixed;
-                    if (k < npack) {
-                        float* wf = reinterpret_cast<float*>(W[u]);
-                        float* mf = reinterpret_cast<float*>(M[u]);
-                        float* vf = reinterpret_cast<float*>(V[u]);
-                        const uint32_t gw[4] = {G[u].x, G[u].y, G[u].z, G[u].w};
-                        uint32_t pw[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const f32x2 gg = widen2<F16>(gw[j]);
-                            const float a = mixed_elem(gg.x, wf[2 * j], mf[2 * j], vf[2 * j], c);
-                            const float b = mixed_elem(gg.y, wf[2 * j + 1], mf[2 * j + 1], vf[2 * j + 1], c);
-                            pw[j] = narrow2<F16>(a, b);
-                        }
-                        st<NTM>(w4 + 2 * k, W[u][0]); st<NTM>(w4 + 2 * k + 1, W[u][1]);
-                        st<NTM>(m4 + 2 * k, M[u][0]); st<NTM>(m4 + 2 * k + 1, M[u][1]);
-                        st<NTM>(v4 + 2 * k, V[u][0]); st<NTM>(v4 + 2 * k + 1, V[u][1]);
-                        st<NTM>(p4 + k, u32x4{pw[0], pw[1], pw[2], pw[3]});
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const f32x2 gg = widen2<F16>(gw[j]);
+                    const float a = mixed_elem(gg.x, wf[2 * j], mf[2 * j], vf[2 * j], c);
+                    const float b = mixed_elem(gg.y, wf[2 * j + 1], mf[2 * j + 1], vf[2 * j + 1], c);
+                    pw[j] = narrow2<F16>(a, b);
                 }
+                st<NTM>(w4 + 2 * k, W[0]); st<NTM>(w4 + 2 * k + 1, W[1]);
+                st<NTM>(m4 + 2 * k, M[0]); st<NTM>(m4 + 2 * k + 1, M[1]);
+                st<NTM>(v4 + 2 * k, V[0]); st<NTM>(v4 + 2 * k + 1, V[1]);
+                st<NTM>(p4 + k, u32x4{pw[0], pw[1], pw[2], pw[3]});
             }
         } else {
             fused_coef<FUSED>(fs, t, scale, c);
-            for (uint32_t i = tid; i < n; i += kBlockMixed) {
+            for (uint32_t i = part * kBlockMixed + tid; i < n; i += kStride) {
                 float wi = w[i], mi = m[i], vi = v[i];
                 const float nw = mixed_elem(widen1<F16>(g[i]), wi, mi, vi, c);
                 w[i] = wi;
@@ -615,7 +586,10 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
     float scale = 0.0f;
     if (!begin_step<FUSED>(sc, fs, c, t, scale)) return;
     constexpr int NT = ADAMW_NT_PURE;
-    const DevChunk ch = chunks[chunk_index(blockIdx.x, gridDim.x)];
+    constexpr int P = tile_packs(M32 || V32 ? 4 : 2);   // 1 KiB tiles of the widest state stream
+    constexpr uint32_t kStride = kXcdParts * kBlockPure;
+    const uint32_t part = blockIdx.x % kXcdParts;
+    const DevChunk ch = chunks[blockIdx.x / kXcdParts];
     const DevSeg& sg = segs[ch.seg];
     const uint32_t n = ch.n_kind & kCountMask;
     const uint64_t off = ch.off;
@@ -637,92 +611,79 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
         constexpr int MW = M32 ? 2 : 1, VW = V32 ? 2 : 1;
         GLOBAL u32x4* __restrict__ m4 = reinterpret_cast<GLOBAL u32x4*>(m);
         GLOBAL u32x4* __restrict__ v4 = reinterpret_cast<GLOBAL u32x4*>(v);
-        for (uint32_t k0 = tid; k0 < npack; k0 += kBlockPure * kUnroll) {
-            u32x4 G[kUnroll], P[kUnroll], C[kUnroll], M[kUnroll][MW], V[kUnroll][VW];
+        for (uint32_t k = first_pack<P, kBlockPure>(tid, part); k < npack; k += kStride) {
+            const u32x4 G = ld<NT>(g4 + k), Pv = ld<NT>(p4 + k);
+            u32x4 C, M[MW], V[VW];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const uint32_t k = k0 + u * kBlockPure;
-                if (k < npack) {
-                    G[u] = ld<NT>(g4 + k);
-                    P[u] = ld<NT>(p4 + k);
+            for (int q = 0; q < MW; ++q) M[q] = ld<NT>(m4 + MW * k + q);
 #pragma unroll
-                    for (int q = 0; q < MW; ++q) M[u][q] = ld<NT>(m4 + MW * k + q);
-#pragma unroll
-                    for (int q = 0; q < VW; ++q) V[u][q] = ld<NT>(v4 + VW * k + q);
-                    if constexpr (KAHAN) C[u] = ld<NT>(c4 + k);
-                }
-            }
+            for (int q = 0; q < VW; ++q) V[q] = ld<NT>(v4 + VW * k + q);
+            if constexpr (KAHAN) C = ld<NT>(c4 + k);
             fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
+            const uint32_t* gw = reinterpret_cast<const uint32_t*>(&G);
+            const uint32_t* pw = reinterpret_cast<const uint32_t*>(&Pv);
+            const uint32_t* cw = reinterpret_cast<const uint32_t*>(&C);
+            uint32_t* mw = reinterpret_cast<uint32_t*>(M);   // 4 (bf16) or 8 (fp32) words
+            uint32_t* vw = reinterpret_cast<uint32_t*>(V);
+            uint32_t po[4], co[4];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const uint32_t k = k0 + u * kBlockPure;
-                if (k < npack) {
-                    const uint32_t* gw = reinterpret_cast<const uint32_t*>(&G[u]);
-                    const uint32_t* pw = reinterpret_cast<const uint32_t*>(&P[u]);
-                    const uint32_t* cw = reinterpret_cast<const uint32_t*>(&C[u]);
-                    uint32_t* mw = reinterpret_cast<uint32_t*>(M[u]);   // 4 (bf16) or 8 (fp32) words
-                    uint32_t* vw = reinterpret_cast<uint32_t*>(V[u]);
-                    uint32_t po[4], co[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const f32x2 gg = widen2<false>(gw[j]);
-                        const f32x2 pp = widen2<false>(pw[j]);
-                        float ma, mb, va, vb;
-                        if constexpr (M32) {
-                            ma = __uint_as_float(mw[2 * j]);
-                            mb = __uint_as_float(mw[2 * j + 1]);
-                        } else {
-                            const f32x2 t2 = widen2<false>(mw[j]);
-                            ma = t2.x;
-                            mb = t2.y;
-                        }
-                        if constexpr (V32) {
-                            va = __uint_as_float(vw[2 * j]);
-                            vb = __uint_as_float(vw[2 * j + 1]);
-                        } else {
-                            const f32x2 t2 = widen2<false>(vw[j]);
-                            va = t2.x;
-                            vb = t2.y;
-                        }
-                        if constexpr (KAHAN) {
-                            const f32x2 cf = widen2<false>(cw[j]);
-                            float sa, sb;
-                            const float ta = kahan_sum(gg.x, pp.x, cf.x, ma, va, c, sa);
-                            const float tb = kahan_sum(gg.y, pp.y, cf.y, mb, vb, c, sb);
-                            po[j] = narrow2<false>(ta, tb);
-                            const f32x2 pn = widen2<false>(po[j]);
-                            co[j] = narrow2<false>(sa - (pn.x - pp.x), sb - (pn.y - pp.y));
-                        } else {
-                            float wa = pp.x, wb = pp.y;
-                            mixed_elem(gg.x, wa, ma, va, c);
-                            mixed_elem(gg.y, wb, mb, vb, c);
-                            po[j] = narrow2<false>(wa, wb);
-                        }
-                        if constexpr (M32) {
-                            mw[2 * j] = __float_as_uint(ma);
-                            mw[2 * j + 1] = __float_as_uint(mb);
-                        } else {
-                            mw[j] = narrow2<false>(ma, mb);
-                        }
-                        if constexpr (V32) {
-                            vw[2 * j] = __float_as_uint(va);
-                            vw[2 * j + 1] = __float_as_uint(vb);
-                        } else {
-                            vw[j] = narrow2<false>(va, vb);
-                        }
-                    }
-                    st<NT>(p4 + k, u32x4{po[0], po[1], po[2], po[3]});
-#pragma unroll
-                    for (int q = 0; q < MW; ++q) st<NT>(m4 + MW * k + q, M[u][q]);
-#pragma unroll
-                    for (int q = 0; q < VW; ++q) st<NT>(v4 + VW * k + q, V[u][q]);
-                    if constexpr (KAHAN) st<NT>(c4 + k, u32x4{co[0], co[1], co[2], co[3]});
+            for (int j = 0; j < 4; ++j) {
+                const f32x2 gg = widen2<false>(gw[j]);
+                const f32x2 pp = widen2<false>(pw[j]);
+                float ma, mb, va, vb;
+                if constexpr (M32) {
+                    ma = __uint_as_float(mw[2 * j]);
+                    mb = __uint_as_float(mw[2 * j + 1]);
+                } else {
+                    const f32x2 t2 = widen2<false>(mw[j]);
+                    ma = t2.x;
+                    mb = t2.y;
+                }
+                if constexpr (V32) {
+                    va = __uint_as_float(vw[2 * j]);
+                    vb = __uint_as_float(vw[2 * j + 1]);
+                } else {
+                    const f32x2 t2 = widen2<false>(vw[j]);
+                    va = t2.x;
+                    vb = t2.y;
+                }
+                if constexpr (KAHAN) {
+                    const f32x2 cf = widen2<false>(cw[j]);
+                    float sa, sb;
+                    const float ta = kahan_sum(gg.x, pp.x, cf.x, ma, va, c, sa);
+                    const float tb = kahan_sum(gg.y, pp.y, cf.y, mb, vb, c, sb);
+                    po[j] = narrow2<false>(ta, tb);
+                    const f32x2 pn = widen2<false>(po[j]);
+                    co[j] = narrow2<false>(sa - (pn.x - pp.x), sb - (pn.y - pp.y));
+                } else {
+                    float wa = pp.x, wb = pp.y;
+                    mixed_elem(gg.x, wa, ma, va, c);
+                    mixed_elem(gg.y, wb, mb, vb, c);
+                    po[j] = narrow2<false>(wa, wb);
+                }
+                if constexpr (M32) {
+                    mw[2 * j] = __float_as_uint(ma);
+                    mw[2 * j + 1] = __float_as_uint(mb);
+                } else {
+                    mw[j] = narrow2<false>(ma, mb);
+                }
+                if constexpr (V32) {
+                    vw[2 * j] = __float_as_uint(va);
+                    vw[2 * j + 1] = __float_as_uint(vb);
+                } else {
+                    vw[j] = narrow2<false>(va, vb);
                 }
             }
+            st<NT>(p4 + k, u32x4{po[0], po[1], po[2], po[3]});
+#pragma unroll
+            for (int q = 0; q < MW; ++q) st<NT>(m4 + MW * k + q, M[q]);
+#pragma unroll
+            for (int q = 0; q < VW; ++q) st<NT>(v4 + VW * k + q, V[q]);
+            if constexpr (KAHAN) st<NT>(c4 + k, u32x4{co[0], co[1], co[2], co[3]});
         }
     } else {
         fused_coef<FUSED>(fs, t, scale, c);
-        for (uint32_t i = tid; i < n; i += kBlockPure) {
+        for (uint32_t i = part * kBlockPure + tid; i < n; i += kStride) {
             const float pf = widen1<false>(p[i]);
             float mi, vi;
             if constexpr (M32) mi = m[i]; else mi = widen1<false>(m[i]);
@@ -778,8 +739,8 @@ __global__ __launch_bounds__(kBlockCheck) void check_kernel(const DevSeg* __rest
     const uint32_t n = ch.n_kind & kCountMask;
     uint32_t bad = 0;
     if (ch.n_kind & kVecBit) {
-        // a check chunk is kCheckUnroll times a step chunk: each lane issues all
-        // its loads before testing any, so one pass covers the chunk
+        // each lane issues kCheckUnroll loads before testing any: one pass
+        // covers a default check chunk
         const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
         const uint32_t npack = n / kPack;
         for (uint32_t k0 = threadIdx.x; k0 < npack; k0 += kBlockCheck * kCheckUnroll) {
@@ -841,7 +802,8 @@ template <bool FUSED>
 static hipError_t launch_update_as(int kernel, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
                                    const LaunchScalars* d_scalars, const FusedStep& fs, hipStream_t stream)
 {
-    const dim3 grid((unsigned)n_chunks), block(kBlockMixed), block_pure(kBlockPure);
+    // kXcdParts workgroups per chunk (the plan's chunk limit keeps the grid in range)
+    const dim3 grid((unsigned)(n_chunks * kXcdParts)), block(kBlockMixed), block_pure(kBlockPure);
     switch (kernel) {
     case kKernelMixedBf16:
         hipLaunchKernelGGL((update_kernel<0, FUSED>), grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars, fs);

@@ -23,7 +23,8 @@ constexpr int kStreams = 5;            // param, grad, exp_avg, exp_avg_sq, aux
 // Chosen by interleaved A/B runs on MI355X (OPT-1.3B list, state in the blocked
 // layout and per tensor): for the pure family 256 x 4 and 512 x 2 beat 1024 x 1
 // by 5% on blocked state and tie with it per tensor; for the mixed family
-// 256 x 2 leads every other shape tried, by 0-10% on blocked state.
+// 256 x 2 leads every other shape tried, by 0-10% on blocked state.  The chunk
+// and tile shapes below assume these sizes.
 #ifndef ADAMW_BLOCK_MIXED
 #define ADAMW_BLOCK_MIXED 256
 #endif
@@ -37,23 +38,52 @@ constexpr int kPack = 8;               // elements per lane per dwordx4 of a 16-
 constexpr uint32_t kVecBit = 0x80000000u;
 constexpr uint32_t kCountMask = 0x7fffffffu;
 constexpr int64_t kElemChunkElems = 4096;       // element chunk
-// bytes of the largest state sub-stream in one block of a blocked state buffer
-constexpr int64_t kStateBlockBytes = ADAMW_STATE_BLOCK_BYTES;
-// Default vector chunk of a kernel: one 8-element pack per lane, one pass.
-constexpr int64_t chunk_elems_for_block(int block) { return (int64_t)block * 8; }
-// The overflow check moves 2 B per element (the step 18-28 B): each lane reads
-// this many packs in one pass, so a workgroup's fixed cost (two dependent table
-// loads) is spread over as many bytes as a step workgroup moves.
+// An update kernel's chunk is shared by kXcdParts workgroups, consecutive in
+// launch order, so one on each XCD (the dispatcher hands workgroup b to XCD
+// b % 8).  The chunk is cut into tiles of kTileBytes of the widest state
+// stream (256 elements with an fp32 state stream, 512 when all state is
+// 16-bit); tile t goes to part t % 8, and each lane of a part takes one 8-element
+// pack.  All XCDs thus sweep one contiguous region together, interleaved at
+// 1 KiB.  On MI355X (OPT-1.3B list, against giving each XCD one contiguous run
+// of 2048-element chunks) this streamed the mixed step 7 % faster on blocked
+// state (with 16384-element blocks) and 6.5 % per tensor, and the Kahan step
+// 1 % faster blocked and 5 % per tensor; tiles of 64-128 and 512-1024 elements
+// (fp32 state) or 256 and 1024-2048 (bf16 state) were slower.
+constexpr int kXcdParts = 8;
+constexpr int kTileBytes = 1024;
+// packs per tile for a widest state element of `bytes` bytes (4 or 2)
+constexpr int tile_packs(int bytes) { return kTileBytes / (bytes * kPack); }
+// The pack of a chunk taken by lane tid of part `part` (per kXcdParts * block
+// packs): tile t of p packs belongs to part t % kXcdParts, so
+//     ((tid / p) * kXcdParts + part) * p + tid % p,
+// a bijection of (part, tid) onto [0, kXcdParts * block) whenever p divides
+// the workgroup size.
+constexpr uint32_t tile_pack(uint32_t tid, uint32_t part, uint32_t p)
+{
+    return ((tid / p) * kXcdParts + part) * p + tid % p;
+}
+// Default vector chunk of an update kernel: one pack per lane of each part.
+constexpr int64_t update_chunk_elems(int block) { return (int64_t)kXcdParts * block * kPack; }
+// Blocked state: elements per block, one update chunk (every mode).
+constexpr int64_t kStateBlockElems = ADAMW_STATE_BLOCK_ELEMS;
+static_assert(kStateBlockElems % update_chunk_elems(kBlockMixed) == 0 &&
+                  kStateBlockElems % update_chunk_elems(kBlockPure) == 0,
+              "a state block holds whole default chunks");
+// The overflow check moves 2 B per element (the step 18-28 B): one workgroup
+// per chunk, each lane reading this many packs in one pass, so that a
+// workgroup's fixed cost (two dependent table loads) is spread over as many
+// bytes as a step workgroup moves.
 #ifndef ADAMW_CHECK_CHUNK_MULT
 #define ADAMW_CHECK_CHUNK_MULT 8
 #endif
 constexpr int kCheckChunkMult = ADAMW_CHECK_CHUNK_MULT;
-constexpr int64_t kCheckChunkElems = chunk_elems_for_block(kBlockCheck) * kCheckChunkMult;
-// A launch's grid counts at most 2^32 - 1 lanes: the chunk limit of one plan
-// follows from the widest workgroup.
-constexpr int kMaxBlock = kBlockMixed > kBlockPure ? (kBlockMixed > kBlockCheck ? kBlockMixed : kBlockCheck)
-                                                   : (kBlockPure > kBlockCheck ? kBlockPure : kBlockCheck);
-constexpr int64_t kMaxChunks = (int64_t)UINT32_MAX / kMaxBlock;
+constexpr int64_t kCheckChunkElems = (int64_t)kBlockCheck * kPack * kCheckChunkMult;
+// A launch's grid counts at most 2^32 - 1 lanes: the chunk limit of a plan
+// follows from the lanes one chunk takes (kXcdParts workgroups of an update
+// kernel, one check workgroup).
+constexpr int kMaxUpdateBlock = kBlockMixed > kBlockPure ? kBlockMixed : kBlockPure;
+constexpr int64_t kMaxUpdateChunks = (int64_t)UINT32_MAX / ((int64_t)kXcdParts * kMaxUpdateBlock);
+constexpr int64_t kMaxCheckChunks = (int64_t)UINT32_MAX / kBlockCheck;
 
 // Workgroup b of a grid of nb -> the chunk it processes.  The dispatcher hands
 // workgroup b to XCD b % 8 (the MI355X has 8 XCDs, each with its own L2); this
@@ -119,11 +149,11 @@ constexpr int64_t kDoneOffset = kScalarsBytes;
 constexpr int64_t kDoneWords = (kDoneLanes + 1) * kDoneStrideWords;
 constexpr int64_t kWorkspaceBytes = kDoneOffset + kDoneWords * 4;
 
-// Default largest plan, in chunks, that runs as a single launch.  Measured on
-// MI355X (mixed step, one tensor): the single launch takes 30 % off a step of
-// 64k-256k elements, 11 % at 1M and 4 % at 4M, and ties from 8M (4096 chunks)
-// up, where the prologue launch no longer shows.
-constexpr int64_t kSingleLaunchMaxChunks = 4096;
+// Default largest grid, in workgroups, that runs as a single launch.  Measured
+// on MI355X (mixed step, one tensor): the single launch takes 30 % off a step
+// of 64k-256k elements, 11 % at 1M and 4 % at 4M, and ties from 8M (4096
+// workgroups) up, where the prologue launch no longer shows.
+constexpr int64_t kSingleLaunchMaxWorkgroups = 4096;
 
 // A single-launch step: the update kernel forms the step's scalars itself in
 // every workgroup, and the last workgroup to finish stores the advanced counter.

@@ -81,8 +81,8 @@ static void push_chunks(Plan& p, bool build, int64_t& n_chunks, uint32_t seg, in
     }
 }
 
-adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* list, int64_t chunk_elems, Plan* outp,
-                        std::string& err)
+adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* list, int64_t chunk_elems,
+                        int64_t max_chunks, Plan* outp, std::string& err)
 {
     char buf[256];
     Plan scratch;
@@ -127,14 +127,11 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
     int esz[kStreams];
     bool flat[kStreams];
     // blocked state: exp_avg, exp_avg_sq and aux share one flat buffer of the
-    // shard in blocks of state_block elements, [exp_avg][exp_avg_sq][aux] each;
-    // the largest sub-stream of a block spans kStateBlockBytes
+    // shard in blocks of state_block elements, [exp_avg][exp_avg_sq][aux] each
     int64_t soff[kStreams] = {0, 0, 0, 0, 0}, block_bytes = 0, state_block = 1;
     uintptr_t state_base = 0;
     if (blocked) {
-        int max_esz = 0;
-        for (int s = ADAMW_STREAM_EXP_AVG; s <= ADAMW_STREAM_AUX; ++s) max_esz = esz_in[s] > max_esz ? esz_in[s] : max_esz;
-        state_block = kStateBlockBytes / max_esz;
+        state_block = kStateBlockElems;
         int64_t acc = 0;
         for (int s = ADAMW_STREAM_EXP_AVG; s <= ADAMW_STREAM_AUX; ++s) {
             soff[s] = acc;
@@ -233,11 +230,11 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
                 push_chunks(out, build, n_chunks, seg, head, body, chunk_elems, true);
                 push_chunks(out, build, n_chunks, seg, head + body, cnt - head - body, kElemChunkElems, false);
             }
-            if (n_chunks > kMaxChunks) {
+            if (n_chunks > max_chunks) {
                 snprintf(buf, sizeof buf,
                          "more than %lld chunks in one launch (a grid holds at most 2^32 - 1 lanes): "
                          "split the list or raise the chunk size",
-                         (long long)kMaxChunks);
+                         (long long)max_chunks);
                 err = buf;
                 return ADAMW_E_INVALID;
             }

@@ -35,9 +35,10 @@ void mode_esizes(adamw_mode mode, adamw_dtype p_dtype, bool for_check, int esz[k
 
 // Validates the list against per-stream element sizes `esz` (0 = stream
 // unused) and, if `out` is non-null, builds the plan with vector chunks of
-// `chunk_elems` elements.  No HIP call.
-adamw_status build_plan(const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems, Plan* out,
-                        std::string& err);
+// `chunk_elems` elements; a plan of more than `max_chunks` chunks (the grid
+// limit of the kernel that runs it) is rejected.  No HIP call.
+adamw_status build_plan(const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems,
+                        int64_t max_chunks, Plan* out, std::string& err);
 
 // The exact inputs a plan depends on, for caching (`tag` distinguishes kernels).
 void plan_key(int64_t tag, const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems,

@@ -212,9 +212,9 @@ def probes(n, stream):
     w, m, v = (torch.ones(n, dtype=torch.float32, device=dev) for _ in range(3))
     run(0, [g, w, m, v, p], n, 28 * n, "mixed_mix")
     del w, m, v
-    # whole blocks of the blocked state layout: 32 KiB per state stream and block
-    nb = -(-n // 8192)
-    blk = torch.ones(nb * 8192 * 3, dtype=torch.float32, device=dev)
+    # whole blocks of the blocked state layout: 16384 elements per block
+    nb = -(-n // 16384)
+    blk = torch.ones(nb * 16384 * 3, dtype=torch.float32, device=dev)
     run(6, [g, blk, p], n, 28 * n, "mixed_blocked_mix")
     del blk
     nb = -(-n // 16384)
@@ -258,7 +258,7 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
     streams = [[arena.view(k, i) for i in range(len(numels))] for k in keys]
     if blocked:
         import adamw_optimizer_step_apply_amd as A
-        B = A.state_block(max(arena.bufs[k].element_size() for k in keys[2:]))
+        B = A.STATE_BLOCK_ELEMS
         n = sum(-(-m // 8) * 8 for m in numels)     # padded flat index
         nb = -(-n // B)
         cols = []
@@ -519,8 +519,7 @@ def main():
                            f"exp_avg_sq, {'bf16 Kahan compensation' if kahan else 'no compensation'}")
         if base != mode:
             names[mode] = (names[base] + f", exp_avg/exp_avg_sq/{'master' if base == 'mixed' else 'aux'} "
-                           "interleaved per block of one optimizer-owned buffer (32 KiB per block of the widest "
-                           "state stream)")
+                           "interleaved per block of 16384 elements of one optimizer-owned buffer")
     out = {
         "metric": "AdamW step Gparams/s + achieved HBM GB/s (% of peak), OPT-1.3B shape, 1 GPU",
         "value": round(value, 3),

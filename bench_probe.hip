@@ -2,8 +2,9 @@
 //
 // Kernels that move exactly the bytes of the fused AdamW step's streams, in the
 // same launch shape as the library's update kernel (256 lanes, one 8-element
-// pack per lane, one pass per workgroup, XCD-contiguous chunk order, two
-// workgroups per CU), but do no optimizer arithmetic.  Their rate is the ceiling
+// pack per lane, each chunk of 2048 packs shared by 8 consecutive workgroups,
+// one per XCD, in 1 KiB tiles of the widest state stream; two workgroups per
+// CU), but do no optimizer arithmetic.  Their rate is the ceiling
 // of the access pattern itself; the update kernel's rate divided by it says how
 // much of the pattern's bandwidth the arithmetic costs.  A plain copy, a
 // read-only and a write-only kernel give the HBM ceilings of simpler mixes.
@@ -18,17 +19,30 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
-__device__ __forceinline__ uint64_t chunk_of(uint32_t b, uint32_t nb)
+// Unit (pack or 16-byte word) of lane threadIdx.x of workgroup b: chunk b / 8
+// of 2048 units, part b % 8 taking the tiles of P units whose index is
+// congruent to it mod 8.
+template <int P>
+__device__ __forceinline__ uint64_t unit_of(uint32_t b)
+{
+    const uint32_t x = b & 7u, tid = threadIdx.x;
+    return (uint64_t)(b >> 3) * 2048u + ((tid / P) * 8u + x) * P + tid % P;
+}
+
+// The plain ceilings (copy, read, write) keep the simplest order: workgroup b
+// takes 256 consecutive words of chunk run b % 8, each XCD walking one
+// contiguous eighth of the buffer.
+__device__ __forceinline__ uint64_t word_of(uint32_t b, uint32_t nb)
 {
     const uint32_t q = nb >> 3, r = nb & 7u, x = b & 7u, j = b >> 3;
-    return (uint64_t)x * q + (x < r ? x : r) + j;
+    return ((uint64_t)x * q + (x < r ? x : r) + j) * 256u + threadIdx.x;
 }
 
 // mixed mix: read g (2 B) and w, m, v (4 B); write w, m, v (4 B) and p (2 B)
 __global__ __launch_bounds__(256) void mixed_mix(const GLOBAL u32x4* g, GLOBAL f32x4* w, GLOBAL f32x4* m,
                                                  GLOBAL f32x4* v, GLOBAL u32x4* p, uint64_t npack)
 {
-    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    const uint64_t k = unit_of<32>(blockIdx.x);
     if (k >= npack) return;
     const u32x4 gv = g[k];
     const f32x4 w0 = w[2 * k], w1 = w[2 * k + 1], m0 = m[2 * k], m1 = m[2 * k + 1], v0 = v[2 * k], v1 = v[2 * k + 1];
@@ -46,7 +60,7 @@ __global__ __launch_bounds__(256) void mixed_mix(const GLOBAL u32x4* g, GLOBAL f
 __global__ __launch_bounds__(256) void split_mix(const GLOBAL u32x4* g, GLOBAL u32x4* p, GLOBAL u32x4* r,
                                                  GLOBAL f32x4* m, GLOBAL f32x4* v, uint64_t npack)
 {
-    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    const uint64_t k = unit_of<32>(blockIdx.x);
     if (k >= npack) return;
     const u32x4 gv = g[k], pv = p[k], rv = r[k];
     const f32x4 m0 = m[2 * k], m1 = m[2 * k + 1], v0 = v[2 * k], v1 = v[2 * k + 1];
@@ -62,7 +76,7 @@ __global__ __launch_bounds__(256) void split_mix(const GLOBAL u32x4* g, GLOBAL u
 __global__ __launch_bounds__(256) void kahan_mix(const GLOBAL u32x4* g, GLOBAL u32x4* p, GLOBAL u32x4* m,
                                                  GLOBAL u32x4* v, GLOBAL u32x4* c, uint64_t npack)
 {
-    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    const uint64_t k = unit_of<64>(blockIdx.x);
     if (k >= npack) return;
     const u32x4 a = __builtin_nontemporal_load(g + k), b = __builtin_nontemporal_load(p + k);
     const u32x4 d = __builtin_nontemporal_load(m + k), e = __builtin_nontemporal_load(v + k);
@@ -73,12 +87,11 @@ __global__ __launch_bounds__(256) void kahan_mix(const GLOBAL u32x4* g, GLOBAL u
     __builtin_nontemporal_store(f ^ a, c + k);
 }
 
-// The blocked state layout: per block, the state streams one after another
-// ([m][v][w] fp32 for the mixed mix, [m][v][c] bf16 for Kahan), each spanning
-// 32 KiB as in the library (8192 fp32 / 16384 bf16 elements); g and p keep their
-// own buffers.  Pack k (elements 8k..8k+7) lies in block k / (kBlock / 8) at
-// pack offset k % (kBlock / 8).
-constexpr uint64_t kBlock = 8192;            // fp32 state
+// The blocked state layout: per block of 16384 elements, as in the library,
+// the state streams one after another ([m][v][w] fp32 for the mixed mix,
+// [m][v][c] bf16 for Kahan); g and p keep their own buffers.  Pack k (elements
+// 8k..8k+7) lies in block k / (kBlock / 8) at pack offset k % (kBlock / 8).
+constexpr uint64_t kBlock = 16384;           // fp32 state
 constexpr uint64_t kPacksPerBlock = kBlock / 8;
 constexpr uint64_t kBlock16 = 16384;         // 16-bit state
 constexpr uint64_t kPacksPerBlock16 = kBlock16 / 8;
@@ -86,7 +99,7 @@ constexpr uint64_t kPacksPerBlock16 = kBlock16 / 8;
 __global__ __launch_bounds__(256) void mixed_blocked_mix(const GLOBAL u32x4* g, GLOBAL f32x4* s, GLOBAL u32x4* p,
                                                          uint64_t npack)
 {
-    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    const uint64_t k = unit_of<32>(blockIdx.x);
     if (k >= npack) return;
     // one block of fp32 state = 3 x kBlock floats = 3 x kBlock / 4 f32x4
     const uint64_t base = (k / kPacksPerBlock) * (3 * kBlock / 4) + 2 * (k % kPacksPerBlock);
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(256) void mixed_blocked_mix(const GLOBAL u32x4* g, 
 __global__ __launch_bounds__(256) void kahan_blocked_mix(const GLOBAL u32x4* g, GLOBAL u32x4* p, GLOBAL u32x4* s,
                                                          uint64_t npack)
 {
-    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    const uint64_t k = unit_of<64>(blockIdx.x);
     if (k >= npack) return;
     // one block of bf16 state = 3 x kBlock16 halves = 3 x kBlock16 / 8 u32x4
     GLOBAL u32x4* m = s + (k / kPacksPerBlock16) * (3 * kBlock16 / 8) + (k % kPacksPerBlock16);
@@ -125,13 +138,13 @@ __global__ __launch_bounds__(256) void kahan_blocked_mix(const GLOBAL u32x4* g, 
 
 __global__ __launch_bounds__(256) void copy_mix(const GLOBAL f32x4* src, GLOBAL f32x4* dst, uint64_t n4)
 {
-    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    const uint64_t k = word_of(blockIdx.x, gridDim.x);
     if (k < n4) __builtin_nontemporal_store(__builtin_nontemporal_load(src + k), dst + k);
 }
 
 __global__ __launch_bounds__(256) void read_mix(const GLOBAL f32x4* src, GLOBAL float* sink, uint64_t n4)
 {
-    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    const uint64_t k = word_of(blockIdx.x, gridDim.x);
     if (k >= n4) return;
     const f32x4 x = src[k];
     // never true for the finite inputs bench.py uses; keeps the load live
@@ -140,7 +153,7 @@ __global__ __launch_bounds__(256) void read_mix(const GLOBAL f32x4* src, GLOBAL 
 
 __global__ __launch_bounds__(256) void write_mix(GLOBAL f32x4* dst, uint64_t n4)
 {
-    const uint64_t k = chunk_of(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    const uint64_t k = word_of(blockIdx.x, gridDim.x);
     if (k < n4) dst[k] = f32x4{1.0f, 2.0f, 3.0f, (float)(k & 1023)};
 }
 
@@ -151,15 +164,16 @@ constexpr size_t kLds = 81920;   // two resident workgroups per CU, as the updat
 // kind: 0 mixed, 1 Kahan, 5 split master, 6 mixed with blocked state, 7 Kahan with
 // blocked state (n elements); 2 copy, 3 read, 4 write (n floats).
 // a..e: the buffers of the kind, in the order of the kernel's parameters; a
-// blocked state buffer holds whole blocks: ceil(n / 8192) of them for kind 6,
-// ceil(n / 16384) for kind 7.
+// blocked state buffer holds whole blocks: ceil(n / 16384) of them.
 // n must be a multiple of 8.  Returns the hipError_t of the launch.
 extern "C" int probe_launch(int kind, void* a, void* b, void* c, void* d, void* e, uint64_t n, void* stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (n % 8) return (int)hipErrorInvalidValue;
     const uint64_t items = (kind <= 1 || kind >= 5) ? n / 8 : n / 4;
-    const uint64_t grid = (items + 255) / 256;
+    // the step mixes: 8 workgroups per 2048-unit chunk; the plain ceilings: one
+    // workgroup per 256 words
+    const uint64_t grid = (kind == 2 || kind == 3 || kind == 4) ? (items + 255) / 256 : (items + 2047) / 2048 * 8;
     if (grid == 0 || grid > 0x7fffffffull) return (int)hipErrorInvalidValue;
     switch (kind) {
     case 0:

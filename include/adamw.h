@@ -86,9 +86,10 @@
  * nothing is enqueued, no buffer is touched, and adamw_last_error() describes
  * it.  A HIP failure while enqueuing returns ADAMW_E_HIP.  Faults inside a
  * kernel surface at the caller's next synchronisation.  One launch's grid
- * holds at most 2^32 - 1 lanes, so a plan of more than 16,777,215 chunks
- * (256-lane workgroups: about 34e9 elements at the default chunk, or that
- * many tensors of under 8 elements) is rejected with ADAMW_E_INVALID.
+ * holds at most 2^32 - 1 lanes, so a step plan of more than 2,097,151 chunks
+ * (8 workgroups of 256 lanes each: about 34e9 elements at the default chunk,
+ * or that many tensors of under 8 elements), or a check plan of more than
+ * 16,777,215, is rejected with ADAMW_E_INVALID.
  *
  * Concurrency.  Calls may come from several host threads.  Calls on different
  * streams run independently (each stream has its own workspace); two calls
@@ -103,7 +104,7 @@
 extern "C" {
 #endif
 
-#define ADAMW_ABI_VERSION 3
+#define ADAMW_ABI_VERSION 4
 
 typedef enum {
     ADAMW_OK = 0,
@@ -161,30 +162,25 @@ typedef struct {
 /* flat_mask bit: the blocked state layout.  exp_avg, exp_avg_sq and aux share
  * ONE flat buffer of the shard, ptr[2][0] (16-byte aligned; ptr[3], ptr[4] and
  * flat_mask bits 2-4 are ignored), made of ceil((shard_end - shard_begin) / B)
- * blocks of B elements, B = ADAMW_STATE_BLOCK_ELEMS(largest element size in
- * bytes among the step's state streams): 8192 when any of them is fp32 (the
- * mixed and split modes, fp32 AnyPrecision moments), 16384 when all are 16-bit
- * (ADAMW_PURE_KAHAN, bf16 AnyPrecision moments).  Block k holds the state of
- * the shard's elements [k*B, (k+1)*B), stream after stream:
+ * blocks of B = ADAMW_STATE_BLOCK_ELEMS = 16384 elements (every mode).  Block k
+ * holds the state of the shard's elements [k*B, (k+1)*B), stream after stream:
  *     [exp_avg x B][exp_avg_sq x B][aux x B]
- * each in its stream's dtype (an unused aux stream takes no room); the last
+ * each in its stream's dtype (an unused aux stream takes no room; a block is
+ * 192 KiB in the mixed and split modes, 96 KiB in ADAMW_PURE_KAHAN); the last
  * block is padded to B.  For optimizer-owned ZeRO state: the step's per-element
- * state traffic becomes one contiguous region per workgroup instead of three
+ * state traffic becomes one contiguous region per block instead of three
  * separate streams (fewer concurrently open DRAM rows; measured faster on
- * MI355X, and fastest when the largest sub-stream of a block spans 32 KiB).
- * param and grad keep their own layout (adamw_check_finite, which reads only
- * grads, ignores the bit).  B is a multiple of every update kernel's default
- * chunk, so splitting work at block edges never leaves a workgroup's lanes
- * idle.  The 16-byte vector path needs an element's state address and its
- * param/grad addresses to share their alignment: with per-tensor param/grad
- * buffers that start 16-byte aligned, a tensor whose flat start is not a
- * multiple of 8 elements runs element-wise (correct, but slower: on 10,000
- * tensors of random lengths the mixed fp16 step fell from 5.6 to 4.2 TB/s on
- * MI355X), so give such lists tensor lengths, or padding, that are multiples
- * of 8 (see ADAMW_FLAT_PAD8). */
+ * MI355X).  B is one default update chunk, so splitting work at block edges
+ * never leaves a workgroup's lanes idle.  param and grad keep their own layout
+ * (adamw_check_finite, which reads only grads, ignores the bit).  The 16-byte
+ * vector path needs an element's state address and its param/grad addresses
+ * to share their alignment: with per-tensor param/grad buffers that start
+ * 16-byte aligned, a tensor whose flat start is not a multiple of 8 elements
+ * runs element-wise (correct, but slower: on 10,000 tensors of random lengths
+ * the mixed fp16 step fell from 5.6 to 4.2 TB/s on MI355X), so give such lists
+ * tensor lengths, or padding, that are multiples of 8 (see ADAMW_FLAT_PAD8). */
 #define ADAMW_BLOCKED_STATE (1u << 8)
-#define ADAMW_STATE_BLOCK_BYTES 32768
-#define ADAMW_STATE_BLOCK_ELEMS(max_state_elem_bytes) (ADAMW_STATE_BLOCK_BYTES / (max_state_elem_bytes))
+#define ADAMW_STATE_BLOCK_ELEMS 16384
 /* flat_mask bit: the padded flat index.  The list's flat concatenation places
  * every tensor at a multiple of 8 elements: tensor i starts at the sum over
  * j < i of numel[j] rounded up to a multiple of 8, and the gaps hold no
@@ -313,27 +309,28 @@ int adamw_abi_version(void);
 int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, int for_check,
                            int64_t* out, int64_t cap);
 
-/* Launch form.  A step whose plan has at most max_chunks chunks (default
- * 4096, about 8.4e6 elements in 2048-element chunks) runs as ONE kernel
- * launch: every workgroup reads *d_found_inf, *d_step and the loss scale
- * itself, forms the step's scalars (the same binary64 formulas, so the same
- * bits), and the last workgroup to finish stores t into *d_step and advances
- * the loss scale.  Larger plans and empty lists run a one-lane prologue kernel
- * first.  Likewise adamw_check_finite over a plan of at most max_chunks of its
- * chunks is one launch whose last workgroup stores the flag, instead of a
- * zeroing kernel and the check.  The results are bit-identical either way; the
- * single launch saves a kernel launch and its dependency, which dominate
- * steps of a few million elements.  max_chunks: 0 = always two launches,
- * < 0 = restore the default.  Affects later calls on every stream.  Returns
- * the value now in force. */
-int64_t adamw_set_single_launch_max_chunks(int64_t max_chunks);
+/* Launch form.  A step whose grid has at most max_workgroups workgroups
+ * (default 4096: 512 chunks of 16384 elements, about 8.4e6 elements) runs as
+ * ONE kernel launch: every workgroup reads *d_found_inf, *d_step and the loss
+ * scale itself, forms the step's scalars (the same binary64 formulas, so the
+ * same bits), and the last workgroup to finish stores t into *d_step and
+ * advances the loss scale.  Larger plans and empty lists run a one-lane
+ * prologue kernel first.  Likewise adamw_check_finite over a grid of at most
+ * max_workgroups (one per check chunk) is one launch whose last workgroup
+ * stores the flag, instead of a zeroing kernel and the check.  The results are
+ * bit-identical either way; the single launch saves a kernel launch and its
+ * dependency, which dominate steps of a few million elements.  An update plan
+ * of c chunks launches 8c workgroups.  max_workgroups: 0 = always two
+ * launches, < 0 = restore the default.  Affects later calls on every stream.
+ * Returns the value now in force. */
+int64_t adamw_set_single_launch_max_workgroups(int64_t max_workgroups);
 
-/* Tuning knob: elements per vector chunk (one workgroup's share), a multiple
- * of 2048 in [2048, 1<<22], for every kernel (the overflow check uses 8x it);
- * 0 restores the built-in per-kernel defaults (workgroup size x 8: 2048 for the
- * update kernels, 16384 for the check).  Affects
- * plans built after the call.  Returns the value now in force (0 = defaults),
- * or -1 if rejected. */
+/* Tuning knob: elements per vector chunk, a multiple of 2048 in [2048, 1<<22],
+ * for every kernel (an update chunk is shared by 8 workgroups, one per XCD,
+ * each lane taking one 8-element pack per 16384 elements; a check chunk is one
+ * workgroup's); 0 restores the built-in defaults (16384 for the update kernels
+ * and the check).  Affects plans built after the call.  Returns the value now
+ * in force (0 = defaults), or -1 if rejected. */
 int64_t adamw_set_chunk_elems(int64_t elems);
 
 #ifdef __cplusplus

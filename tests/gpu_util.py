@@ -289,8 +289,8 @@ def blocked_state_keys(case) -> tuple:
 
 
 def state_block_of(dtypes) -> int:
-    """Elements per block of a blocked state buffer with state streams of these dtypes."""
-    return A.state_block(max(torch.empty(0, dtype=dt).element_size() for dt in dtypes))
+    """Elements per block of a blocked state buffer (the same for every set of state dtypes)."""
+    return A.STATE_BLOCK_ELEMS
 
 
 def build_blocked(case, b, e) -> torch.Tensor:

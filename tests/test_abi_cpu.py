@@ -47,8 +47,7 @@ def test_binding_constants_match_the_header():
 
     assert define("ADAMW_BLOCKED_STATE") == A.BLOCKED_STATE
     assert define("ADAMW_FLAT_PAD8") == A.FLAT_PAD8
-    assert define("ADAMW_STATE_BLOCK_BYTES") == A.STATE_BLOCK_BYTES
-    assert A.state_block(4) == 8192 and A.state_block(2) == 16384
+    assert define("ADAMW_STATE_BLOCK_ELEMS") == A.STATE_BLOCK_ELEMS == 16384
     for name, value in (("ADAMW_OK", A.OK), ("ADAMW_E_INVALID", A.E_INVALID), ("ADAMW_E_UNSUPPORTED", A.E_UNSUPPORTED),
                         ("ADAMW_E_NOMEM", A.E_NOMEM), ("ADAMW_E_HIP", A.E_HIP), ("ADAMW_F32", A.F32),
                         ("ADAMW_BF16", A.BF16), ("ADAMW_F16", A.F16), ("ADAMW_MIXED", A.MIXED),
@@ -179,7 +178,7 @@ def test_valid_call_reaches_hip():
 # ---------------------------------------------------------------------------
 
 # workgroup size x 8 of each kernel family
-DEFAULT_CHUNK = {A.MIXED: 2048, A.MIXED_SPLIT: 2048, A.PURE_KAHAN: 2048}
+DEFAULT_CHUNK = {A.MIXED: 16384, A.MIXED_SPLIT: 16384, A.PURE_KAHAN: 16384}
 
 
 def check_plan(rows, numels, b, e, ptrs, esz, chunk_elems):
@@ -271,9 +270,9 @@ def test_chunk_size_knob():
         A.adamw_set_chunk_elems(0)
     assert A.adamw_set_chunk_elems(0) == 0
     rows = A.adamw_plan_inspect(A.MIXED, A.BF16, tl)
-    assert max(r[2] for r in rows) == 2048
+    assert max(r[2] for r in rows) == 16384
     rows = A.adamw_plan_inspect(A.PURE_KAHAN, A.BF16, _tl(numels, esz=(2, 2, 2, 2, 2)))
-    assert max(r[2] for r in rows) == 2048
+    assert max(r[2] for r in rows) == 16384
 
 
 C_PROGRAM = r"""
@@ -345,7 +344,7 @@ def test_plan_blocked_state_never_straddles_a_block(seed):
     pos = b
     for (t, off, n, vec, flat, seg) in rows:
         assert flat == pos
-        assert (flat - b) // A.state_block(4) == (flat + n - 1 - b) // A.state_block(4)
+        assert (flat - b) // A.STATE_BLOCK_ELEMS == (flat + n - 1 - b) // A.STATE_BLOCK_ELEMS
         pos += n
     assert pos == e
 
@@ -374,7 +373,7 @@ def test_plan_padded_flat_index(seed):
     covered = []
     for (t, off, n, vec, flat, seg) in rows:
         assert slots[flat] == (t, off)
-        assert (flat - b) // A.state_block(4) == (flat + n - 1 - b) // A.state_block(4)
+        assert (flat - b) // A.STATE_BLOCK_ELEMS == (flat + n - 1 - b) // A.STATE_BLOCK_ELEMS
         covered += [(t, off + j) for j in range(n)]
         if seed % 2 == 0 and not vec:
             assert n < 8 and (off + n == numels[t] or flat + n == e), (t, off, n, numels[t])
@@ -394,14 +393,16 @@ def test_check_plan_ignores_blocked_bit():
     blocked = A.adamw_plan_inspect(A.MIXED, A.F16, A.TensorList(numels, [None, g, None, None, None],
                                                                 flat_mask=A.BLOCKED_STATE), True)
     assert blocked == plain
-    assert max(r[2] for r in plain) > A.state_block(4)
+    B = A.STATE_BLOCK_ELEMS
+    assert any(flat // B != (flat + n - 1) // B for (_, _, n, _, flat, _) in plain)   # a blocked plan would cut here
 
 
-@pytest.mark.parametrize("mode,esz,block", [(A.MIXED, (2, 2, 4, 4, 4), 8192), (A.PURE_KAHAN, (2, 2, 2, 2, 2), 16384)])
-def test_blocked_state_block_follows_the_widest_state_stream(mode, esz, block):
-    """B = 32 KiB / (widest state element): the segments of a blocked plan are
+@pytest.mark.parametrize("mode,esz", [(A.MIXED, (2, 2, 4, 4, 4)), (A.PURE_KAHAN, (2, 2, 2, 2, 2))])
+def test_blocked_state_blocks_cut_the_plan(mode, esz):
+    """B = 16384 elements in every mode: the segments of a blocked plan are
     exactly the pieces of the list cut at tensor edges and at multiples of B
     from the shard start, and no more."""
+    block = A.STATE_BLOCK_ELEMS
     rng = np.random.default_rng(7)
     numels = [int(x) for x in rng.integers(1, 60000, size=9)]
     total = sum(numels)
@@ -449,13 +450,14 @@ def test_blocked_state_needs_aligned_buffer():
 
 
 def test_plan_beyond_the_grid_limit_is_rejected():
-    """A launch's grid holds at most 2^32 - 1 lanes: with 256-lane workgroups a
-    plan may have at most 16,777,215 chunks.  One flat shard of exactly that
-    many 2048-element chunks is counted without building the table and passes
-    validation (then needs a GPU); one chunk more is rejected before any HIP call."""
-    limit = (2 ** 32 - 1) // 256
+    """A launch's grid holds at most 2^32 - 1 lanes: with 8 workgroups of 256
+    lanes per chunk a step plan may have at most 2,097,151 chunks.  One flat
+    shard of exactly that many 16384-element chunks is counted without building
+    the table and passes validation (then needs a GPU); one chunk more is
+    rejected before any HIP call."""
+    limit = (2 ** 32 - 1) // (8 * 256)
     for n_chunks, ok in ((limit, True), (limit + 1, False)):
-        n = n_chunks * 2048
+        n = n_chunks * 16384
         ptrs = [[FAKE + s * (1 << 40)] for s in range(5)]
         tl = A.TensorList([n], ptrs, 0, -1, 0x1f)
         with pytest.raises(A.AdamWError) as e:
@@ -481,14 +483,14 @@ def test_many_tiny_tensors_count_one_chunk_each():
 
 def test_single_launch_limit_knob():
     """The single-launch limit: any value >= 0 is taken as given, a negative one
-    restores the default (4096 chunks), and the call needs no GPU."""
+    restores the default (4096 workgroups), and the call needs no GPU."""
     try:
-        assert A.adamw_set_single_launch_max_chunks(0) == 0
-        assert A.adamw_set_single_launch_max_chunks(123) == 123
-        assert A.adamw_set_single_launch_max_chunks(-1) == 4096
-        assert A.adamw_set_single_launch_max_chunks(-7) == 4096
+        assert A.adamw_set_single_launch_max_workgroups(0) == 0
+        assert A.adamw_set_single_launch_max_workgroups(123) == 123
+        assert A.adamw_set_single_launch_max_workgroups(-1) == 4096
+        assert A.adamw_set_single_launch_max_workgroups(-7) == 4096
     finally:
-        A.adamw_set_single_launch_max_chunks(-1)
+        A.adamw_set_single_launch_max_workgroups(-1)
 
 
 def _plan_rows(mode, tl):
@@ -506,7 +508,7 @@ def _plan_rows(mode, tl):
 def test_plan_beyond_32_bit_offsets(shard, mode):
     """One tensor longer than 2^32 elements (a ragged tail of 5 after the last
     pack) and a short one behind it: the plan covers the range exactly, with
-    64-bit offsets inside the tensor, whole 2,048-element vector chunks between
+    64-bit offsets inside the tensor, whole 16,384-element vector chunks between
     the peeled ends, and every row inside its tensor (the layout of the GPU test
     at this size: arenas with tensors at 128-element offsets)."""
     big = 2 ** 32 + 6157
@@ -524,13 +526,13 @@ def test_plan_beyond_32_bit_offsets(shard, mode):
     assert (off + n <= np.array(numels, dtype=np.int64)[t]).all()
     assert off.max() > 2 ** 32 if e > 2 ** 32 else True
     v = vec == 1
-    assert (n[v] % 8 == 0).all() and (n[v] <= 2048).all() and (n[~v] <= 4096).all()
+    assert (n[v] % 8 == 0).all() and (n[v] <= 16384).all() and (n[~v] <= 4096).all()
     for s in range(5):
         base = np.array([ptrs[s][0], ptrs[s][1]], dtype=np.int64)
         assert ((base[t[v]] + off[v] * esz[s]) % 16 == 0).all()
     # inside the big tensor, only its peeled ends run element-wise
     big_rows = t == 0
-    assert (~v[big_rows]).sum() <= 2 and (n[big_rows & v] == 2048).sum() >= (min(e, big) - b) // 2048 - 2
+    assert (~v[big_rows]).sum() <= 2 and (n[big_rows & v] == 16384).sum() >= (min(e, big) - b) // 16384 - 2
 
 
 XCD_MAP_PROGRAM = r"""
@@ -554,7 +556,27 @@ static int check(uint32_t nb) {
     }
     return 0;
 }
+// the lanes of an update chunk's parts take each of its packs exactly once
+static int check_tiles(uint32_t block, uint32_t p) {
+    const uint32_t packs = adamw::kXcdParts * block;
+    std::vector<unsigned char> seen(packs, 0);
+    for (uint32_t part = 0; part < (uint32_t)adamw::kXcdParts; ++part)
+        for (uint32_t tid = 0; tid < block; ++tid) {
+            const uint32_t k = adamw::tile_pack(tid, part, p);
+            if (k >= packs || seen[k]) return 1;
+            seen[k] = 1;
+            // a tile of p packs lies with one part
+            if ((k / p) % adamw::kXcdParts != part) return 2;
+        }
+    return 0;
+}
 int main() {
+    const uint32_t shapes[][2] = {{(uint32_t)adamw::kBlockMixed, (uint32_t)adamw::tile_packs(4)},
+                                  {(uint32_t)adamw::kBlockPure, (uint32_t)adamw::tile_packs(2)},
+                                  {(uint32_t)adamw::kBlockPure, (uint32_t)adamw::tile_packs(4)},
+                                  {256u, 1u}, {256u, 256u}, {128u, 16u}};
+    for (auto& sp : shapes)
+        if (int e = check_tiles(sp[0], sp[1])) { printf("tiles %u/%u err=%d\n", sp[0], sp[1], e); return 1; }
     for (uint32_t nb = 1; nb <= 20000; ++nb)
         if (int e = check(nb)) { printf("nb=%u err=%d\n", nb, e); return 1; }
     const uint32_t big[] = {642458u, 1283467u, 16777215u};
@@ -567,8 +589,9 @@ int main() {
 
 
 def test_xcd_chunk_map_is_a_bijection(tmp_path):
-    """The workgroup -> chunk map the update and check kernels use (constexpr in
-    layout.hpp, compiled here by the host compiler from the same header)."""
+    """The overflow check's workgroup -> chunk map, and the update kernels'
+    (part, lane) -> pack map inside a chunk (constexpr in layout.hpp, compiled
+    here by the host compiler from the same header): each a bijection."""
     src = tmp_path / "xcd.cpp"
     src.write_text(XCD_MAP_PROGRAM)
     exe = tmp_path / "xcd"

@@ -1,6 +1,6 @@
-"""GPU: the two launch forms of a step give the same bits.  Plans of at most
-adamw_set_single_launch_max_chunks chunks run as one launch of the update
-kernel, which forms the step's scalars in every workgroup and lets the last
+"""GPU: the two launch forms of a step give the same bits.  Grids of at most
+adamw_set_single_launch_max_workgroups workgroups (8 per chunk of a step) run
+as one launch of the update kernel, which forms the step's scalars in every workgroup and lets the last
 workgroup advance the counter; larger plans run the prologue kernel first.
 Every element, the counter and the skip behaviour must not depend on the form,
 and both must match the oracle."""
@@ -19,9 +19,9 @@ SIZES = [0, 1, 7, 8, 9, 2047, 2048, 2049, 16385, 100_003, 3, 40_000]
 def single_launch_limit():
     """Sets the single-launch limit for one test and restores the default."""
     def set_limit(n):
-        return A.adamw_set_single_launch_max_chunks(n)
+        return A.adamw_set_single_launch_max_workgroups(n)
     yield set_limit
-    A.adamw_set_single_launch_max_chunks(-1)
+    A.adamw_set_single_launch_max_workgroups(-1)
 
 
 def _plan_chunks(case: Case) -> int:
@@ -41,7 +41,7 @@ def test_forms_are_bit_identical_and_match_the_oracle(mode, p_dtype, single_laun
     kw = dict(p_dtype=p_dtype, align_elems=3, loss_scale=scale, random_moments=True)
     one, two = Case(mode, SIZES, seed=911, **kw), Case(mode, SIZES, seed=911, **kw)
     if not mode.startswith("pure"):
-        assert 0 < _plan_chunks(one) <= 4096
+        assert 0 < 8 * _plan_chunks(one) <= 4096
     hg, ho = hp_pair(inv_scale=1.0 / scale)
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     for s in range(5):
@@ -65,11 +65,11 @@ def test_forms_are_bit_identical_and_match_the_oracle(mode, p_dtype, single_laun
 
 @pytest.mark.parametrize("extra", [0, 1])
 def test_limit_boundary(extra, single_launch_limit):
-    """A plan of exactly the limit runs as one launch; one chunk more takes the
-    prologue.  Both match the oracle over 3 steps."""
+    """A grid of exactly the limit (8 workgroups per chunk) runs as one launch;
+    one workgroup more takes the prologue.  Both match the oracle over 3 steps."""
     case = Case("mixed", SIZES, seed=912, align_elems=3, random_moments=True)
     k = _plan_chunks(case)
-    single_launch_limit(k - extra)
+    single_launch_limit(8 * k - extra)
     hg, ho = hp_pair()
     for s in range(3):
         if s:
