@@ -456,7 +456,7 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
     constexpr bool F16 = (MODE == 1);   // MODE 3 uses bf16 param/grad
     constexpr int NTM = ADAMW_NT_MIXED;
     constexpr int NTG = ADAMW_NT_MIXED | (ADAMW_NT_MIXED_GRAD ? 1 : 0);   // the gradient's loads
-    constexpr int P = tile_packs(4);   // every mixed-family mode keeps fp32 moments
+    constexpr int P = MODE == 3 ? kTilePacks : kTilePacksMixed;   // tiles of 512 / 256 elements
     constexpr uint32_t kStride = kXcdParts * kBlockMixed;
     const uint32_t part = blockIdx.x % kXcdParts;
     const DevChunk ch = chunks[blockIdx.x / kXcdParts];
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
     float scale = 0.0f;
     if (!begin_step<FUSED>(sc, fs, c, t, scale)) return;
     constexpr int NT = ADAMW_NT_PURE;
-    constexpr int P = tile_packs(M32 || V32 ? 4 : 2);   // 1 KiB tiles of the widest state stream
+    constexpr int P = kTilePacks;   // tiles of 512 elements
     constexpr uint32_t kStride = kXcdParts * kBlockPure;
     const uint32_t part = blockIdx.x % kXcdParts;
     const DevChunk ch = chunks[blockIdx.x / kXcdParts];
@@ -788,12 +788,18 @@ hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32
 // workgroups on a CU.  Measured on MI355X with the OPT-1.3B list, 8 waves per CU
 // (mixed: two 256-lane workgroups) and 16 (pure: four 256-lane workgroups)
 // stream faster than the register-limited 20-32 waves: fewer concurrent address
-// streams per CU keep more DRAM rows open.
+// streams per CU keep more DRAM rows open.  The widest pure-bf16 step (fp32
+// exp_avg and exp_avg_sq plus compensation, 26 B per element) runs at the mixed
+// family's 8 waves: 4 % faster than at 16 on blocked state, while the other
+// pure steps lost 2-5 % at 8.
 #ifndef ADAMW_LDS_MIXED
 #define ADAMW_LDS_MIXED 81920
 #endif
 #ifndef ADAMW_LDS_PURE
 #define ADAMW_LDS_PURE 40960
+#endif
+#ifndef ADAMW_LDS_PURE_WIDE
+#define ADAMW_LDS_PURE_WIDE 81920
 #endif
 
 // Two-launch form (fused == nullptr): the update kernel reads the prologue's
@@ -816,7 +822,8 @@ static hipError_t launch_update_as(int kernel, const DevSeg* segs, const DevChun
         break;
 #define ADAMW_PURE_CASE(M, V, K)                                                                          \
     case kKernelPure + (M) * 4 + (V) * 2 + (K):                                                            \
-        hipLaunchKernelGGL((update_pure_kernel<M, V, K, FUSED>), grid, block_pure, ADAMW_LDS_PURE, stream, segs, \
+        hipLaunchKernelGGL((update_pure_kernel<M, V, K, FUSED>), grid, block_pure,                            \
+                           (M) && (V) && (K) ? ADAMW_LDS_PURE_WIDE : ADAMW_LDS_PURE, stream, segs,              \
                            chunks, d_scalars, fs);                                                         \
         break;
         ADAMW_PURE_CASE(0, 0, 0) ADAMW_PURE_CASE(0, 0, 1) ADAMW_PURE_CASE(0, 1, 0) ADAMW_PURE_CASE(0, 1, 1)

@@ -40,19 +40,20 @@ constexpr uint32_t kCountMask = 0x7fffffffu;
 constexpr int64_t kElemChunkElems = 4096;       // element chunk
 // An update kernel's chunk is shared by kXcdParts workgroups, consecutive in
 // launch order, so one on each XCD (the dispatcher hands workgroup b to XCD
-// b % 8).  The chunk is cut into tiles of kTileBytes of the widest state
-// stream (256 elements with an fp32 state stream, 512 when all state is
-// 16-bit); tile t goes to part t % 8, and each lane of a part takes one 8-element
-// pack.  All XCDs thus sweep one contiguous region together, interleaved at
-// 1 KiB.  On MI355X (OPT-1.3B list, against giving each XCD one contiguous run
-// of 2048-element chunks) this streamed the mixed step 7 % faster on blocked
-// state (with 16384-element blocks) and 6.5 % per tensor, and the Kahan step
-// 1 % faster blocked and 5 % per tensor; tiles of 64-128 and 512-1024 elements
-// (fp32 state) or 256 and 1024-2048 (bf16 state) were slower.
+// b % 8).  The chunk is cut into tiles of packs; tile t goes to part t % 8, and
+// each lane of a part takes one 8-element pack per 2048 packs of the chunk.
+// All XCDs thus sweep one contiguous region together.  On MI355X (OPT-1.3B
+// list, against giving each XCD one contiguous run of 2048-element chunks)
+// this streamed the mixed step 5-7 % faster on blocked state (16384-element
+// blocks) and per tensor, and the Kahan step 1-2 % faster blocked and 5-9 % per
+// tensor.  Tile sizes, from interleaved A/B runs: 256 elements (1 KiB of the
+// fp32 master) for the mixed step, whose param stream is written only; 512
+// elements (1 KiB of a 16-bit param) for every step that reads and writes the
+// param (split master, the pure-bf16 family), 1-2 % ahead of 256 there.
+// Smaller and larger tiles (64-128, 1024-2048 elements) were slower.
 constexpr int kXcdParts = 8;
-constexpr int kTileBytes = 1024;
-// packs per tile for a widest state element of `bytes` bytes (4 or 2)
-constexpr int tile_packs(int bytes) { return kTileBytes / (bytes * kPack); }
+constexpr int kTilePacksMixed = 32;
+constexpr int kTilePacks = 64;
 // The pack of a chunk taken by lane tid of part `part` (per kXcdParts * block
 // packs): tile t of p packs belongs to part t % kXcdParts, so
 //     ((tid / p) * kXcdParts + part) * p + tid % p,

@@ -3,8 +3,8 @@
 // Kernels that move exactly the bytes of the fused AdamW step's streams, in the
 // same launch shape as the library's update kernel (256 lanes, one 8-element
 // pack per lane, each chunk of 2048 packs shared by 8 consecutive workgroups,
-// one per XCD, in 1 KiB tiles of the widest state stream; two workgroups per
-// CU), but do no optimizer arithmetic.  Their rate is the ceiling
+// one per XCD, in tiles of 256 elements for the mixed step and 512 for the
+// others; two workgroups per CU), but do no optimizer arithmetic.  Their rate is the ceiling
 // of the access pattern itself; the update kernel's rate divided by it says how
 // much of the pattern's bandwidth the arithmetic costs.  A plain copy, a
 // read-only and a write-only kernel give the HBM ceilings of simpler mixes.
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void mixed_mix(const GLOBAL u32x4* g, GLOBAL f
 __global__ __launch_bounds__(256) void split_mix(const GLOBAL u32x4* g, GLOBAL u32x4* p, GLOBAL u32x4* r,
                                                  GLOBAL f32x4* m, GLOBAL f32x4* v, uint64_t npack)
 {
-    const uint64_t k = unit_of<32>(blockIdx.x);
+    const uint64_t k = unit_of<64>(blockIdx.x);
     if (k >= npack) return;
     const u32x4 gv = g[k], pv = p[k], rv = r[k];
     const f32x4 m0 = m[2 * k], m1 = m[2 * k + 1], v0 = v[2 * k], v1 = v[2 * k + 1];

@@ -571,9 +571,9 @@ static int check_tiles(uint32_t block, uint32_t p) {
     return 0;
 }
 int main() {
-    const uint32_t shapes[][2] = {{(uint32_t)adamw::kBlockMixed, (uint32_t)adamw::tile_packs(4)},
-                                  {(uint32_t)adamw::kBlockPure, (uint32_t)adamw::tile_packs(2)},
-                                  {(uint32_t)adamw::kBlockPure, (uint32_t)adamw::tile_packs(4)},
+    const uint32_t shapes[][2] = {{(uint32_t)adamw::kBlockMixed, (uint32_t)adamw::kTilePacksMixed},
+                                  {(uint32_t)adamw::kBlockMixed, (uint32_t)adamw::kTilePacks},
+                                  {(uint32_t)adamw::kBlockPure, (uint32_t)adamw::kTilePacks},
                                   {256u, 1u}, {256u, 256u}, {128u, 16u}};
     for (auto& sp : shapes)
         if (int e = check_tiles(sp[0], sp[1])) { printf("tiles %u/%u err=%d\n", sp[0], sp[1], e); return 1; }
