@@ -2,7 +2,7 @@
 // per-(device, stream) workspace, and the launch sequence
 //   [check: zero flag -> check kernel]   (adamw_check_finite)
 //   [step:  prologue  -> update kernel]  (adamw_step / adamw_multi_tensor_step[_amp])
-//   small plans (up to a few thousand chunks): the check kernel alone, the
+//   small grids (up to a few thousand workgroups): the check kernel alone, the
 //   update kernel alone
 // Nothing here synchronises with the device except when a workspace has to
 // grow (the old buffer may still be read by work queued on its stream).

@@ -44,13 +44,14 @@ constexpr int64_t kElemChunkElems = 4096;       // element chunk
 // each lane of a part takes one 8-element pack per 2048 packs of the chunk.
 // All XCDs thus sweep one contiguous region together.  On MI355X (OPT-1.3B
 // list, against giving each XCD one contiguous run of 2048-element chunks)
-// this streamed the mixed step 5-7 % faster on blocked state (16384-element
-// blocks) and per tensor, and the Kahan step 1-2 % faster blocked and 5-9 % per
-// tensor.  Tile sizes, from interleaved A/B runs: 256 elements (1 KiB of the
+// this streamed the mixed step 7 % faster on blocked state (16384-element
+// blocks) and 4-6.5 % per tensor, and the Kahan step 1 % faster blocked and
+// 5-9 % per tensor; only the split-master step on blocked state lost (4 %).  Tile sizes, from interleaved A/B runs: 256 elements (1 KiB of the
 // fp32 master) for the mixed step, whose param stream is written only; 512
 // elements (1 KiB of a 16-bit param) for every step that reads and writes the
 // param (split master, the pure-bf16 family), 1-2 % ahead of 256 there.
-// Smaller and larger tiles (64-128, 1024-2048 elements) were slower.
+// Smaller and larger tiles (64-128, 512-1024 elements for the mixed step;
+// 256 and 1024-2048 for Kahan) were slower.
 constexpr int kXcdParts = 8;
 constexpr int kTilePacksMixed = 32;
 constexpr int kTilePacks = 64;
@@ -151,9 +152,9 @@ constexpr int64_t kDoneWords = (kDoneLanes + 1) * kDoneStrideWords;
 constexpr int64_t kWorkspaceBytes = kDoneOffset + kDoneWords * 4;
 
 // Default largest grid, in workgroups, that runs as a single launch.  Measured
-// on MI355X (mixed step, one tensor): the single launch takes 30 % off a step
-// of 64k-256k elements, 11 % at 1M and 4 % at 4M, and ties from 8M (4096
-// workgroups) up, where the prologue launch no longer shows.
+// on MI355X (mixed step, one tensor, pipelined steps): the single launch takes
+// 28-32 % off a step of 64k-256k elements, 7 % at 1M and 2 % at 4M, and ties
+// from 8M (4096 workgroups) up, where the prologue launch no longer shows.
 constexpr int64_t kSingleLaunchMaxWorkgroups = 4096;
 
 // A single-launch step: the update kernel forms the step's scalars itself in
