@@ -234,6 +234,11 @@ def probes(n, stream):
     run(2, [src, dst], f, 8 * f, "copy")
     run(3, [src, dst], f, 4 * f, "read")
     run(4, [dst], f, 4 * f, "write")
+    # the same in the update kernels' shape (8 workgroups per chunk, 1 KiB tiles), 2 per CU,
+    # four 16-byte words in flight per lane
+    run(8, [src, dst], f, 8 * f, "copy_wide")
+    run(9, [src, dst], f, 4 * f, "read_wide")
+    run(10, [dst], f, 4 * f, "write_wide")
     del src, dst
     torch.cuda.empty_cache()
     return out
