@@ -42,7 +42,7 @@ _STATUS = {0: "ADAMW_OK", 1: "ADAMW_E_INVALID", 2: "ADAMW_E_UNSUPPORTED", 3: "AD
 EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_amp", "adamw_pure_multi_tensor_step",
             "adamw_check_finite",
             "adamw_last_error", "adamw_release_workspace", "adamw_abi_version", "adamw_plan_inspect",
-            "adamw_set_chunk_elems", "adamw_set_single_launch_max_workgroups")
+            "adamw_plan_inspect_bytes", "adamw_set_chunk_elems", "adamw_set_single_launch_max_workgroups")
 
 
 class adamw_hparams(ctypes.Structure):
@@ -102,6 +102,10 @@ def _declare(_lib):
     _lib.adamw_plan_inspect.restype = ctypes.c_int64
     _lib.adamw_plan_inspect.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list), ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
+    _lib.adamw_plan_inspect_bytes.restype = ctypes.c_int64
+    _lib.adamw_plan_inspect_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_pure_precision),
+                                              ctypes.POINTER(adamw_tensor_list), ctypes.c_int,
+                                              ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64]
     _lib.adamw_set_chunk_elems.restype = ctypes.c_int64
     _lib.adamw_set_chunk_elems.argtypes = [ctypes.c_int64]
     _lib.adamw_set_single_launch_max_workgroups.restype = ctypes.c_int64
@@ -285,6 +289,24 @@ def adamw_plan_inspect(mode: int, p_dtype: int, tensors: TensorList, for_check: 
     n2 = _lib.adamw_plan_inspect(mode, p_dtype, ctypes.byref(tensors.c), int(for_check), buf, n)
     assert n2 == n
     return [tuple(buf[6 * i:6 * i + 6]) for i in range(n)]
+
+
+def adamw_plan_inspect_bytes(mode: int, p_dtype: int, tensors: TensorList, for_check: bool = False,
+                             prec: "PurePrecision" = None):
+    """The chunk plan with the device bytes of every chunk: (rows, ranges), rows
+    an int64 array (chunks, 6) of adamw_plan_inspect's fields, ranges a uint64
+    array (chunks, 5, 2) of [lo, hi) per stream, (0, 0) for an untouched stream."""
+    import numpy as np
+    pc = ctypes.byref(prec.c()) if prec is not None else None
+    n = _lib.adamw_plan_inspect_bytes(mode, p_dtype, pc, ctypes.byref(tensors.c), int(for_check), None, 0)
+    if n < 0:
+        raise AdamWError(E_INVALID, adamw_last_error())
+    out = np.zeros((max(n, 1), 16), dtype=np.uint64)
+    n2 = _lib.adamw_plan_inspect_bytes(mode, p_dtype, pc, ctypes.byref(tensors.c), int(for_check),
+                                       out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), n)
+    assert n2 == n
+    out = out[:n]
+    return out[:, :6].view(np.int64), out[:, 6:].reshape(n, NUM_STREAMS, 2)
 
 
 def adamw_set_chunk_elems(elems: int) -> int:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libadamw_amd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["kernels.hip", "plan.cpp", "api.cpp"]
+SOURCES = ["kernels.hip", "plan.cpp", "validate.cpp", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -36,20 +36,16 @@ FLAGS = [
 ]
 
 
-PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
-PROBE_LIB = os.path.join(ROOT, "libbench_probe.so")
-
-
 def build(verbose: bool = False) -> str:
-    _hipcc([os.path.join(CSRC, s) for s in SOURCES], LIB_PATH, verbose)
-    # the benchmark's memory-ceiling probes (never loaded by the library)
-    _hipcc([PROBE_SRC], PROBE_LIB, verbose)
+    hipcc([os.path.join(CSRC, s) for s in SOURCES], LIB_PATH, verbose, include=[INCLUDE, CSRC])
     return LIB_PATH
 
 
-def _hipcc(srcs, out, verbose):
+def hipcc(srcs, out, verbose=False, include=()):
+    """Compiles `srcs` into the shared library `out` for gfx950 with FLAGS."""
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
+    inc = [a for d in include for a in ("-I", d)]
+    cmd = [HIPCC, *FLAGS, *inc, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

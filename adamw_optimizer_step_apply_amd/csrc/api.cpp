@@ -62,6 +62,7 @@ struct PlanSlot {
     bool upload_in_flight = false;
     std::vector<int64_t> key;
     bool valid = false;
+    bool pinned = false;   // used under graph capture: never evicted, resized or rewritten
     int64_t n_segs = 0, n_chunks = 0;
 
     const DevSeg* segs() const { return static_cast<const DevSeg*>(dev); }
@@ -79,11 +80,13 @@ struct PlanSlot {
         uploaded = nullptr;
         dev_cap = host_cap = 0;
         valid = false;
+        pinned = false;
         key.clear();
     }
 };
 
-// Plans cached per stream, most recently used first.  A training loop that
+// Plans cached per stream, most recently used first: at most this many slots
+// that no captured graph holds, plus every pinned one.  A training loop that
 // alternates a few lists (e.g. two parameter groups, or a step and its
 // overflow check) keeps each one's table resident instead of re-uploading it.
 constexpr size_t kPlansPerStream = 8;
@@ -146,11 +149,18 @@ private:
 // Returns (in *out) a slot of `ws` holding the device plan of (mode, dtype,
 // list, for_check): a cached one if every input matches (the key holds every
 // input the plan depends on, so a hit was validated when it was built), else
-// the list is validated and planned, and the least recently used slot takes
-// the new plan.  An invalid list returns its error before any HIP call and
-// leaves the cache as it was.
+// the list is validated and planned, and a slot chosen by choose_plan_slot
+// takes the new plan.  An invalid list returns its error before any HIP call
+// and leaves the cache as it was.
+//
+// Under graph capture the graph records the slot's device address: a hit pins
+// the slot, so that later calls never evict, resize or rewrite it while the
+// graph may replay (pinned slots are freed by adamw_release_workspace only).
+// A miss under capture is refused: uploading a table would need a copy, and a
+// table that grows a stream synchronisation, neither of which belongs in the
+// graph.
 adamw_status ensure_plan(StreamWorkspace& ws, int64_t tag, const int esz[kStreams], const adamw_tensor_list* list,
-                         int64_t chunk_elems, hipStream_t stream, PlanSlot** out)
+                         int64_t chunk_elems, hipStream_t stream, bool under_capture, PlanSlot** out)
 {
     std::vector<int64_t> key;
     plan_key(tag, esz, list, chunk_elems, key);
@@ -159,6 +169,7 @@ adamw_status ensure_plan(StreamWorkspace& ws, int64_t tag, const int esz[kStream
         if (plans[i]->valid && plans[i]->key == key) {
             std::rotate(plans.begin(), plans.begin() + (ptrdiff_t)i, plans.begin() + (ptrdiff_t)i + 1);
             *out = plans.front().get();
+            if (under_capture) (*out)->pinned = true;
             return ADAMW_OK;
         }
     }
@@ -166,9 +177,16 @@ adamw_status ensure_plan(StreamWorkspace& ws, int64_t tag, const int esz[kStream
     std::string err;
     adamw_status st = build_plan(esz, list, chunk_elems, max_chunks_of(tag), &plan, err);
     if (st != ADAMW_OK) return fail(st, err);
+    if (under_capture)
+        return fail(ADAMW_E_INVALID,
+                    "this list's chunk table is not on the device: make the same call once on this stream "
+                    "before capturing it into a graph");
 
-    if (plans.size() < kPlansPerStream) plans.emplace_back(new PlanSlot());
-    std::rotate(plans.begin(), plans.end() - 1, plans.end());   // LRU slot to the front
+    std::vector<bool> pinned(plans.size());
+    for (size_t i = 0; i < plans.size(); ++i) pinned[i] = plans[i]->pinned;
+    const size_t pick = choose_plan_slot(pinned, kPlansPerStream);
+    if (pick == plans.size()) plans.emplace_back(new PlanSlot());
+    std::rotate(plans.begin(), plans.begin() + (ptrdiff_t)pick, plans.begin() + (ptrdiff_t)pick + 1);
     PlanSlot& slot = *plans.front();
     slot.valid = false;
     *out = &slot;
@@ -267,44 +285,45 @@ adamw_status validate_list(int64_t tag, const int esz[kStreams], const adamw_ten
 
 adamw_status check_hparams(const adamw_hparams* hp)
 {
-    if (!hp) return fail(ADAMW_E_INVALID, "hparams is null");
-    const float v[6] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->inv_loss_scale};
-    for (float x : v)
-        if (!std::isfinite(x)) return fail(ADAMW_E_INVALID, "hyper-parameters must be finite");
-    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
-        return fail(ADAMW_E_INVALID, "beta1 and beta2 must lie in [0, 1)");
-    if (hp->eps < 0.0f) return fail(ADAMW_E_INVALID, "eps < 0");
-    if (hp->lr < 0.0f) return fail(ADAMW_E_INVALID, "lr < 0");
-    if (hp->weight_decay < 0.0f) return fail(ADAMW_E_INVALID, "weight_decay < 0");
-    if (!(hp->inv_loss_scale > 0.0f)) return fail(ADAMW_E_INVALID, "inv_loss_scale must be > 0");
-    return ADAMW_OK;
+    std::string err;
+    adamw_status st = adamw::check_hparams(hp, err);
+    return st == ADAMW_OK ? st : fail(st, err);
 }
 
 adamw_status basic_list_check(const adamw_tensor_list* list)
 {
-    if (!list) return fail(ADAMW_E_INVALID, "tensor list is null");
-    if (list->n_tensors < 0) return fail(ADAMW_E_INVALID, "n_tensors < 0");
-    if (list->n_tensors > 0 && !list->numel) return fail(ADAMW_E_INVALID, "numel array is null");
-    return ADAMW_OK;
+    std::string err;
+    adamw_status st = adamw::basic_list_check(list, err);
+    return st == ADAMW_OK ? st : fail(st, err);
 }
 
 adamw_status check_scaler(const adamw_loss_scaler* sc)
 {
-    if (!sc) return fail(ADAMW_E_INVALID, "loss scaler is null");
-    if (!std::isfinite(sc->growth_factor) || !(sc->growth_factor >= 1.0f))
-        return fail(ADAMW_E_INVALID, "growth_factor must be finite and >= 1");
-    if (!(sc->backoff_factor > 0.0f && sc->backoff_factor <= 1.0f))
-        return fail(ADAMW_E_INVALID, "backoff_factor must lie in (0, 1]");
-    if (sc->growth_interval < 1) return fail(ADAMW_E_INVALID, "growth_interval must be >= 1");
+    std::string err;
+    adamw_status st = adamw::check_scaler(sc, err);
+    return st == ADAMW_OK ? st : fail(st, err);
+}
+
+// Whether `stream` is being captured into a HIP graph right now.
+adamw_status capturing(hipStream_t stream, bool* out)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail("hipStreamIsCapturing", e);
+    *out = cs != hipStreamCaptureStatusNone;
     return ADAMW_OK;
 }
 
 // The stream's 256-byte scalar block and the single-launch completion counters
 // after it, allocated on first use (the counters start at zero, and every
 // single launch leaves them at zero).  Returns the counters in *done.
-adamw_status ensure_workspace_block(StreamWorkspace& ws, hipStream_t stream, uint32_t** done)
+adamw_status ensure_workspace_block(StreamWorkspace& ws, hipStream_t stream, bool under_capture, uint32_t** done)
 {
     if (!ws.scalars) {
+        if (under_capture)
+            return fail(ADAMW_E_INVALID,
+                        "this stream has no workspace yet: make the same call once on it before capturing it "
+                        "into a graph");
         hipError_t e = hipMalloc(reinterpret_cast<void**>(&ws.scalars), kWorkspaceBytes);
         if (e != hipSuccess) { ws.scalars = nullptr; return fail(ADAMW_E_NOMEM, "hipMalloc of the scalar block failed"); }
         uint32_t* d = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws.scalars) + kDoneOffset);
@@ -345,6 +364,32 @@ int64_t check_chunk_elems()
     return c ? c : kCheckChunkElems;
 }
 
+// Row i of adamw_plan_inspect: {tensor, offset in the tensor, count, kind, flat position, segment}.
+void inspect_row(const Plan& plan, size_t i, int64_t* r)
+{
+    const DevChunk& c = plan.chunks[i];
+    const SegInfo& si = plan.info[c.seg];
+    r[0] = si.tensor;
+    r[1] = si.tensor_off + (int64_t)c.off;
+    r[2] = (int64_t)(c.n_kind & kCountMask);
+    r[3] = (c.n_kind & kVecBit) ? 1 : 0;
+    r[4] = si.flat + (int64_t)c.off;
+    r[5] = (int64_t)c.seg;
+}
+
+StepKind kind_of_pure(const adamw_pure_precision& prec)
+{
+    const int m32 = prec.exp_avg == ADAMW_F32, v32 = prec.exp_avg_sq == ADAMW_F32, kahan = prec.kahan != 0;
+    StepKind kind{};
+    kind.kernel = kKernelPure + 4 * m32 + 2 * v32 + kahan;
+    kind.esz[ADAMW_STREAM_PARAM] = 2;
+    kind.esz[ADAMW_STREAM_GRAD] = 2;
+    kind.esz[ADAMW_STREAM_EXP_AVG] = m32 ? 4 : 2;
+    kind.esz[ADAMW_STREAM_EXP_AVG_SQ] = v32 ? 4 : 2;
+    kind.esz[ADAMW_STREAM_AUX] = kahan ? 2 : 0;
+    return kind;
+}
+
 StepKind kind_of_mode(adamw_mode mode, adamw_dtype p_dtype)
 {
     StepKind k{};
@@ -375,10 +420,12 @@ adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const 
     std::lock_guard<std::mutex> lk(ws->mu);
     DeviceGuard dg(ws->device);
     hipError_t e;
+    bool cap = false;
+    if ((st = capturing(stream, &cap)) != ADAMW_OK) return st;
     uint32_t* done = nullptr;
-    if ((st = ensure_workspace_block(*ws, stream, &done)) != ADAMW_OK) return st;
+    if ((st = ensure_workspace_block(*ws, stream, cap, &done)) != ADAMW_OK) return st;
     PlanSlot* plan = nullptr;
-    if ((st = ensure_plan(*ws, kind.kernel, kind.esz, list, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
+    if ((st = ensure_plan(*ws, kind.kernel, kind.esz, list, chunk_elems, stream, cap, &plan)) != ADAMW_OK) return st;
     // Small plans: one launch.  An empty plan, whose step still advances the
     // counter (and the loss scale), keeps the prologue kernel.
     if (single_launch(plan->n_chunks * kXcdParts)) {
@@ -427,19 +474,10 @@ adamw_status adamw_pure_multi_tensor_step(const adamw_pure_precision* prec, cons
                                           void* hip_stream)
 {
     g_err.clear();
-    if (!prec) return fail(ADAMW_E_INVALID, "precision descriptor is null");
-    const bool ok_m = prec->exp_avg == ADAMW_F32 || prec->exp_avg == ADAMW_BF16;
-    const bool ok_v = prec->exp_avg_sq == ADAMW_F32 || prec->exp_avg_sq == ADAMW_BF16;
-    if (!ok_m || !ok_v) return fail(ADAMW_E_UNSUPPORTED, "exp_avg / exp_avg_sq dtype must be ADAMW_F32 or ADAMW_BF16");
-    const int m32 = prec->exp_avg == ADAMW_F32, v32 = prec->exp_avg_sq == ADAMW_F32, kahan = prec->kahan != 0;
-    StepKind kind{};
-    kind.kernel = kKernelPure + 4 * m32 + 2 * v32 + kahan;
-    kind.esz[ADAMW_STREAM_PARAM] = 2;
-    kind.esz[ADAMW_STREAM_GRAD] = 2;
-    kind.esz[ADAMW_STREAM_EXP_AVG] = m32 ? 4 : 2;
-    kind.esz[ADAMW_STREAM_EXP_AVG_SQ] = v32 ? 4 : 2;
-    kind.esz[ADAMW_STREAM_AUX] = kahan ? 2 : 0;
-    return do_step(kind, list, hp, d_step, d_found_inf, hip_stream);
+    std::string err;
+    adamw_status st = check_pure_precision(prec, err);
+    if (st != ADAMW_OK) return fail(st, err);
+    return do_step(kind_of_pure(*prec), list, hp, d_step, d_found_inf, hip_stream);
 }
 
 adamw_status adamw_multi_tensor_step_amp(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
@@ -511,10 +549,12 @@ adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* gr
     if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
     std::lock_guard<std::mutex> lk(ws->mu);
     DeviceGuard dg(ws->device);
+    bool cap = false;
+    if ((st = capturing(stream, &cap)) != ADAMW_OK) return st;
     uint32_t* done = nullptr;
-    if ((st = ensure_workspace_block(*ws, stream, &done)) != ADAMW_OK) return st;
+    if ((st = ensure_workspace_block(*ws, stream, cap, &done)) != ADAMW_OK) return st;
     PlanSlot* plan = nullptr;
-    if ((st = ensure_plan(*ws, -1, esz, grads, chunk_elems, stream, &plan)) != ADAMW_OK) return st;
+    if ((st = ensure_plan(*ws, -1, esz, grads, chunk_elems, stream, cap, &plan)) != ADAMW_OK) return st;
     hipError_t e = launch_check(g_dtype, plan->segs(), plan->chunks(), plan->n_chunks, d_found_inf, done,
                                 single_launch(plan->n_chunks), stream);
     if (e != hipSuccess) return hip_fail("check launch", e);
@@ -555,16 +595,48 @@ int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_ten
         return -1;
     }
     const int64_t n = (int64_t)plan.chunks.size();
+    for (int64_t i = 0; i < n && i < cap && out; ++i) inspect_row(plan, (size_t)i, out + 6 * i);
+    return n;
+}
+
+int64_t adamw_plan_inspect_bytes(adamw_mode mode, adamw_dtype p_dtype, const adamw_pure_precision* prec,
+                                 const adamw_tensor_list* list, int for_check, uint64_t* out, int64_t cap)
+{
+    g_err.clear();
+    std::string err;
+    adamw_status st = ADAMW_OK;
+    StepKind kind{};
+    int64_t chunk = 0, max_chunks = kMaxUpdateChunks;
+    if (for_check) {
+        st = check_mode(mode, p_dtype, true, err);
+        mode_esizes(mode, p_dtype, true, kind.esz);
+        chunk = check_chunk_elems();
+        max_chunks = kMaxCheckChunks;
+    } else if (prec) {
+        st = check_pure_precision(prec, err);
+        if (st == ADAMW_OK) kind = kind_of_pure(*prec);
+    } else {
+        st = check_mode(mode, p_dtype, false, err);
+        if (st == ADAMW_OK) kind = kind_of_mode(mode, p_dtype);
+    }
+    if (st == ADAMW_OK && !for_check) chunk = chunk_elems_of(kind.kernel);
+    Plan plan;
+    if (st == ADAMW_OK) st = build_plan(kind.esz, list, chunk, max_chunks, &plan, err);
+    if (st != ADAMW_OK) {
+        g_err = err;
+        return -1;
+    }
+    const int64_t n = (int64_t)plan.chunks.size();
+    constexpr int64_t kRow = 6 + 2 * kStreams;
     for (int64_t i = 0; i < n && i < cap && out; ++i) {
-        const DevChunk& c = plan.chunks[(size_t)i];
-        const SegInfo& si = plan.info[c.seg];
-        int64_t* r = out + 6 * i;
-        r[0] = si.tensor;
-        r[1] = si.tensor_off + (int64_t)c.off;
-        r[2] = (int64_t)(c.n_kind & kCountMask);
-        r[3] = (c.n_kind & kVecBit) ? 1 : 0;
-        r[4] = si.flat + (int64_t)c.off;
-        r[5] = (int64_t)c.seg;
+        uint64_t* r = out + kRow * i;
+        inspect_row(plan, (size_t)i, reinterpret_cast<int64_t*>(r));
+        uint64_t lo[kStreams], hi[kStreams];
+        chunk_bytes(plan, (size_t)i, kind.esz, lo, hi);
+        for (int s = 0; s < kStreams; ++s) {
+            r[6 + 2 * s] = lo[s];
+            r[6 + 2 * s + 1] = hi[s];
+        }
     }
     return n;
 }

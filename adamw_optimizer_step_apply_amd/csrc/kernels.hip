@@ -217,12 +217,24 @@ __device__ __forceinline__ void advance_loss_scale(adamw_loss_scale_state* amp, 
     }
 }
 
+// A step is taken only from a counter in [0, INT32_MAX): the step it takes,
+// t = counter + 1, must be a positive int32.  From any other value the call
+// writes nothing at all (no buffer, no counter, no loss scale), as on a skip.
+__device__ __forceinline__ bool counter_in_range(int32_t step) { return step >= 0 && step != INT32_MAX; }
+
 __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, const int32_t* __restrict__ found_inf,
                                 LaunchScalars* __restrict__ out, adamw_loss_scale_state* __restrict__ amp,
                                 adamw_loss_scaler scaler)
 {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     LaunchScalars s{};
+    const int32_t step0 = *step;
+    if (!counter_in_range(step0)) {
+        // no step t = step0 + 1 exists in int32: write nothing but the skip mark
+        s.skip = 1;
+        *out = s;
+        return;
+    }
     const bool skip = found_inf && *found_inf != 0;
     float inv_scale = hp.inv_loss_scale;
     if (amp) {
@@ -237,7 +249,7 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
         *out = s;
         return;
     }
-    const int64_t t = (int64_t)*step + 1;
+    const int64_t t = (int64_t)step0 + 1;
     const Coef c = step_coef(hp, t, inv_scale);
     s.skip = 0;
     s.t = (int32_t)t;
@@ -329,7 +341,8 @@ __device__ __forceinline__ Coef load_coef(const LaunchScalars* sc)
 // reads the flag, the counter and (with a dynamic loss scale) the scale
 // itself; its scalars are formed by fused_coef once its data loads are in
 // flight.  Returns false on a skipped step (uniform over the grid: nothing is
-// written, the counter is kept; workgroup 0 backs the loss scale off).
+// written, the counter is kept; workgroup 0 backs the loss scale off) and on a
+// counter out of range (nothing is written at all).
 template <bool FUSED>
 __device__ __forceinline__ bool begin_step(const LaunchScalars* sc, const FusedStep& fs, Coef& c, int64_t& t,
                                            float& scale)
@@ -342,6 +355,7 @@ __device__ __forceinline__ bool begin_step(const LaunchScalars* sc, const FusedS
         const int32_t flag = fs.found_inf ? *fs.found_inf : 0;
         const int32_t step = *fs.step;
         scale = fs.amp ? fs.amp->scale : 0.0f;
+        if (!counter_in_range(step)) return false;
         if (flag != 0) {
             if (fs.amp && blockIdx.x == 0 && threadIdx.x == 0) advance_loss_scale(fs.amp, fs.scaler, scale, true);
             return false;

@@ -245,6 +245,32 @@ adamw_status build_plan(const int esz_in[kStreams], const adamw_tensor_list* lis
     return ADAMW_OK;
 }
 
+void chunk_bytes(const Plan& plan, size_t c, const int esz[kStreams], uint64_t lo[kStreams], uint64_t hi[kStreams])
+{
+    const DevChunk& ch = plan.chunks[c];
+    const DevSeg& sg = plan.segs[ch.seg];
+    const uint64_t n = ch.n_kind & kCountMask;
+    for (int s = 0; s < kStreams; ++s) {
+        if (!esz[s]) {
+            lo[s] = hi[s] = 0;
+            continue;
+        }
+        lo[s] = sg.ptr[s] + ch.off * (uint64_t)esz[s];
+        hi[s] = lo[s] + n * (uint64_t)esz[s];
+    }
+}
+
+size_t choose_plan_slot(const std::vector<bool>& pinned, size_t cap)
+{
+    size_t unpinned = 0, lru = pinned.size();
+    for (size_t i = 0; i < pinned.size(); ++i) {
+        if (pinned[i]) continue;
+        ++unpinned;
+        lru = i;   // the last unpinned slot in MRU order
+    }
+    return unpinned < cap ? pinned.size() : lru;
+}
+
 void plan_key(int64_t tag, const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems,
               std::vector<int64_t>& key)
 {

@@ -1,5 +1,6 @@
-// plan.hpp -- host-side planner: tensor list (or ZeRO shard of it) -> segments
-// and workgroup chunks for the fused AdamW kernels.
+// plan.hpp -- host-side logic of the fused AdamW launch, free of HIP calls:
+// the planner (tensor list, or ZeRO shard of it -> segments and workgroup
+// chunks) and the argument checks made before anything is enqueued.
 #pragma once
 
 #include <stdint.h>
@@ -39,6 +40,28 @@ void mode_esizes(adamw_mode mode, adamw_dtype p_dtype, bool for_check, int esz[k
 // limit of the kernel that runs it) is rejected.  No HIP call.
 adamw_status build_plan(const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems,
                         int64_t max_chunks, Plan* out, std::string& err);
+
+// Device bytes of chunk `c` of `plan` in each stream: [lo[s], hi[s]) holds the
+// elements [off, off + count) of the chunk's segment at the stream's element
+// size esz[s]; lo = hi = 0 for a stream the plan does not touch.  These are
+// exactly the bytes the kernels read and write for the chunk: a vector chunk's
+// lanes take its 8-element packs [0, count / 8), an element chunk's lanes its
+// elements [0, count).
+void chunk_bytes(const Plan& plan, size_t c, const int esz[kStreams], uint64_t lo[kStreams], uint64_t hi[kStreams]);
+
+// The argument checks of the entry points (error text in `err`).
+adamw_status check_hparams(const adamw_hparams* hp, std::string& err);
+adamw_status check_scaler(const adamw_loss_scaler* sc, std::string& err);
+adamw_status basic_list_check(const adamw_tensor_list* list, std::string& err);
+adamw_status check_pure_precision(const adamw_pure_precision* prec, std::string& err);
+
+// Plan cache policy of one stream.  `pinned` lists the stream's slots in
+// most-recently-used order, true for a slot that a captured HIP graph holds
+// (its device table must stay as it is for as long as the graph may replay).
+// Returns the slot a new plan goes to: `pinned.size()` (a new slot) while fewer
+// than `cap` slots are unpinned, else the least recently used unpinned slot.
+// A pinned slot is never chosen.
+size_t choose_plan_slot(const std::vector<bool>& pinned, size_t cap);
 
 // The exact inputs a plan depends on, for caching (`tag` distinguishes kernels).
 void plan_key(int64_t tag, const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems,

@@ -27,6 +27,7 @@ Usage:
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-probe] [--compare]
   python bench.py --workload ragged_10k                  (overflow check + fp16 step, 10k tensors)
   python bench.py --probe-only                            (memory ceilings only)
+  python bench.py --build-probe                           (compile the ceiling probes; no GPU)
   python bench.py --calib-copy                            (plain 4 GiB copy, to scale rocprofv3 byte counters)
   python bench.py --traffic-from F.csv W.csv CF.csv CW.csv (rocprofv3 counters -> profiles/traffic_<workload>.json)
 """
@@ -43,6 +44,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published peak
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "libbench_probe.so")
 BYTES = {"mixed": 28, "kahan": 18, "split": 26, "f16amp": 28, "check": 2}
 
 
@@ -62,6 +65,7 @@ def parse():
                          "default run serves the headline layout only")
     ap.add_argument("--no-compare", action="store_true", help="the default (no per-tensor-state timing)")
     ap.add_argument("--probe-only", action="store_true")
+    ap.add_argument("--build-probe", action="store_true", help="compile bench_probe.hip and exit (no GPU needed)")
     ap.add_argument("--cpu-sample", type=int, default=256_000_000,
                     help="elements of the list the oracle steps once per mode")
     ap.add_argument("--calib-copy", action="store_true")
@@ -186,10 +190,26 @@ def _time_launches(fn, reps, stream):
     return ms[len(ms) // 2]
 
 
+def build_probe(verbose: bool = False) -> str:
+    """Compiles the memory-ceiling probes (bench_probe.hip, measurement support of
+    this benchmark and not part of the library) into libbench_probe.so with the
+    library's hipcc flags."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_adamw_amd_build", os.path.join(ROOT, "adamw_optimizer_step_apply_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod.hipcc([PROBE_SRC], PROBE_LIB, verbose)
+    return PROBE_LIB
+
+
 def probes(n, stream):
     """Same-mix ceilings at n elements (median of 7 launches each), in GB/s."""
     import torch
-    lib = ctypes.CDLL(os.path.join(ROOT, "libbench_probe.so"))
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is missing: build it first (python bench.py --build-probe, "
+                         "or __graft_entry__.build())")
+    lib = ctypes.CDLL(PROBE_LIB)
     lib.probe_launch.restype = ctypes.c_int
     lib.probe_launch.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 5 + [ctypes.c_uint64, ctypes.c_void_p]
     n = n // 8 * 8
@@ -244,28 +264,40 @@ def probes(n, stream):
     return out
 
 
+STATE_BLOCK_ELEMS = 16384     # elements per block of the blocked state layout (ADAMW_STATE_BLOCK_ELEMS)
+BLOCKED_FLAGS = (1 << 8) | (1 << 9)   # ADAMW_BLOCKED_STATE | ADAMW_FLAT_PAD8
+
+
+def state_layout(mode, numels):
+    """How make_mode_state lays out a mode's buffers, apart from their base
+    addresses: (arena alignment in elements of the per-tensor buffers, the
+    list's flat_mask, blocks of the blocked state buffer or 0).  A "-blocked"
+    mode keeps every tensor at a multiple of 8 elements in its arenas, so that a
+    state arena is already the padded flat concatenation (the same offsets as
+    128 when all lengths are multiples of 128, as in the OPT and BERT lists)."""
+    if not mode.endswith("-blocked"):
+        return 128, 0, 0
+    n = sum(-(-int(m) // 8) * 8 for m in numels)     # padded flat index
+    return 8, BLOCKED_FLAGS, -(-n // STATE_BLOCK_ELEMS)
+
+
 def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
     """Per-tensor buffers for every stream; a "-blocked" mode instead keeps
     exp_avg / exp_avg_sq / aux in one blocked flat buffer of the whole list
     (the optimizer-owned layout; param and grad stay per tensor), indexed by
-    the padded flat index (every tensor at a multiple of 8 elements)."""
+    the padded flat index (every tensor at a multiple of 8 elements).
+    Returns (arena, streams, flat_mask)."""
     import torch
 
     import workloads
     base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
-    blocked = base != mode
-    # blocked: tensors at multiples of 8 in every arena, so that a state arena
-    # is already the padded flat concatenation (the same offsets as 128 when all
-    # lengths are multiples of 128, as in the OPT and BERT lists)
-    arena = workloads.make_state(base, numels, device, seed, align_elems=8 if blocked else 128, p_dtype=p_dtype,
+    align, flags, nb = state_layout(mode, numels)
+    arena = workloads.make_state(base, numels, device, seed, align_elems=align, p_dtype=p_dtype,
                                  loss_scale=loss_scale)
     keys = workloads.streams_of(base)
     streams = [[arena.view(k, i) for i in range(len(numels))] for k in keys]
-    if blocked:
-        import adamw_optimizer_step_apply_amd as A
-        B = A.STATE_BLOCK_ELEMS
-        n = sum(-(-m // 8) * 8 for m in numels)     # padded flat index
-        nb = -(-n // B)
+    if nb:
+        B = STATE_BLOCK_ELEMS
         cols = []
         for k in keys[2:]:
             src = arena.bufs[k]
@@ -275,7 +307,7 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
         arena.bufs["blocked"] = torch.cat(cols, dim=1).contiguous()
         del cols
         streams = streams[:2] + [[arena.bufs["blocked"]], None, None]
-    return arena, streams
+    return arena, streams, flags
 
 
 def cpu_baseline(numels, sample, modes):
@@ -393,6 +425,9 @@ def main():
         print("bench.py measures one GPU: the step runs on one rank's share; runs on "
               f"{args.gpus} GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
+    if args.build_probe:
+        print(build_probe(verbose=True))
+        return
     if args.traffic_from:
         write_traffic(args.workload, default_modes(args).split(","), *args.traffic_from)
         return
@@ -429,11 +464,11 @@ def main():
     state = {}
     for i, mode in enumerate(modes + compare):
         if mode.startswith("f16amp"):
-            arena, streams = make_mode_state("mixed" + mode[len("f16amp"):], numels, dev, 100 + i, p_dtype="f16",
-                                             loss_scale=wl.loss_scale)
+            arena, streams, flags = make_mode_state("mixed" + mode[len("f16amp"):], numels, dev, 100 + i,
+                                                    p_dtype="f16", loss_scale=wl.loss_scale)
         else:
-            arena, streams = make_mode_state(mode, numels, dev, seed=100 + i)
-        flags = (A.BLOCKED_STATE | A.FLAT_PAD8) if mode.endswith("-blocked") else 0
+            arena, streams, flags = make_mode_state(mode, numels, dev, seed=100 + i)
+        assert A.STATE_BLOCK_ELEMS == STATE_BLOCK_ELEMS and A.BLOCKED_STATE | A.FLAT_PAD8 == BLOCKED_FLAGS
         state[mode] = (arena, A.TensorList(numels, streams, 0, -1, flags), torch.zeros(1, dtype=torch.int32, device=dev))
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     hp = A.HParams()

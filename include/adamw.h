@@ -61,6 +61,10 @@
  * d_found_inf is non-null and *d_found_inf != 0 when the step runs (stream
  * order), nothing is written at all and *d_step is left as it is: the fp16
  * loss-scaling skip.  The caller fills the flag with adamw_check_finite.
+ * The counter must lie in [0, INT32_MAX) when the step runs: at INT32_MAX (or
+ * below 0) no step t fits in int32, and the call writes nothing at all -- no
+ * buffer, no counter, no loss scale -- so the parameters stay finite and a
+ * caller can detect the saturated counter by reading it.
  *
  * Ownership and execution.  The caller owns every tensor, d_step, d_found_inf
  * and the stream; the library never frees or reallocates them.  All work is
@@ -74,13 +78,19 @@
  *
  * HIP graphs.  After one call on a stream with a given list (which allocates
  * the workspace and uploads the list's chunk table), the same call captured on
- * that stream records kernel launches only: no allocation, copy or memset.
- * A captured step may be replayed any number of times.  It uses the capture
- * stream's workspace (launch scalars, completion counters, chunk table), so
- * adamw_release_workspace() must not run while such a graph is in use, and a
- * replay must not overlap other work that uses that workspace: steps enqueued
- * on the capture stream, or replays of other graphs captured on it.  Replaying
- * on the capture stream itself keeps all of these in stream order.
+ * that stream records kernel launches only: no allocation, copy or memset.  A
+ * call under capture whose table is not yet on the device (or on a stream
+ * without a workspace) is refused with ADAMW_E_INVALID.  A captured step may be
+ * replayed any number of times.  It uses the capture stream's workspace
+ * (launch scalars, completion counters, chunk table).  The chunk table a
+ * capture used is pinned: later calls on the stream, with however many other
+ * lists, never evict, move or rewrite it (the stream keeps up to 8 unpinned
+ * tables besides the pinned ones); pinned tables are freed only by
+ * adamw_release_workspace(), which therefore must not run while such a graph
+ * is in use.  A replay must not overlap other work that uses that workspace:
+ * steps enqueued on the capture stream, or replays of other graphs captured on
+ * it.  Replaying on the capture stream itself keeps all of these in stream
+ * order.
  *
  * Errors.  Arguments are validated before anything is enqueued; on an error
  * nothing is enqueued, no buffer is touched, and adamw_last_error() describes
@@ -104,7 +114,7 @@
 extern "C" {
 #endif
 
-#define ADAMW_ABI_VERSION 4
+#define ADAMW_ABI_VERSION 5
 
 typedef enum {
     ADAMW_OK = 0,
@@ -201,8 +211,12 @@ typedef struct {
     uint32_t flat_mask;
 } adamw_tensor_list;
 
-/* One AdamW step over one contiguous range of n elements (a single tensor, or
- * one rank's flat shard with every pointer already offset to it).
+/* One AdamW step over one contiguous range of n elements: a single tensor, or
+ * one data-parallel rank's flat shard with every pointer already offset to it
+ * -- the unit of work of the ZeRO-sharded optimizer of "Distributed optimizer
+ * support for BERT" (the remark under the 4 x A40 table: each of the DP ranks
+ * keeps the fp32 optimizer state and the 16-bit master copy of 1/DP of the
+ * parameters, and steps only that share).
  * param, grad, exp_avg, exp_avg_sq, aux: device buffers of n elements in the
  * layouts above.  p_dtype: ADAMW_BF16 or ADAMW_F16 in ADAMW_MIXED, ADAMW_BF16
  * in ADAMW_PURE_KAHAN and ADAMW_MIXED_SPLIT.  n == 0 is valid (the counter still advances unless
@@ -276,7 +290,11 @@ adamw_status adamw_multi_tensor_step_amp(adamw_mode mode, adamw_dtype p_dtype, c
                                          adamw_loss_scale_state* d_scale, const adamw_loss_scaler* scaler,
                                          void* hip_stream);
 
-/* fp16-AMP overflow check: stores 0 to *d_found_inf (stream ordered), then 1
+/* fp16-AMP overflow check, for the fp16 mixed-precision training of the
+ * "opt-125m / fp16-amp training from scratch" run on the page "[pure bf16
+ * training] w/ AnyPrecisionAdamW and Kahan summation": its loss is scaled, and
+ * a step whose scaled gradients hold an inf or NaN must be skipped (see the
+ * skip flag in the file comment).  Stores 0 to *d_found_inf (stream ordered), then 1
  * if any gradient element of the list (stream 1 only; shard range and
  * flat_mask bit 1 honoured) has an all-ones exponent field, i.e. is inf or NaN.
  * g_dtype: ADAMW_F16 or ADAMW_BF16.  Scaled gradients are tested as stored,
@@ -308,6 +326,19 @@ int adamw_abi_version(void);
  * argument (see adamw_last_error). */
 int64_t adamw_plan_inspect(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list, int for_check,
                            int64_t* out, int64_t cap);
+
+/* Planner introspection, for tests: no GPU work, no HIP call.  The device
+ * bytes each chunk of the plan covers: for the step of (mode, p_dtype), or with
+ * prec non-null the step of adamw_pure_multi_tensor_step with *prec (mode and
+ * p_dtype ignored), or with for_check the check of adamw_check_finite
+ * (g_dtype = p_dtype), writes up to cap rows of 16 uint64 to out:
+ *   {the 6 fields of an adamw_plan_inspect row, lo[0], hi[0], ..., lo[4], hi[4]}
+ * where [lo[s], hi[s]) is the address range of stream s that the chunk's
+ * workgroups read and write (lo = hi = 0 for a stream the launch does not
+ * touch; a blocked state buffer shows as streams 2-4 at their places inside
+ * the blocks).  Returns the number of chunks, or -1 on an invalid argument. */
+int64_t adamw_plan_inspect_bytes(adamw_mode mode, adamw_dtype p_dtype, const adamw_pure_precision* prec,
+                                 const adamw_tensor_list* list, int for_check, uint64_t* out, int64_t cap);
 
 /* Launch form.  A step whose grid has at most max_workgroups workgroups
  * (default 4096: 512 chunks of 16384 elements, about 8.4e6 elements) runs as
