@@ -35,11 +35,13 @@ STREAM_PARAM, STREAM_GRAD, STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_AUX = range
 BLOCKED_STATE = 1 << 8        # flat_mask bit: exp_avg / exp_avg_sq / aux in one blocked buffer
 FLAT_PAD8 = 1 << 9            # flat_mask bit: every tensor starts at a multiple of 8 in the flat index
 STATE_BLOCK_ELEMS = 16384     # elements per block of a blocked state buffer (ADAMW_STATE_BLOCK_ELEMS)
+NOALLOC_SCRATCH_BYTES = 16 << 20   # the allocation-free step's per-GPU workspace (ADAMW_NOALLOC_SCRATCH_BYTES)
 NUM_STREAMS = 5
 _STATUS = {0: "ADAMW_OK", 1: "ADAMW_E_INVALID", 2: "ADAMW_E_UNSUPPORTED", 3: "ADAMW_E_NOMEM", 4: "ADAMW_E_HIP"}
 
 
-EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_amp", "adamw_pure_multi_tensor_step",
+EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_noalloc", "adamw_multi_tensor_step_amp",
+            "adamw_pure_multi_tensor_step",
             "adamw_check_finite",
             "adamw_last_error", "adamw_release_workspace", "adamw_abi_version", "adamw_plan_inspect",
             "adamw_plan_inspect_bytes", "adamw_set_chunk_elems", "adamw_set_single_launch_max_workgroups")
@@ -83,6 +85,9 @@ def _declare(_lib):
     _lib.adamw_multi_tensor_step.restype = ctypes.c_int
     _lib.adamw_multi_tensor_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list),
                                              ctypes.POINTER(adamw_hparams), _vp, _vp, _vp]
+    _lib.adamw_multi_tensor_step_noalloc.restype = ctypes.c_int
+    _lib.adamw_multi_tensor_step_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list),
+                                                     ctypes.POINTER(adamw_hparams), _vp, _vp, _vp]
     _lib.adamw_multi_tensor_step_amp.restype = ctypes.c_int
     _lib.adamw_multi_tensor_step_amp.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_tensor_list),
                                                  ctypes.POINTER(adamw_hparams), _vp, _vp, _vp,
@@ -209,6 +214,15 @@ def adamw_multi_tensor_step(mode: int, p_dtype: int, tensors: TensorList, hp, d_
     h = _hp(hp)
     _check(_lib.adamw_multi_tensor_step(mode, p_dtype, ctypes.byref(tensors.c), ctypes.byref(h), _addr(d_step),
                                         _addr(d_found_inf), _stream(stream)))
+
+
+def adamw_multi_tensor_step_noalloc(mode: int, p_dtype: int, tensors: TensorList, hp, d_step, d_found_inf=None,
+                                    stream=None) -> None:
+    """adamw_multi_tensor_step without any device allocation: the workspace is
+    the library's static per-GPU array (C ABI adamw_multi_tensor_step_noalloc)."""
+    h = _hp(hp)
+    _check(_lib.adamw_multi_tensor_step_noalloc(mode, p_dtype, ctypes.byref(tensors.c), ctypes.byref(h),
+                                                _addr(d_step), _addr(d_found_inf), _stream(stream)))
 
 
 @dataclass

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libadamw_amd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["kernels.hip", "plan.cpp", "validate.cpp", "api.cpp"]
+SOURCES = ["kernels.hip", "plan.cpp", "validate.cpp", "api.cpp", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

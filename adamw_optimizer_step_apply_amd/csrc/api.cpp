@@ -23,21 +23,13 @@
 #include "adamw.h"
 #include "layout.hpp"
 #include "plan.hpp"
+#include "step.hpp"
 
 namespace adamw {
 
-hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32_t* d_found_inf,
-                           LaunchScalars* d_scalars, adamw_loss_scale_state* d_amp, const adamw_loss_scaler& scaler,
-                           hipStream_t stream);
-hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
-                         const LaunchScalars* d_scalars, const FusedStep* fused, hipStream_t stream);
-hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
-hipError_t launch_check(adamw_dtype g_dtype, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
-                        int32_t* d_flag, uint32_t* done, bool fused, hipStream_t stream);
-
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
 adamw_status fail(adamw_status st, const std::string& msg)
 {
@@ -50,6 +42,8 @@ adamw_status hip_fail(const char* what, hipError_t e)
     g_err = std::string(what) + ": " + hipGetErrorString(e);
     return ADAMW_E_HIP;
 }
+
+namespace {
 
 // A device-resident copy of one plan (segment table followed by chunk table),
 // uploaded through a pinned staging buffer.
@@ -109,13 +103,12 @@ std::atomic<int64_t> g_single_launch_max_workgroups{kSingleLaunchMaxWorkgroups};
 // overflow check): the grid of one launch holds at most 2^32 - 1 lanes.
 int64_t max_chunks_of(int64_t tag) { return tag < 0 ? kMaxCheckChunks : kMaxUpdateChunks; }
 
-// The workspace of a stream, on the stream's own device (the null stream
-// belongs to the calling thread's current device).
+// The workspace of a stream, on the stream's own device.
 adamw_status get_workspace(hipStream_t stream, StreamWorkspace** out)
 {
     int dev = 0;
-    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(stream ? "hipStreamGetDevice" : "hipGetDevice", e);
+    adamw_status st = stream_device(stream, &dev);
+    if (st != ADAMW_OK) return st;
     std::lock_guard<std::mutex> lk(g_mu);
     auto& ws = g_ws[{dev, (uintptr_t)stream}];
     if (!ws) {
@@ -125,26 +118,6 @@ adamw_status get_workspace(hipStream_t stream, StreamWorkspace** out)
     *out = ws.get();
     return ADAMW_OK;
 }
-
-// Makes `dev` the current device for the lifetime of the guard (allocations
-// and launches of a call then land on its stream's device).
-class DeviceGuard {
-public:
-    explicit DeviceGuard(int dev)
-    {
-        if (hipGetDevice(&prev_) == hipSuccess && prev_ != dev && hipSetDevice(dev) == hipSuccess) switched_ = true;
-    }
-    ~DeviceGuard()
-    {
-        if (switched_) (void)hipSetDevice(prev_);
-    }
-    DeviceGuard(const DeviceGuard&) = delete;
-    DeviceGuard& operator=(const DeviceGuard&) = delete;
-
-private:
-    int prev_ = 0;
-    bool switched_ = false;
-};
 
 // Returns (in *out) a slot of `ws` holding the device plan of (mode, dtype,
 // list, for_check): a cached one if every input matches (the key holds every
@@ -304,16 +277,6 @@ adamw_status check_scaler(const adamw_loss_scaler* sc)
     return st == ADAMW_OK ? st : fail(st, err);
 }
 
-// Whether `stream` is being captured into a HIP graph right now.
-adamw_status capturing(hipStream_t stream, bool* out)
-{
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    hipError_t e = hipStreamIsCapturing(stream, &cs);
-    if (e != hipSuccess) return hip_fail("hipStreamIsCapturing", e);
-    *out = cs != hipStreamCaptureStatusNone;
-    return ADAMW_OK;
-}
-
 // The stream's 256-byte scalar block and the single-launch completion counters
 // after it, allocated on first use (the counters start at zero, and every
 // single launch leaves them at zero).  Returns the counters in *done.
@@ -344,19 +307,7 @@ bool single_launch(int64_t n_workgroups)
     return n_workgroups > 0 && n_workgroups <= g_single_launch_max_workgroups.load(std::memory_order_relaxed);
 }
 
-// What one step launches: the update kernel and its streams' element sizes.
-struct StepKind {
-    int kernel;
-    int esz[kStreams];
-};
-
 int kernel_block(int kernel) { return kernel >= kKernelPure ? kBlockPure : kBlockMixed; }
-
-int64_t chunk_elems_of(int kernel)
-{
-    const int64_t c = g_chunk_elems.load(std::memory_order_relaxed);
-    return c ? c : update_chunk_elems(kernel_block(kernel));
-}
 
 int64_t check_chunk_elems()
 {
@@ -376,6 +327,32 @@ void inspect_row(const Plan& plan, size_t i, int64_t* r)
     r[4] = si.flat + (int64_t)c.off;
     r[5] = (int64_t)c.seg;
 }
+
+// One step through the stream's workspace and plan cache.
+adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const adamw_hparams* hp, int32_t* d_step,
+                     const int32_t* d_found_inf, void* hip_stream, adamw_loss_scale_state* d_amp = nullptr,
+                     const adamw_loss_scaler* scaler = nullptr)
+{
+    adamw_status st;
+    if ((st = check_step_call(kind, list, hp, d_step, d_found_inf)) != ADAMW_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    StreamWorkspace* ws = nullptr;
+    if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
+    std::lock_guard<std::mutex> lk(ws->mu);
+    DeviceGuard dg(ws->device);
+    bool cap = false;
+    if ((st = capturing(stream, &cap)) != ADAMW_OK) return st;
+    uint32_t* done = nullptr;
+    if ((st = ensure_workspace_block(*ws, stream, cap, &done)) != ADAMW_OK) return st;
+    PlanSlot* plan = nullptr;
+    if ((st = ensure_plan(*ws, kind.kernel, kind.esz, list, chunk_elems_of(kind.kernel), stream, cap, &plan)) !=
+        ADAMW_OK)
+        return st;
+    return enqueue_step(kind, plan->segs(), plan->chunks(), plan->n_chunks, ws->scalars, done, *hp, d_step,
+                        d_found_inf, d_amp, scaler, stream);
+}
+
+}  // namespace
 
 StepKind kind_of_pure(const adamw_pure_precision& prec)
 {
@@ -400,48 +377,6 @@ StepKind kind_of_mode(adamw_mode mode, adamw_dtype p_dtype)
     return k;
 }
 
-adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const adamw_hparams* hp, int32_t* d_step,
-                     const int32_t* d_found_inf, void* hip_stream, adamw_loss_scale_state* d_amp = nullptr,
-                     const adamw_loss_scaler* scaler = nullptr)
-{
-    adamw_status st;
-    if ((st = check_hparams(hp)) != ADAMW_OK) return st;
-    if (!d_step) return fail(ADAMW_E_INVALID, "d_step is null");
-    if ((uintptr_t)d_step % 4 || (uintptr_t)d_found_inf % 4)
-        return fail(ADAMW_E_INVALID, "d_step / d_found_inf must be 4-byte aligned");
-    if ((st = basic_list_check(list)) != ADAMW_OK) return st;
-
-    // the whole list is validated before the first HIP call
-    const int64_t chunk_elems = chunk_elems_of(kind.kernel);
-    if ((st = validate_list(kind.kernel, kind.esz, list, chunk_elems)) != ADAMW_OK) return st;
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    StreamWorkspace* ws = nullptr;
-    if ((st = get_workspace(stream, &ws)) != ADAMW_OK) return st;
-    std::lock_guard<std::mutex> lk(ws->mu);
-    DeviceGuard dg(ws->device);
-    hipError_t e;
-    bool cap = false;
-    if ((st = capturing(stream, &cap)) != ADAMW_OK) return st;
-    uint32_t* done = nullptr;
-    if ((st = ensure_workspace_block(*ws, stream, cap, &done)) != ADAMW_OK) return st;
-    PlanSlot* plan = nullptr;
-    if ((st = ensure_plan(*ws, kind.kernel, kind.esz, list, chunk_elems, stream, cap, &plan)) != ADAMW_OK) return st;
-    // Small plans: one launch.  An empty plan, whose step still advances the
-    // counter (and the loss scale), keeps the prologue kernel.
-    if (single_launch(plan->n_chunks * kXcdParts)) {
-        const FusedStep fs{*hp, d_step, d_found_inf, done, d_amp, scaler ? *scaler : adamw_loss_scaler{1.0f, 1.0f, 1}};
-        e = launch_update(kind.kernel, plan->segs(), plan->chunks(), plan->n_chunks, nullptr, &fs, stream);
-        if (e != hipSuccess) return hip_fail("update launch", e);
-        return ADAMW_OK;
-    }
-    const adamw_loss_scaler no_scaler{1.0f, 1.0f, 1};
-    e = launch_prologue(*hp, d_step, d_found_inf, ws->scalars, d_amp, scaler ? *scaler : no_scaler, stream);
-    if (e != hipSuccess) return hip_fail("prologue launch", e);
-    e = launch_update(kind.kernel, plan->segs(), plan->chunks(), plan->n_chunks, ws->scalars, nullptr, stream);
-    if (e != hipSuccess) return hip_fail("update launch", e);
-    return ADAMW_OK;
-}
-
 adamw_status mode_kind(adamw_mode mode, adamw_dtype p_dtype, StepKind* out)
 {
     std::string err;
@@ -451,7 +386,64 @@ adamw_status mode_kind(adamw_mode mode, adamw_dtype p_dtype, StepKind* out)
     return ADAMW_OK;
 }
 
-}  // namespace
+adamw_status check_step_call(const StepKind& kind, const adamw_tensor_list* list, const adamw_hparams* hp,
+                             const int32_t* d_step, const int32_t* d_found_inf)
+{
+    adamw_status st;
+    if ((st = check_hparams(hp)) != ADAMW_OK) return st;
+    if (!d_step) return fail(ADAMW_E_INVALID, "d_step is null");
+    if ((uintptr_t)d_step % 4 || (uintptr_t)d_found_inf % 4)
+        return fail(ADAMW_E_INVALID, "d_step / d_found_inf must be 4-byte aligned");
+    if ((st = basic_list_check(list)) != ADAMW_OK) return st;
+    // the whole list is validated before the first HIP call
+    return validate_list(kind.kernel, kind.esz, list, chunk_elems_of(kind.kernel));
+}
+
+adamw_status enqueue_step(const StepKind& kind, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
+                          LaunchScalars* scalars, uint32_t* done, const adamw_hparams& hp, int32_t* d_step,
+                          const int32_t* d_found_inf, adamw_loss_scale_state* d_amp, const adamw_loss_scaler* scaler,
+                          hipStream_t stream)
+{
+    const adamw_loss_scaler rule = scaler ? *scaler : adamw_loss_scaler{1.0f, 1.0f, 1};
+    hipError_t e;
+    // Small plans: one launch.  An empty plan, whose step still advances the
+    // counter (and the loss scale), keeps the prologue kernel.
+    if (single_launch(n_chunks * kXcdParts)) {
+        const FusedStep fs{hp, d_step, d_found_inf, done, d_amp, rule};
+        e = launch_update(kind.kernel, segs, chunks, n_chunks, nullptr, &fs, stream);
+        if (e != hipSuccess) return hip_fail("update launch", e);
+        return ADAMW_OK;
+    }
+    e = launch_prologue(hp, d_step, d_found_inf, scalars, d_amp, rule, stream);
+    if (e != hipSuccess) return hip_fail("prologue launch", e);
+    e = launch_update(kind.kernel, segs, chunks, n_chunks, scalars, nullptr, stream);
+    if (e != hipSuccess) return hip_fail("update launch", e);
+    return ADAMW_OK;
+}
+
+adamw_status stream_device(hipStream_t stream, int* dev)
+{
+    hipError_t e = stream ? hipStreamGetDevice(stream, dev) : hipGetDevice(dev);
+    if (e != hipSuccess) return hip_fail(stream ? "hipStreamGetDevice" : "hipGetDevice", e);
+    return ADAMW_OK;
+}
+
+// Whether `stream` is being captured into a HIP graph right now.
+adamw_status capturing(hipStream_t stream, bool* out)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail("hipStreamIsCapturing", e);
+    *out = cs != hipStreamCaptureStatusNone;
+    return ADAMW_OK;
+}
+
+int64_t chunk_elems_of(int kernel)
+{
+    const int64_t c = g_chunk_elems.load(std::memory_order_relaxed);
+    return c ? c : update_chunk_elems(kernel_block(kernel));
+}
+
 }  // namespace adamw
 
 using namespace adamw;

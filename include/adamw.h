@@ -114,7 +114,7 @@
 extern "C" {
 #endif
 
-#define ADAMW_ABI_VERSION 5
+#define ADAMW_ABI_VERSION 6
 
 typedef enum {
     ADAMW_OK = 0,
@@ -233,6 +233,31 @@ adamw_status adamw_step(adamw_mode mode, adamw_dtype p_dtype, int64_t n,
 adamw_status adamw_multi_tensor_step(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
                                      const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
                                      void* hip_stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the step of
+ * adamw_multi_tensor_step -- same arguments, same results bit for bit -- with
+ * no device allocation, free or allocating library call.  Its workspace (the
+ * launch scalars, the single-launch completion counters and the list's chunk
+ * table) lives in one static device array of ADAMW_NOALLOC_SCRATCH_BYTES per
+ * GPU, which the library's code object holds on every GPU it runs on until
+ * the process ends.  The chunk table takes 64 bytes per segment and 16 per
+ * chunk (adamw_plan_inspect lists both) and must fit in
+ * ADAMW_NOALLOC_SCRATCH_BYTES - 16384 bytes: about a million chunks of a few
+ * large tensors (every chunk 16384 elements: some 1.7e10 elements), about
+ * 200,000 of a list with blocked state (one segment per block: some 3.3e9
+ * elements; OPT-1.3B takes 6.4 MB).  A larger list is rejected with
+ * ADAMW_E_INVALID before anything is enqueued.  A call copies the list's table
+ * into the array (a host-to-device copy on hip_stream) unless the last call on
+ * this GPU used the same list; under graph capture that copy is refused, as in
+ * adamw_multi_tensor_step.  Every call on a GPU shares that GPU's array and
+ * its contents: calls on one GPU that may overlap (on different streams, or
+ * from host threads without an order between them) race on it and must be
+ * ordered by the caller, e.g. by issuing them on one stream. */
+#define ADAMW_NOALLOC_SCRATCH_BYTES (16u << 20)
+adamw_status adamw_multi_tensor_step_noalloc(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
+                                             const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
+                                             void* hip_stream);
 
 /* State precisions of a pure-bf16 step (the AnyPrecisionAdamW knobs of
  * "[pure bf16 training] w/ AnyPrecisionAdamW and Kahan summation":
