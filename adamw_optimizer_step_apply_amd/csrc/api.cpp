@@ -307,7 +307,7 @@ bool single_launch(int64_t n_workgroups)
     return n_workgroups > 0 && n_workgroups <= g_single_launch_max_workgroups.load(std::memory_order_relaxed);
 }
 
-int kernel_block(int kernel) { return kernel >= kKernelPure ? kBlockPure : kBlockMixed; }
+int kernel_block(int kernel) { return kernel == kKernelSplit || kernel >= kKernelPure ? kBlockPure : kBlockMixed; }
 
 int64_t check_chunk_elems()
 {

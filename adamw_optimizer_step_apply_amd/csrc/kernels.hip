@@ -11,7 +11,7 @@
 // Kernels:
 //   prologue_kernel      one lane: reads the skip flag and the step counter,
 //                        forms the step's scalars in binary64, advances the counter
-//   update_kernel<MODE, FUSED> / update_pure_kernel<M32, V32, KAHAN, FUSED>
+//   update_kernel<MODE, FUSED> / update_pure_kernel<M32, V32, AUX, FUSED>
 //                        eight workgroups per chunk, one on each XCD, the chunk
 //                        interleaved between them in 1 KiB tiles: the AdamW
 //                        element update;
@@ -148,10 +148,14 @@ __device__ __forceinline__ uint32_t join_bits(uint32_t p16, uint32_t r16)
 // p = nearest bf16 of w, ties away from zero (bit 15 of the dropped half rounds the
 // magnitude up), so the remainder w - (p << 16) lies in [-32768, 32767]; a NaN
 // keeps its high half with the quiet bit set.  Returns p; r through `r16`.
+// Both candidates are formed and one is picked with a mask: written as a
+// conditional, the NaN case compiled to a divergent branch per element.
 __device__ __forceinline__ uint32_t split_bits(uint32_t w, uint32_t& r16)
 {
-    const bool nan = (w & 0x7fffffffu) > 0x7f800000u;
-    const uint32_t hi = nan ? ((w >> 16) | 0x0040u) : (w >> 16) + ((w >> 15) & 1u);
+    const uint32_t nan_mask = 0u - (uint32_t)((w & 0x7fffffffu) > 0x7f800000u);
+    const uint32_t rounded = (w >> 16) + ((w >> 15) & 1u);
+    const uint32_t quieted = (w >> 16) | 0x0040u;
+    const uint32_t hi = (rounded & ~nan_mask) | (quieted & nan_mask);
     r16 = (w - (hi << 16)) & 0xffffu;
     return hi & 0xffffu;
 }
@@ -283,8 +287,19 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
 #ifndef ADAMW_NT_MIXED_GRAD
 #define ADAMW_NT_MIXED_GRAD 1
 #endif
+// The pure family (every stream alike, the gradient included): non-temporal loads
+// and stores while all state is bf16; with fp32 moments (26 B per element: the
+// split master, and fp32 exp_avg + exp_avg_sq with compensation) non-temporal
+// stores only, measured 5-6 % faster there on MI355X (OPT-1.3B list, blocked
+// state), while the bf16 Kahan step loses 8 % without non-temporal loads.
 #ifndef ADAMW_NT_PURE
 #define ADAMW_NT_PURE 3
+#endif
+#ifndef ADAMW_NT_PURE_WIDE
+#define ADAMW_NT_PURE_WIDE 2
+#endif
+#ifndef ADAMW_NT_SPLIT
+#define ADAMW_NT_SPLIT 2
 #endif
 #ifndef ADAMW_NT_CHECK
 #define ADAMW_NT_CHECK 1
@@ -456,8 +471,8 @@ __device__ __forceinline__ void end_step(const FusedStep& fs, int64_t t, float s
 #define ADAMW_WPE_ATTR
 #endif
 
-// MODE 0: mixed bf16, 1: mixed fp16, 3: mixed bf16 with the master split into
-// param + int16 remainder
+// MODE 0: mixed bf16, 1: mixed fp16 (the split-master step is a pure-family
+// kernel below: its param is read as well as written)
 template <int MODE, bool FUSED>
 __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(const DevSeg* __restrict__ segs,
                                                         const DevChunk* __restrict__ chunks,
@@ -467,10 +482,10 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
     int64_t t = 0;
     float scale = 0.0f;
     if (!begin_step<FUSED>(sc, fs, c, t, scale)) return;
-    constexpr bool F16 = (MODE == 1);   // MODE 3 uses bf16 param/grad
+    constexpr bool F16 = (MODE == 1);
     constexpr int NTM = ADAMW_NT_MIXED;
-    constexpr int NTG = ADAMW_NT_MIXED | (ADAMW_NT_MIXED_GRAD ? 1 : 0);   // the gradient's loads
-    constexpr int P = MODE == 3 ? kTilePacks : kTilePacksMixed;   // tiles of 512 / 256 elements
+    constexpr int NTG = NTM | (ADAMW_NT_MIXED_GRAD ? 1 : 0);   // the gradient's loads
+    constexpr int P = kTilePacksMixed;   // tiles of 256 elements
     constexpr uint32_t kStride = kXcdParts * kBlockMixed;
     const uint32_t part = blockIdx.x % kXcdParts;
     const DevChunk ch = chunks[blockIdx.x / kXcdParts];
@@ -479,117 +494,65 @@ __global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(cons
     const uint64_t off = ch.off;
     const uint32_t tid = threadIdx.x;
 
-    if constexpr (MODE == 3) {
-        GLOBAL uint16_t* __restrict__ p = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_PARAM], off);
-        const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
-        GLOBAL float* __restrict__ m = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
-        GLOBAL float* __restrict__ v = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG_SQ], off);
-        GLOBAL uint16_t* __restrict__ r = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_AUX], off);
-        if (ch.n_kind & kVecBit) {
-            const uint32_t npack = n / kPack;
-            const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
-            GLOBAL u32x4* __restrict__ p4 = reinterpret_cast<GLOBAL u32x4*>(p);
-            GLOBAL u32x4* __restrict__ r4 = reinterpret_cast<GLOBAL u32x4*>(r);
-            GLOBAL f32x4* __restrict__ m4 = reinterpret_cast<GLOBAL f32x4*>(m);
-            GLOBAL f32x4* __restrict__ v4 = reinterpret_cast<GLOBAL f32x4*>(v);
-            for (uint32_t k = first_pack<P, kBlockMixed>(tid, part); k < npack; k += kStride) {
-                const u32x4 G = ld<NTG>(g4 + k), Pv = ld<NTM>(p4 + k), R = ld<NTM>(r4 + k);
-                f32x4 M[2] = {ld<NTM>(m4 + 2 * k), ld<NTM>(m4 + 2 * k + 1)};
-                f32x4 V[2] = {ld<NTM>(v4 + 2 * k), ld<NTM>(v4 + 2 * k + 1)};
-                fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
-                float* mf = reinterpret_cast<float*>(M);
-                float* vf = reinterpret_cast<float*>(V);
-                const uint32_t gw[4] = {G.x, G.y, G.z, G.w};
-                const uint32_t pw[4] = {Pv.x, Pv.y, Pv.z, Pv.w};
-                const uint32_t rw[4] = {R.x, R.y, R.z, R.w};
-                uint32_t po[4], ro[4];
+    GLOBAL uint16_t* __restrict__ p = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_PARAM], off);
+    const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
+    GLOBAL float* __restrict__ m = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
+    GLOBAL float* __restrict__ v = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG_SQ], off);
+    GLOBAL float* __restrict__ w = gptr<float>(sg.ptr[ADAMW_STREAM_AUX], off);
+    if (ch.n_kind & kVecBit) {
+        const uint32_t npack = n / kPack;
+        const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
+        GLOBAL u32x4* __restrict__ p4 = reinterpret_cast<GLOBAL u32x4*>(p);
+        GLOBAL f32x4* __restrict__ m4 = reinterpret_cast<GLOBAL f32x4*>(m);
+        GLOBAL f32x4* __restrict__ v4 = reinterpret_cast<GLOBAL f32x4*>(v);
+        GLOBAL f32x4* __restrict__ w4 = reinterpret_cast<GLOBAL f32x4*>(w);
+        for (uint32_t k = first_pack<P, kBlockMixed>(tid, part); k < npack; k += kStride) {
+            const u32x4 G = ld<NTG>(g4 + k);
+            f32x4 W[2] = {ld<NTM>(w4 + 2 * k), ld<NTM>(w4 + 2 * k + 1)};
+            f32x4 M[2] = {ld<NTM>(m4 + 2 * k), ld<NTM>(m4 + 2 * k + 1)};
+            f32x4 V[2] = {ld<NTM>(v4 + 2 * k), ld<NTM>(v4 + 2 * k + 1)};
+            fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
+            float* wf = reinterpret_cast<float*>(W);
+            float* mf = reinterpret_cast<float*>(M);
+            float* vf = reinterpret_cast<float*>(V);
+            const uint32_t gw[4] = {G.x, G.y, G.z, G.w};
+            uint32_t pw[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x2 gg = widen2<false>(gw[j]);
-                    float wa = __uint_as_float(join_bits(pw[j] & 0xffffu, rw[j] & 0xffffu));
-                    float wb = __uint_as_float(join_bits(pw[j] >> 16, rw[j] >> 16));
-                    mixed_elem(gg.x, wa, mf[2 * j], vf[2 * j], c);
-                    mixed_elem(gg.y, wb, mf[2 * j + 1], vf[2 * j + 1], c);
-                    uint32_t ra, rb;
-                    const uint32_t pa = split_bits(__float_as_uint(wa), ra);
-                    const uint32_t pb = split_bits(__float_as_uint(wb), rb);
-                    po[j] = pa | (pb << 16);
-                    ro[j] = ra | (rb << 16);
-                }
-                st<NTM>(m4 + 2 * k, M[0]); st<NTM>(m4 + 2 * k + 1, M[1]);
-                st<NTM>(v4 + 2 * k, V[0]); st<NTM>(v4 + 2 * k + 1, V[1]);
-                st<NTM>(p4 + k, u32x4{po[0], po[1], po[2], po[3]});
-                st<NTM>(r4 + k, u32x4{ro[0], ro[1], ro[2], ro[3]});
+            for (int j = 0; j < 4; ++j) {
+                const f32x2 gg = widen2<F16>(gw[j]);
+                const float a = mixed_elem(gg.x, wf[2 * j], mf[2 * j], vf[2 * j], c);
+                const float b = mixed_elem(gg.y, wf[2 * j + 1], mf[2 * j + 1], vf[2 * j + 1], c);
+                pw[j] = narrow2<F16>(a, b);
             }
-        } else {
-            fused_coef<FUSED>(fs, t, scale, c);
-            for (uint32_t i = part * kBlockMixed + tid; i < n; i += kStride) {
-                float wi = __uint_as_float(join_bits(p[i], r[i])), mi = m[i], vi = v[i];
-                mixed_elem(widen1<false>(g[i]), wi, mi, vi, c);
-                uint32_t ri;
-                const uint32_t pi = split_bits(__float_as_uint(wi), ri);
-                m[i] = mi;
-                v[i] = vi;
-                p[i] = (uint16_t)pi;
-                r[i] = (uint16_t)ri;
-            }
+            st<NTM>(w4 + 2 * k, W[0]); st<NTM>(w4 + 2 * k + 1, W[1]);
+            st<NTM>(m4 + 2 * k, M[0]); st<NTM>(m4 + 2 * k + 1, M[1]);
+            st<NTM>(v4 + 2 * k, V[0]); st<NTM>(v4 + 2 * k + 1, V[1]);
+            st<NTM>(p4 + k, u32x4{pw[0], pw[1], pw[2], pw[3]});
         }
     } else {
-        GLOBAL uint16_t* __restrict__ p = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_PARAM], off);
-        const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
-        GLOBAL float* __restrict__ m = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
-        GLOBAL float* __restrict__ v = gptr<float>(sg.ptr[ADAMW_STREAM_EXP_AVG_SQ], off);
-        GLOBAL float* __restrict__ w = gptr<float>(sg.ptr[ADAMW_STREAM_AUX], off);
-        if (ch.n_kind & kVecBit) {
-            const uint32_t npack = n / kPack;
-            const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
-            GLOBAL u32x4* __restrict__ p4 = reinterpret_cast<GLOBAL u32x4*>(p);
-            GLOBAL f32x4* __restrict__ m4 = reinterpret_cast<GLOBAL f32x4*>(m);
-            GLOBAL f32x4* __restrict__ v4 = reinterpret_cast<GLOBAL f32x4*>(v);
-            GLOBAL f32x4* __restrict__ w4 = reinterpret_cast<GLOBAL f32x4*>(w);
-            for (uint32_t k = first_pack<P, kBlockMixed>(tid, part); k < npack; k += kStride) {
-                const u32x4 G = ld<NTG>(g4 + k);
-                f32x4 W[2] = {ld<NTM>(w4 + 2 * k), ld<NTM>(w4 + 2 * k + 1)};
-                f32x4 M[2] = {ld<NTM>(m4 + 2 * k), ld<NTM>(m4 + 2 * k + 1)};
-                f32x4 V[2] = {ld<NTM>(v4 + 2 * k), ld<NTM>(v4 + 2 * k + 1)};
-                fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
-                float* wf = reinterpret_cast<float*>(W);
-                float* mf = reinterpret_cast<float*>(M);
-                float* vf = reinterpret_cast<float*>(V);
-                const uint32_t gw[4] = {G.x, G.y, G.z, G.w};
-                uint32_t pw[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x2 gg = widen2<F16>(gw[j]);
-                    const float a = mixed_elem(gg.x, wf[2 * j], mf[2 * j], vf[2 * j], c);
-                    const float b = mixed_elem(gg.y, wf[2 * j + 1], mf[2 * j + 1], vf[2 * j + 1], c);
-                    pw[j] = narrow2<F16>(a, b);
-                }
-                st<NTM>(w4 + 2 * k, W[0]); st<NTM>(w4 + 2 * k + 1, W[1]);
-                st<NTM>(m4 + 2 * k, M[0]); st<NTM>(m4 + 2 * k + 1, M[1]);
-                st<NTM>(v4 + 2 * k, V[0]); st<NTM>(v4 + 2 * k + 1, V[1]);
-                st<NTM>(p4 + k, u32x4{pw[0], pw[1], pw[2], pw[3]});
-            }
-        } else {
-            fused_coef<FUSED>(fs, t, scale, c);
-            for (uint32_t i = part * kBlockMixed + tid; i < n; i += kStride) {
-                float wi = w[i], mi = m[i], vi = v[i];
-                const float nw = mixed_elem(widen1<F16>(g[i]), wi, mi, vi, c);
-                w[i] = wi;
-                m[i] = mi;
-                v[i] = vi;
-                p[i] = narrow1<F16>(nw);
-            }
+        fused_coef<FUSED>(fs, t, scale, c);
+        for (uint32_t i = part * kBlockMixed + tid; i < n; i += kStride) {
+            float wi = w[i], mi = m[i], vi = v[i];
+            const float nw = mixed_elem(widen1<F16>(g[i]), wi, mi, vi, c);
+            w[i] = wi;
+            m[i] = mi;
+            v[i] = vi;
+            p[i] = narrow1<F16>(nw);
         }
     }
     end_step<FUSED>(fs, t, scale);
 }
 
-// Pure bf16 parameters with chosen state precisions: M32 / V32 = fp32 exp_avg /
-// exp_avg_sq (else bf16), KAHAN = bf16 compensation buffer in the aux stream
-// (else none: p' = round(p * decay - step_size * u)).  <false, false, true> is
-// the pure-bf16 Kahan mode.
-template <bool M32, bool V32, bool KAHAN, bool FUSED>
+// The aux stream of a pure-family step.
+constexpr int kAuxNone = 0;    // no aux stream: p' = round(p * decay - step_size * u)
+constexpr int kAuxKahan = 1;   // bf16 Kahan compensation c
+constexpr int kAuxSplit = 2;   // int16 remainder r of the split fp32 master w = join(p, r)
+
+// Steps whose param is read as well as written, over bf16 params: the pure-bf16
+// family with chosen state precisions (M32 / V32 = fp32 exp_avg / exp_avg_sq,
+// else bf16; aux none or Kahan; <false, false, kAuxKahan> is the pure-bf16 Kahan
+// mode), and the split-master mixed step (<true, true, kAuxSplit>).
+template <bool M32, bool V32, int AUX, bool FUSED>
 __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(const DevSeg* __restrict__ segs,
                                                                             const DevChunk* __restrict__ chunks,
                                                                             const LaunchScalars* __restrict__ sc,
@@ -599,8 +562,14 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
     int64_t t = 0;
     float scale = 0.0f;
     if (!begin_step<FUSED>(sc, fs, c, t, scale)) return;
-    constexpr int NT = ADAMW_NT_PURE;
-    constexpr int P = kTilePacks;   // tiles of 512 elements
+    constexpr bool KAHAN = AUX == kAuxKahan, SPLIT = AUX == kAuxSplit;
+    static_assert(!SPLIT || (M32 && V32), "the split master keeps fp32 moments");
+#ifndef ADAMW_PURE_WIDE_RULE
+#define ADAMW_PURE_WIDE_RULE 0
+#endif
+    constexpr bool WIDE = ADAMW_PURE_WIDE_RULE == 0 ? (M32 && V32 && AUX != kAuxNone) : (M32 || V32);
+    constexpr int NT = SPLIT ? ADAMW_NT_SPLIT : WIDE ? ADAMW_NT_PURE_WIDE : ADAMW_NT_PURE;
+    constexpr int P = SPLIT ? kTilePacksSplit : WIDE ? kTilePacksPureWide : kTilePacks;   // tiles of 512 elements
     constexpr uint32_t kStride = kXcdParts * kBlockPure;
     const uint32_t part = blockIdx.x % kXcdParts;
     const DevChunk ch = chunks[blockIdx.x / kXcdParts];
@@ -632,7 +601,7 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
             for (int q = 0; q < MW; ++q) M[q] = ld<NT>(m4 + MW * k + q);
 #pragma unroll
             for (int q = 0; q < VW; ++q) V[q] = ld<NT>(v4 + VW * k + q);
-            if constexpr (KAHAN) C = ld<NT>(c4 + k);
+            if constexpr (AUX != kAuxNone) C = ld<NT>(c4 + k);
             fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
             const uint32_t* gw = reinterpret_cast<const uint32_t*>(&G);
             const uint32_t* pw = reinterpret_cast<const uint32_t*>(&Pv);
@@ -661,7 +630,17 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
                     va = t2.x;
                     vb = t2.y;
                 }
-                if constexpr (KAHAN) {
+                if constexpr (SPLIT) {
+                    float wa = __uint_as_float(join_bits(pw[j] & 0xffffu, cw[j] & 0xffffu));
+                    float wb = __uint_as_float(join_bits(pw[j] >> 16, cw[j] >> 16));
+                    mixed_elem(gg.x, wa, ma, va, c);
+                    mixed_elem(gg.y, wb, mb, vb, c);
+                    uint32_t ra, rb;
+                    const uint32_t pa = split_bits(__float_as_uint(wa), ra);
+                    const uint32_t pb = split_bits(__float_as_uint(wb), rb);
+                    po[j] = pa | (pb << 16);
+                    co[j] = ra | (rb << 16);
+                } else if constexpr (KAHAN) {
                     const f32x2 cf = widen2<false>(cw[j]);
                     float sa, sb;
                     const float ta = kahan_sum(gg.x, pp.x, cf.x, ma, va, c, sa);
@@ -693,7 +672,7 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
             for (int q = 0; q < MW; ++q) st<NT>(m4 + MW * k + q, M[q]);
 #pragma unroll
             for (int q = 0; q < VW; ++q) st<NT>(v4 + VW * k + q, V[q]);
-            if constexpr (KAHAN) st<NT>(c4 + k, u32x4{co[0], co[1], co[2], co[3]});
+            if constexpr (AUX != kAuxNone) st<NT>(c4 + k, u32x4{co[0], co[1], co[2], co[3]});
         }
     } else {
         fused_coef<FUSED>(fs, t, scale, c);
@@ -703,7 +682,14 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
             if constexpr (M32) mi = m[i]; else mi = widen1<false>(m[i]);
             if constexpr (V32) vi = v[i]; else vi = widen1<false>(v[i]);
             const float gi = widen1<false>(g[i]);
-            if constexpr (KAHAN) {
+            if constexpr (SPLIT) {
+                float w = __uint_as_float(join_bits(p[i], cc[i]));
+                mixed_elem(gi, w, mi, vi, c);
+                uint32_t ri;
+                const uint32_t pi = split_bits(__float_as_uint(w), ri);
+                p[i] = (uint16_t)pi;
+                cc[i] = (uint16_t)ri;
+            } else if constexpr (KAHAN) {
                 float s;
                 const float tot = kahan_sum(gi, pf, widen1<false>(cc[i]), mi, vi, c, s);
                 const uint16_t pn = narrow1<false>(tot);
@@ -815,6 +801,9 @@ hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32
 #ifndef ADAMW_LDS_PURE_WIDE
 #define ADAMW_LDS_PURE_WIDE 81920
 #endif
+#ifndef ADAMW_LDS_SPLIT
+#define ADAMW_LDS_SPLIT 81920
+#endif
 
 // Two-launch form (fused == nullptr): the update kernel reads the prologue's
 // scalars at d_scalars.  Single launch: the kernel forms them from *fused.
@@ -832,11 +821,12 @@ static hipError_t launch_update_as(int kernel, const DevSeg* segs, const DevChun
         hipLaunchKernelGGL((update_kernel<1, FUSED>), grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars, fs);
         break;
     case kKernelSplit:
-        hipLaunchKernelGGL((update_kernel<3, FUSED>), grid, block, ADAMW_LDS_MIXED, stream, segs, chunks, d_scalars, fs);
+        hipLaunchKernelGGL((update_pure_kernel<true, true, kAuxSplit, FUSED>), grid, block_pure, ADAMW_LDS_SPLIT, stream,
+                           segs, chunks, d_scalars, fs);
         break;
 #define ADAMW_PURE_CASE(M, V, K)                                                                          \
     case kKernelPure + (M) * 4 + (V) * 2 + (K):                                                            \
-        hipLaunchKernelGGL((update_pure_kernel<M, V, K, FUSED>), grid, block_pure,                            \
+        hipLaunchKernelGGL((update_pure_kernel<M, V, (K) ? kAuxKahan : kAuxNone, FUSED>), grid, block_pure,    \
                            (M) && (V) && (K) ? ADAMW_LDS_PURE_WIDE : ADAMW_LDS_PURE, stream, segs,              \
                            chunks, d_scalars, fs);                                                         \
         break;

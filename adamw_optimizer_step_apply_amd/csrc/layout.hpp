@@ -53,8 +53,22 @@ constexpr int64_t kElemChunkElems = 4096;       // element chunk
 // Smaller and larger tiles (64-128, 512-1024 elements for the mixed step;
 // 256 and 1024-2048 for Kahan) were slower.
 constexpr int kXcdParts = 8;
-constexpr int kTilePacksMixed = 32;
-constexpr int kTilePacks = 64;
+#ifndef ADAMW_TILE_PACKS_MIXED
+#define ADAMW_TILE_PACKS_MIXED 32
+#endif
+#ifndef ADAMW_TILE_PACKS_SPLIT
+#define ADAMW_TILE_PACKS_SPLIT 32
+#endif
+#ifndef ADAMW_TILE_PACKS_PURE
+#define ADAMW_TILE_PACKS_PURE 64
+#endif
+#ifndef ADAMW_TILE_PACKS_PURE_WIDE
+#define ADAMW_TILE_PACKS_PURE_WIDE ADAMW_TILE_PACKS_PURE
+#endif
+constexpr int kTilePacksMixed = ADAMW_TILE_PACKS_MIXED;
+constexpr int kTilePacksSplit = ADAMW_TILE_PACKS_SPLIT;
+constexpr int kTilePacks = ADAMW_TILE_PACKS_PURE;
+constexpr int kTilePacksPureWide = ADAMW_TILE_PACKS_PURE_WIDE;   // fp32 exp_avg and exp_avg_sq + compensation
 // The pack of a chunk taken by lane tid of part `part` (per kXcdParts * block
 // packs): tile t of p packs belongs to part t % kXcdParts, so
 //     ((tid / p) * kXcdParts + part) * p + tid % p,
