@@ -44,7 +44,8 @@ EXPORTED = ("adamw_step", "adamw_multi_tensor_step", "adamw_multi_tensor_step_no
             "adamw_pure_multi_tensor_step",
             "adamw_check_finite",
             "adamw_last_error", "adamw_release_workspace", "adamw_abi_version", "adamw_plan_inspect",
-            "adamw_plan_inspect_bytes", "adamw_set_chunk_elems", "adamw_set_single_launch_max_workgroups")
+            "adamw_plan_inspect_bytes", "adamw_set_chunk_elems", "adamw_set_single_launch_max_workgroups",
+            "adamw_blocked_state_bytes", "adamw_blocked_state_copy")
 
 
 class adamw_hparams(ctypes.Structure):
@@ -111,6 +112,12 @@ def _declare(_lib):
     _lib.adamw_plan_inspect_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_pure_precision),
                                               ctypes.POINTER(adamw_tensor_list), ctypes.c_int,
                                               ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64]
+    _lib.adamw_blocked_state_bytes.restype = ctypes.c_int64
+    _lib.adamw_blocked_state_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_pure_precision),
+                                               ctypes.POINTER(adamw_tensor_list)]
+    _lib.adamw_blocked_state_copy.restype = ctypes.c_int
+    _lib.adamw_blocked_state_copy.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(adamw_pure_precision),
+                                              ctypes.POINTER(adamw_tensor_list), _vp, ctypes.c_int, _vp]
     _lib.adamw_set_chunk_elems.restype = ctypes.c_int64
     _lib.adamw_set_chunk_elems.argtypes = [ctypes.c_int64]
     _lib.adamw_set_single_launch_max_workgroups.restype = ctypes.c_int64
@@ -321,6 +328,49 @@ def adamw_plan_inspect_bytes(mode: int, p_dtype: int, tensors: TensorList, for_c
     assert n2 == n
     out = out[:n]
     return out[:, :6].view(np.int64), out[:, 6:].reshape(n, NUM_STREAMS, 2)
+
+
+def adamw_blocked_state_bytes(mode: int, p_dtype: int, tensors: TensorList, prec: "PurePrecision" = None) -> int:
+    """Bytes of the blocked state buffer for the per-tensor state that ``tensors``
+    describes (C ABI adamw_blocked_state_bytes)."""
+    pc = ctypes.byref(prec.c()) if prec is not None else None
+    n = _lib.adamw_blocked_state_bytes(mode, p_dtype, pc, ctypes.byref(tensors.c))
+    if n < 0:
+        raise AdamWError(E_INVALID, adamw_last_error())
+    return n
+
+
+def adamw_blocked_state_copy(mode: int, p_dtype: int, tensors: TensorList, blocked, to_blocked: bool = True,
+                             prec: "PurePrecision" = None, stream=None) -> None:
+    """Copies the state between per-tensor buffers and a blocked buffer, either way
+    (C ABI adamw_blocked_state_copy); returns when the copy is done."""
+    pc = ctypes.byref(prec.c()) if prec is not None else None
+    _check(_lib.adamw_blocked_state_copy(mode, p_dtype, pc, ctypes.byref(tensors.c), _addr(blocked),
+                                         int(bool(to_blocked)), _stream(stream)))
+
+
+def make_blocked_state(mode: int, p_dtype: int, numels: Sequence[int], exp_avg, exp_avg_sq, aux=None,
+                       shard_begin: int = 0, shard_end: int = -1, pad8: bool = True, flat_mask: int = 0,
+                       prec: "PurePrecision" = None, stream=None):
+    """Optimizer-owned state in the blocked layout, filled from per-tensor state.
+
+    ``exp_avg``, ``exp_avg_sq`` and ``aux`` are sequences of per-tensor tensors
+    (one per entry of ``numels``; with flat_mask bits 2-4, one flat shard tensor)
+    holding the state to start from -- e.g. zero moments and the fp32 master
+    weights.  Allocates one zero-filled uint8 tensor on their device, copies the
+    state in with the library's copy kernel, and returns ``(blocked, step_mask)``:
+    a step then takes ``TensorList(numels, [params, grads, [blocked], None, None],
+    shard_begin, shard_end, step_mask)``.  ``pad8`` lays the buffer out in the
+    padded flat index (ADAMW_FLAT_PAD8), which keeps every tensor of any length on
+    the 16-byte vector path when params and grads are 16-byte aligned."""
+    streams = [None, None, list(exp_avg), list(exp_avg_sq), None if aux is None else list(aux)]
+    mask = (flat_mask & 0x1c) | (FLAT_PAD8 if pad8 else 0)
+    tl = TensorList(numels, streams, shard_begin, shard_end, mask)
+    nbytes = adamw_blocked_state_bytes(mode, p_dtype, tl, prec)
+    dev = next(t.device for t in streams[2] if isinstance(t, torch.Tensor))
+    blocked = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    adamw_blocked_state_copy(mode, p_dtype, tl, blocked, True, prec, stream)
+    return blocked, mask | BLOCKED_STATE
 
 
 def adamw_set_chunk_elems(elems: int) -> int:

@@ -633,6 +633,71 @@ int64_t adamw_plan_inspect_bytes(adamw_mode mode, adamw_dtype p_dtype, const ada
     return n;
 }
 
+// The element sizes of a step of (mode, p_dtype), or of the pure step of *prec.
+static adamw_status state_kind(adamw_mode mode, adamw_dtype p_dtype, const adamw_pure_precision* prec, StepKind* kind)
+{
+    if (!prec) return mode_kind(mode, p_dtype, kind);
+    std::string err;
+    adamw_status st = check_pure_precision(prec, err);
+    if (st != ADAMW_OK) return fail(st, err);
+    *kind = kind_of_pure(*prec);
+    return ADAMW_OK;
+}
+
+int64_t adamw_blocked_state_bytes(adamw_mode mode, adamw_dtype p_dtype, const adamw_pure_precision* prec,
+                                  const adamw_tensor_list* list)
+{
+    g_err.clear();
+    StepKind kind;
+    if (state_kind(mode, p_dtype, prec, &kind) != ADAMW_OK) return -1;
+    CopyPlan cp;
+    std::string err;
+    // the blocked side's base is only an address to plan with: nothing is accessed
+    if (build_copy_plan(kind.esz, list, 4096, &cp, err) != ADAMW_OK) {
+        g_err = err;
+        return -1;
+    }
+    return cp.blocked_bytes;
+}
+
+adamw_status adamw_blocked_state_copy(adamw_mode mode, adamw_dtype p_dtype, const adamw_pure_precision* prec,
+                                      const adamw_tensor_list* list, void* blocked, int to_blocked, void* hip_stream)
+{
+    g_err.clear();
+    StepKind kind;
+    adamw_status st = state_kind(mode, p_dtype, prec, &kind);
+    if (st != ADAMW_OK) return st;
+    if (!blocked || (uintptr_t)blocked % 16) return fail(ADAMW_E_INVALID, "blocked buffer is null or not 16-byte aligned");
+    CopyPlan cp;
+    std::string err;
+    if ((st = build_copy_plan(kind.esz, list, (uint64_t)(uintptr_t)blocked, &cp, err)) != ADAMW_OK) return fail(st, err);
+    if (cp.chunks.empty()) return ADAMW_OK;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    int dev = 0;
+    if ((st = stream_device(stream, &dev)) != ADAMW_OK) return st;
+    DeviceGuard dg(dev);
+    const size_t seg_bytes = cp.segs.size() * sizeof(DevCopySeg);
+    const size_t bytes = seg_bytes + cp.chunks.size() * sizeof(DevChunk);
+    std::vector<unsigned char> host(bytes);
+    memcpy(host.data(), cp.segs.data(), seg_bytes);
+    memcpy(host.data() + seg_bytes, cp.chunks.data(), cp.chunks.size() * sizeof(DevChunk));
+    void* table = nullptr;
+    hipError_t e = hipMalloc(&table, bytes);
+    if (e != hipSuccess) return fail(ADAMW_E_NOMEM, "hipMalloc of the copy table failed");
+    const int esz[3] = {kind.esz[2], kind.esz[3], kind.esz[4]};
+    e = hipMemcpyAsync(table, host.data(), bytes, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+        e = launch_state_copy(static_cast<const DevCopySeg*>(table),
+                              reinterpret_cast<const DevChunk*>(static_cast<char*>(table) + seg_bytes),
+                              (int64_t)cp.chunks.size(), esz, to_blocked != 0, stream);
+    // the table is freed once the copy has run: the call returns with the copy done
+    const hipError_t e2 = hipStreamSynchronize(stream);
+    (void)hipFree(table);
+    if (e != hipSuccess) return hip_fail("state copy", e);
+    if (e2 != hipSuccess) return hip_fail("hipStreamSynchronize (state copy)", e2);
+    return ADAMW_OK;
+}
+
 int64_t adamw_set_single_launch_max_workgroups(int64_t max_workgroups)
 {
     const int64_t v = max_workgroups < 0 ? kSingleLaunchMaxWorkgroups : max_workgroups;

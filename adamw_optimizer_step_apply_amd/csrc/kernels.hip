@@ -847,6 +847,45 @@ hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks,
     return launch_update_as<false>(kernel, segs, chunks, n_chunks, d_scalars, FusedStep{}, stream);
 }
 
+// ---------------------------------------------------------------------------
+// State copy between per-tensor (or flat) state buffers and the blocked buffer
+// ---------------------------------------------------------------------------
+
+// One workgroup per chunk of the copy plan: the chunk's elements of each state
+// stream, element by element (the two sides need not share their alignment).
+template <typename T>
+__device__ __forceinline__ void copy_elems(uint64_t dst, uint64_t src, uint64_t off, uint32_t n)
+{
+    GLOBAL T* __restrict__ d = gptr<T>(dst, off);
+    const GLOBAL T* __restrict__ s = gptr<const T>(src, off);
+    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
+}
+
+__global__ __launch_bounds__(256) void state_copy_kernel(const DevCopySeg* __restrict__ segs,
+                                                         const DevChunk* __restrict__ chunks, int esz_m, int esz_v,
+                                                         int esz_aux, int to_blocked)
+{
+    const DevChunk ch = chunks[blockIdx.x];
+    const DevCopySeg& sg = segs[ch.seg];
+    const uint32_t n = ch.n_kind & kCountMask;
+    const int esz[3] = {esz_m, esz_v, esz_aux};
+    for (int s = 0; s < 3; ++s) {
+        const uint64_t dst = to_blocked ? sg.blocked_side[s] : sg.tensor_side[s];
+        const uint64_t src = to_blocked ? sg.tensor_side[s] : sg.blocked_side[s];
+        if (esz[s] == 4) copy_elems<uint32_t>(dst, src, ch.off, n);
+        else if (esz[s] == 2) copy_elems<uint16_t>(dst, src, ch.off, n);
+    }
+}
+
+hipError_t launch_state_copy(const DevCopySeg* segs, const DevChunk* chunks, int64_t n_chunks, const int esz[3],
+                             bool to_blocked, hipStream_t stream)
+{
+    if (n_chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)n_chunks), dim3(256), 0, stream, segs, chunks, esz[0],
+                       esz[1], esz[2], to_blocked ? 1 : 0);
+    return hipGetLastError();
+}
+
 __global__ void zero_words_kernel(uint32_t* __restrict__ p, int64_t n)
 {
     for (int64_t i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;

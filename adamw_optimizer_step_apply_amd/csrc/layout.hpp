@@ -136,6 +136,15 @@ struct alignas(16) DevChunk {
     uint64_t off;
 };
 
+// One piece of a state copy between the blocked buffer and per-tensor (or flat)
+// state buffers: the address of the piece's first element on each side, per
+// state stream (exp_avg, exp_avg_sq, aux; 0 for a stream the step does not use).
+struct alignas(64) DevCopySeg {
+    uint64_t tensor_side[3];
+    uint64_t blocked_side[3];
+    uint64_t pad[2];
+};
+
 // Scalars of one step, written by the prologue kernel and read by the update
 // kernel on the same stream.
 struct alignas(64) LaunchScalars {

@@ -260,6 +260,49 @@ void chunk_bytes(const Plan& plan, size_t c, const int esz[kStreams], uint64_t l
     }
 }
 
+adamw_status build_copy_plan(const int esz_in[kStreams], const adamw_tensor_list* list, uint64_t blocked,
+                             CopyPlan* out, std::string& err)
+{
+    if (!list) { err = "tensor list is null"; return ADAMW_E_INVALID; }
+    if (list->flat_mask & ADAMW_BLOCKED_STATE) {
+        err = "the list describes the per-tensor state: leave ADAMW_BLOCKED_STATE out of its flat_mask "
+              "(the blocked buffer is its own argument)";
+        return ADAMW_E_INVALID;
+    }
+    int esz[kStreams] = {0, 0, esz_in[2], esz_in[3], esz_in[4]};
+    // the per-tensor side: pointers, alignment, shard range
+    adamw_status st = build_plan(esz, list, kStateBlockElems, INT64_MAX, nullptr, err);
+    if (st != ADAMW_OK) return st;
+    // the blocked side: the pieces of the blocked plan and their addresses there
+    void* const blocked_ptr[1] = {reinterpret_cast<void*>((uintptr_t)blocked)};
+    adamw_tensor_list bl = *list;
+    bl.flat_mask |= ADAMW_BLOCKED_STATE;
+    bl.ptr[ADAMW_STREAM_EXP_AVG] = blocked_ptr;
+    Plan plan;
+    st = build_plan(esz, &bl, kStateBlockElems, INT64_MAX, &plan, err);
+    if (st != ADAMW_OK) return st;
+    out->segs.resize(plan.segs.size());
+    for (size_t i = 0; i < plan.segs.size(); ++i) {
+        const SegInfo& si = plan.info[i];
+        DevCopySeg& c = out->segs[i];
+        c = DevCopySeg{};
+        for (int s = ADAMW_STREAM_EXP_AVG; s <= ADAMW_STREAM_AUX; ++s) {
+            if (!esz[s]) continue;
+            const uint64_t e = (uint64_t)esz[s];
+            c.blocked_side[s - 2] = plan.segs[i].ptr[s];
+            if ((list->flat_mask >> s) & 1u)
+                c.tensor_side[s - 2] = (uint64_t)(uintptr_t)list->ptr[s][0] + (uint64_t)(si.flat - list->shard_begin) * e;
+            else
+                c.tensor_side[s - 2] = (uint64_t)(uintptr_t)list->ptr[s][si.tensor] + (uint64_t)si.tensor_off * e;
+        }
+    }
+    out->chunks.swap(plan.chunks);
+    int64_t block_bytes = 0;
+    for (int s = ADAMW_STREAM_EXP_AVG; s <= ADAMW_STREAM_AUX; ++s) block_bytes += kStateBlockElems * esz[s];
+    out->blocked_bytes = (plan.total + kStateBlockElems - 1) / kStateBlockElems * block_bytes;
+    return ADAMW_OK;
+}
+
 size_t choose_plan_slot(const std::vector<bool>& pinned, size_t cap)
 {
     size_t unpinned = 0, lru = pinned.size();

@@ -41,6 +41,20 @@ void mode_esizes(adamw_mode mode, adamw_dtype p_dtype, bool for_check, int esz[k
 adamw_status build_plan(const int esz[kStreams], const adamw_tensor_list* list, int64_t chunk_elems,
                         int64_t max_chunks, Plan* out, std::string& err);
 
+// The plan of a state copy between per-tensor (or flat) state buffers and one
+// blocked buffer: `list` describes the state as a step would see it without
+// ADAMW_BLOCKED_STATE (streams 2-4, flat_mask bits 2-4 and ADAMW_FLAT_PAD8 as for
+// a step; streams 0 and 1 are not used), `esz` the step's element sizes.  The
+// pieces are those of the blocked plan (split at block edges), one copy segment
+// each, with both sides' addresses; `blocked_bytes` is the blocked buffer's size.
+struct CopyPlan {
+    std::vector<DevCopySeg> segs;
+    std::vector<DevChunk> chunks;
+    int64_t blocked_bytes = 0;
+};
+adamw_status build_copy_plan(const int esz[kStreams], const adamw_tensor_list* list, uint64_t blocked,
+                             CopyPlan* out, std::string& err);
+
 // Device bytes of chunk `c` of `plan` in each stream: [lo[s], hi[s]) holds the
 // elements [off, off + count) of the chunk's segment at the stream's element
 // size esz[s]; lo = hi = 0 for a stream the plan does not touch.  These are

@@ -78,5 +78,7 @@ hipError_t launch_update(int kernel, const DevSeg* segs, const DevChunk* chunks,
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
 hipError_t launch_check(adamw_dtype g_dtype, const DevSeg* segs, const DevChunk* chunks, int64_t n_chunks,
                         int32_t* d_flag, uint32_t* done, bool fused, hipStream_t stream);
+hipError_t launch_state_copy(const DevCopySeg* segs, const DevChunk* chunks, int64_t n_chunks, const int esz[3],
+                             bool to_blocked, hipStream_t stream);
 
 }  // namespace adamw

@@ -285,10 +285,9 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
     """Per-tensor buffers for every stream; a "-blocked" mode instead keeps
     exp_avg / exp_avg_sq / aux in one blocked flat buffer of the whole list
     (the optimizer-owned layout; param and grad stay per tensor), indexed by
-    the padded flat index (every tensor at a multiple of 8 elements).
+    the padded flat index (every tensor at a multiple of 8 elements), filled
+    from the per-tensor state by the library's layout copy (make_blocked_state).
     Returns (arena, streams, flat_mask)."""
-    import torch
-
     import workloads
     base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
     align, flags, nb = state_layout(mode, numels)
@@ -297,16 +296,21 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
     keys = workloads.streams_of(base)
     streams = [[arena.view(k, i) for i in range(len(numels))] for k in keys]
     if nb:
-        B = STATE_BLOCK_ELEMS
-        cols = []
+        import adamw_optimizer_step_apply_amd as A
+        if base.startswith("pure"):
+            m32, v32, kahan = workloads.parse_pure(base)
+            code, prec = A.MIXED, A.PurePrecision(A.F32 if m32 else A.BF16, A.F32 if v32 else A.BF16, kahan)
+        else:
+            code, prec = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[base], None
+        dt = A.F16 if p_dtype == "f16" else A.BF16
+        state = streams[2:] + [None] * (5 - len(streams))
+        blocked, mask = A.make_blocked_state(code, dt, numels, *state, prec=prec)
+        assert mask == flags and blocked.numel() == nb * STATE_BLOCK_ELEMS * sum(
+            arena.bufs[k].element_size() for k in keys[2:])
         for k in keys[2:]:
-            src = arena.bufs[k]
-            flat = torch.cat([src, torch.zeros(nb * B - src.numel(), dtype=src.dtype, device=device)])
-            cols.append(flat.view(nb, B).view(torch.uint8))
-            del arena.bufs[k], src, flat
-        arena.bufs["blocked"] = torch.cat(cols, dim=1).contiguous()
-        del cols
-        streams = streams[:2] + [[arena.bufs["blocked"]], None, None]
+            del arena.bufs[k]
+        arena.bufs["blocked"] = blocked
+        streams = streams[:2] + [[blocked], None, None]
     return arena, streams, flags
 
 

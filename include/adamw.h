@@ -114,7 +114,7 @@
 extern "C" {
 #endif
 
-#define ADAMW_ABI_VERSION 6
+#define ADAMW_ABI_VERSION 7
 
 typedef enum {
     ADAMW_OK = 0,
@@ -340,6 +340,38 @@ void adamw_release_workspace(void);
 
 /* ADAMW_ABI_VERSION of the built library. */
 int adamw_abi_version(void);
+
+/* Optimizer-owned state in the blocked layout (ADAMW_BLOCKED_STATE), set up and
+ * read back from ordinary per-tensor (or flat) state buffers: the layout of the
+ * fastest steps made easy to adopt, and a blocked state checkpointed in the
+ * usual per-tensor form.  Layout only, no arithmetic.
+ *
+ * `list` describes the per-tensor state as a step of (mode, p_dtype) -- or,
+ * with prec non-null, of adamw_pure_multi_tensor_step with *prec -- would see
+ * it WITHOUT ADAMW_BLOCKED_STATE: numel, the shard range, ptr[2..4] and
+ * flat_mask bits 2-4 for exp_avg, exp_avg_sq and aux, and ADAMW_FLAT_PAD8,
+ * which selects the flat index the blocked buffer is laid out in.  ptr[0] and
+ * ptr[1] (param, grad) are not used.  The blocked buffer then serves the step
+ * whose list has the same numel, shard and ADAMW_FLAT_PAD8 choice,
+ * ADAMW_BLOCKED_STATE set and ptr[2][0] = the buffer.
+ *
+ * adamw_blocked_state_bytes: the size in bytes of that blocked buffer (whole
+ * blocks of ADAMW_STATE_BLOCK_ELEMS elements), or -1 on an invalid argument.
+ * No GPU work, no HIP call.
+ *
+ * adamw_blocked_state_copy: copies every element of the shard's state between
+ * the per-tensor buffers and `blocked` (device memory, 16-byte aligned,
+ * adamw_blocked_state_bytes long): to_blocked != 0 fills the blocked buffer
+ * from the per-tensor buffers, 0 the reverse.  The blocked buffer's padding
+ * (the ends of the last block and, with ADAMW_FLAT_PAD8, the gaps between
+ * tensors) is neither read nor written.  The copy runs on hip_stream, after
+ * the work already queued there, and the call returns once it is done (it
+ * allocates and frees a small device table: a setup and checkpoint routine,
+ * not for the training loop). */
+int64_t adamw_blocked_state_bytes(adamw_mode mode, adamw_dtype p_dtype, const adamw_pure_precision* prec,
+                                  const adamw_tensor_list* list);
+adamw_status adamw_blocked_state_copy(adamw_mode mode, adamw_dtype p_dtype, const adamw_pure_precision* prec,
+                                      const adamw_tensor_list* list, void* blocked, int to_blocked, void* hip_stream);
 
 /* Planner introspection, for tests: no GPU work, no HIP call.  Builds the
  * chunk plan that adamw_multi_tensor_step (for_check = 0) or

@@ -235,6 +235,87 @@ void test_random_plans()
     }
 }
 
+// The copy plan between per-tensor state and the blocked buffer: every piece's
+// two sides lie inside their buffers (the per-tensor buffer of the piece's
+// tensor, or the flat shard buffer; one block's sub-array) and the pieces
+// cover the owned elements once.
+void test_copy_plans()
+{
+    Rng r{0x51ed2701a3c4f5e9ull};
+    int planned = 0;
+    for (int it = 0; it < 300; ++it) {
+        const int* esz = kEszModes[r.below(5)];
+        List L;
+        random_list(r, L, esz, false);
+        L.flat_mask &= ~ADAMW_BLOCKED_STATE;
+        if (L.ptr[3].empty() && esz[3]) continue;   // random_list gave these streams to a blocked buffer
+        const uint64_t blocked = ((uint64_t)7 << 36) + ((uint64_t)1 << 40) + 256 * (uint64_t)r.below(64);
+        CopyPlan cp;
+        std::string err;
+        const adamw_status st = build_copy_plan(esz, L.get(), blocked, &cp, err);
+        CHECK(st == ADAMW_OK);
+        if (st != ADAMW_OK) {
+            fprintf(stderr, "copy plan refused: %s\n", err.c_str());
+            continue;
+        }
+        ++planned;
+        const int64_t fa = (L.flat_mask & ADAMW_FLAT_PAD8) ? 8 : 1;
+        int64_t total = 0;
+        std::vector<int64_t> start;
+        for (int64_t n : L.numel) {
+            start.push_back(total);
+            total += (n + fa - 1) / fa * fa;
+        }
+        const int64_t b = L.shard_begin, e = L.shard_end < 0 ? total : L.shard_end;
+        int64_t block_bytes = 0, soff[3] = {0, 0, 0};
+        for (int s = 0; s < 3; ++s) {
+            soff[s] = block_bytes;
+            block_bytes += kStateBlockElems * esz[s + 2];
+        }
+        const int64_t nb = (e - b + kStateBlockElems - 1) / kStateBlockElems;
+        CHECK(cp.blocked_bytes == nb * block_bytes);
+        int64_t covered = 0;
+        for (const DevChunk& ch : cp.chunks) {
+            CHECK(ch.seg < cp.segs.size());
+            const DevCopySeg& sg = cp.segs[ch.seg];
+            const uint64_t n = ch.n_kind & kCountMask;
+            covered += (int64_t)n;
+            for (int s = 0; s < 3; ++s) {
+                const int es = esz[s + 2];
+                if (!es) {
+                    CHECK(sg.tensor_side[s] == 0 && sg.blocked_side[s] == 0);
+                    continue;
+                }
+                // blocked side: inside one block's sub-array for stream s
+                const uint64_t lo = sg.blocked_side[s] + ch.off * (uint64_t)es, hi = lo + n * (uint64_t)es;
+                CHECK(lo >= blocked && hi <= blocked + (uint64_t)(nb * block_bytes));
+                const uint64_t in_block = (lo - blocked) % (uint64_t)block_bytes;
+                CHECK(in_block >= (uint64_t)soff[s] && in_block + (hi - lo) <= (uint64_t)(soff[s] + kStateBlockElems * es));
+                // tensor side: inside the flat shard buffer, or inside one tensor's buffer
+                const uint64_t tlo = sg.tensor_side[s] + ch.off * (uint64_t)es, thi = tlo + n * (uint64_t)es;
+                const std::vector<void*>& P = L.ptr[s + 2];
+                bool inside = false;
+                if ((L.flat_mask >> (s + 2)) & 1u) {
+                    inside = tlo >= addr(P[0]) && thi <= addr(P[0]) + (uint64_t)((e - b) * es);
+                } else {
+                    for (size_t i = 0; i < P.size() && !inside; ++i)
+                        inside = tlo >= addr(P[i]) && thi <= addr(P[i]) + (uint64_t)(L.numel[i] * es);
+                }
+                CHECK(inside);
+            }
+        }
+        int64_t owned = 0;
+        for (size_t i = 0; i < L.numel.size(); ++i) {
+            const int64_t lo = start[i] > b ? start[i] : b;
+            const int64_t hi = start[i] + L.numel[i] < e ? start[i] + L.numel[i] : e;
+            if (hi > lo) owned += hi - lo;
+        }
+        CHECK(covered == owned);
+        mix((uint64_t)cp.blocked_bytes);
+    }
+    CHECK(planned > 100);
+}
+
 void expect_invalid(const int esz[kStreams], List& L, const char* what)
 {
     Plan plan;
@@ -443,6 +524,7 @@ void test_slot_policy()
 int main()
 {
     test_random_plans();
+    test_copy_plans();
     test_invalid_lists();
     test_argument_checks();
     test_slot_policy();

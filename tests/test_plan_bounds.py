@@ -298,3 +298,40 @@ def test_checker_is_not_vacuous():
     bad.soff[4] += 4
     with pytest.raises(AssertionError):
         check_plan(bad, A.MIXED, A.BF16)
+
+
+@pytest.mark.parametrize("mode,prec,state_bytes", [
+    ("mixed", None, 12), ("kahan", None, 6), ("split", None, 10),
+    ("pure", (True, False, True), 8), ("pure", (False, True, False), 6)])
+@pytest.mark.parametrize("pad8,shard", [(True, (0, -1)), (False, (0, -1)), (False, (1000, 300000)),
+                                        (True, (16384, 16384 * 3 + 8))])
+def test_blocked_state_bytes(mode, prec, state_bytes, pad8, shard):
+    """Whole blocks of 16384 elements over the shard's length, each holding the
+    state streams' bytes (no GPU: the query plans only)."""
+    numels = [100_000, 7, 65_536, 3, 250_001]
+    pc = None if prec is None else A.PurePrecision(A.F32 if prec[0] else A.BF16, A.F32 if prec[1] else A.BF16,
+                                                   prec[2])
+    esz = pure_esz(*prec) if prec else ESZ[(mode, "bf16")]
+    ptrs = [None, None] + [arena_ptrs((1 << 40) + s * (1 << 34), numels, 8, esz[s]) if esz[s] else None
+                           for s in (2, 3, 4)]
+    tl = A.TensorList(numels, ptrs, shard[0], shard[1], A.FLAT_PAD8 if pad8 else 0)
+    fa = 8 if pad8 else 1
+    total = sum(-(-n // fa) * fa for n in numels)
+    length = (total if shard[1] < 0 else shard[1]) - shard[0]
+    assert A.adamw_blocked_state_bytes(CODE.get(mode, A.MIXED), A.BF16, tl, pc) == \
+        -(-length // B) * B * state_bytes
+
+
+def test_blocked_state_bytes_refuses_bad_lists():
+    numels = [1000, 5]
+    ptrs = [None, None] + [arena_ptrs((1 << 40) + s * (1 << 34), numels, 8, 4) for s in (2, 3, 4)]
+    with pytest.raises(A.AdamWError, match="BLOCKED_STATE"):
+        A.adamw_blocked_state_bytes(A.MIXED, A.BF16, A.TensorList(numels, ptrs, 0, -1, A.BLOCKED_STATE))
+    bad = list(ptrs)
+    bad[3] = None
+    with pytest.raises(A.AdamWError, match="exp_avg_sq"):
+        A.adamw_blocked_state_bytes(A.MIXED, A.BF16, A.TensorList(numels, bad))
+    misaligned = list(ptrs)
+    misaligned[4] = [p + 2 for p in ptrs[4]]
+    with pytest.raises(A.AdamWError, match="aligned"):
+        A.adamw_blocked_state_bytes(A.MIXED, A.BF16, A.TensorList(numels, misaligned))
