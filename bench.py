@@ -95,8 +95,8 @@ CALIB_COPY_BYTES = 4 << 30
 # the kernel each timed mode launches, as rocprofv3 names it (a substring of the symbol)
 # the timed kernel of each mode, as a prefix of its name in rocprofv3 output (the
 # last template argument, the launch form, is left open)
-KERNEL_OF = {"mixed": "update_kernel<0,", "split": "update_kernel<3,",
-             "kahan": "update_pure_kernel<false, false, true,", "f16amp": "update_kernel<1,",
+KERNEL_OF = {"mixed": "update_kernel<0,", "split": "update_pure_kernel<true, true, 2,",
+             "kahan": "update_pure_kernel<false, false, 1,", "f16amp": "update_kernel<1,",
              "check": "check_kernel"}
 
 
@@ -611,8 +611,9 @@ def main():
 
 def _kernel_sha():
     """Hash of the code that decides a launch's HBM traffic (kernels, planner,
-    layout constants), comments and blank lines left out, so that a recorded
-    counter summary stays valid across edits of the documentation alone."""
+    layout constants, and the header's #define lines), comments and blank lines
+    left out, so that a recorded counter summary stays valid across edits of the
+    documentation and of declarations alone."""
     import hashlib
     import re
     h = hashlib.sha256()
@@ -622,7 +623,10 @@ def _kernel_sha():
             src = fh.read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
         src = re.sub(r"//[^\n]*", "", src)
-        h.update("\n".join(ln.rstrip() for ln in src.splitlines() if ln.strip()).encode())
+        lines = [ln.rstrip() for ln in src.splitlines() if ln.strip()]
+        if f.endswith(".h"):
+            lines = [ln for ln in lines if ln.lstrip().startswith("#define")]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 
