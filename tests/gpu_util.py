@@ -380,3 +380,93 @@ def unpack_blocked(case, blocked: torch.Tensor, b, e) -> dict:
         out[k] = to_np(part)
         col += nbytes
     return out
+
+
+PIECE = 1 << 26          # elements per comparison piece (a multiple of the state block)
+RANGE = 1 << 24          # elements per oracle work item
+
+
+def host_threads() -> int:
+    """Host threads for the oracle (the machine's CPU share is 16 threads)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_ranges(mode, host: dict, ranges, ho: oracle.HParams, t: int, p_is_f16=False):
+    """Steps the arena ranges [a, b) of `host` in place on all host threads: the
+    update is elementwise, so any cut of a tensor's elements steps them as the
+    whole tensor would, and the oracle's C loops release the GIL."""
+    from concurrent.futures import ThreadPoolExecutor
+    work = [(a + o, min(b, a + o + RANGE)) for a, b in ranges for o in range(0, b - a, RANGE)]
+
+    def run(ab):
+        a, b = ab
+        h = {k: v[a:b] for k, v in host.items()}
+        if mode == "mixed":
+            oracle.adamw_mixed(h["p"], h["g"], h["master"], h["m"], h["v"], ho, t, p_is_f16=p_is_f16)
+        elif mode == "split":
+            oracle.adamw_mixed_split(h["p"], h["g"], h["r"], h["m"], h["v"], ho, t)
+        elif mode == "kahan":
+            oracle.adamw_kahan(h["p"], h["g"], h["m"], h["v"], h["c"], ho, t)
+        else:
+            oracle.adamw_pure(h["p"], h["g"], h["m"], h["v"], h.get("c"), ho, t)
+
+    with ThreadPoolExecutor(host_threads()) as pool:
+        list(pool.map(run, work))
+
+
+class FullCase(Case):
+    """A full-size workload compared on every element: the oracle steps the
+    owned pieces of the arenas on all host threads, and the comparison runs
+    over the whole arenas in pieces (untouched elements and gaps included)."""
+
+    def oracle_step(self, hp: oracle.HParams, shard=(0, -1), skip=False, flat_align=1):
+        if skip:
+            return
+        t = self.step + 1
+        end = None if shard[1] < 0 else shard[1]
+        ranges = [(self.arena.offsets[i] + lo, self.arena.offsets[i] + hi)
+                  for i, lo, hi, _ in oracle.shard_pieces(self.numels, shard[0], end, flat_align)]
+        oracle_ranges(self.mode, self.host, ranges, hp, t, self.p_dtype == "f16")
+        self.step = t
+
+    def compare_all(self, label="", skip_keys=()):
+        torch.cuda.synchronize()
+        assert int(self.d_step.item()) == self.step, f"{label}: step counter {int(self.d_step.item())} != {self.step}"
+        stats = []
+        f16 = self.p_dtype == "f16"
+        for k in self.keys:
+            if k == "g" or k in skip_keys:
+                continue
+            n = self.arena.bufs[k].numel()
+            parts = [compare(f"{label}:{k}", to_np(self.arena.bufs[k][a:a + PIECE]), self.host[k][a:a + PIECE],
+                             k in f32_keys(self.mode), f16) for a in range(0, n, PIECE)]
+            stats.append(merge_stats(f"{label}:{k}", parts))
+        log_stats(stats)
+        return stats
+
+    def compare_blocked(self, blocked: torch.Tensor, label=""):
+        """The state streams read out of a blocked buffer of the whole list whose
+        padded flat index is this case's arena index (arenas at multiples of 8),
+        against the host arenas, every element (gaps carried over at packing)."""
+        torch.cuda.synchronize()
+        B = A.STATE_BLOCK_ELEMS
+        rows = PIECE // B
+        col, stats = 0, []
+        for k in self.keys[2:]:
+            dt = self.arena.bufs[k].dtype
+            width = B * torch.empty(0, dtype=dt).element_size()
+            n = self.host[k].size
+            parts = []
+            for r0 in range(0, blocked.shape[0], rows):
+                a = r0 * B
+                if a >= n:
+                    break
+                piece = blocked[r0:r0 + rows, col:col + width].contiguous().view(dt).reshape(-1)
+                m = min(piece.numel(), n - a)
+                parts.append(compare(f"{label}:{k}", to_np(piece[:m]), self.host[k][a:a + m], k in f32_keys(self.mode),
+                                     self.p_dtype == "f16"))
+            stats.append(merge_stats(f"{label}:{k}", parts))
+            col += width
+        log_stats(stats)
+        return stats

@@ -1,7 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configuration that
-bench.py times (allocation-aligned arenas, default chunking).  The oracle follows
-sampled elements (every tensor's first and last 8 plus ~2M uniform positions) or,
-where it finishes in seconds, every element.  Bar: see gpu_util."""
+bench.py times (allocation-aligned arenas, default chunking).  The oracle steps
+every element (on all host threads) and every element of every stream is
+compared, the arenas' untouched parts included; only the tensor past 2^32
+elements is followed on samples.  Bar: see gpu_util.  The OPT-1.3B list is in
+test_gpu_full_size.py."""
 import numpy as np
 import pytest
 import torch
@@ -9,8 +11,7 @@ import torch
 import adamw_optimizer_step_apply_amd as A
 import oracle
 import workloads
-from gpu_util import (Case, SampledCase, blocked_gather, build_blocked_padded, free, hp_pair, padded_starts,
-                      same_bits, to_np)
+from gpu_util import Case, FullCase, SampledCase, build_blocked_padded, free, hp_pair, same_bits, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -38,27 +39,30 @@ def test_bert_rank0_shard_all_elements_20_steps():
 
 
 @pytest.mark.parametrize("rank", [1, 2, 3])
-def test_bert_other_rank_shards_sampled(rank):
-    """Ranks 1-3: shards that start and end inside tensors and span several."""
+def test_bert_other_rank_shards_all_elements(rank):
+    """Ranks 1-3: shards that start and end inside tensors and span several;
+    20 steps, every element of the list compared (the other ranks' elements
+    must stay untouched)."""
     wl = workloads.get("bert_52m")
     shard = wl.shard(rank)
-    case = SampledCase("mixed", wl.numels, seed=2100 + rank, shard=shard, n_random=1 << 20)
+    case = FullCase("mixed", wl.numels, seed=2100 + rank)
     hg, ho = hp_pair()
-    tl = case.tensor_list()
+    tl = case.tensor_list(*shard)
     for s in range(wl.steps):
         if s:
             case.refill_grads(s)
         A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl, hg, case.d_step)
-        case.oracle_step(ho)
+        case.oracle_step(ho, shard=shard)
     _print(case.compare_all(f"bert-r{rank}"))
     free()
 
 
 def test_opt125m_kahan_100_steps_warmup():
     """OPT-125m list, pure bf16 + Kahan, 100 steps of the linear warmup schedule
-    (lr 2e-4 * t/500), a fresh seeded gradient every step."""
+    (lr 2e-4 * t/500), a fresh seeded gradient every step; every element
+    compared at t = 10 and t = 100."""
     wl = workloads.get("opt_125m")
-    case = SampledCase("kahan", wl.numels, seed=3001)
+    case = FullCase("kahan", wl.numels, seed=3001)
     tl = case.tensor_list()
     for s in range(wl.steps):
         if s:
@@ -69,55 +73,6 @@ def test_opt125m_kahan_100_steps_warmup():
         case.oracle_step(ho)
         if s + 1 in (10, 100):
             _print(case.compare_all(f"opt125m-t{s + 1}"))
-    free()
-
-
-@pytest.mark.parametrize("mode", ["mixed", "kahan", "split"])
-def test_opt13b_full_size_10_steps(mode):
-    """OPT-1.3B list (1,315,753,984 params), 10 steps, the shape bench.py times."""
-    wl = workloads.get("opt_1_3b")
-    case = SampledCase(mode, wl.numels, seed={"mixed": 4001, "kahan": 4002, "split": 4003}[mode])
-    tl = case.tensor_list()
-    hg, ho = hp_pair()
-    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
-    for s in range(wl.steps):
-        if s:
-            case.refill_grads(s)
-        A.adamw_multi_tensor_step(code, A.BF16, tl, hg, case.d_step)
-        case.oracle_step(ho)
-    _print(case.compare_all(f"opt13b-{mode}"))
-    del case, tl
-    free()
-
-
-@pytest.mark.parametrize("mode", ["mixed", "kahan", "split"])
-def test_opt13b_full_size_blocked_state(mode):
-    """OPT-1.3B list with exp_avg / exp_avg_sq / aux in one blocked buffer of the
-    whole list (bench.py's "-blocked" modes), the workload's 10 steps; the sampled
-    elements are read back out of their blocks and compared with the oracle."""
-    wl = workloads.get("opt_1_3b")
-    case = SampledCase(mode, wl.numels, seed={"mixed": 4101, "kahan": 4102, "split": 4103}[mode])
-    state = case.keys[2:]
-    blocked = build_blocked_padded(case.arena, state, wl.numels)
-    streams = [[case.arena.view(k, i) for i in range(len(wl.numels))] for k in case.keys[:2]]
-    tl = A.TensorList(wl.numels, streams + [[blocked], None, None], 0, -1, A.BLOCKED_STATE | A.FLAT_PAD8)
-    hg, ho = hp_pair()
-    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
-    for s in range(wl.steps):
-        if s:
-            case.refill_grads(s)
-        A.adamw_multi_tensor_step(code, A.BF16, tl, hg, case.d_step)
-        case.oracle_step(ho)
-    torch.cuda.synchronize()
-    # every OPT-1.3B length is a multiple of 8: the padded flat index is the plain one
-    got = blocked_gather(blocked, {k: case.arena.bufs[k].dtype for k in state},
-                         torch.from_numpy(case.flat).to(blocked.device))
-    for k in state:
-        # the per-tensor arena copy of this stream was not stepped: put the blocked
-        # values of the sampled elements there so the usual comparison reads them
-        case.arena.bufs[k][case.idx] = got[k]
-    _print(case.compare_all(f"opt13b-{mode}-blocked"))
-    del case, tl, blocked
     free()
 
 
@@ -164,10 +119,11 @@ def test_ragged_10k_fp16_overflow_skip():
     params and grads scaled by 65536, fp32 master/m/v.  Every step runs the
     overflow check, then the step with the flag.  One seeded step plants +inf at
     a seeded tensor and element: the flag must be set (as the oracle's scan of
-    all gradients says) and every buffer and the counter left bit-identical."""
+    all gradients says) and every buffer and the counter left bit-identical.
+    Every element compared at the end."""
     wl = workloads.get("ragged_10k")
     scale = wl.loss_scale
-    case = SampledCase("mixed", wl.numels, seed=5001, p_dtype="f16", loss_scale=scale, n_random=1 << 21)
+    case = FullCase("mixed", wl.numels, seed=5001, p_dtype="f16", loss_scale=scale)
     tl = case.tensor_list()
     hg, ho = hp_pair(inv_scale=1.0 / scale)
     rng = np.random.default_rng(np.random.SeedSequence([5, 1]))
@@ -196,6 +152,7 @@ def test_ragged_10k_fp16_overflow_skip():
             for k, v in before.items():
                 assert same_bits(case.arena.bufs[k], v), f"{k} changed on a skipped step"
             del before
+        _print(f"ragged10k: step {s} done")
     _print(case.compare_all("ragged10k"))
     del case, tl
     free()
@@ -206,20 +163,19 @@ def test_ragged_10k_fp16_blocked_padded_state():
     it: exp_avg / exp_avg_sq / master in the blocked layout of the padded flat
     index (every tensor at a multiple of 8), params and grads per tensor.  Check
     + step for 3 steps, an overflow planted in the second (skipped: nothing
-    written, counter kept); sampled elements against the oracle."""
+    written, counter kept); every element of every stream against the oracle."""
     wl = workloads.get("ragged_10k")
     scale = wl.loss_scale
-    case = SampledCase("mixed", wl.numels, seed=5101, p_dtype="f16", loss_scale=scale, n_random=1 << 21,
-                       align_elems=8)
+    case = FullCase("mixed", wl.numels, seed=5101, p_dtype="f16", loss_scale=scale, align_elems=8)
     state = case.keys[2:]
     blocked = build_blocked_padded(case.arena, state, wl.numels)
+    for k in state:                      # the per-tensor copies are not stepped: let them go
+        case.arena.bufs[k] = case.arena.bufs[k][:0]
+    free()
     streams = [[case.arena.view(k, i) for i in range(len(wl.numels))] for k in case.keys[:2]]
     tl = A.TensorList(wl.numels, streams + [[blocked], None, None], 0, -1, A.BLOCKED_STATE | A.FLAT_PAD8)
     hg, ho = hp_pair(inv_scale=1.0 / scale)
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
-    starts = np.concatenate([[0], np.cumsum(wl.numels)]).astype(np.int64)
-    tens = np.searchsorted(starts, case.flat, side="right") - 1
-    pos = torch.from_numpy(padded_starts(wl.numels)[tens] + (case.flat - starts[tens])).to("cuda")
     t_inj = int(np.argmax(wl.numels))
     for s in range(3):
         if s:
@@ -228,15 +184,12 @@ def test_ragged_10k_fp16_blocked_padded_state():
             case.arena.view("g", t_inj)[12345] = float("inf")
         A.adamw_check_finite(A.F16, tl, flag)
         A.adamw_multi_tensor_step(A.MIXED, A.F16, tl, hg, case.d_step, flag)
-        case.oracle_step(ho, skip=(s == 1))
+        case.oracle_step(ho, skip=(s == 1), flat_align=8)
         torch.cuda.synchronize()
         assert int(flag.item()) == int(s == 1), s
+        _print(f"ragged10k-blocked: step {s} done")
     assert case.step == 2
-    got = blocked_gather(blocked, {k: case.arena.bufs[k].dtype for k in state}, pos)
-    for k in state:
-        # the per-tensor arena copy of this stream was not stepped: put the blocked
-        # values of the sampled elements there so the usual comparison reads them
-        case.arena.bufs[k][case.idx] = got[k]
-    _print(case.compare_all("ragged10k-blocked"))
-    del case, tl, blocked, got
+    _print(case.compare_all("ragged10k-blocked", skip_keys=state))
+    _print(case.compare_blocked(blocked, "ragged10k-blocked"))
+    del case, tl, blocked
     free()

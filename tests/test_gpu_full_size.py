@@ -1,64 +1,42 @@
 """GPU parity on every element of the OPT-1.3B list (386 tensors,
 1,315,753,984 parameters), the shape of the "opt-1.3b / bf16-pure training from
 scratch" run and memory tables of "[pure bf16 training] w/ AnyPrecisionAdamW
-and Kahan summation", in the launch configurations bench.py times.
+and Kahan summation", in the launch configurations bench.py times: the mixed
+and Kahan modes and the split master.
 
 One seeded initial state is stepped 10 times three ways from the same bytes:
 on the GPU with per-tensor state buffers, on the GPU with the state in the
 blocked layout (its own param copy, the gradient shared), and by the CPU
-oracle on the host (the list cut into equal ranges, one host thread each: the
+oracle on the host (the list cut into ranges stepped on all host threads: the
 update is elementwise and the oracle's C loops release the GIL).  A fresh
 seeded gradient each step (generated on the GPU, copied to the host).  Then
 every element of every stream of both GPU layouts is compared with the oracle,
 in pieces, to the bar of gpu_util (bit-exact).
 """
-import os
 import time
-from concurrent.futures import ThreadPoolExecutor
 
-import numpy as np
 import pytest
 import torch
 
 import adamw_optimizer_step_apply_amd as A
-import oracle
 import workloads
-from gpu_util import build_blocked_padded, compare, free, hp_pair, log_stats, merge_stats, to_np
+from gpu_util import (PIECE, build_blocked_padded, compare, f32_keys, free, host_threads, hp_pair, log_stats, merge_stats,
+                      oracle_ranges, to_np)
 
 pytestmark = pytest.mark.gpu
-
-PIECE = 1 << 26          # elements per comparison piece (a multiple of the state block)
 
 
 def _print(*a):
     print(*a, flush=True)
 
 
-def _threads():
-    return max(1, min(16, len(os.sched_getaffinity(0))))
-
-
-def _oracle_step(mode, host, n, ho, t, pool, threads):
-    cuts = [n * i // threads for i in range(threads + 1)]
-
-    def run(i):
-        a, b = cuts[i], cuts[i + 1]
-        h = {k: v[a:b] for k, v in host.items()}
-        if mode == "mixed":
-            oracle.adamw_mixed(h["p"], h["g"], h["master"], h["m"], h["v"], ho, t)
-        else:
-            oracle.adamw_kahan(h["p"], h["g"], h["m"], h["v"], h["c"], ho, t)
-
-    list(pool.map(run, range(threads)))
-
-
-@pytest.mark.parametrize("mode", ["mixed", "kahan"])
+@pytest.mark.parametrize("mode", ["mixed", "kahan", "split"])
 def test_opt13b_every_element_10_steps(mode):
     wl = workloads.get("opt_1_3b")
     numels = wl.numels
     n = wl.total
-    seed = {"mixed": 4501, "kahan": 4502}[mode]
-    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN}[mode]
+    seed = {"mixed": 4501, "kahan": 4502, "split": 4503}[mode]
+    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
     keys = workloads.streams_of(mode)          # p, g, m, v, aux
     t0 = time.time()
     arena = workloads.make_state(mode, numels, "cuda", seed, align_elems=128)
@@ -74,21 +52,19 @@ def test_opt13b_every_element_10_steps(mode):
     d_step = torch.zeros(1, dtype=torch.int32, device="cuda")
     d_step_blk = torch.zeros(1, dtype=torch.int32, device="cuda")
     hg, ho = hp_pair()
-    threads = _threads()
-    _print(f"opt13b-{mode}: state ready in {time.time() - t0:.1f} s; oracle on {threads} threads")
-    with ThreadPoolExecutor(threads) as pool:
-        for s in range(wl.steps):
-            if s:
-                workloads.refill_grads(arena, seed, s)
-                host["g"] = to_np(arena.bufs["g"])
-            A.adamw_multi_tensor_step(code, A.BF16, tl, hg, d_step)
-            A.adamw_multi_tensor_step(code, A.BF16, tl_blk, hg, d_step_blk)
-            t1 = time.time()
-            _oracle_step(mode, host, n, ho, s + 1, pool, threads)
-            torch.cuda.synchronize()
-            _print(f"opt13b-{mode}: step {s + 1} done (oracle {time.time() - t1:.1f} s)")
+    _print(f"opt13b-{mode}: state ready in {time.time() - t0:.1f} s; oracle on {host_threads()} threads")
+    for s in range(wl.steps):
+        if s:
+            workloads.refill_grads(arena, seed, s)
+            host["g"] = to_np(arena.bufs["g"])
+        A.adamw_multi_tensor_step(code, A.BF16, tl, hg, d_step)
+        A.adamw_multi_tensor_step(code, A.BF16, tl_blk, hg, d_step_blk)
+        t1 = time.time()
+        oracle_ranges(mode, host, [(0, n)], ho, s + 1)
+        torch.cuda.synchronize()
+        _print(f"opt13b-{mode}: step {s + 1} done (oracle {time.time() - t1:.1f} s)")
     assert int(d_step.item()) == int(d_step_blk.item()) == wl.steps
-    f32 = set(k for k in keys if arena.bufs[k].dtype == torch.float32)
+    f32 = set(f32_keys(mode))
     stats = []
     # per-tensor layout: the arenas themselves
     for k in keys:
@@ -100,6 +76,7 @@ def test_opt13b_every_element_10_steps(mode):
     parts = [compare(f"opt13b-{mode}-blocked:p", to_np(p_blk[a:a + PIECE]), host["p"][a:a + PIECE], False)
              for a in range(0, n, PIECE)]
     stats.append(merge_stats(f"opt13b-{mode}-blocked:p", parts))
+    arena_dtypes = {k: arena.bufs[k].dtype for k in keys}
     del arena, tl, per_tensor
     free()
     # blocked layout: each state stream read out of its blocks, a run of blocks at a time
@@ -107,7 +84,7 @@ def test_opt13b_every_element_10_steps(mode):
     rows = PIECE // B
     col = 0
     for k in keys[2:]:
-        dt = {np.dtype(np.float32): torch.float32, np.dtype(np.uint16): torch.bfloat16}[host[k].dtype]
+        dt = arena_dtypes[k]
         width = B * torch.empty(0, dtype=dt).element_size()
         parts = []
         for r0 in range(0, blocked.shape[0], rows):
