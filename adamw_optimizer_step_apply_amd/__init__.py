@@ -351,14 +351,15 @@ def adamw_blocked_state_copy(mode: int, p_dtype: int, tensors: TensorList, block
 
 def make_blocked_state(mode: int, p_dtype: int, numels: Sequence[int], exp_avg, exp_avg_sq, aux=None,
                        shard_begin: int = 0, shard_end: int = -1, pad8: bool = True, flat_mask: int = 0,
-                       prec: "PurePrecision" = None, stream=None):
+                       prec: "PurePrecision" = None, stream=None, device=None):
     """Optimizer-owned state in the blocked layout, filled from per-tensor state.
 
     ``exp_avg``, ``exp_avg_sq`` and ``aux`` are sequences of per-tensor tensors
     (one per entry of ``numels``; with flat_mask bits 2-4, one flat shard tensor)
     holding the state to start from -- e.g. zero moments and the fp32 master
-    weights.  Allocates one zero-filled uint8 tensor on their device, copies the
-    state in with the library's copy kernel, and returns ``(blocked, step_mask)``:
+    weights (tensors, or device addresses with ``device`` given).  Allocates one
+    zero-filled uint8 tensor on their device, copies the state in with the
+    library's copy kernel, and returns ``(blocked, step_mask)``:
     a step then takes ``TensorList(numels, [params, grads, [blocked], None, None],
     shard_begin, shard_end, step_mask)``.  ``pad8`` lays the buffer out in the
     padded flat index (ADAMW_FLAT_PAD8), which keeps every tensor of any length on
@@ -367,8 +368,12 @@ def make_blocked_state(mode: int, p_dtype: int, numels: Sequence[int], exp_avg, 
     mask = (flat_mask & 0x1c) | (FLAT_PAD8 if pad8 else 0)
     tl = TensorList(numels, streams, shard_begin, shard_end, mask)
     nbytes = adamw_blocked_state_bytes(mode, p_dtype, tl, prec)
-    dev = next(t.device for t in streams[2] if isinstance(t, torch.Tensor))
-    blocked = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    if device is None:
+        tensors = [t for t in streams[2] if isinstance(t, torch.Tensor)]
+        if not tensors:
+            raise ValueError("make_blocked_state: pass device= when the state is given as addresses")
+        device = tensors[0].device
+    blocked = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
     adamw_blocked_state_copy(mode, p_dtype, tl, blocked, True, prec, stream)
     return blocked, mask | BLOCKED_STATE
 

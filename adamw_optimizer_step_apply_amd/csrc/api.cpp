@@ -37,6 +37,8 @@ adamw_status fail(adamw_status st, const std::string& msg)
     return st;
 }
 
+void clear_error() { g_err.clear(); }
+
 adamw_status hip_fail(const char* what, hipError_t e)
 {
     g_err = std::string(what) + ": " + hipGetErrorString(e);

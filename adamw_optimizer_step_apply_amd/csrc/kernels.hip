@@ -861,7 +861,7 @@ __device__ __forceinline__ void copy_elems(uint64_t dst, uint64_t src, uint64_t 
     for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
 }
 
-__global__ __launch_bounds__(256) void state_copy_kernel(const DevCopySeg* __restrict__ segs,
+__global__ __launch_bounds__(kBlockCopy) void state_copy_kernel(const DevCopySeg* __restrict__ segs,
                                                          const DevChunk* __restrict__ chunks, int esz_m, int esz_v,
                                                          int esz_aux, int to_blocked)
 {
@@ -881,7 +881,7 @@ hipError_t launch_state_copy(const DevCopySeg* segs, const DevChunk* chunks, int
                              bool to_blocked, hipStream_t stream)
 {
     if (n_chunks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)n_chunks), dim3(256), 0, stream, segs, chunks, esz[0],
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)n_chunks), dim3(kBlockCopy), 0, stream, segs, chunks, esz[0],
                        esz[1], esz[2], to_blocked ? 1 : 0);
     return hipGetLastError();
 }

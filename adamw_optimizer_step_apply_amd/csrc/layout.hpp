@@ -100,6 +100,9 @@ constexpr int64_t kCheckChunkElems = (int64_t)kBlockCheck * kPack * kCheckChunkM
 constexpr int kMaxUpdateBlock = kBlockMixed > kBlockPure ? kBlockMixed : kBlockPure;
 constexpr int64_t kMaxUpdateChunks = (int64_t)UINT32_MAX / ((int64_t)kXcdParts * kMaxUpdateBlock);
 constexpr int64_t kMaxCheckChunks = (int64_t)UINT32_MAX / kBlockCheck;
+// The state copy (setup and checkpoint) runs one 256-lane workgroup per chunk.
+constexpr int kBlockCopy = 256;
+constexpr int64_t kMaxCopyChunks = (int64_t)UINT32_MAX / kBlockCopy;
 
 // Workgroup b of a grid of nb -> the chunk it processes.  The dispatcher hands
 // workgroup b to XCD b % 8 (the MI355X has 8 XCDs, each with its own L2); this

@@ -129,7 +129,7 @@ extern "C" adamw_status adamw_multi_tensor_step_noalloc(adamw_mode mode, adamw_d
                                                         const adamw_tensor_list* list, const adamw_hparams* hp,
                                                         int32_t* d_step, const int32_t* d_found_inf, void* hip_stream)
 {
-    fail(ADAMW_OK, "");
+    clear_error();
     StepKind kind;
     adamw_status st = mode_kind(mode, p_dtype, &kind);
     if (st != ADAMW_OK) return st;

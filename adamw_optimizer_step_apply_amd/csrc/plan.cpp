@@ -271,7 +271,7 @@ adamw_status build_copy_plan(const int esz_in[kStreams], const adamw_tensor_list
     }
     int esz[kStreams] = {0, 0, esz_in[2], esz_in[3], esz_in[4]};
     // the per-tensor side: pointers, alignment, shard range
-    adamw_status st = build_plan(esz, list, kStateBlockElems, INT64_MAX, nullptr, err);
+    adamw_status st = build_plan(esz, list, kStateBlockElems, kMaxCopyChunks, nullptr, err);
     if (st != ADAMW_OK) return st;
     // the blocked side: the pieces of the blocked plan and their addresses there
     void* const blocked_ptr[1] = {reinterpret_cast<void*>((uintptr_t)blocked)};
@@ -279,7 +279,7 @@ adamw_status build_copy_plan(const int esz_in[kStreams], const adamw_tensor_list
     bl.flat_mask |= ADAMW_BLOCKED_STATE;
     bl.ptr[ADAMW_STREAM_EXP_AVG] = blocked_ptr;
     Plan plan;
-    st = build_plan(esz, &bl, kStateBlockElems, INT64_MAX, &plan, err);
+    st = build_plan(esz, &bl, kStateBlockElems, kMaxCopyChunks, &plan, err);
     if (st != ADAMW_OK) return st;
     out->segs.resize(plan.segs.size());
     for (size_t i = 0; i < plan.segs.size(); ++i) {

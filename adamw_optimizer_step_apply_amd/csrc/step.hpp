@@ -17,6 +17,7 @@ namespace adamw {
 // The calling thread's last-error text (adamw_last_error) is set to `msg`
 // (or to `what` and the HIP error string); returns the status given.
 adamw_status fail(adamw_status st, const std::string& msg);
+void clear_error();
 adamw_status hip_fail(const char* what, hipError_t e);
 
 // What one step launches: the update kernel and its streams' element sizes.
