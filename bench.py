@@ -27,6 +27,8 @@ Usage:
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-probe] [--compare]
   python bench.py --workload ragged_10k                  (overflow check + fp16 step, 10k tensors)
   python bench.py --probe-only                            (memory ceilings only)
+  python bench.py --launch-study --steps 200              (the smaller workloads: eager calls in both
+                                                           launch forms against HIP-graph replays)
   python bench.py --build-probe                           (compile the ceiling probes; no GPU)
   python bench.py --calib-copy                            (plain 4 GiB copy, to scale rocprofv3 byte counters)
   python bench.py --traffic-from F.csv W.csv CF.csv CW.csv (rocprofv3 counters -> profiles/traffic_<workload>.json)
@@ -65,6 +67,9 @@ def parse():
                          "default run serves the headline layout only")
     ap.add_argument("--no-compare", action="store_true", help="the default (no per-tensor-state timing)")
     ap.add_argument("--probe-only", action="store_true")
+    ap.add_argument("--launch-study", action="store_true",
+                    help="per-step cost of the 1M tensor, the BERT rank-0 shard and OPT-125m as eager calls "
+                         "(single-launch and two-launch forms) and as HIP-graph replays")
     ap.add_argument("--build-probe", action="store_true", help="compile bench_probe.hip and exit (no GPU needed)")
     ap.add_argument("--cpu-sample", type=int, default=256_000_000,
                     help="elements of the list the oracle steps once per mode")
@@ -92,7 +97,6 @@ def calib_copy():
 
 
 CALIB_COPY_BYTES = 4 << 30
-# the kernel each timed mode launches, as rocprofv3 names it (a substring of the symbol)
 # the timed kernel of each mode, as a prefix of its name in rocprofv3 output (the
 # last template argument, the launch form, is left open)
 KERNEL_OF = {"mixed": "update_kernel<0,", "split": "update_pure_kernel<true, true, 2,",
@@ -314,6 +318,106 @@ def make_mode_state(mode, numels, device, seed, p_dtype="bf16", loss_scale=1.0):
     return arena, streams, flags
 
 
+# (workload, mode, ZeRO rank or None): the smaller parity workloads in their own modes
+LAUNCH_STUDY = (("single_1m", "mixed", None), ("bert_52m", "mixed", 0), ("opt_125m", "kahan", None),
+                ("opt_125m", "kahan-blocked", None), ("opt_125m", "mixed-blocked", None))
+
+
+def launch_study(K, dev):
+    """Steps of one to a hundred million parameters last microseconds to a few
+    hundred, so the host's cost per call and the prologue launch weigh.  For
+    each workload of LAUNCH_STUDY, the per-step time of K calls issued back to
+    back (the host's loop included, wall clock over all K) in the two-launch
+    form (prologue kernel + update kernel) and in the single-launch form (the
+    default for plans of at most 512 chunks, 4,096 workgroups; forced here at
+    every size), the GPU time of one call (HIP events around each call on its
+    stream), and the per-step time of HIP graphs holding 1 and 10 captured
+    steps in the default form, replayed back to back."""
+    import torch
+
+    import adamw_optimizer_step_apply_amd as A
+    import workloads
+    stream = torch.cuda.Stream(dev)             # capture needs a stream other than the legacy default
+    hp = A.HParams()
+    rows = []
+    for wname, mode, rank in LAUNCH_STUDY:
+        wl = workloads.get(wname)
+        numels = wl.numels
+        b, e = wl.shard(rank) if rank is not None else (0, wl.total)
+        with torch.cuda.stream(stream):
+            arena, streams, flags = make_mode_state(mode, numels, dev, seed=300)
+        torch.cuda.synchronize()
+        tl = A.TensorList(numels, streams, b, e if rank is not None else -1, flags)
+        base = mode[:-len("-blocked")] if mode.endswith("-blocked") else mode
+        code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN}[base]
+        ctr = torch.zeros(1, dtype=torch.int32, device=dev)
+        s = stream.cuda_stream
+
+        def call():
+            A.adamw_multi_tensor_step(code, A.BF16, tl, hp, ctr, None, s)
+
+        def eager():
+            call()                                       # plan cached before the timed loops
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(K):
+                call()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / K
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+            for a, c in ev:
+                a.record(stream)
+                call()
+                c.record(stream)
+            torch.cuda.synchronize()
+            gpu = sorted(a.elapsed_time(c) for a, c in ev)[K // 2] * 1e-3
+            return wall, gpu
+
+        def graphed(per_graph):
+            call()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(per_graph):
+                    call()
+            torch.cuda.synchronize()
+            reps = max(1, K // per_graph)
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / (reps * per_graph)
+            del g
+            return wall
+
+        chunks = len(A.adamw_plan_inspect(code, A.BF16, tl))
+        forms = {}
+        for form, knob in (("two_launch", 0), ("single_launch", 1 << 40)):
+            A.adamw_set_single_launch_max_workgroups(knob)
+            try:
+                forms[form] = eager()
+            finally:
+                A.adamw_set_single_launch_max_workgroups(-1)
+        g1, g10 = graphed(1), graphed(10)
+        n = e - b
+        nbytes = n * BYTES[base]
+
+        def rate(t):
+            return {"us": round(t * 1e6, 2), "gb_s": round(nbytes / t / 1e9, 1),
+                    "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        rows.append({"workload": wname + (f" rank {rank} of {wl.dp_size}" if rank is not None else ""),
+                     "mode": mode, "elements": n, "bytes_per_step": nbytes,
+                     "chunks": chunks,
+                     "default_form": "single_launch" if 8 * chunks <= 4096 else "two_launch",
+                     **{f: {"eager_wall": rate(w_), "gpu_per_call": rate(g_)} for f, (w_, g_) in forms.items()},
+                     "graph_1_step": rate(g1), "graph_10_steps": rate(g10)})
+        del arena, streams, tl
+        torch.cuda.empty_cache()
+    return {"study": "launch", "steps": K, "rows": rows, "device": torch.cuda.get_device_name(dev)}
+
+
 def cpu_baseline(numels, sample, modes):
     """The oracle as it is, one step per mode over the first `sample` elements
     of the list, scaled to param-updates/s of the bench step: on one host
@@ -453,6 +557,9 @@ def main():
     stream = torch.cuda.current_stream()
     if args.probe_only:
         print(json.dumps({"probes_gb_s": probes(N, stream), "n": N}), flush=True)
+        return
+    if args.launch_study:
+        print(json.dumps(launch_study(args.steps, dev)), flush=True)
         return
     modes = default_modes(args).split(",")
     # with --compare, the same steps on per-tensor state buffers, timed after the headline region
