@@ -568,6 +568,7 @@ void adamw_release_workspace(void)
         ws->plans.clear();
     }
     g_ws.clear();
+    release_noalloc_tables();
 }
 
 int adamw_abi_version(void) { return ADAMW_ABI_VERSION; }

@@ -41,6 +41,7 @@ struct DeviceScratch {
     std::mutex mu;                     // one call at a time per device
     unsigned char* ptr = nullptr;      // this device's `scratch` (hipGetSymbolAddress)
     std::vector<int64_t> key;          // the plan whose table the array holds (empty: none)
+    bool pinned = false;               // a graph captured a step with that table
     int64_t n_segs = 0, n_chunks = 0;
     std::vector<unsigned char> table;  // host image of that table
 };
@@ -75,20 +76,30 @@ adamw_status init_device(DeviceScratch& ds, hipStream_t stream)
 }
 
 // Makes the array hold the plan of (kind, list): the table is planned on the
-// host and copied in on `stream`, unless the array already holds it.
+// host and copied in on `stream`, unless the array already holds it.  A call
+// under capture pins the table it uses: the graph reads it at every replay, so
+// from then on a call with another list is refused instead of rewriting it,
+// until adamw_release_workspace.
 adamw_status ensure_table(DeviceScratch& ds, const StepKind& kind, const adamw_tensor_list* list, hipStream_t stream)
 {
     const int64_t chunk_elems = chunk_elems_of(kind.kernel);
     std::vector<int64_t> key;
     plan_key(kind.kernel, kind.esz, list, chunk_elems, key);
-    if (!ds.key.empty() && key == ds.key) return ADAMW_OK;
     bool cap = false;
     adamw_status st = capturing(stream, &cap);
     if (st != ADAMW_OK) return st;
+    if (!ds.key.empty() && key == ds.key) {
+        if (cap) ds.pinned = true;
+        return ADAMW_OK;
+    }
     if (cap)
         return fail(ADAMW_E_INVALID,
                     "the allocation-free workspace holds another list's table: make this call once outside "
                     "graph capture first");
+    if (ds.pinned)
+        return fail(ADAMW_E_INVALID,
+                    "the allocation-free workspace holds the table of a step captured into a graph, which "
+                    "replays read: it serves only that list until adamw_release_workspace()");
     Plan plan;
     std::string err;
     st = build_plan(kind.esz, list, chunk_elems, kMaxUpdateChunks, &plan, err);
@@ -121,6 +132,19 @@ adamw_status ensure_table(DeviceScratch& ds, const StepKind& kind, const adamw_t
 }
 
 }  // namespace
+
+// Called by adamw_release_workspace: forgets every device's table and its pin
+// (the array itself stays; the next call uploads its list's table again).
+void release_noalloc_tables()
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto& kv : g_dev) {
+        std::lock_guard<std::mutex> lk2(kv.second->mu);
+        kv.second->key.clear();
+        kv.second->pinned = false;
+    }
+}
+
 }  // namespace adamw
 
 using namespace adamw;

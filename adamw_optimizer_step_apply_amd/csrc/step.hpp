@@ -50,6 +50,10 @@ adamw_status enqueue_step(const StepKind& kind, const DevSeg* segs, const DevChu
 adamw_status stream_device(hipStream_t stream, int* dev);
 adamw_status capturing(hipStream_t stream, bool* out);
 
+// Forgets the allocation-free entry point's table on every device, and its pin
+// (noalloc.hip; part of adamw_release_workspace).
+void release_noalloc_tables();
+
 // Makes `dev` the current device for the lifetime of the guard (allocations
 // and launches of a call then land on its stream's device).
 class DeviceGuard {

@@ -250,7 +250,11 @@ adamw_status adamw_multi_tensor_step(adamw_mode mode, adamw_dtype p_dtype, const
  * ADAMW_E_INVALID before anything is enqueued.  A call copies the list's table
  * into the array (a host-to-device copy on hip_stream) unless the last call on
  * this GPU used the same list; under graph capture that copy is refused, as in
- * adamw_multi_tensor_step.  Every call on a GPU shares that GPU's array and
+ * adamw_multi_tensor_step.  A call captured into a graph pins the table it
+ * used, since every replay reads it: later calls on that GPU with another list
+ * are then refused with ADAMW_E_INVALID (calls with the same list still run)
+ * until adamw_release_workspace(), which unpins it and must not run while
+ * such a graph may still be replayed.  Every call on a GPU shares that GPU's array and
  * its contents: calls on one GPU that may overlap (on different streams, or
  * from host threads without an order between them) race on it and must be
  * ordered by the caller, e.g. by issuing them on one stream. */
@@ -333,8 +337,10 @@ adamw_status adamw_check_finite(adamw_dtype g_dtype, const adamw_tensor_list* gr
  * until the next call into the library on that thread. */
 const char* adamw_last_error(void);
 
-/* Frees every workspace the library holds (all devices and streams).  The
- * caller must make sure no enqueued step is still running and that no other
+/* Frees every workspace the library holds (all devices and streams) and
+ * releases the allocation-free entry point's table on every GPU (its static
+ * array stays).  The caller must make sure no enqueued step is still running,
+ * no graph holding a captured step will be replayed again, and no other
  * thread is inside a library call. */
 void adamw_release_workspace(void);
 

@@ -126,3 +126,53 @@ def test_noalloc_on_a_side_stream_and_blocked_state():
     assert same_bits(tl["a"][1], tl["b"][1])
     assert same_bits(a.arena.bufs["p"], b.arena.bufs["p"])
     free()
+
+
+def test_noalloc_table_pinned_by_a_captured_graph():
+    """A step captured into a HIP graph through the allocation-free entry point
+    pins the table that its replays read: a later call with another list is
+    refused with nothing enqueued, calls with the same list still run, and every
+    replay matches the allocating entry point's eager step bit for bit (and the
+    oracle).  adamw_release_workspace releases the pin: the other list runs
+    afterwards."""
+    hg, ho = hp_pair()
+    g_case, e_case = _pair("mixed", LARGE, 7400)
+    other_a, other_b = _pair("mixed", SMALL, 7401)
+    tl_g, tl_e = g_case.tensor_list(), e_case.tensor_list()
+    s = torch.cuda.Stream()
+
+    def eager_pair(noalloc=True):
+        if noalloc:
+            A.adamw_multi_tensor_step_noalloc(A.MIXED, A.BF16, tl_g, hg, g_case.d_step, None, s)
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl_e, hg, e_case.d_step, None, s)
+        s.synchronize()
+        g_case.oracle_step(ho)
+        _same(g_case, e_case, "eager")
+
+    eager_pair()                         # the table goes in outside capture
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        A.adamw_multi_tensor_step_noalloc(A.MIXED, A.BF16, tl_g, hg, g_case.d_step, None, s)
+    torch.cuda.synchronize()
+    before = {k: other_a.arena.bufs[k].clone() for k in other_a.keys}
+    with pytest.raises(A.AdamWError, match="captured into a graph"):
+        A.adamw_multi_tensor_step_noalloc(A.MIXED, A.BF16, other_a.tensor_list(), hg, other_a.d_step, None, s)
+    torch.cuda.synchronize()
+    assert int(other_a.d_step.item()) == 0
+    for k, v in before.items():
+        assert same_bits(other_a.arena.bufs[k], v), k
+    for r in range(3):
+        with torch.cuda.stream(s):
+            graph.replay()
+        eager_pair(noalloc=False)
+        assert int(g_case.d_step.item()) == r + 2
+    eager_pair()                         # the same list, eagerly, while pinned
+    g_case.compare_all("noalloc-graph")
+    del graph
+    torch.cuda.synchronize()
+    A.adamw_release_workspace()
+    _both("mixed", other_a, other_b, hg)
+    other_a.oracle_step(ho)
+    _same(other_a, other_b, "after the release")
+    other_a.compare_all("noalloc-after-release")
+    free()
