@@ -678,6 +678,11 @@ adamw_status adamw_blocked_state_copy(adamw_mode mode, adamw_dtype p_dtype, cons
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     int dev = 0;
     if ((st = stream_device(stream, &dev)) != ADAMW_OK) return st;
+    bool cap = false;
+    if ((st = capturing(stream, &cap)) != ADAMW_OK) return st;
+    if (cap)
+        return fail(ADAMW_E_INVALID,
+                    "adamw_blocked_state_copy allocates and waits for the copy: it cannot be captured into a graph");
     DeviceGuard dg(dev);
     const size_t seg_bytes = cp.segs.size() * sizeof(DevCopySeg);
     const size_t bytes = seg_bytes + cp.chunks.size() * sizeof(DevChunk);

@@ -373,7 +373,8 @@ int adamw_abi_version(void);
  * tensors) is neither read nor written.  The copy runs on hip_stream, after
  * the work already queued there, and the call returns once it is done (it
  * allocates and frees a small device table: a setup and checkpoint routine,
- * not for the training loop). */
+ * not for the training loop; on a stream under graph capture it is refused
+ * with ADAMW_E_INVALID). */
 int64_t adamw_blocked_state_bytes(adamw_mode mode, adamw_dtype p_dtype, const adamw_pure_precision* prec,
                                   const adamw_tensor_list* list);
 adamw_status adamw_blocked_state_copy(adamw_mode mode, adamw_dtype p_dtype, const adamw_pure_precision* prec,

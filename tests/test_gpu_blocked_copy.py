@@ -179,3 +179,26 @@ def test_invalid_copy_is_refused_before_any_work():
         A.adamw_blocked_state_copy(A.MIXED, A.BF16, bad, blocked, True)
     assert bool((blocked == 0).all())
     free()
+
+
+def test_copy_under_graph_capture_is_refused():
+    """The copy allocates its table and waits for itself: on a stream under
+    capture it is refused before anything is recorded, and the capture goes on
+    (the graph holds the other work and replays it)."""
+    case = Case("mixed", [100, 7], seed=8600)
+    tl = _state_list(case)
+    blocked = torch.zeros(A.adamw_blocked_state_bytes(A.MIXED, A.BF16, tl), dtype=torch.uint8, device="cuda")
+    x = torch.zeros(4, device="cuda")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        x.add_(1.0)
+        with pytest.raises(A.AdamWError, match="cannot be captured"):
+            A.adamw_blocked_state_copy(A.MIXED, A.BF16, tl, blocked, True, stream=s)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    assert float(x[0]) == 2.0
+    assert bool((blocked == 0).all())
+    del g
+    free()
