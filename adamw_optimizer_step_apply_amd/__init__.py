@@ -180,15 +180,18 @@ def _hp(hp) -> adamw_hparams:
 
 class TensorList:
     """Marshals a tensor list into an ``adamw_tensor_list`` and keeps the ctypes
-    arrays alive.  ``streams`` is a sequence of 5 sequences (param, grad,
-    exp_avg, exp_avg_sq, aux) of tensors or addresses; a stream flagged in
-    ``flat_mask`` holds one flat shard buffer; ``None`` leaves a stream unset."""
+    arrays, and every tensor given, alive as long as it lives (addresses given
+    as integers are the caller's to keep valid).  ``streams`` is a sequence of
+    5 sequences (param, grad, exp_avg, exp_avg_sq, aux) of tensors or
+    addresses; a stream flagged in ``flat_mask`` holds one flat shard buffer;
+    ``None`` leaves a stream unset."""
 
     def __init__(self, numels: Sequence[int], streams, shard_begin: int = 0, shard_end: int = -1,
                  flat_mask: int = 0):
         n = len(numels)
         self._numel = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in numels])
         self._arrays = []
+        self._tensors = [x for items in streams if items is not None for x in items if isinstance(x, torch.Tensor)]
         s = adamw_tensor_list()
         s.n_tensors = n
         s.numel = ctypes.cast(self._numel, ctypes.POINTER(ctypes.c_int64))
