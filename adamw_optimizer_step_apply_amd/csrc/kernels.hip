@@ -462,19 +462,10 @@ __device__ __forceinline__ void end_step(const FusedStep& fs, int64_t t, float s
     }
 }
 
-#ifndef ADAMW_WPE
-#define ADAMW_WPE 0
-#endif
-#if ADAMW_WPE
-#define ADAMW_WPE_ATTR __attribute__((amdgpu_waves_per_eu(1, ADAMW_WPE)))
-#else
-#define ADAMW_WPE_ATTR
-#endif
-
 // MODE 0: mixed bf16, 1: mixed fp16 (the split-master step is a pure-family
 // kernel below: its param is read as well as written)
 template <int MODE, bool FUSED>
-__global__ __launch_bounds__(kBlockMixed) ADAMW_WPE_ATTR void update_kernel(const DevSeg* __restrict__ segs,
+__global__ __launch_bounds__(kBlockMixed) void update_kernel(const DevSeg* __restrict__ segs,
                                                         const DevChunk* __restrict__ chunks,
                                                         const LaunchScalars* __restrict__ sc, FusedStep fs)
 {
@@ -553,7 +544,7 @@ constexpr int kAuxSplit = 2;   // int16 remainder r of the split fp32 master w =
 // else bf16; aux none or Kahan; <false, false, kAuxKahan> is the pure-bf16 Kahan
 // mode), and the split-master mixed step (<true, true, kAuxSplit>).
 template <bool M32, bool V32, int AUX, bool FUSED>
-__global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(const DevSeg* __restrict__ segs,
+__global__ __launch_bounds__(kBlockPure) void update_pure_kernel(const DevSeg* __restrict__ segs,
                                                                             const DevChunk* __restrict__ chunks,
                                                                             const LaunchScalars* __restrict__ sc,
                                                                             FusedStep fs)
@@ -564,12 +555,11 @@ __global__ __launch_bounds__(kBlockPure) ADAMW_WPE_ATTR void update_pure_kernel(
     if (!begin_step<FUSED>(sc, fs, c, t, scale)) return;
     constexpr bool KAHAN = AUX == kAuxKahan, SPLIT = AUX == kAuxSplit;
     static_assert(!SPLIT || (M32 && V32), "the split master keeps fp32 moments");
-#ifndef ADAMW_PURE_WIDE_RULE
-#define ADAMW_PURE_WIDE_RULE 0
-#endif
-    constexpr bool WIDE = ADAMW_PURE_WIDE_RULE == 0 ? (M32 && V32 && AUX != kAuxNone) : (M32 || V32);
+    // fp32 moments and an aux stream: the widest pure-family mix
+    constexpr bool WIDE = M32 && V32 && AUX != kAuxNone;
     constexpr int NT = SPLIT ? ADAMW_NT_SPLIT : WIDE ? ADAMW_NT_PURE_WIDE : ADAMW_NT_PURE;
-    constexpr int P = SPLIT ? kTilePacksSplit : WIDE ? kTilePacksPureWide : kTilePacks;   // tiles of 512 elements
+    // tiles of 256 elements (split master) or 512 (the rest)
+    constexpr int P = SPLIT ? kTilePacksSplit : WIDE ? kTilePacksPureWide : kTilePacks;
     constexpr uint32_t kStride = kXcdParts * kBlockPure;
     const uint32_t part = blockIdx.x % kXcdParts;
     const DevChunk ch = chunks[blockIdx.x / kXcdParts];

@@ -46,12 +46,14 @@ constexpr int64_t kElemChunkElems = 4096;       // element chunk
 // list, against giving each XCD one contiguous run of 2048-element chunks)
 // this streamed the mixed step 7 % faster on blocked state (16384-element
 // blocks) and 4-6.5 % per tensor, and the Kahan step 1 % faster blocked and
-// 5-9 % per tensor; only the split-master step on blocked state lost (4 %).  Tile sizes, from interleaved A/B runs: 256 elements (1 KiB of the
-// fp32 master) for the mixed step, whose param stream is written only; 512
-// elements (1 KiB of a 16-bit param) for every step that reads and writes the
-// param (split master, the pure-bf16 family), 1-2 % ahead of 256 there.
-// Smaller and larger tiles (64-128, 512-1024 elements for the mixed step;
-// 256 and 1024-2048 for Kahan) were slower.
+// 5-9 % per tensor; only the split-master step on blocked state lost (4 %),
+// before its master split became branch-free.  Tile sizes, from interleaved
+// A/B runs: 256 elements (1 KiB of an fp32 stream) for the mixed step, whose
+// param stream is written only, and for the split-master step (ahead of 512
+// by 0.7 points of peak on blocked state, 2.2 per tensor); 512 elements
+// (1 KiB of a 16-bit param) for the pure-bf16 family, 1-2 % ahead of 256
+// there.  Smaller and larger tiles (64-128, 512-1024 elements for the mixed
+// step; 256 and 1024-2048 for Kahan) were slower.
 constexpr int kXcdParts = 8;
 #ifndef ADAMW_TILE_PACKS_MIXED
 #define ADAMW_TILE_PACKS_MIXED 32
