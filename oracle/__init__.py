@@ -79,7 +79,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "oracle_split_join_n": (None, [_U16P, _U16P, _U32P, _I64]),
         "oracle_inv_scale": (_F, [_F]),
         "oracle_adamw_pure": (None, [_I64, _U16P, _U16P, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
-                                     ctypes.c_int, ctypes.c_void_p, _F, _F, _F, _F, _F, _F, _I64]),
+                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_int, _F, _F, _F, _F, _F, _F, _I64]),
         "oracle_update_loss_scale": (None, [ctypes.POINTER(_F), ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
                                             _F, _F, ctypes.c_int32]),
     }
@@ -253,20 +253,18 @@ def adamw_mixed_split(p, g, r, m, v, hp: HParams, t: int, lib=None):
 
 def adamw_pure(p, g, m, v, c, hp: HParams, t: int, lib=None):
     """Pure bf16 step with chosen state precisions: m and v are float32 (fp32
-    state) or uint16 (bf16 bits) arrays; c is the bf16 compensation buffer or None
-    (no Kahan summation)."""
+    state) or uint16 (bf16 bits) arrays; c is the compensation buffer, float32
+    (fp32) or uint16 (bf16 bits), or None (no Kahan summation)."""
     lib = lib or load()
     n = p.size
     for a in (p, g):
         assert a.dtype == np.uint16 and a.flags.c_contiguous and a.size == n
-    for a in (m, v):
+    for a in (m, v) + (() if c is None else (c,)):
         assert a.dtype in (np.float32, np.uint16) and a.flags.c_contiguous and a.size == n
-    if c is not None:
-        assert c.dtype == np.uint16 and c.flags.c_contiguous and c.size == n
     lr, b1, b2, eps, wd, s = hp.f32()
     lib.oracle_adamw_pure(n, p.reshape(-1), g.reshape(-1), m.ctypes.data, int(m.dtype == np.float32),
                           v.ctypes.data, int(v.dtype == np.float32), None if c is None else c.ctypes.data,
-                          lr, b1, b2, eps, wd, s, int(t))
+                          int(c is not None and c.dtype == np.float32), lr, b1, b2, eps, wd, s, int(t))
 
 
 def any_nonfinite(g16, is_f16: bool, lib=None) -> bool:

@@ -323,13 +323,15 @@ void oracle_split_join_n(const uint16_t* p, const uint16_t* r, uint32_t* w, int6
 
 /* Pure bf16 parameters with separately chosen state precisions (the
  * AnyPrecisionAdamW knobs of "[pure bf16 training] w/ AnyPrecisionAdamW and
- * Kahan summation": momentum_dtype, variance_dtype, use_kahan_summation with a
- * bf16 compensation buffer).  m_f32 / v_f32 select fp32 moments (float arrays)
+ * Kahan summation": momentum_dtype, variance_dtype, use_kahan_summation and
+ * compensation_buffer_dtype).  m_f32 / v_f32 select fp32 moments (float arrays)
  * instead of bf16 ones (uint16 bit arrays); c == NULL means no compensation:
  * then p' = round_bf16(p * (1 - lr*wd) - step_size * u).  With c, the Kahan rule
- * of oracle_adamw_kahan. */
+ * of oracle_adamw_kahan, the compensation held in bf16 (uint16 bits) or, with
+ * c_f32, in fp32 (a float array): the same sum, with the residual kept as the
+ * fp32 value it is computed in instead of rounded to bf16. */
 void oracle_adamw_pure(int64_t n, uint16_t* p, const uint16_t* g, void* m, int m_f32, void* v, int v_f32,
-                       uint16_t* c, float lr, float beta1, float beta2, float eps, float wd,
+                       void* c, int c_f32, float lr, float beta1, float beta2, float eps, float wd,
                        float inv_scale, int64_t t)
 {
     float s[6];
@@ -339,6 +341,8 @@ void oracle_adamw_pure(int64_t n, uint16_t* p, const uint16_t* g, void* m, int m
     float* vf = (float*)v;
     uint16_t* mh = (uint16_t*)m;
     uint16_t* vh = (uint16_t*)v;
+    float* cf = (float*)c;
+    uint16_t* ch = (uint16_t*)c;
     for (int64_t i = 0; i < n; ++i) {
         float gi = oracle_bf16_to_f32(g[i]) * inv_scale;
         float mi = m_f32 ? mf[i] : oracle_bf16_to_f32(mh[i]);
@@ -347,9 +351,10 @@ void oracle_adamw_pure(int64_t n, uint16_t* p, const uint16_t* g, void* m, int m
         float pf = oracle_bf16_to_f32(p[i]);
         if (c) {
             float d = -(lrwd * pf) - step_size * u;
-            float sum = oracle_bf16_to_f32(c[i]) + d;
+            float sum = (c_f32 ? cf[i] : oracle_bf16_to_f32(ch[i])) + d;
             uint16_t pn = oracle_f32_to_bf16(pf + sum);
-            c[i] = oracle_f32_to_bf16(sum - (oracle_bf16_to_f32(pn) - pf));
+            float rest = sum - (oracle_bf16_to_f32(pn) - pf);
+            if (c_f32) cf[i] = rest; else ch[i] = oracle_f32_to_bf16(rest);
             p[i] = pn;
         } else {
             p[i] = oracle_f32_to_bf16(pf * decay - step_size * u);

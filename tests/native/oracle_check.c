@@ -46,7 +46,7 @@ void oracle_adamw_mixed_split(int64_t n, uint16_t* p, const uint16_t* g16, uint1
 void oracle_split_make_n(const uint32_t* w, uint16_t* p, uint16_t* r, int64_t n);
 void oracle_split_join_n(const uint16_t* p, const uint16_t* r, uint32_t* w, int64_t n);
 void oracle_adamw_pure(int64_t n, uint16_t* p, const uint16_t* g, void* m, int m_f32, void* v, int v_f32,
-                       uint16_t* c, float lr, float beta1, float beta2, float eps, float wd, float inv_scale,
+                       void* c, int c_f32, float lr, float beta1, float beta2, float eps, float wd, float inv_scale,
                        int64_t t);
 
 static uint64_t g_rng = 0x243f6a8885a308d3ull, g_sum = 1469598103934665603ull;
@@ -198,13 +198,18 @@ static void run_length(int64_t n)
             fill_16(p, n, 0, 0);
             fill_16(c, n, 0, 0);
             fill_f32(m32, n, 1);
+            float* c32 = arr(n, 4);
+            for (int64_t i = 0; i < n; ++i) c32[i] = (float)((int64_t)(next() % 2001) - 1000) * 1e-9f;
             for (int mf = 0; mf < 2; ++mf)
                 for (int vf = 0; vf < 2; ++vf)
-                    for (int k = 0; k < 2; ++k) {
+                    for (int k = 0; k < 3; ++k) {   /* no compensation, bf16, fp32 */
                         oracle_adamw_pure(n, p, g, mf ? (void*)m32 : (void*)m, mf, vf ? (void*)v32 : (void*)v, vf,
-                                          k ? c : NULL, 2e-4f, 0.9f, 0.95f, 1e-8f, 0.1f, 1.0f, t);
+                                          k == 0 ? NULL : k == 1 ? (void*)c : (void*)c32, k == 2, 2e-4f, 0.9f,
+                                          0.95f, 1e-8f, 0.1f, 1.0f, t);
                         mix_h(p, n, 0);
                     }
+            mix_f32(c32, n);
+            free(c32);
             uint32_t* w = arr(n, 4);
             for (int64_t i = 0; i < n; ++i) w[i] = rand_f32_bits();
             oracle_split_make_n(w, p, c, n);

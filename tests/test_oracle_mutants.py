@@ -48,6 +48,13 @@ MUTANTS = [
     ("growth without finiteness test", "if (isfinite(grown)) *scale = grown;", "*scale = grown;"),
     ("inverse scale in float", "return (float)(1.0 / (double)scale);", "return 1.0f / (scale * 1.0000001f);"),
     ("split decay dropped", "w = w * decay - step_size * u;\n        oracle_split_make", "w = w - step_size * u;\n        oracle_split_make"),
+    ("pure fp32 residual rounded to bf16", "if (c_f32) cf[i] = rest;",
+     "if (c_f32) cf[i] = oracle_bf16_to_f32(oracle_f32_to_bf16(rest));"),
+    ("pure fp32 compensation never read", "float sum = (c_f32 ? cf[i] : oracle_bf16_to_f32(ch[i])) + d;",
+     "float sum = (c_f32 ? 0.0f : oracle_bf16_to_f32(ch[i])) + d;"),
+    ("pure residual sign", "float rest = sum - (oracle_bf16_to_f32(pn) - pf);",
+     "float rest = sum + (oracle_bf16_to_f32(pn) - pf);"),
+    ("pure fp32 moment kept from before", "if (m_f32) mf[i] = mi;", "if (m_f32) mf[i] = mf[i];"),
 ]
 
 # fastest first; each entry is (pin, extra args)
@@ -75,6 +82,13 @@ AMP_PINS = [
     (pins.test_inv_scale, ()),
     (pins.test_amp_step_skips_and_backs_off, ()),
 ]
+PURE_PINS = [
+    (pins.test_pure_bf16_state_reduces_to_kahan_and_naive, ()),
+    (pins.test_pure_fp32_moments_follow_the_mixed_moments, (True, True)),
+    (pins.test_pure_fp32_compensation_tracks_tiny_updates_closely, ()),
+    (pins.test_pure_fp32_compensation_follows_the_mixed_master, ()),
+    (pins.test_compensation_dtype_changes_only_the_residual, (False, False)),
+]
 SPLIT_PINS = [
     (pins.test_split_step_equals_mixed_step, (pins.HParams(),)),
     (pins.test_split_join_roundtrip, ()),
@@ -101,7 +115,11 @@ def test_mutant_is_killed(tmpdir_mut, name, orig, bad):
     lib = _bind(ctypes.CDLL(so))
     amp = any(w in name for w in ("growth", "backoff", "inverse scale"))
     split = name.startswith("split") or "remainder" in name
-    order = AMP_PINS + PINS + SPLIT_PINS if amp else SPLIT_PINS + PINS + AMP_PINS if split else PINS + SPLIT_PINS + AMP_PINS
+    if name.startswith("pure"):
+        order = PURE_PINS
+    else:
+        order = AMP_PINS + PINS + SPLIT_PINS if amp else SPLIT_PINS + PINS + AMP_PINS if split else \
+            PINS + SPLIT_PINS + AMP_PINS
     for pin, args in order:
         try:
             pin(lib, *args)

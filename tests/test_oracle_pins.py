@@ -779,3 +779,82 @@ def test_pure_fp32_moments_kahan_tracks_tiny_updates(olib):
         oracle.adamw_pure(pn, g, mn, vn, None, hp, t, lib=olib)
     got = bf16_val(p).astype(np.float64) + bf16_val(c)
     assert np.all(np.abs(got - 2.0) <= 0.1) and np.all(bf16_val(pn) == 1.0)
+
+
+def test_pure_fp32_compensation_tracks_tiny_updates_closely(olib):
+    """An fp32 compensation buffer (compensation_buffer_dtype=float32): 10,000
+    constant +1e-4 updates from 1.0 bring p + c within 1e-5 of the fp64 sum 2.0
+    (a bf16 buffer only gets within 5 %: it rounds each residual to 8 bits), and p
+    itself reaches the bf16 nearest to 2.0."""
+    n, k = 64, 10_000
+    hp = HParams(lr=1e-4, weight_decay=0.0, eps=0.0)
+    p = bf16_bits(np.ones(n))
+    m, v, c = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    pb, mb, vb, cb = p.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    g = bf16_bits(-np.ones(n))
+    for t in range(1, k + 1):
+        oracle.adamw_pure(p, g, m, v, c, hp, t, lib=olib)
+        oracle.adamw_pure(pb, g, mb, vb, cb, hp, t, lib=olib)
+    got = bf16_val(p).astype(np.float64) + c
+    got_b = bf16_val(pb).astype(np.float64) + bf16_val(cb)
+    assert np.all(np.abs(got - 2.0) <= 1e-5), np.abs(got - 2.0).max()
+    assert np.all(bf16_val(p) == 2.0)
+    assert np.all(np.abs(got_b - 2.0) > 1e-3)      # the bf16 buffer is measurably coarser
+
+
+def test_pure_fp32_compensation_follows_the_mixed_master(olib):
+    """bf16 p plus an fp32 compensation c carry an fp32 master: after 10 steps
+    from w = p (c = 0), p + c stays within the bound that the two rules' one
+    difference allows of the mixed step's fp32 master w.  Per step that
+    difference is the decay of c, which the Kahan reading leaves undecayed
+    (|lr*wd*c| with |c| at most half a bf16 ulp of p, <= 2^-8 |p|), plus a few
+    fp32 roundings; the fp32 moments are the mixed ones exactly.  A bf16
+    compensation buffer lands outside the same bound on many elements."""
+    rng = np.random.default_rng(43)
+    n, steps = 30_000, 10
+    hp = HParams()
+    p = bf16_bits(rng.standard_normal(n) * 0.02)
+    w = bf16_val(p).copy()
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    c = np.zeros(n, np.float32)
+    pb, mb, vb, cb = p.copy(), m.copy(), v.copy(), np.zeros(n, np.uint16)
+    mm, vm, p16 = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    for t in range(1, steps + 1):
+        g = bf16_bits(rng.standard_normal(n) * 1e-3)
+        oracle.adamw_pure(p, g, m, v, c, hp, t, lib=olib)
+        oracle.adamw_pure(pb, g, mb, vb, cb, hp, t, lib=olib)
+        oracle.adamw_mixed(p16, g, w, mm, vm, hp, t, lib=olib)
+    assert np.array_equal(m, mm) and np.array_equal(v, vm)
+    aw = np.abs(w).astype(np.float64)
+    ulp = np.spacing(np.float32(1.0)) * np.maximum(aw, hp.lr)        # an fp32 ulp of w (or of one step)
+    bound = steps * (hp.lr * hp.weight_decay * 2.0 ** -8 * aw + 4 * ulp)
+    err = np.abs(bf16_val(p).astype(np.float64) + c - w)
+    assert np.all(err <= bound), (err / bound).max()
+    err_b = np.abs(bf16_val(pb).astype(np.float64) + bf16_val(cb) - w)
+    assert (err_b > bound).mean() > 1 / 3          # the bound is not vacuous
+
+
+@pytest.mark.parametrize("m32,v32", [(True, True), (False, False), (True, False)])
+def test_compensation_dtype_changes_only_the_residual(olib, m32, v32):
+    """The compensation buffer's dtype touches nothing but the residual: over 6
+    steps the moments are bit-identical with an fp32 buffer, a bf16 buffer and
+    none (the moment update reads neither p nor c), and after the first step
+    from c = 0 both buffers give the same param while the bf16 residual is the
+    fp32 residual rounded to nearest even."""
+    rng = np.random.default_rng(44)
+    n = 20_000
+    p0 = bf16_bits(rng.standard_normal(n) * 0.02)
+    runs = {}
+    for name, c in (("f32", np.zeros(n, np.float32)), ("bf16", np.zeros(n, np.uint16)), ("none", None)):
+        runs[name] = [p0.copy(), np.zeros(n, np.float32) if m32 else np.zeros(n, np.uint16),
+                      np.zeros(n, np.float32) if v32 else np.zeros(n, np.uint16), c]
+    for t in range(1, 7):
+        g = bf16_bits(rng.standard_normal(n) * 1e-3)
+        for r in runs.values():
+            oracle.adamw_pure(r[0], g, r[1], r[2], r[3], HParams(), t, lib=olib)
+        if t == 1:
+            assert np.array_equal(runs["f32"][0], runs["bf16"][0])
+            assert np.array_equal(runs["bf16"][3], bf16_bits(runs["f32"][3]))
+            assert np.any(runs["f32"][3] != bf16_val(runs["bf16"][3]))
+    for k in (1, 2):
+        assert np.array_equal(runs["f32"][k], runs["bf16"][k]) and np.array_equal(runs["f32"][k], runs["none"][k])
