@@ -31,6 +31,7 @@ _lib = None
 OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_HIP = 0, 1, 2, 3, 4
 F32, BF16, F16 = 0, 1, 2
 MIXED, PURE_KAHAN, MIXED_SPLIT = 0, 1, 2
+KAHAN_NONE, KAHAN_BF16, KAHAN_F32 = 0, 1, 2   # compensation buffer of a pure-bf16 step (PurePrecision.kahan)
 STREAM_PARAM, STREAM_GRAD, STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_AUX = range(5)
 BLOCKED_STATE = 1 << 8        # flat_mask bit: exp_avg / exp_avg_sq / aux in one blocked buffer
 FLAT_PAD8 = 1 << 9            # flat_mask bit: every tensor starts at a multiple of 8 in the flat index
@@ -269,13 +270,14 @@ def adamw_multi_tensor_step_amp(mode: int, p_dtype: int, tensors: TensorList, hp
 @dataclass
 class PurePrecision:
     """State precisions of a pure-bf16 step: exp_avg / exp_avg_sq dtype (F32 or
-    BF16) and whether the aux stream is a bf16 Kahan compensation buffer."""
+    BF16) and the aux stream's compensation buffer: KAHAN_NONE (False),
+    KAHAN_BF16 (True) or KAHAN_F32."""
     exp_avg: int = BF16
     exp_avg_sq: int = BF16
-    kahan: bool = True
+    kahan: int = KAHAN_BF16
 
     def c(self) -> adamw_pure_precision:
-        return adamw_pure_precision(int(self.exp_avg), int(self.exp_avg_sq), int(bool(self.kahan)))
+        return adamw_pure_precision(int(self.exp_avg), int(self.exp_avg_sq), int(self.kahan))
 
 
 def adamw_pure_multi_tensor_step(prec: PurePrecision, tensors: TensorList, hp, d_step, d_found_inf=None,

@@ -358,14 +358,15 @@ adamw_status do_step(const StepKind& kind, const adamw_tensor_list* list, const 
 
 StepKind kind_of_pure(const adamw_pure_precision& prec)
 {
-    const int m32 = prec.exp_avg == ADAMW_F32, v32 = prec.exp_avg_sq == ADAMW_F32, kahan = prec.kahan != 0;
+    const int m32 = prec.exp_avg == ADAMW_F32, v32 = prec.exp_avg_sq == ADAMW_F32;
+    const int kahan = prec.kahan != ADAMW_KAHAN_NONE, c32 = prec.kahan == ADAMW_KAHAN_F32;
     StepKind kind{};
-    kind.kernel = kKernelPure + 4 * m32 + 2 * v32 + kahan;
+    kind.kernel = c32 ? kKernelPureC32 + 2 * m32 + v32 : kKernelPure + 4 * m32 + 2 * v32 + kahan;
     kind.esz[ADAMW_STREAM_PARAM] = 2;
     kind.esz[ADAMW_STREAM_GRAD] = 2;
     kind.esz[ADAMW_STREAM_EXP_AVG] = m32 ? 4 : 2;
     kind.esz[ADAMW_STREAM_EXP_AVG_SQ] = v32 ? 4 : 2;
-    kind.esz[ADAMW_STREAM_AUX] = kahan ? 2 : 0;
+    kind.esz[ADAMW_STREAM_AUX] = c32 ? 4 : kahan ? 2 : 0;
     return kind;
 }
 

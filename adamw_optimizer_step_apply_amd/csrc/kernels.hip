@@ -288,10 +288,13 @@ __global__ void prologue_kernel(adamw_hparams hp, int32_t* __restrict__ step, co
 #define ADAMW_NT_MIXED_GRAD 1
 #endif
 // The pure family (every stream alike, the gradient included): non-temporal loads
-// and stores while all state is bf16; with fp32 moments (26 B per element: the
-// split master, and fp32 exp_avg + exp_avg_sq with compensation) non-temporal
-// stores only, measured 5-6 % faster there on MI355X (OPT-1.3B list, blocked
-// state), while the bf16 Kahan step loses 8 % without non-temporal loads.
+// and stores while the state is bf16 or has one fp32 moment; in the wide mixes
+// (both moments fp32, or an fp32 compensation buffer; the split master)
+// non-temporal stores only, measured on MI355X (OPT-1.3B list, blocked state)
+// 5-6 % faster with fp32 moments and compensation, 3.5 % with fp32 moments
+// alone, and 57 % -> 77 % of peak with bf16 moments and an fp32 compensation
+// buffer, while the bf16 Kahan step loses 8 % without non-temporal loads and
+// the one-fp32-moment mixes tie.
 #ifndef ADAMW_NT_PURE
 #define ADAMW_NT_PURE 3
 #endif
@@ -538,11 +541,13 @@ __global__ __launch_bounds__(kBlockMixed) void update_kernel(const DevSeg* __res
 constexpr int kAuxNone = 0;    // no aux stream: p' = round(p * decay - step_size * u)
 constexpr int kAuxKahan = 1;   // bf16 Kahan compensation c
 constexpr int kAuxSplit = 2;   // int16 remainder r of the split fp32 master w = join(p, r)
+constexpr int kAuxKahan32 = 3; // fp32 Kahan compensation c (the residual kept unrounded)
 
 // Steps whose param is read as well as written, over bf16 params: the pure-bf16
 // family with chosen state precisions (M32 / V32 = fp32 exp_avg / exp_avg_sq,
-// else bf16; aux none or Kahan; <false, false, kAuxKahan> is the pure-bf16 Kahan
-// mode), and the split-master mixed step (<true, true, kAuxSplit>).
+// else bf16; aux none, bf16 or fp32 compensation; <false, false, kAuxKahan> is
+// the pure-bf16 Kahan mode), and the split-master mixed step (<true, true,
+// kAuxSplit>).
 template <bool M32, bool V32, int AUX, bool FUSED>
 __global__ __launch_bounds__(kBlockPure) void update_pure_kernel(const DevSeg* __restrict__ segs,
                                                                             const DevChunk* __restrict__ chunks,
@@ -553,10 +558,12 @@ __global__ __launch_bounds__(kBlockPure) void update_pure_kernel(const DevSeg* _
     int64_t t = 0;
     float scale = 0.0f;
     if (!begin_step<FUSED>(sc, fs, c, t, scale)) return;
-    constexpr bool KAHAN = AUX == kAuxKahan, SPLIT = AUX == kAuxSplit;
+    constexpr bool KAHAN = AUX == kAuxKahan, SPLIT = AUX == kAuxSplit, KAHAN32 = AUX == kAuxKahan32;
     static_assert(!SPLIT || (M32 && V32), "the split master keeps fp32 moments");
-    // fp32 moments and an aux stream: the widest pure-family mix
-    constexpr bool WIDE = M32 && V32 && AUX != kAuxNone;
+    // The wide pure-family mixes (both moments in fp32, or an fp32
+    // compensation buffer: 8-14 B of state per element, half or more of it in
+    // fp32 streams): non-temporal stores only and the mixed family's occupancy.
+    constexpr bool WIDE = (M32 && V32) || KAHAN32;
     constexpr int NT = SPLIT ? ADAMW_NT_SPLIT : WIDE ? ADAMW_NT_PURE_WIDE : ADAMW_NT_PURE;
     // tiles of 256 elements (split master) or 512 (the rest)
     constexpr int P = SPLIT ? kTilePacksSplit : WIDE ? kTilePacksPureWide : kTilePacks;
@@ -573,32 +580,36 @@ __global__ __launch_bounds__(kBlockPure) void update_pure_kernel(const DevSeg* _
     const GLOBAL uint16_t* __restrict__ g = gptr<const uint16_t>(sg.ptr[ADAMW_STREAM_GRAD], off);
     GLOBAL MT* __restrict__ m = gptr<MT>(sg.ptr[ADAMW_STREAM_EXP_AVG], off);
     GLOBAL VT* __restrict__ v = gptr<VT>(sg.ptr[ADAMW_STREAM_EXP_AVG_SQ], off);
-    GLOBAL uint16_t* __restrict__ cc = gptr<uint16_t>(sg.ptr[ADAMW_STREAM_AUX], off);
+    using CT = typename std::conditional<KAHAN32, float, uint16_t>::type;
+    GLOBAL CT* __restrict__ cc = gptr<CT>(sg.ptr[ADAMW_STREAM_AUX], off);
 
     if (ch.n_kind & kVecBit) {
         const uint32_t npack = n / kPack;
         const GLOBAL u32x4* __restrict__ g4 = reinterpret_cast<const GLOBAL u32x4*>(g);
         GLOBAL u32x4* __restrict__ p4 = reinterpret_cast<GLOBAL u32x4*>(p);
         GLOBAL u32x4* __restrict__ c4 = reinterpret_cast<GLOBAL u32x4*>(cc);
-        // a pack of 8 moments is one dwordx4 in bf16, two in fp32
-        constexpr int MW = M32 ? 2 : 1, VW = V32 ? 2 : 1;
+        // a pack of 8 moments (or compensations) is one dwordx4 in bf16, two in fp32
+        constexpr int MW = M32 ? 2 : 1, VW = V32 ? 2 : 1, CW = KAHAN32 ? 2 : 1;
         GLOBAL u32x4* __restrict__ m4 = reinterpret_cast<GLOBAL u32x4*>(m);
         GLOBAL u32x4* __restrict__ v4 = reinterpret_cast<GLOBAL u32x4*>(v);
         for (uint32_t k = first_pack<P, kBlockPure>(tid, part); k < npack; k += kStride) {
             const u32x4 G = ld<NT>(g4 + k), Pv = ld<NT>(p4 + k);
-            u32x4 C, M[MW], V[VW];
+            u32x4 C[CW], M[MW], V[VW];
 #pragma unroll
             for (int q = 0; q < MW; ++q) M[q] = ld<NT>(m4 + MW * k + q);
 #pragma unroll
             for (int q = 0; q < VW; ++q) V[q] = ld<NT>(v4 + VW * k + q);
-            if constexpr (AUX != kAuxNone) C = ld<NT>(c4 + k);
+            if constexpr (AUX != kAuxNone) {
+#pragma unroll
+                for (int q = 0; q < CW; ++q) C[q] = ld<NT>(c4 + CW * k + q);
+            }
             fused_coef<FUSED>(fs, t, scale, c);   // while the loads are in flight
             const uint32_t* gw = reinterpret_cast<const uint32_t*>(&G);
             const uint32_t* pw = reinterpret_cast<const uint32_t*>(&Pv);
-            const uint32_t* cw = reinterpret_cast<const uint32_t*>(&C);
+            uint32_t* cw = reinterpret_cast<uint32_t*>(C);   // 4 (bf16) or 8 (fp32) words
             uint32_t* mw = reinterpret_cast<uint32_t*>(M);   // 4 (bf16) or 8 (fp32) words
             uint32_t* vw = reinterpret_cast<uint32_t*>(V);
-            uint32_t po[4], co[4];
+            uint32_t po[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const f32x2 gg = widen2<false>(gw[j]);
@@ -629,7 +640,7 @@ __global__ __launch_bounds__(kBlockPure) void update_pure_kernel(const DevSeg* _
                     const uint32_t pa = split_bits(__float_as_uint(wa), ra);
                     const uint32_t pb = split_bits(__float_as_uint(wb), rb);
                     po[j] = pa | (pb << 16);
-                    co[j] = ra | (rb << 16);
+                    cw[j] = ra | (rb << 16);
                 } else if constexpr (KAHAN) {
                     const f32x2 cf = widen2<false>(cw[j]);
                     float sa, sb;
@@ -637,7 +648,15 @@ __global__ __launch_bounds__(kBlockPure) void update_pure_kernel(const DevSeg* _
                     const float tb = kahan_sum(gg.y, pp.y, cf.y, mb, vb, c, sb);
                     po[j] = narrow2<false>(ta, tb);
                     const f32x2 pn = widen2<false>(po[j]);
-                    co[j] = narrow2<false>(sa - (pn.x - pp.x), sb - (pn.y - pp.y));
+                    cw[j] = narrow2<false>(sa - (pn.x - pp.x), sb - (pn.y - pp.y));
+                } else if constexpr (KAHAN32) {
+                    float sa, sb;
+                    const float ta = kahan_sum(gg.x, pp.x, __uint_as_float(cw[2 * j]), ma, va, c, sa);
+                    const float tb = kahan_sum(gg.y, pp.y, __uint_as_float(cw[2 * j + 1]), mb, vb, c, sb);
+                    po[j] = narrow2<false>(ta, tb);
+                    const f32x2 pn = widen2<false>(po[j]);
+                    cw[2 * j] = __float_as_uint(sa - (pn.x - pp.x));
+                    cw[2 * j + 1] = __float_as_uint(sb - (pn.y - pp.y));
                 } else {
                     float wa = pp.x, wb = pp.y;
                     mixed_elem(gg.x, wa, ma, va, c);
@@ -662,7 +681,10 @@ __global__ __launch_bounds__(kBlockPure) void update_pure_kernel(const DevSeg* _
             for (int q = 0; q < MW; ++q) st<NT>(m4 + MW * k + q, M[q]);
 #pragma unroll
             for (int q = 0; q < VW; ++q) st<NT>(v4 + VW * k + q, V[q]);
-            if constexpr (AUX != kAuxNone) st<NT>(c4 + k, u32x4{co[0], co[1], co[2], co[3]});
+            if constexpr (AUX != kAuxNone) {
+#pragma unroll
+                for (int q = 0; q < CW; ++q) st<NT>(c4 + CW * k + q, C[q]);
+            }
         }
     } else {
         fused_coef<FUSED>(fs, t, scale, c);
@@ -684,6 +706,12 @@ __global__ __launch_bounds__(kBlockPure) void update_pure_kernel(const DevSeg* _
                 const float tot = kahan_sum(gi, pf, widen1<false>(cc[i]), mi, vi, c, s);
                 const uint16_t pn = narrow1<false>(tot);
                 cc[i] = narrow1<false>(s - (widen1<false>(pn) - pf));
+                p[i] = pn;
+            } else if constexpr (KAHAN32) {
+                float s;
+                const float tot = kahan_sum(gi, pf, cc[i], mi, vi, c, s);
+                const uint16_t pn = narrow1<false>(tot);
+                cc[i] = s - (widen1<false>(pn) - pf);
                 p[i] = pn;
             } else {
                 float w = pf;
@@ -778,10 +806,10 @@ hipError_t launch_prologue(const adamw_hparams& hp, int32_t* d_step, const int32
 // workgroups on a CU.  Measured on MI355X with the OPT-1.3B list, 8 waves per CU
 // (mixed: two 256-lane workgroups) and 16 (pure: four 256-lane workgroups)
 // stream faster than the register-limited 20-32 waves: fewer concurrent address
-// streams per CU keep more DRAM rows open.  The widest pure-bf16 step (fp32
-// exp_avg and exp_avg_sq plus compensation, 26 B per element) runs at the mixed
-// family's 8 waves: 4 % faster than at 16 on blocked state, while the other
-// pure steps lost 2-5 % at 8.
+// streams per CU keep more DRAM rows open.  The wide pure-bf16 mixes (both
+// moments fp32, or an fp32 compensation buffer) run at the mixed family's 8
+// waves: 4 % faster than at 16 with fp32 moments and compensation on blocked
+// state, while the bf16-state steps lost 2-5 % at 8.
 #ifndef ADAMW_LDS_MIXED
 #define ADAMW_LDS_MIXED 81920
 #endif
@@ -817,12 +845,19 @@ static hipError_t launch_update_as(int kernel, const DevSeg* segs, const DevChun
 #define ADAMW_PURE_CASE(M, V, K)                                                                          \
     case kKernelPure + (M) * 4 + (V) * 2 + (K):                                                            \
         hipLaunchKernelGGL((update_pure_kernel<M, V, (K) ? kAuxKahan : kAuxNone, FUSED>), grid, block_pure,    \
-                           (M) && (V) && (K) ? ADAMW_LDS_PURE_WIDE : ADAMW_LDS_PURE, stream, segs,              \
+                           (M) && (V) ? ADAMW_LDS_PURE_WIDE : ADAMW_LDS_PURE, stream, segs,                     \
                            chunks, d_scalars, fs);                                                         \
         break;
         ADAMW_PURE_CASE(0, 0, 0) ADAMW_PURE_CASE(0, 0, 1) ADAMW_PURE_CASE(0, 1, 0) ADAMW_PURE_CASE(0, 1, 1)
         ADAMW_PURE_CASE(1, 0, 0) ADAMW_PURE_CASE(1, 0, 1) ADAMW_PURE_CASE(1, 1, 0) ADAMW_PURE_CASE(1, 1, 1)
 #undef ADAMW_PURE_CASE
+#define ADAMW_PURE_C32_CASE(M, V)                                                                         \
+    case kKernelPureC32 + (M) * 2 + (V):                                                                   \
+        hipLaunchKernelGGL((update_pure_kernel<M, V, kAuxKahan32, FUSED>), grid, block_pure,                 \
+                           ADAMW_LDS_PURE_WIDE, stream, segs, chunks, d_scalars, fs);                     \
+        break;
+        ADAMW_PURE_C32_CASE(0, 0) ADAMW_PURE_C32_CASE(0, 1) ADAMW_PURE_C32_CASE(1, 0) ADAMW_PURE_C32_CASE(1, 1)
+#undef ADAMW_PURE_C32_CASE
     default:
         return hipErrorInvalidValue;
     }

@@ -119,12 +119,15 @@ constexpr uint32_t xcd_chunk(uint32_t b, uint32_t nb)
 }
 
 // Update kernels, by launch id.  The pure-bf16 family adds
-// 4 * (fp32 exp_avg) + 2 * (fp32 exp_avg_sq) + (Kahan compensation).
+// 4 * (fp32 exp_avg) + 2 * (fp32 exp_avg_sq) + (bf16 Kahan compensation) to
+// kKernelPure; with an fp32 compensation buffer, 2 * (fp32 exp_avg) + (fp32
+// exp_avg_sq) to kKernelPureC32.
 constexpr int kKernelMixedBf16 = 0;
 constexpr int kKernelMixedF16 = 1;
 constexpr int kKernelSplit = 3;
 constexpr int kKernelPure = 4;
 constexpr int kKernelKahan = kKernelPure + 1;   // bf16 moments + compensation
+constexpr int kKernelPureC32 = kKernelPure + 8;
 
 // One segment: the device address of its element 0 in each stream (0 for a
 // stream the launch does not touch).

@@ -57,6 +57,10 @@ adamw_status check_pure_precision(const adamw_pure_precision* prec, std::string&
         err = "exp_avg / exp_avg_sq dtype must be ADAMW_F32 or ADAMW_BF16";
         return ADAMW_E_UNSUPPORTED;
     }
+    if (prec->kahan != ADAMW_KAHAN_NONE && prec->kahan != ADAMW_KAHAN_BF16 && prec->kahan != ADAMW_KAHAN_F32) {
+        err = "kahan must be ADAMW_KAHAN_NONE, ADAMW_KAHAN_BF16 or ADAMW_KAHAN_F32";
+        return ADAMW_E_INVALID;
+    }
     return ADAMW_OK;
 }
 

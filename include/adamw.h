@@ -265,19 +265,26 @@ adamw_status adamw_multi_tensor_step_noalloc(adamw_mode mode, adamw_dtype p_dtyp
 
 /* State precisions of a pure-bf16 step (the AnyPrecisionAdamW knobs of
  * "[pure bf16 training] w/ AnyPrecisionAdamW and Kahan summation":
- * momentum_dtype, variance_dtype, use_kahan_summation with a bf16
- * compensation buffer). */
+ * momentum_dtype, variance_dtype, use_kahan_summation and
+ * compensation_buffer_dtype). */
+#define ADAMW_KAHAN_NONE 0   /* no compensation: stream 4 (aux) is unused */
+#define ADAMW_KAHAN_BF16 1   /* stream 4 (aux) is a bf16 compensation buffer */
+#define ADAMW_KAHAN_F32 2    /* stream 4 (aux) is an fp32 compensation buffer */
 typedef struct {
     adamw_dtype exp_avg;     /* ADAMW_F32 or ADAMW_BF16 */
     adamw_dtype exp_avg_sq;  /* ADAMW_F32 or ADAMW_BF16 */
-    int32_t kahan;           /* nonzero: stream 4 (aux) is a bf16 compensation buffer; 0: aux is unused */
+    int32_t kahan;           /* ADAMW_KAHAN_NONE, ADAMW_KAHAN_BF16 or ADAMW_KAHAN_F32; other values are rejected */
 } adamw_pure_precision;
 
 /* Pure-bf16 step with chosen state precisions: param and grad bf16, exp_avg and
  * exp_avg_sq in the dtypes of *prec (fp32 moments are kept and used exactly;
  * bf16 ones are widened, updated in fp32 and stored rounded to nearest even).
- * With kahan: the ADAMW_PURE_KAHAN rule; without: p = round_bf16(p*(1 - lr*wd)
- * - (lr/(1-beta1^t))*u).  {ADAMW_BF16, ADAMW_BF16, 1} is ADAMW_PURE_KAHAN.
+ * With a compensation buffer: the ADAMW_PURE_KAHAN rule, the residual
+ * s - (p' - p) stored rounded to bf16 (ADAMW_KAHAN_BF16) or kept as the fp32
+ * value it is computed in (ADAMW_KAHAN_F32: 2 more bytes per element each way,
+ * and p + c then carries an fp32 master); without: p = round_bf16(p*(1 - lr*wd)
+ * - (lr/(1-beta1^t))*u).  {ADAMW_BF16, ADAMW_BF16, ADAMW_KAHAN_BF16} is
+ * ADAMW_PURE_KAHAN.
  * Everything else (list, shard, counter, skip flag, errors) as
  * adamw_multi_tensor_step. */
 adamw_status adamw_pure_multi_tensor_step(const adamw_pure_precision* prec, const adamw_tensor_list* list,

@@ -28,8 +28,8 @@ F32_KEYS = {"mixed": ("m", "v", "master"), "kahan": (), "split": ("m", "v")}
 
 def f32_keys(mode):
     if mode.startswith("pure"):
-        m32, v32, _ = workloads.parse_pure(mode)
-        return tuple(k for k, f in (("m", m32), ("v", v32)) if f)
+        m32, v32, kahan = workloads.parse_pure(mode)
+        return tuple(k for k, f in (("m", m32), ("v", v32), ("c", kahan == 2)) if f)
     return F32_KEYS[mode]
 
 

@@ -56,6 +56,9 @@ def test_binding_constants_match_the_header():
                         ("ADAMW_STREAM_EXP_AVG", A.STREAM_EXP_AVG), ("ADAMW_STREAM_EXP_AVG_SQ", A.STREAM_EXP_AVG_SQ),
                         ("ADAMW_STREAM_AUX", A.STREAM_AUX), ("ADAMW_NUM_STREAMS", A.NUM_STREAMS)):
         assert int(re.search(rf"\b{name} = (\d+)", src).group(1)) == value, name
+    for name, value in (("ADAMW_KAHAN_NONE", A.KAHAN_NONE), ("ADAMW_KAHAN_BF16", A.KAHAN_BF16),
+                        ("ADAMW_KAHAN_F32", A.KAHAN_F32)):
+        assert define(name) == value, name
 
 
 LAYOUT_PROGRAM = r"""
@@ -153,6 +156,8 @@ def _tl(numels, base=FAKE, esz=(2, 2, 4, 4, 4), **kw):
                                            A.LossScaler(2.0, 0.5, 0), stream=0), "growth_interval"),
     (lambda: A.adamw_multi_tensor_step(A.MIXED_SPLIT, A.F16, _tl([10], esz=(2, 2, 4, 4, 2)), A.HParams(), FAKE,
                                        stream=0), "MIXED_SPLIT"),
+    (lambda: A.adamw_pure_multi_tensor_step(A.PurePrecision(A.BF16, A.BF16, 3), _tl([10], esz=(2, 2, 2, 2, 2)),
+                                            A.HParams(), FAKE, stream=0), "ADAMW_KAHAN_F32"),
     (lambda: A.adamw_check_finite(A.F32, _tl([10]), FAKE, stream=0), "g_dtype"),
     (lambda: A.adamw_check_finite(A.F16, _tl([10]), 0, stream=0), "d_found_inf"),
     (lambda: A.adamw_check_finite(A.F16, _tl([10, 3], shard_begin=0, shard_end=14), FAKE, stream=0), "shard"),

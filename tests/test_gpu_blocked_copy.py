@@ -39,7 +39,7 @@ def _state_list(case, shard=(0, -1), pad8=True):
     return A.TensorList(case.numels, streams, shard[0], shard[1], A.FLAT_PAD8 if pad8 else 0)
 
 
-@pytest.mark.parametrize("mode", ["mixed", "kahan", "split", "pure-f32-bf16-k", "pure-bf16-f32-n"])
+@pytest.mark.parametrize("mode", ["mixed", "kahan", "split", "pure-f32-bf16-k", "pure-bf16-f32-n", "pure-bf16-bf16-k32"])
 def test_pack_matches_the_tests_own_layout(mode):
     case = Case(mode, NUMELS, seed=8100, align_elems=8, random_moments=True)
     code, prec = _code_prec(mode)
@@ -119,7 +119,7 @@ def test_round_trip_and_padding(mode, pad8, shard):
     free()
 
 
-@pytest.mark.parametrize("mode", ["mixed", "kahan", "split", "pure-f32-f32-k"])
+@pytest.mark.parametrize("mode", ["mixed", "kahan", "split", "pure-f32-f32-k", "pure-f32-bf16-k32"])
 def test_steps_on_packed_state_equal_per_tensor_steps(mode):
     """make_blocked_state from the per-tensor state, then 3 steps each way."""
     a = Case(mode, NUMELS, seed=8300, align_elems=8, random_moments=True)

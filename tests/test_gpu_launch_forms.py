@@ -32,7 +32,8 @@ def _plan_chunks(case: Case) -> int:
 
 
 @pytest.mark.parametrize("mode,p_dtype", [("mixed", "bf16"), ("mixed", "f16"), ("kahan", "bf16"), ("split", "bf16"),
-                                          ("pure-f32-f32-k", "bf16"), ("pure-bf16-f32-n", "bf16")])
+                                          ("pure-f32-f32-k", "bf16"), ("pure-bf16-f32-n", "bf16"),
+                                          ("pure-bf16-bf16-k32", "bf16")])
 def test_forms_are_bit_identical_and_match_the_oracle(mode, p_dtype, single_launch_limit):
     """The same list stepped 4 times in each form (one copy each), a skipped step
     in the middle: every buffer and the counter bitwise equal between the forms,

@@ -590,14 +590,15 @@ def test_blocked_state_fp16_amp_sequence():
     free()
 
 
-PURE_MODES = [f"pure-{m}-{v}-{k}" for m in ("f32", "bf16") for v in ("f32", "bf16") for k in ("k", "n")]
+PURE_MODES = [f"pure-{m}-{v}-{k}" for m in ("f32", "bf16") for v in ("f32", "bf16") for k in ("k", "k32", "n")]
 
 
 @pytest.mark.parametrize("mode", PURE_MODES)
 @pytest.mark.parametrize("align", [128, 3])
 def test_pure_precision_matrix(mode, align):
-    """Every AnyPrecision combination (fp32/bf16 exp_avg and exp_avg_sq, Kahan on
-    or off) against the oracle on the edge sizes, from a random state, 4 steps."""
+    """Every AnyPrecision combination (fp32/bf16 exp_avg and exp_avg_sq; no
+    compensation, a bf16 or an fp32 compensation buffer) against the oracle on
+    the edge sizes, from a random state, 4 steps."""
     case = Case(mode, EDGE_SIZES, seed=1800 + align, align_elems=align, random_moments=True)
     _run(case, 4, label=f"{mode}-a{align}")
     free()

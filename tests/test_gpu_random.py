@@ -18,7 +18,7 @@ from gpu_util import Case, build_blocked, compare_streams, hp_pair, pure_precisi
 
 pytestmark = pytest.mark.gpu
 
-PURE = [f"pure-{m}-{v}-{k}" for m in ("f32", "bf16") for v in ("f32", "bf16") for k in ("k", "n")]
+PURE = [f"pure-{m}-{v}-{k}" for m in ("f32", "bf16") for v in ("f32", "bf16") for k in ("k", "k32", "n")]
 MODES = ["mixed", "mixed-f16", "kahan", "split"] + PURE
 
 

@@ -44,7 +44,8 @@ DT = {"bf16": A.BF16, "f16": A.F16}
 
 
 def pure_esz(m32, v32, kahan):
-    return (2, 2, 4 if m32 else 2, 4 if v32 else 2, 2 if kahan else 0)
+    """Element sizes of a pure step's streams; kahan 0 (none), 1 (bf16) or 2 (fp32 compensation)."""
+    return (2, 2, 4 if m32 else 2, 4 if v32 else 2, (0, 2, 4)[int(kahan)])
 
 
 class Spec:
@@ -222,7 +223,8 @@ def _random_spec(rng):
     kind, dt = kinds[int(rng.integers(len(kinds)))]
     prec = None
     if kind == "pure":
-        m32, v32, kahan = (bool(rng.integers(2)) for _ in range(3))
+        m32, v32 = (bool(rng.integers(2)) for _ in range(2))
+        kahan = int(rng.integers(3))
         prec = A.PurePrecision(A.F32 if m32 else A.BF16, A.F32 if v32 else A.BF16, kahan)
         esz = pure_esz(m32, v32, kahan)
     else:
@@ -302,7 +304,7 @@ def test_checker_is_not_vacuous():
 
 @pytest.mark.parametrize("mode,prec,state_bytes", [
     ("mixed", None, 12), ("kahan", None, 6), ("split", None, 10),
-    ("pure", (True, False, True), 8), ("pure", (False, True, False), 6)])
+    ("pure", (True, False, True), 8), ("pure", (False, True, False), 6), ("pure", (False, False, 2), 8)])
 @pytest.mark.parametrize("pad8,shard", [(True, (0, -1)), (False, (0, -1)), (False, (1000, 300000)),
                                         (True, (16384, 16384 * 3 + 8))])
 def test_blocked_state_bytes(mode, prec, state_bytes, pad8, shard):

@@ -243,8 +243,9 @@ def make_state(mode, numels, device, seed, *, p_dtype="bf16", align_elems=128, l
                 x = x.square()
             a.bufs[k] = x if f32 else x.to(torch.bfloat16)
         if kahan:
-            a.bufs["c"] = (normal(total, 1e-6, device, "c", seed, dtype=torch.bfloat16) if random_moments else
-                           torch.zeros(total, dtype=torch.bfloat16, device=device))
+            cdt = torch.float32 if kahan == 2 else torch.bfloat16
+            a.bufs["c"] = (normal(total, 1e-6, device, "c", seed, dtype=cdt) if random_moments else
+                           torch.zeros(total, dtype=cdt, device=device))
     elif mode == "kahan":
         a.bufs["p"] = master.to(torch.bfloat16)
         del master
@@ -275,10 +276,12 @@ STREAMS = {"mixed": ("p", "g", "m", "v", "master"), "kahan": ("p", "g", "m", "v"
 
 
 def parse_pure(mode: str):
-    """'pure-<m>-<v>-<k|n>' with m, v in {f32, bf16}: (fp32 exp_avg, fp32 exp_avg_sq, Kahan)."""
+    """'pure-<m>-<v>-<k|k32|n>' with m, v in {f32, bf16}: (fp32 exp_avg, fp32
+    exp_avg_sq, compensation), the compensation 0 (n: none), 1 (k: a bf16
+    buffer) or 2 (k32: an fp32 buffer)."""
     _, m, v, k = mode.split("-")
-    assert m in ("f32", "bf16") and v in ("f32", "bf16") and k in ("k", "n"), mode
-    return m == "f32", v == "f32", k == "k"
+    assert m in ("f32", "bf16") and v in ("f32", "bf16") and k in ("k", "k32", "n"), mode
+    return m == "f32", v == "f32", {"n": 0, "k": 1, "k32": 2}[k]
 
 
 def streams_of(mode: str):
@@ -291,7 +294,7 @@ def streams_of(mode: str):
 def pure_traffic(mode: str) -> int:
     """Bytes moved per parameter by a pure-bf16 step of this precision."""
     m32, v32, kahan = parse_pure(mode)
-    state = (4 if m32 else 2) + (4 if v32 else 2) + (2 if kahan else 0)
+    state = (4 if m32 else 2) + (4 if v32 else 2) + (0, 2, 4)[kahan]
     return (2 + 2 + state) + (2 + state)
 
 # Resident bytes per parameter of each stream layout (what one rank holds).
