@@ -19,7 +19,8 @@ buffer, or the blocked state buffer of the padded flat index) and require:
 
 Layouts: the exact ones bench.py builds (the 10,000-tensor fp16 list on
 blocked state in the padded index, and per tensor; OPT-1.3B on both), the BERT
-list's four ZeRO shards, and 200 random lists.  Base addresses are synthetic
+list's four ZeRO shards, 200 seeded random lists, and 150 more that hypothesis
+draws (and shrinks on a failure).  Base addresses are synthetic
 (never dereferenced); torch allocations start on 2 MiB boundaries for buffers
 this large, which the synthetic bases follow.
 """
@@ -337,3 +338,58 @@ def test_blocked_state_bytes_refuses_bad_lists():
     misaligned[4] = [p + 2 for p in ptrs[4]]
     with pytest.raises(A.AdamWError, match="aligned"):
         A.adamw_blocked_state_bytes(A.MIXED, A.BF16, A.TensorList(numels, misaligned))
+
+
+# The same check driven by hypothesis: it draws the list, the layout and the
+# shard itself, and shrinks a failing case to a small one.
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+_KINDS = [("mixed", "bf16"), ("mixed", "f16"), ("kahan", "bf16"), ("split", "bf16"), ("pure", "bf16"),
+          ("check", "f16")]
+
+
+@st.composite
+def _plans(draw):
+    kind, dt = draw(st.sampled_from(_KINDS))
+    prec = None
+    if kind == "pure":
+        m32, v32 = draw(st.booleans()), draw(st.booleans())
+        kahan = draw(st.integers(0, 2))
+        prec = A.PurePrecision(A.F32 if m32 else A.BF16, A.F32 if v32 else A.BF16, kahan)
+        esz = pure_esz(m32, v32, kahan)
+    else:
+        esz = ESZ[(kind, dt)]
+    numels = np.array(draw(st.lists(st.one_of(st.integers(0, 20), st.integers(0, 3 * B + 17)), max_size=12)),
+                      dtype=np.int64)
+    blocked = kind != "check" and draw(st.booleans())
+    pad8 = draw(st.booleans())
+    mask = (A.BLOCKED_STATE if blocked else 0) | (A.FLAT_PAD8 if pad8 else 0)
+    fa = 8 if pad8 else 1
+    total = int((-(-numels // fa) * fa).sum())
+    shard = (0, -1)
+    if total and draw(st.booleans()):
+        b = draw(st.integers(0, total))
+        shard = (b, draw(st.integers(b, total)))
+    ptrs = []
+    for s in range(5):
+        if not esz[s]:
+            ptrs.append(None)
+            continue
+        base = (1 << 40) + s * (1 << 34) + MiB2 * draw(st.integers(0, 7))
+        if not (blocked and s >= 2) and shard[1] >= 0 and draw(st.booleans()):
+            mask |= 1 << s                                   # one flat shard buffer, any element phase
+            ptrs.append([base + esz[s] * draw(st.integers(0, 7))])
+            continue
+        shift, align = draw(st.integers(0, 7)), draw(st.sampled_from([1, 8, 128]))
+        ptrs.append(arena_ptrs(base + shift * esz[s], numels, align, esz[s]))
+    if blocked:
+        ptrs[2], ptrs[3], ptrs[4] = [(1 << 40) + 5 * (1 << 34) + 256 * draw(st.integers(0, 63))], None, None
+    return Spec(numels, esz, ptrs, shard, mask), kind, dt, prec
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(_plans())
+def test_random_plans_hypothesis(case):
+    spec, kind, dt, prec = case
+    check_plan(spec, CODE.get(kind, A.MIXED), DT[dt], for_check=kind == "check", prec=prec)
