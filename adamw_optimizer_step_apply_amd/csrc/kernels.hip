@@ -13,14 +13,17 @@
 //                        forms the step's scalars in binary64, advances the counter
 //   update_kernel<MODE, FUSED> / update_pure_kernel<M32, V32, AUX, FUSED>
 //                        eight workgroups per chunk, one on each XCD, the chunk
-//                        interleaved between them in 1 KiB tiles: the AdamW
-//                        element update;
+//                        interleaved between them in tiles of 256 or 512
+//                        elements: the AdamW element update;
 //                        FUSED: without a prologue, for small plans (each
 //                        workgroup forms the scalars, the last one advances
 //                        the counter)
 //   zero_flag_kernel /
 //   check_kernel<F16, FUSED>  the fp16-AMP overflow test (any inf/NaN gradient);
 //                        FUSED: one launch that also sets the flag to 0 or 1
+//   state_copy_kernel    layout only: state between per-tensor buffers and the
+//                        blocked buffer
+//   zero_words_kernel    clears the completion counters of a new workspace
 //
 // Element rule (the AdamW of Loshchilov & Hutter, Algorithm 2, with Adam's bias
 // correction from Kingma & Ba, Algorithm 1; named on the pages "Distributed
@@ -29,6 +32,7 @@
 //   m = b1*m + (1-b1)*g ; v = b2*v + (1-b2)*(g*g) ; u = m / (sqrt(v*rbc2) + eps)
 //   mixed: w = w*decay - step_size*u, p = round16(w)
 //   Kahan: d = -(lrwd*p) - step_size*u ; s = c + d ; p' = rbf16(p + s) ; c = rbf16(s - (p' - p))
+//          (with an fp32 compensation buffer c = s - (p' - p), unrounded)
 // Each operation is one binary32 operation in that order; the library is
 // compiled with -ffp-contract=off so no multiply-add is fused, sqrt and
 // division are the correctly rounded ones, and fp32 subnormals are kept.
