@@ -2,7 +2,8 @@
 1,315,753,984 parameters), the shape of the "opt-1.3b / bf16-pure training from
 scratch" run and memory tables of "[pure bf16 training] w/ AnyPrecisionAdamW
 and Kahan summation", in the launch configurations bench.py times: the mixed
-and Kahan modes and the split master.
+and Kahan modes, the split master, and pure bf16 with bf16 moments and an fp32
+compensation buffer.
 
 One seeded initial state is stepped 10 times three ways from the same bytes:
 on the GPU with per-tensor state buffers, on the GPU with the state in the
@@ -21,7 +22,7 @@ import torch
 import adamw_optimizer_step_apply_amd as A
 import workloads
 from gpu_util import (PIECE, build_blocked_padded, compare, f32_keys, free, host_threads, hp_pair, log_stats, merge_stats,
-                      oracle_ranges, to_np)
+                      oracle_ranges, pure_precision, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,13 +31,19 @@ def _print(*a):
     print(*a, flush=True)
 
 
-@pytest.mark.parametrize("mode", ["mixed", "kahan", "split"])
+@pytest.mark.parametrize("mode", ["mixed", "kahan", "split", "pure-bf16-bf16-k32"])
 def test_opt13b_every_element_10_steps(mode):
     wl = workloads.get("opt_1_3b")
     numels = wl.numels
     n = wl.total
-    seed = {"mixed": 4501, "kahan": 4502, "split": 4503}[mode]
-    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
+    seed = {"mixed": 4501, "kahan": 4502, "split": 4503, "pure-bf16-bf16-k32": 4504}[mode]
+
+    def gpu_step(tl, d_step):
+        if mode.startswith("pure"):
+            A.adamw_pure_multi_tensor_step(pure_precision(mode), tl, hg, d_step)
+        else:
+            code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN, "split": A.MIXED_SPLIT}[mode]
+            A.adamw_multi_tensor_step(code, A.BF16, tl, hg, d_step)
     keys = workloads.streams_of(mode)          # p, g, m, v, aux
     t0 = time.time()
     arena = workloads.make_state(mode, numels, "cuda", seed, align_elems=128)
@@ -57,8 +64,8 @@ def test_opt13b_every_element_10_steps(mode):
         if s:
             workloads.refill_grads(arena, seed, s)
             host["g"] = to_np(arena.bufs["g"])
-        A.adamw_multi_tensor_step(code, A.BF16, tl, hg, d_step)
-        A.adamw_multi_tensor_step(code, A.BF16, tl_blk, hg, d_step_blk)
+        gpu_step(tl, d_step)
+        gpu_step(tl_blk, d_step_blk)
         t1 = time.time()
         oracle_ranges(mode, host, [(0, n)], ho, s + 1)
         torch.cuda.synchronize()
