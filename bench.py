@@ -718,7 +718,7 @@ def main():
 
 def _kernel_sha():
     """Hash of the code that decides a launch's HBM traffic (kernels, planner,
-    layout constants, and the header's #define lines), comments and blank lines
+    layout constants, and the header's #define lines but its version), comments and blank lines
     left out, so that a recorded counter summary stays valid across edits of the
     documentation and of declarations alone."""
     import hashlib
@@ -731,8 +731,8 @@ def _kernel_sha():
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
         src = re.sub(r"//[^\n]*", "", src)
         lines = [ln.rstrip() for ln in src.splitlines() if ln.strip()]
-        if f.endswith(".h"):
-            lines = [ln for ln in lines if ln.lstrip().startswith("#define")]
+        if f.endswith(".h"):    # the header's constants, its version number aside
+            lines = [ln for ln in lines if ln.lstrip().startswith("#define") and "ADAMW_ABI_VERSION" not in ln]
         h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 

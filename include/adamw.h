@@ -114,7 +114,7 @@
 extern "C" {
 #endif
 
-#define ADAMW_ABI_VERSION 7
+#define ADAMW_ABI_VERSION 8
 
 typedef enum {
     ADAMW_OK = 0,
