@@ -235,3 +235,50 @@ def test_amp_sequence_forms_agree(single_launch_limit):
         assert same_bits(one.arena.bufs[k], two.arena.bufs[k]), k
     one.compare_all("amp-single-launch")
     free()
+
+
+@pytest.mark.parametrize("mode,amp", [("kahan", False), ("mixed", True)])
+def test_single_launch_forced_on_a_large_grid(mode, amp, single_launch_limit):
+    """The single launch does not depend on the grid's size: forced on the
+    OPT-125m list (7,760 chunks, 62,080 workgroups, about 1,940 per first-level
+    completion counter) it equals the two-launch form bit for bit over 4 steps
+    with a skipped one, and stores the same counter (and, with a dynamic loss
+    scale, the same scale and tracker, including a back-off and a growth)."""
+    import workloads
+    wl = workloads.get("opt_125m")
+    numels = wl.numels
+    p_dtype = "f16" if amp else "bf16"
+    scale = 1024.0 if amp else 1.0
+    arenas = [workloads.make_state(mode, numels, "cuda", 917, p_dtype=p_dtype, loss_scale=scale,
+                                   random_moments=True) for _ in range(2)]
+    keys = workloads.streams_of(mode)
+    lists = [A.TensorList(numels, [[a.view(k, i) for i in range(len(numels))] for k in keys]) for a in arenas]
+    steps = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(2)]
+    scales = [A.loss_scale_state(scale) for _ in range(2)]
+    scaler = A.LossScaler(2.0, 0.5, 2)
+    code = {"mixed": A.MIXED, "kahan": A.PURE_KAHAN}[mode]
+    dt = A.F16 if amp else A.BF16
+    hg, _ = hp_pair()
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    assert 8 * len(A.adamw_plan_inspect(code, dt, lists[0])) > 60_000
+    for s in range(4):
+        if s:
+            for a in arenas:
+                workloads.refill_grads(a, 917, s, p_dtype=p_dtype, loss_scale=scale)
+        flag.fill_(1 if s == 1 else 0)
+        for i, limit in enumerate((1 << 40, 0)):
+            single_launch_limit(limit)
+            if amp:
+                A.adamw_multi_tensor_step_amp(code, dt, lists[i], hg, steps[i], flag, scales[i], scaler)
+            else:
+                A.adamw_multi_tensor_step(code, dt, lists[i], hg, steps[i], flag)
+    torch.cuda.synchronize()
+    assert int(steps[0].item()) == int(steps[1].item()) == 3
+    if amp:
+        assert same_bits(scales[0], scales[1])
+        st = scales[0].view(torch.int32)
+        assert float(scales[0][0]) == scale and int(st[1]) == 0     # backed off to 512, grown back after 2 clean steps
+    for k in keys:
+        assert same_bits(arenas[0].bufs[k], arenas[1].bufs[k]), f"{mode}: stream {k} differs between the forms"
+    del arenas, lists
+    free()
