@@ -604,6 +604,38 @@ def test_pure_precision_matrix(mode, align):
     free()
 
 
+def test_compensation_tracks_tiny_updates_on_the_gpu():
+    """The reason for the compensation buffer, shown on the GPU: 10,000 steps of
+    a constant +1e-4 update (lr 1e-4, constant gradient -1, no decay, eps 0)
+    from 1.0.  The fp64 sum is 2.0; plain bf16 never leaves 1.0 (each update is
+    below half an ulp); a bf16 buffer ends within 5 % of 2.0 and an fp32 buffer
+    within 1e-5, with p at the bf16 nearest 2.0."""
+    n, k = 256, 10_000
+    hp = A.HParams(lr=1e-4, weight_decay=0.0, eps=0.0)
+    one = torch.full((n,), 1.0, dtype=torch.bfloat16, device="cuda")
+    g = torch.full((n,), -1.0, dtype=torch.bfloat16, device="cuda")
+    got = {}
+    for kahan, cdt in ((A.KAHAN_NONE, None), (A.KAHAN_BF16, torch.bfloat16), (A.KAHAN_F32, torch.float32)):
+        p = one.clone()
+        m = torch.zeros(n, dtype=torch.float32, device="cuda")
+        v = torch.zeros(n, dtype=torch.float32, device="cuda")
+        c = None if cdt is None else torch.zeros(n, dtype=cdt, device="cuda")
+        tl = A.TensorList([n], [[p], [g], [m], [v], None if c is None else [c]])
+        prec = A.PurePrecision(A.F32, A.F32, kahan)
+        d_step = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for _ in range(k):
+            A.adamw_pure_multi_tensor_step(prec, tl, hp, d_step)
+        torch.cuda.synchronize()
+        assert int(d_step.item()) == k
+        total = p.double() + (0 if c is None else c.double())
+        got[kahan] = (p.float().cpu(), total.cpu())
+    assert bool((got[A.KAHAN_NONE][0] == 1.0).all())
+    assert float((got[A.KAHAN_BF16][1] - 2.0).abs().max()) <= 0.1
+    assert float((got[A.KAHAN_F32][1] - 2.0).abs().max()) <= 1e-5
+    assert bool((got[A.KAHAN_F32][0] == 2.0).all())
+    free()
+
+
 def test_pure_bf16_kahan_equals_kahan_mode():
     """{bf16, bf16, Kahan} through adamw_pure_multi_tensor_step is ADAMW_PURE_KAHAN."""
     a = Case("kahan", [30000, 17, 4099], seed=1900, random_moments=True)
