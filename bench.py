@@ -697,6 +697,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "device": torch.cuda.get_device_name(dev),
+        "device_arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", None),
+        "hip_runtime": torch.version.hip,
     }
     if not args.no_probe:
         del state
