@@ -282,3 +282,30 @@ def test_single_launch_forced_on_a_large_grid(mode, amp, single_launch_limit):
         assert same_bits(arenas[0].bufs[k], arenas[1].bufs[k]), f"{mode}: stream {k} differs between the forms"
     del arenas, lists
     free()
+
+
+def test_many_single_launches_in_a_row(single_launch_limit):
+    """2,000 single-launch steps back to back, an overflow check between them
+    (both single-launch kernels sharing the stream's completion counters): the
+    counter ends at exactly 2,000 and the state equals 2,000 two-launch steps
+    bit for bit, so no launch ever miscounts its grid."""
+    numels = [70_000, 3, 4099, 1, 16384 * 3 + 5]
+    one, two = (Case("mixed", numels, seed=918, random_moments=True) for _ in range(2))
+    tl1, tl2 = one.tensor_list(), two.tensor_list()
+    hg = A.HParams(lr=1e-6)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    k = 2000
+    single_launch_limit(-1)
+    assert 8 * _plan_chunks(one) <= 4096
+    for _ in range(k):
+        A.adamw_check_finite(A.BF16, tl1, flag)
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl1, hg, one.d_step, flag)
+    single_launch_limit(0)
+    for _ in range(k):
+        A.adamw_check_finite(A.BF16, tl2, flag)
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl2, hg, two.d_step, flag)
+    torch.cuda.synchronize()
+    assert int(one.d_step.item()) == int(two.d_step.item()) == k and int(flag.item()) == 0
+    for key in one.keys:
+        assert same_bits(one.arena.bufs[key], two.arena.bufs[key]), key
+    free()
