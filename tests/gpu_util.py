@@ -387,7 +387,7 @@ RANGE = 1 << 24          # elements per oracle work item
 
 
 def host_threads() -> int:
-    """Host threads for the oracle (the machine's CPU share is 16 threads)."""
+    """Host threads for the oracle: the affinity set, at most 16 (the CPU share one GPU gets)."""
     import os
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
