@@ -193,3 +193,31 @@ def test_ragged_10k_fp16_blocked_padded_state():
     _print(case.compare_blocked(blocked, "ragged10k-blocked"))
     del case, tl, blocked
     free()
+
+
+def test_bert_zero_shard_with_flat_grad_and_state():
+    """The ZeRO layout proper: rank 2 of 4 holds its gradient shard and its
+    optimizer state (fp32 master, exp_avg, exp_avg_sq) as flat buffers of the
+    shard's length, while the params stay the model's per-tensor tensors.  20
+    steps of the BERT list, a fresh reduce-scattered gradient each step; every
+    element compared (the flat buffers written back to their place in the list)."""
+    wl = workloads.get("bert_52m")
+    b, e = wl.shard(2)
+    case = FullCase("mixed", wl.numels, seed=2200, align_elems=1)
+    assert case.arena.offsets[-1] + wl.numels[-1] == wl.total      # the arenas are the flat index itself
+    flat = {k: case.arena.bufs[k][b:e].clone() for k in ("g", "m", "v", "master")}
+    params = [case.arena.view("p", i) for i in range(len(wl.numels))]
+    tl = A.TensorList(wl.numels, [params, [flat["g"]], [flat["m"]], [flat["v"]], [flat["master"]]], b, e,
+                      0b11110)
+    hg, ho = hp_pair()
+    for s in range(wl.steps):
+        if s:
+            case.refill_grads(s)
+            flat["g"].copy_(case.arena.bufs["g"][b:e])
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl, hg, case.d_step)
+        case.oracle_step(ho, shard=(b, e))
+    for k in ("m", "v", "master"):
+        case.arena.bufs[k][b:e].copy_(flat[k])
+    _print(case.compare_all("bert-r2-flat"))
+    del case, tl, flat, params
+    free()
