@@ -273,9 +273,9 @@ void oracle_adamw_kahan(int64_t n, uint16_t* p, const uint16_t* g,
 
 /* Split master: the fp32 master w is held as two 16-bit halves, the bf16 model
  * parameter p and an int16 remainder r, with w's bit pattern equal to
- * (p << 16) + r in 32-bit two's-complement arithmetic (a reading of the "16-bit
- * master param" in the ZeRO saving estimate of "Distributed optimizer support
- * for BERT").  Splitting picks the p that leaves the smallest remainder: the
+ * (p << 16) + r in 32-bit two's-complement arithmetic (a reading of the 16-bit
+ * master copy counted in the ZeRO saving estimate of "Distributed optimizer
+ * support for BERT").  Splitting picks the p that leaves the smallest remainder: the
  * nearest bf16, ties away from zero, which keeps r within [-32768, 32767]; a
  * NaN master keeps a quiet-NaN p. */
 uint32_t oracle_split_join(uint16_t p, uint16_t r)
