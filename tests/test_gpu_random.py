@@ -1,7 +1,7 @@
 """Randomised GPU parity: seeded draws over the whole configuration space of the
 C ABI, each checked element by element against the oracle.
 
-Every case draws a mode (mixed bf16 / fp16, Kahan, split master, the eight
+Every case draws a mode (mixed bf16 / fp16, Kahan, split master, the twelve
 AnyPrecision combinations), a ragged tensor list (empty tensors included), a
 ZeRO shard range, the flat index (back to back, or padded to multiples of 8),
 buffer alignment, the layout of param, grad and state (per tensor, flat shard
