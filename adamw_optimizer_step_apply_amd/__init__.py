@@ -126,6 +126,10 @@ def _declare(_lib):
 
 
 _load(LIB_PATH)
+ABI_VERSION = 8               # ADAMW_ABI_VERSION of the header this binding follows
+if _lib.adamw_abi_version() != ABI_VERSION:
+    raise ImportError(f"{LIB_PATH} has ABI version {_lib.adamw_abi_version()}, this binding expects {ABI_VERSION}: "
+                      "rebuild the library")
 
 
 class AdamWError(RuntimeError):
