@@ -202,3 +202,47 @@ def test_copy_under_graph_capture_is_refused():
     assert bool((blocked == 0).all())
     del g
     free()
+
+
+def test_full_size_checkpoint_round_trip():
+    """Checkpointing blocked state at the OPT-1.3B size: 3 mixed steps on blocked
+    state, then the state unpacked into fresh per-tensor tensors (the usual
+    checkpoint form) and packed again into a new blocked buffer; the two buffers
+    are byte-identical, and 2 more steps from each (each with its own copy of the
+    params) stay bit-identical with each other."""
+    wl = workloads.get("opt_1_3b")
+    numels = wl.numels
+    arena = workloads.make_state("mixed", numels, "cuda", 8700, align_elems=8, random_moments=True)
+    view = lambda k: [arena.view(k, i) for i in range(len(numels))]   # noqa: E731
+    blocked_a, mask = A.make_blocked_state(A.MIXED, A.BF16, numels, view("m"), view("v"), view("master"))
+    for k in ("m", "v", "master"):
+        arena.bufs[k] = arena.bufs[k][:0]        # the per-tensor state is not used again
+    free()
+    params_a = arena.bufs["p"]
+    grads = view("g")
+    hg, _ = hp_pair()
+    d_a = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tl_a = A.TensorList(numels, [view("p"), grads, [blocked_a], None, None], 0, -1, mask)
+    for _ in range(3):
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl_a, hg, d_a)
+    # checkpoint: out to per-tensor tensors, then into a new blocked buffer
+    ck = {k: [torch.empty(n, dtype=torch.float32, device="cuda") for n in numels] for k in ("m", "v", "master")}
+    state_tl = A.TensorList(numels, [None, None, ck["m"], ck["v"], ck["master"]], 0, -1, A.FLAT_PAD8)
+    A.adamw_blocked_state_copy(A.MIXED, A.BF16, state_tl, blocked_a, False)
+    blocked_b, mask_b = A.make_blocked_state(A.MIXED, A.BF16, numels, ck["m"], ck["v"], ck["master"])
+    assert mask_b == mask and same_bits(blocked_a, blocked_b)
+    del ck, state_tl
+    free()
+    params_b = params_a.clone()
+    d_b = d_a.clone()
+    offs = arena.offsets
+    tl_b = A.TensorList(numels, [[params_b[o:o + n] for o, n in zip(offs, numels)], grads, [blocked_b], None, None],
+                        0, -1, mask)
+    for _ in range(2):
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl_a, hg, d_a)
+        A.adamw_multi_tensor_step(A.MIXED, A.BF16, tl_b, hg, d_b)
+    torch.cuda.synchronize()
+    assert int(d_a.item()) == int(d_b.item()) == 5
+    assert same_bits(blocked_a, blocked_b) and same_bits(params_a, params_b)
+    del tl_a, tl_b, blocked_a, blocked_b, params_b, arena
+    free()
