@@ -283,6 +283,32 @@ class PurePrecision:
     def c(self) -> adamw_pure_precision:
         return adamw_pure_precision(int(self.exp_avg), int(self.exp_avg_sq), int(self.kahan))
 
+    @classmethod
+    def from_optim_args(cls, text: str) -> "PurePrecision":
+        """The precisions named by an AnyPrecisionAdamW option string of the
+        form used with ``--optim_args`` ("key=value, ..."): momentum_dtype and
+        variance_dtype (bfloat16 or float32, default bfloat16),
+        use_kahan_summation (true/false, default false) and
+        compensation_buffer_dtype (bfloat16 or float32, default bfloat16).
+        Other keys, or other values, raise ValueError."""
+        dtypes = {"bfloat16": BF16, "torch.bfloat16": BF16, "float32": F32, "torch.float32": F32}
+        opts = {"momentum_dtype": "bfloat16", "variance_dtype": "bfloat16", "use_kahan_summation": "false",
+                "compensation_buffer_dtype": "bfloat16"}
+        for item in filter(None, (x.strip() for x in text.split(","))):
+            key, sep, value = (x.strip() for x in item.partition("="))
+            if not sep or key not in opts:
+                raise ValueError(f"optim_args: unknown or malformed entry {item!r}")
+            opts[key] = value.lower()
+        for key in ("momentum_dtype", "variance_dtype", "compensation_buffer_dtype"):
+            if opts[key] not in dtypes:
+                raise ValueError(f"optim_args: {key}={opts[key]} (bfloat16 or float32)")
+        if opts["use_kahan_summation"] not in ("true", "false", "1", "0"):
+            raise ValueError(f"optim_args: use_kahan_summation={opts['use_kahan_summation']} (true or false)")
+        kahan = KAHAN_NONE
+        if opts["use_kahan_summation"] in ("true", "1"):
+            kahan = KAHAN_F32 if dtypes[opts["compensation_buffer_dtype"]] == F32 else KAHAN_BF16
+        return cls(dtypes[opts["momentum_dtype"]], dtypes[opts["variance_dtype"]], kahan)
+
 
 def adamw_pure_multi_tensor_step(prec: PurePrecision, tensors: TensorList, hp, d_step, d_found_inf=None,
                                  stream=None) -> None:

@@ -605,3 +605,22 @@ def test_xcd_chunk_map_is_a_bijection(tmp_path):
                    check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.startswith("ok"), (r.returncode, r.stdout, r.stderr)
+
+
+def test_precision_from_the_pages_optim_args():
+    """The option string of the pages' pure-bf16 runs names the ADAMW_PURE_KAHAN
+    precisions; other spellings map to the other instances, and bad entries are
+    refused (no GPU: parsing only)."""
+    import json
+    hp = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_recipe_hparams.json")))
+    text = ", ".join(f"{k}={str(v).lower()}" for k, v in hp["optim_args"].items())
+    assert A.PurePrecision.from_optim_args(text) == A.PurePrecision(A.BF16, A.BF16, A.KAHAN_BF16)
+    assert A.PurePrecision.from_optim_args("momentum_dtype=float32, variance_dtype=bfloat16") == \
+        A.PurePrecision(A.F32, A.BF16, A.KAHAN_NONE)
+    assert A.PurePrecision.from_optim_args(
+        "use_kahan_summation=True,compensation_buffer_dtype=torch.float32,variance_dtype=float32") == \
+        A.PurePrecision(A.BF16, A.F32, A.KAHAN_F32)
+    assert A.PurePrecision.from_optim_args("") == A.PurePrecision(A.BF16, A.BF16, A.KAHAN_NONE)
+    for bad in ("momentum_dtype=float16", "use_kahan=true", "use_kahan_summation=maybe", "momentum_dtype"):
+        with pytest.raises(ValueError):
+            A.PurePrecision.from_optim_args(bad)
