@@ -30,8 +30,8 @@
  *                     int16) and split(w) takes p = w's nearest bf16, ties away from zero
  *                     (so r = w - (p << 16) always fits int16), and p = w's high half with
  *                     the quiet bit set for a NaN w.  join(split(w)) == w for every
- *                     non-NaN w, so the master is exact fp32 (a reading of the "16-bit
- *                     master param" in the ZeRO saving estimate of "Distributed
+ *                     non-NaN w, so the master is exact fp32 (a reading of the 16-bit
+ *                     master copy counted in the ZeRO saving estimate of "Distributed
  *                     optimizer support for BERT").
  *
  * Numerics: every element operation is one IEEE binary32 operation rounded to
