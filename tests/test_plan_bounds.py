@@ -370,14 +370,14 @@ def _plans(draw):
     shard = (0, -1)
     if total and draw(st.booleans()):
         b = draw(st.integers(0, total))
-        shard = (b, draw(st.integers(b, total)))
+        shard = (b, -1 if draw(st.booleans()) else draw(st.integers(b, total)))   # -1: to the list's end
     ptrs = []
     for s in range(5):
         if not esz[s]:
             ptrs.append(None)
             continue
         base = (1 << 40) + s * (1 << 34) + MiB2 * draw(st.integers(0, 7))
-        if not (blocked and s >= 2) and shard[1] >= 0 and draw(st.booleans()):
+        if not (blocked and s >= 2) and shard != (0, -1) and draw(st.booleans()):
             mask |= 1 << s                                   # one flat shard buffer, any element phase
             ptrs.append([base + esz[s] * draw(st.integers(0, 7))])
             continue
