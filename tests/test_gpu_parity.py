@@ -819,14 +819,15 @@ def test_mixed_step_tracks_torch_adamw():
     free()
 
 
-@pytest.mark.parametrize("mode", ["mixed", "kahan", "split", "pure-bf16-f32-k32"])
-def test_arbitrary_bit_patterns_in_every_stream(mode):
+@pytest.mark.parametrize("mode,p_dtype", [("mixed", "bf16"), ("mixed", "f16"), ("kahan", "bf16"), ("split", "bf16"),
+                                          ("pure-bf16-f32-k32", "bf16"), ("pure-f32-bf16-n", "bf16")])
+def test_arbitrary_bit_patterns_in_every_stream(mode, p_dtype):
     """IEEE semantics end to end: every stream (params, gradients, moments,
     master, compensation, remainder) filled with uniformly random bit patterns --
     NaNs, infinities, subnormals, negative second moments and signed zeros
     included -- and stepped twice.  Every result, NaN or not, must have the
     oracle's bit pattern (a NaN's payload aside)."""
-    case = Case(mode, [70_000, 5, 4099, 1], seed=1700)
+    case = Case(mode, [70_000, 5, 4099, 1], seed=1700, p_dtype=p_dtype)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1701)
     for k in case.keys:
@@ -839,5 +840,5 @@ def test_arbitrary_bit_patterns_in_every_stream(mode):
     for s in range(2):
         case.gpu_step(hg)
         case.oracle_step(ho)
-    case.compare_all(f"bits-{mode}")
+    case.compare_all(f"bits-{mode}-{p_dtype}")
     free()
