@@ -667,7 +667,7 @@ def main():
         if base.startswith("pure") and base not in names:
             m32, v32, kahan = workloads.parse_pure(base)
             names[base] = (f"pure bf16 params, {'fp32' if m32 else 'bf16'} exp_avg, {'fp32' if v32 else 'bf16'} "
-                           f"exp_avg_sq, {'bf16 Kahan compensation' if kahan else 'no compensation'}")
+                           f"exp_avg_sq, {('no', 'bf16 Kahan', 'fp32 Kahan')[kahan]} compensation")
         if base != mode:
             names[mode] = (names[base] + f", exp_avg/exp_avg_sq/{'master' if base == 'mixed' else 'aux'} "
                            "interleaved per block of 16384 elements of one optimizer-owned buffer")
