@@ -176,8 +176,9 @@ typedef struct {
  * holds the state of the shard's elements [k*B, (k+1)*B), stream after stream:
  *     [exp_avg x B][exp_avg_sq x B][aux x B]
  * each in its stream's dtype (an unused aux stream takes no room; a block is
- * 192 KiB in the mixed and split modes, 96 KiB in ADAMW_PURE_KAHAN); the last
- * block is padded to B.  For optimizer-owned ZeRO state: the step's per-element
+ * 192 KiB in ADAMW_MIXED, 160 KiB in ADAMW_MIXED_SPLIT, 96 KiB in
+ * ADAMW_PURE_KAHAN, B times the three streams' element sizes for the other
+ * pure-bf16 precisions); the last block is padded to B.  For optimizer-owned ZeRO state: the step's per-element
  * state traffic becomes one contiguous region per block instead of three
  * separate streams (fewer concurrently open DRAM rows; measured faster on
  * MI355X).  B is one default update chunk, so splitting work at block edges
