@@ -220,8 +220,9 @@ typedef struct {
  * parameters, and steps only that share).
  * param, grad, exp_avg, exp_avg_sq, aux: device buffers of n elements in the
  * layouts above.  p_dtype: ADAMW_BF16 or ADAMW_F16 in ADAMW_MIXED, ADAMW_BF16
- * in ADAMW_PURE_KAHAN and ADAMW_MIXED_SPLIT.  n == 0 is valid (the counter still advances unless
- * skipped).  See the file comment for d_step / d_found_inf. */
+ * in ADAMW_PURE_KAHAN and ADAMW_MIXED_SPLIT.  n == 0 is valid (the counter
+ * still advances unless skipped).  See the file comment for d_step /
+ * d_found_inf. */
 adamw_status adamw_step(adamw_mode mode, adamw_dtype p_dtype, int64_t n,
                         void* param, const void* grad, void* exp_avg, void* exp_avg_sq, void* aux,
                         const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
@@ -255,10 +256,10 @@ adamw_status adamw_multi_tensor_step(adamw_mode mode, adamw_dtype p_dtype, const
  * used, since every replay reads it: later calls on that GPU with another list
  * are then refused with ADAMW_E_INVALID (calls with the same list still run)
  * until adamw_release_workspace(), which unpins it and must not run while
- * such a graph may still be replayed.  Every call on a GPU shares that GPU's array and
- * its contents: calls on one GPU that may overlap (on different streams, or
- * from host threads without an order between them) race on it and must be
- * ordered by the caller, e.g. by issuing them on one stream. */
+ * such a graph may still be replayed.  Every call on a GPU shares that GPU's
+ * array and its contents: calls on one GPU that may overlap (on different
+ * streams, or from host threads without an order between them) race on it and
+ * must be ordered by the caller, e.g. by issuing them on one stream. */
 #define ADAMW_NOALLOC_SCRATCH_BYTES (16u << 20)
 adamw_status adamw_multi_tensor_step_noalloc(adamw_mode mode, adamw_dtype p_dtype, const adamw_tensor_list* list,
                                              const adamw_hparams* hp, int32_t* d_step, const int32_t* d_found_inf,
@@ -331,8 +332,8 @@ adamw_status adamw_multi_tensor_step_amp(adamw_mode mode, adamw_dtype p_dtype, c
  * "opt-125m / fp16-amp training from scratch" run on the page "[pure bf16
  * training] w/ AnyPrecisionAdamW and Kahan summation": its loss is scaled, and
  * a step whose scaled gradients hold an inf or NaN must be skipped (see the
- * skip flag in the file comment).  Stores 0 to *d_found_inf (stream ordered), then 1
- * if any gradient element of the list (stream 1 only; shard range and
+ * skip flag in the file comment).  Stores 0 to *d_found_inf (stream
+ * ordered), then 1 if any gradient element of the list (stream 1 only; shard range and
  * flat_mask bit 1 honoured) has an all-ones exponent field, i.e. is inf or NaN.
  * g_dtype: ADAMW_F16 or ADAMW_BF16.  Scaled gradients are tested as stored,
  * before any unscaling.  Intended order: adamw_check_finite, then the step
